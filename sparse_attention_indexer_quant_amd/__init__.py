@@ -1,0 +1,230 @@
+"""MI355X-native DSA lightning-indexer hot path: thin Python binding over libdsaidx.so.
+
+Every call marshals torch tensors into the C-ABI declared in ``include/dsaidx.h``
+and enqueues the HIP kernels on the current torch stream; no step of the path
+runs in Python. The library is loaded on first use and a missing build raises
+``RuntimeError`` -- there is no CPU fallback.
+
+Calls (names follow the pages' problem statement: page
+"vllm.models.kimi_k3.amd.ops.fp4_indexer" quantize_queries / store_keys /
+score_paged / decode_layout, plus the per-row top-k):
+
+  quantize_queries(q, wv, fmt)            -> (q_rows uint8, w_out bf16)
+  store_keys(keys, gamma, beta, eps, slots, cache, num_pages, page_stride, fmt)
+  decode_layout(seq_lens, query_lens, num_rows, dcp_rank, dcp_world_size, interleave)
+  score_paged(q_rows, heads, weights, cache, ..., block_table, query_starts, row_ends, max_query_len)
+  topk(logits, row_ends, k)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libdsaidx.so")
+
+MXFP4, FP8 = 0, 1
+_FORMATS = {"mxfp4": MXFP4, "fp8": FP8}
+SECTION_BYTES = {MXFP4: 4352, FP8: 8448}
+PAGE_TOKENS = 64
+
+_lib = None
+
+
+class DsaidxError(RuntimeError):
+    """A non-zero status from the C-ABI (argument, layout or HIP launch error)."""
+
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"dsaidx_{call}: {message} (status {status})")
+        self.status = status
+
+
+def library():
+    """The loaded C-ABI library; raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is not built: run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+        lib = ctypes.CDLL(LIBRARY)
+        P, I64, I32, F32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                ctypes.c_size_t)
+        sig = {
+            "dsaidx_status_string": (ctypes.c_char_p, [I32]),
+            "dsaidx_query_row_bytes": (I64, [I32, I32]),
+            "dsaidx_quantize_queries": (I32, [I32, P, I64, I32, I64, I64, P, I64, P, I64, P, I64, P]),
+            "dsaidx_store_keys": (I32, [I32, P, I64, I64, P, P, F32, P, P, I64, I64, P]),
+            "dsaidx_decode_layout": (I32, [P, P, I64, I64, I32, I32, I32, P, P, P]),
+            "dsaidx_score_paged": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64, P, P,
+                                         I64, I32, P, I64, P]),
+            "dsaidx_topk_workspace_bytes": (SZ, [I64, I64, I32]),
+            "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _fmt(fmt) -> int:
+    return _FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _check(call: str, status: int):
+    if status != 0:
+        msg = library().dsaidx_status_string(status).decode()
+        raise DsaidxError(call, status, msg)
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def query_row_bytes(fmt, heads: int) -> int:
+    """Bytes of one quantized query row: [H x 64 E2M1 | H x 4 UE8M0] or [H x 128 E4M3]."""
+    return int(library().dsaidx_query_row_bytes(_fmt(fmt), int(heads)))
+
+
+def quantize_queries(q, wv=None, fmt="mxfp4", out=None, w_out=None):
+    """q: bf16 [rows, heads, 128] (128-element heads contiguous); wv: bf16 [rows, heads] raw
+    head weights or None. Returns (q_rows uint8 [rows, row_bytes], w_out bf16 [rows, heads])."""
+    import torch
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != 128 or q.stride(2) != 1:
+        raise ValueError("quantize_queries: q must be [rows, heads, 128] with contiguous heads")
+    rows, heads = q.shape[0], q.shape[1]
+    f = _fmt(fmt)
+    rb = query_row_bytes(f, heads) if heads in (16, 32, 64) else heads * 128
+    if out is None:
+        out = torch.empty((rows, rb), dtype=torch.uint8, device=q.device)
+    _dev(out, "out", torch.uint8)
+    if wv is not None:
+        _dev(wv, "wv", torch.bfloat16)
+        if wv.dim() != 2 or wv.stride(1) != 1:
+            raise ValueError("quantize_queries: wv must be [rows, heads] with unit head stride")
+        if w_out is None:
+            w_out = torch.empty((rows, heads), dtype=torch.bfloat16, device=q.device)
+        _dev(w_out, "w_out", torch.bfloat16)
+    st = library().dsaidx_quantize_queries(
+        f, q.data_ptr(), rows, heads, q.stride(0), q.stride(1),
+        None if wv is None else wv.data_ptr(), 0 if wv is None else wv.stride(0),
+        out.data_ptr(), out.stride(0),
+        None if wv is None else w_out.data_ptr(), 0 if wv is None else w_out.stride(0),
+        _stream(q))
+    _check("quantize_queries", st)
+    return out, w_out
+
+
+def store_keys(keys, gamma, beta, eps, slots, cache, num_pages, page_stride, fmt="mxfp4",
+               section_offset=0):
+    """LayerNorm + quantize + insert keys [T, 128] bf16 into the paged cache.
+
+    cache: flat uint8 tensor; section p starts at byte section_offset + p * page_stride.
+    slots: int64 [T]; negative slots are padding."""
+    import torch
+    _dev(keys, "keys", torch.bfloat16)
+    if keys.dim() != 2 or keys.shape[1] != 128 or keys.stride(1) != 1:
+        raise ValueError("store_keys: keys must be [T, 128] with contiguous rows")
+    _dev(slots, "slots", torch.int64)
+    if slots.dim() != 1 or slots.numel() != keys.shape[0] or slots.stride(0) != 1:
+        raise ValueError("store_keys: one contiguous slot per key")
+    _dev(gamma, "gamma", torch.float32)
+    _dev(beta, "beta", torch.float32)
+    _dev(cache, "cache", torch.uint8)
+    st = library().dsaidx_store_keys(
+        _fmt(fmt), keys.data_ptr(), keys.shape[0], keys.stride(0), gamma.data_ptr(),
+        beta.data_ptr(), float(eps), slots.data_ptr(), cache.data_ptr() + int(section_offset),
+        int(num_pages), int(page_stride), _stream(keys))
+    _check("store_keys", st)
+
+
+def decode_layout(seq_lens, query_lens, num_rows, dcp_rank=0, dcp_world_size=1, interleave=1,
+                  starts=None, row_ends=None):
+    """Device-side row grouping: returns (query_starts int32 [R+1], row_ends int32 [num_rows])."""
+    import torch
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(query_lens, "query_lens", torch.int32)
+    if seq_lens.dim() != 1 or query_lens.dim() != 1:
+        raise ValueError("decode_layout: sequence and query lengths must be one-dimensional")
+    if seq_lens.numel() < query_lens.numel():
+        raise ValueError("decode_layout: each decode request requires a global sequence length")
+    R = query_lens.numel()
+    dev = query_lens.device
+    if starts is None:
+        starts = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    if row_ends is None:
+        row_ends = torch.empty(max(int(num_rows), 0), dtype=torch.int32, device=dev)
+    st = library().dsaidx_decode_layout(
+        seq_lens.contiguous().data_ptr(), query_lens.contiguous().data_ptr(), R, int(num_rows),
+        int(dcp_rank), int(dcp_world_size), int(interleave), starts.data_ptr(),
+        row_ends.data_ptr(), _stream(query_lens))
+    _check("decode_layout", st)
+    return starts, row_ends
+
+
+def score_paged(q_rows, heads, weights, cache, num_pages, page_stride, block_table, query_starts,
+                row_ends, max_query_len, fmt="mxfp4", section_offset=0, out=None):
+    """Score every query row against its request's paged keys.
+
+    Returns FP32 logits [num_rows, max_blocks * 64]; entries at or past a row's bound are
+    not written."""
+    import torch
+    _dev(q_rows, "q_rows", torch.uint8)
+    _dev(weights, "weights", torch.bfloat16)
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(query_starts, "query_starts", torch.int32)
+    _dev(row_ends, "row_ends", torch.int32)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("score_paged: block_table must be [requests, max_blocks], row-major")
+    num_rows = row_ends.numel()
+    R, mb = block_table.shape
+    if out is None:
+        out = torch.empty((num_rows, mb * PAGE_TOKENS), dtype=torch.float32, device=q_rows.device)
+    _dev(out, "out", torch.float32)
+    st = library().dsaidx_score_paged(
+        _fmt(fmt), q_rows.data_ptr(), q_rows.stride(0), int(heads), weights.data_ptr(),
+        weights.stride(0), cache.data_ptr() + int(section_offset), int(num_pages),
+        int(page_stride), block_table.data_ptr(), R, block_table.stride(0),
+        query_starts.data_ptr(), row_ends.data_ptr(), num_rows, int(max_query_len),
+        out.data_ptr(), out.stride(0), _stream(q_rows))
+    _check("score_paged", st)
+    return out
+
+
+def topk_workspace_bytes(rows, width, k) -> int:
+    return int(library().dsaidx_topk_workspace_bytes(int(rows), int(width), int(k)))
+
+
+def topk(logits, row_ends, k, width=None, out=None, workspace=None):
+    """Per-row top-k key positions of logits [rows, >= width] over [0, row_ends[r]).
+
+    Returns int32 [rows, k]; the order within a row is unspecified; unused entries are -1."""
+    import torch
+    _dev(logits, "logits", torch.float32)
+    _dev(row_ends, "row_ends", torch.int32)
+    rows = logits.shape[0]
+    width = logits.shape[1] if width is None else int(width)
+    if out is None:
+        out = torch.empty((rows, int(k)), dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32)
+    need = topk_workspace_bytes(rows, width, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    st = library().dsaidx_topk(
+        logits.data_ptr(), rows, width, logits.stride(0), row_ends.data_ptr(), int(k),
+        out.data_ptr(), out.stride(0), None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel(), _stream(logits))
+    _check("topk", st)
+    return out
