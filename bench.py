@@ -1,0 +1,371 @@
+"""Benchmark of the DSA lightning-indexer hot path on one MI355X.
+
+One step = one pass of the whole path over one decode batch, inputs resident in HBM:
+quantize_queries (all rows), store_keys (the step's new keys), decode_layout,
+score_paged, topk. Prints ONE JSON line: scored (row, key) pairs per second of the whole
+step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
+launch stream around every score launch in the timed region), and the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config long_mxfp4] [--configs all|none|a,b]
+
+The key cache is replicated and the replicas rotate across steps, so every step reads its
+keys from HBM rather than from the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer scored (row,key) pairs/s + key-cache HBM GB/s (fraction of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MAIN_CONFIG = "long_mxfp4"
+PROFILE_PMC = os.path.join(ROOT, "profiles", "score_paged_long_mxfp4_pmc.txt")
+SCORE_SOURCE = os.path.join(ROOT, "sparse_attention_indexer_quant_amd", "csrc", "score.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=MAIN_CONFIG)
+    ap.add_argument("--configs", default="all",
+                    help="other workloads reported under per_config: all, none, or a comma list")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU budget of the oracle baseline sample of the main workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-mb", type=float, default=768.0)
+    return ap.parse_args()
+
+
+class Prepared:
+    """A C-ABI call with its argument tuple marshalled once (plain integers and pointers)."""
+
+    def __init__(self, fn, *args):
+        self.fn, self.args = fn, args
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"{self.fn.__name__} returned status {st}")
+
+
+class Setup:
+    """Device buffers of one workload, the cache replicas, and the prepared step calls."""
+
+    def __init__(self, name, min_rotation_mb):
+        import torch
+        import sparse_attention_indexer_quant_amd as dsa
+        from sparse_attention_indexer_quant_amd.workloads import config
+
+        t0 = time.perf_counter()
+        self.wl = wl = config(name)
+        lib = dsa.library()
+        dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(dev)
+        sp = self.stream.cuda_stream
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        def bf16(bits):
+            return up(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+        fmt = dsa.MXFP4 if wl.fmt == "mxfp4" else dsa.FP8
+        self.gamma, self.beta = up(wl.gamma), up(wl.beta)
+        cache0 = torch.full((wl.cache_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+        chunk = 1 << 21
+        for s in range(0, wl.total_keys, chunk):
+            e = min(wl.total_keys, s + chunk)
+            dsa.store_keys(bf16(wl.key_bits[s:e]), self.gamma, self.beta, wl.eps,
+                           up(wl.key_slots[s:e]), cache0, wl.num_pages, wl.page_stride, wl.fmt,
+                           wl.section_offset)
+        reps = int(np.ceil(min_rotation_mb * 1e6 / max(wl.key_bytes(), 1))) + 1
+        reps = max(2, min(reps, 16))
+        self.caches = [cache0] + [cache0.clone() for _ in range(reps - 1)]
+        self.q = bf16(wl.q_bits)
+        self.wv = bf16(wl.wv_bits)
+        sk = wl.step_key_index()
+        self.new_keys = bf16(wl.key_bits[sk])
+        self.new_slots = up(wl.key_slots[sk])
+        self.seq_lens, self.query_lens = up(wl.seq_lens), up(wl.query_lens)
+        self.block_table = up(wl.block_table)
+        rb = dsa.query_row_bytes(fmt, wl.heads)
+        self.q_rows = torch.empty((wl.num_rows, rb), dtype=torch.uint8, device=dev)
+        self.w_out = torch.empty((wl.num_rows, wl.heads), dtype=torch.bfloat16, device=dev)
+        self.starts = torch.empty(wl.num_requests + 1, dtype=torch.int32, device=dev)
+        self.ends = torch.empty(wl.num_rows, dtype=torch.int32, device=dev)
+        self.logits = torch.empty((wl.num_rows, wl.width), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((wl.num_rows, wl.topk), dtype=torch.int32, device=dev)
+        wsb = dsa.topk_workspace_bytes(wl.num_rows, wl.width, wl.topk)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+        self.quant = Prepared(lib.dsaidx_quantize_queries, fmt, self.q.data_ptr(), wl.num_rows,
+                              wl.heads, self.q.stride(0), self.q.stride(1), self.wv.data_ptr(),
+                              self.wv.stride(0), self.q_rows.data_ptr(), self.q_rows.stride(0),
+                              self.w_out.data_ptr(), self.w_out.stride(0), sp)
+        self.layout = Prepared(lib.dsaidx_decode_layout, self.seq_lens.data_ptr(),
+                               self.query_lens.data_ptr(), wl.num_requests, wl.num_rows, 0, 1, 1,
+                               self.starts.data_ptr(), self.ends.data_ptr(), sp)
+        self.topk = Prepared(lib.dsaidx_topk, self.logits.data_ptr(), wl.num_rows, wl.width,
+                             self.logits.stride(0), self.ends.data_ptr(), wl.topk,
+                             self.idx.data_ptr(), self.idx.stride(0), self.ws.data_ptr(), wsb, sp)
+        self.store, self.score = [], []
+        for c in self.caches:
+            base = c.data_ptr() + wl.section_offset
+            self.store.append(Prepared(
+                lib.dsaidx_store_keys, fmt, self.new_keys.data_ptr(), self.new_keys.shape[0],
+                self.new_keys.stride(0), self.gamma.data_ptr(), self.beta.data_ptr(),
+                ctypes.c_float(wl.eps), self.new_slots.data_ptr(), base, wl.num_pages,
+                wl.page_stride, sp))
+            self.score.append(Prepared(
+                lib.dsaidx_score_paged, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
+                wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
+                wl.page_stride, self.block_table.data_ptr(), wl.num_requests, wl.max_blocks,
+                self.starts.data_ptr(), self.ends.data_ptr(), wl.num_rows, wl.max_query_len,
+                self.logits.data_ptr(), self.logits.stride(0), sp))
+        torch.cuda.synchronize()
+        self.setup_s = time.perf_counter() - t0
+        ends = self.host_row_ends()
+        self.pairs = wl.scored_pairs(ends)
+        # algorithmic bytes of one score launch: unique key bytes + logits written + query rows
+        # + head weights
+        per_row_q = rb + 2 * wl.heads
+        self.score_bytes = wl.key_bytes() + 4 * self.pairs + wl.num_rows * per_row_q
+        self.score_flops = 2 * wl.heads * 128 * self.pairs
+
+    def host_row_ends(self):
+        import oracle  # host-side row bounds for byte accounting only (no GPU data involved)
+        _, e = oracle.decode_layout(self.wl.seq_lens, self.wl.query_lens, self.wl.num_rows)
+        return e
+
+    def step(self, i, ev=None):
+        self.quant()
+        self.store[i % len(self.caches)]()
+        self.layout()
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.score[i % len(self.caches)]()
+        if ev is not None:
+            ev[1].record(self.stream)
+        self.topk()
+
+
+def time_steps(s: Setup, steps: int, warmup: int):
+    import torch
+    for i in range(warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s.step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    score_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return wall, score_ms
+
+
+def kernel_times(s: Setup, reps: int = 30):
+    """Per-kernel HIP-event times (ms, median) of each stage launched alone."""
+    import torch
+    out = {}
+    stages = [("quantize_queries", lambda i: s.quant()),
+              ("store_keys", lambda i: s.store[i % len(s.caches)]()),
+              ("decode_layout", lambda i: s.layout()),
+              ("score_paged", lambda i: s.score[i % len(s.caches)]()),
+              ("topk", lambda i: s.topk())]
+    for name, fn in stages:
+        ts = []
+        for i in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s.stream)
+            fn(i)
+            b.record(s.stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name] = float(np.median(ts))
+    return out
+
+
+def cpu_baseline(s: Setup, budget_s: float):
+    """The oracle, untuned, on the host cores: score + top-k of a bounded sample of rows
+    (plus the step's query quantization and key inserts), scaled to pairs/s."""
+    import oracle
+    wl = s.wl
+    ocache = np.full(wl.cache_bytes, 0xA5, np.uint8)
+    oracle.store_keys(wl.key_bits, wl.gamma, wl.beta, wl.eps, wl.key_slots, ocache, wl.num_pages,
+                      wl.page_stride, wl.section_offset, wl.fmt)
+    starts, ends = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+    live = [r for r in range(wl.num_rows) if ends[r] > 0]
+    # probe one row to size the sample to the budget
+    t0 = time.perf_counter()
+    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+    sk = wl.step_key_index()
+    scratch = ocache.copy()
+    oracle.store_keys(wl.key_bits[sk], wl.gamma, wl.beta, wl.eps, wl.key_slots[sk], scratch,
+                      wl.num_pages, wl.page_stride, wl.section_offset, wl.fmt)
+    del scratch
+    fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    lg = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
+                            starts, ends, wl.fmt, wl.section_offset, rows_subset=[live[0]])
+    oracle.topk(np.nan_to_num(lg[[live[0]]], nan=0.0), ends[[live[0]]], wl.topk)
+    per_row = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(len(live), budget_s / per_row)))
+    rows = live[:: max(1, len(live) // n)][:n]
+    t0 = time.perf_counter()
+    lg = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
+                            starts, ends, wl.fmt, wl.section_offset, rows_subset=rows)
+    oracle.topk(np.nan_to_num(lg[rows], nan=0.0), ends[rows], wl.topk)
+    el = time.perf_counter() - t0
+    pairs = int(np.minimum(ends[rows], wl.width).sum())
+    # the whole step on the CPU would take fixed + el * (all pairs / sampled pairs)
+    step_s = fixed + el * (s.pairs / max(pairs, 1))
+    return {"value": s.pairs / step_s, "unit": "pairs/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{wl.name}: score_paged + topk of {len(rows)} of {len(live)} live rows "
+                      f"({pairs} pairs, {el:.2f} s), plus quantize_queries of all {wl.num_rows} "
+                      f"rows and store_keys of the step's {sk.size} keys ({fixed:.2f} s), scaled "
+                      f"to the whole step",
+            "score_topk_pairs_per_s": pairs / el,
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_traffic(score_bytes):
+    """HBM bytes per score launch from the committed rocprofv3 counter summary, if it was
+    taken on the current score kernel source; else None."""
+    try:
+        text = open(PROFILE_PMC).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()[:16]
+    if vals.get("score_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_config(name, args, steps, warmup, cpu_budget):
+    import torch
+    s = Setup(name, args.min_rotation_mb)
+    wall, score_ms = time_steps(s, steps, warmup)
+    ms_step = wall / steps * 1e3
+    score_us = float(score_ms.mean() * 1e3)
+    res = {
+        "workload": name,
+        "fmt": s.wl.fmt, "heads": s.wl.heads, "rows": s.wl.num_rows, "requests": s.wl.num_requests,
+        "topk": s.wl.topk, "page_stride": s.wl.page_stride, "seed": s.wl.seed,
+        "scored_pairs": s.pairs,
+        "ms_per_step": ms_step,
+        "step_pairs_per_s": s.pairs / (ms_step / 1e3),
+        "score_us_mean": score_us,
+        "score_us_p10_p50_p90": [float(np.percentile(score_ms, p) * 1e3) for p in (10, 50, 90)],
+        "score_pairs_per_s": s.pairs / (score_us / 1e6),
+        "score_key_GBps": s.wl.key_bytes() / (score_us / 1e6) / 1e9,
+        "score_algorithmic_GBps": s.score_bytes / (score_us / 1e6) / 1e9,
+        "score_algorithmic_bytes": s.score_bytes,
+        "score_TFLOPs": s.score_flops / (score_us / 1e6) / 1e12,
+        "cache_replicas": len(s.caches),
+        "kernel_us_alone": {k: v * 1e3 for k, v in kernel_times(s).items()},
+    }
+    res["score_key_frac_of_peak"] = res["score_key_GBps"] / HBM_PEAK_GBPS
+    if cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(s, cpu_budget)
+    del s
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from sparse_attention_indexer_quant_amd.workloads import CONFIG_NAMES
+
+    main_res = run_config(args.config, args, args.steps, args.warmup,
+                          0.0 if args.no_cpu_baseline else args.cpu_seconds)
+    print(f"[bench] {args.config}: {main_res['ms_per_step']:.4f} ms/step, score "
+          f"{main_res['score_us_mean']:.2f} us", file=sys.stderr, flush=True)
+    others = []
+    if args.configs == "all":
+        others = [c for c in CONFIG_NAMES if c != args.config]
+    elif args.configs not in ("none", ""):
+        others = [c for c in args.configs.split(",") if c != args.config]
+    per_config = {args.config: main_res}
+    for name in others:
+        per_config[name] = run_config(name, args, max(20, args.steps // 2), min(args.warmup, 10),
+                                      0.0 if args.no_cpu_baseline else 2.0)
+        print(f"[bench] {name}: {per_config[name]['ms_per_step']:.4f} ms/step, score "
+              f"{per_config[name]['score_us_mean']:.2f} us", file=sys.stderr, flush=True)
+
+    m = main_res
+    traffic = measured_traffic(m["score_algorithmic_bytes"])
+    achieved = m["score_algorithmic_GBps"]
+    line = {
+        "metric": METRIC,
+        "value": m["step_pairs_per_s"],
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m["fmt"],
+        "data": "synthetic",
+        "config": {"workload": args.config, "heads": m["heads"], "rows": m["rows"],
+                   "requests": m["requests"], "topk": m["topk"], "page_stride": m["page_stride"],
+                   "scored_pairs": m["scored_pairs"], "parallelism": "none (1 GPU)"},
+        "key_cache_GBps": m["score_key_GBps"],
+        "key_cache_frac_of_peak": m["score_key_frac_of_peak"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "score_paged", "bytes_per_launch": m["score_algorithmic_bytes"],
+                     "launch_us_mean": m["score_us_mean"]},
+        "cpu_baseline": m.get("cpu_baseline"),
+        "per_config": per_config,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * dsaidx.h -- C-ABI of the MI355X (gfx950) DSA lightning-indexer hot path.
+ *
+ * The path: quantize the per-token indexer query and the LayerNorm'd indexer key to
+ * MXFP4 (E2M1 values, one UE8M0 scale per 32) or FP8 E4M3 (one power-of-two scale),
+ * insert the keys into a paged cache, score every query row against its request's
+ * paged keys as sum_h w[h] * ReLU(q_h . k), and select each row's top-k keys.
+ *
+ * Sources (documentation pages):
+ *   [idx]    vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index
+ *            (module text; quantize_fp4_query; DsaIndex.fp8_query; mxfp4_scale;
+ *             e2m1x2; insert_key; insert_fp4_key; fp4_query_views)
+ *   [fp4ops] vllm.models.kimi_k3.amd.ops.fp4_indexer
+ *            (cache_views; decode_layout; quantize_queries; score_paged; store_keys)
+ *   [ovl]    vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.overlap
+ *            (module text: the indexer path is scoring and top-k)
+ *
+ * Conventions for every call:
+ *  - Pointers named as device pointers must point to device memory on the current
+ *    HIP device; the caller owns all of it. No call allocates, frees or reads device
+ *    memory from the host, and none synchronizes: work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the null stream) and the call returns.
+ *  - Arguments are checked on the host before anything is enqueued; a failing check
+ *    returns a non-zero dsaidx_status and enqueues nothing. Conditions that could only
+ *    be checked by reading device memory are caller contract and are listed per call.
+ *  - Strides of typed arrays are in elements; strides of byte buffers are in bytes.
+ *  - BF16 values are passed as raw 16-bit patterns.
+ *  - Calls on one stream are ordered; calls that write the same memory from several
+ *    streams without ordering race.
+ */
+#ifndef DSAIDX_H_
+#define DSAIDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSAIDX_OK = 0,
+    DSAIDX_EINVAL = 1,      /* a count, size, pointer or scalar argument is invalid */
+    DSAIDX_ELAYOUT = 2,     /* a stride, alignment or buffer layout breaks the required layout */
+    DSAIDX_EUNSUPPORTED = 3,/* a valid shape this build does not implement (heads, max_query_len) */
+    DSAIDX_EHIP = 4         /* the HIP runtime reported an error when enqueuing */
+} dsaidx_status;
+
+typedef enum {
+    DSAIDX_MXFP4 = 0,       /* E2M1 payload + UE8M0 scale per 32 values */
+    DSAIDX_FP8 = 1          /* E4M3FN payload + one power-of-two scale per 128 values */
+} dsaidx_format;
+
+#define DSAIDX_DIM 128                 /* values per head and per key */
+#define DSAIDX_PAGE_TOKENS 64          /* tokens per cache page */
+#define DSAIDX_MXFP4_SECTION_BYTES 4352 /* [64 x 64 B E2M1 | 64 x 4 B UE8M0] */
+#define DSAIDX_FP8_SECTION_BYTES 8448   /* [64 x 128 B E4M3 | 64 x 4 B FP32 scale] */
+#define DSAIDX_MAX_QUERY_LEN 16        /* query rows per request that score_paged accepts */
+
+/* Text of a status code (static storage; never NULL). */
+const char *dsaidx_status_string(int status);
+
+/* Bytes of one quantized query row: heads * 68 (MXFP4) or heads * 128 (FP8); 0 if the
+ * format or head count is invalid. */
+int64_t dsaidx_query_row_bytes(int fmt, int32_t heads);
+
+/*
+ * quantize_queries -- [idx] quantize_fp4_query and DsaIndex.fp8_query; [fp4ops]
+ * quantize_queries (shape rules). One workgroup per row.
+ *
+ *  q        device, BF16 [rows, heads, 128]: element (r, h, i) at q[r*q_row_stride +
+ *           h*q_head_stride + i]. Heads of 128 contiguous values; 16-byte aligned;
+ *           both strides multiples of 8; q_head_stride >= 128.
+ *  heads    16, 32 or 64 (DSAIDX_EUNSUPPORTED otherwise).
+ *  wv       device, BF16 raw head weights [rows, heads] (unit head stride), or NULL:
+ *           then w_out is not written.
+ *  q_out    device bytes, row r at q_out + r*q_out_row_stride (16-byte aligned,
+ *           stride a multiple of 16, >= dsaidx_query_row_bytes).
+ *           MXFP4 row: [heads x 64 B E2M1 | heads x 4 B UE8M0]. Byte h*64 + j holds
+ *           columns 2j (low nibble) and 2j+1 (high nibble) of head h; byte
+ *           heads*64 + h*4 + g is the UE8M0 scale of columns [32g, 32g+32):
+ *           e = the smallest integer with 6 * 2^e >= max(amax, 6 * 2^-126)
+ *           ([idx] mxfp4_scale, read exactly), value E2M1_RNE_satfinite(v * 2^-e).
+ *           FP8 row: [heads x 128 B E4M3FN]: s_h = pow2_ceil(max(1e-10, amax_h) / 448),
+ *           value E4M3_RNE_satfinite(v * (1 / s_h)).
+ *  w_out    device, BF16 [rows, heads]: MXFP4 BF16(wv * c_H) (the MX scales stay inside
+ *           the contraction, [idx] module text); FP8 BF16((wv * s_h) * c_H)
+ *           ([idx] DsaIndex.fp8_query); c_H = FP32((heads * 128)^-1/2).
+ *  rows == 0 enqueues nothing and returns DSAIDX_OK.
+ */
+dsaidx_status dsaidx_quantize_queries(int fmt, const void *q, int64_t rows, int32_t heads,
+                                      int64_t q_row_stride, int64_t q_head_stride,
+                                      const void *wv, int64_t wv_row_stride, void *q_out,
+                                      int64_t q_out_row_stride, void *w_out,
+                                      int64_t w_out_row_stride, void *stream);
+
+/*
+ * store_keys -- [idx] insert_key, insert_fp4_key; [fp4ops] store_keys, cache_views.
+ * One wavefront per key.
+ *
+ *  keys     device, BF16 pre-norm keys [tokens, 128], row t at keys + t*k_row_stride
+ *           (4-byte aligned, k_row_stride even and >= 128).
+ *  gamma, beta  device, FP32 [128] LayerNorm weight and bias (8-byte aligned).
+ *  eps      LayerNorm epsilon (finite, >= 0).
+ *  slots    device, int64 [tokens]: slot = page * 64 + offset. A negative slot is
+ *           padding and writes nothing; a slot >= num_pages * 64 writes nothing.
+ *  cache    device bytes: the section of page p starts at cache + p * page_stride
+ *           (16-byte aligned; page_stride a multiple of 16 and >= the section size,
+ *           4352 for MXFP4, 8448 for FP8). Only section bytes are written, so a
+ *           section may live inside a larger merged page.
+ *           LayerNorm: FP32, mean and variance over 128 values summed in a fixed
+ *           pairwise tree, rstd = 1 / sqrt(var + eps) (IEEE), y = ((x - mean) * rstd) *
+ *           gamma + beta, then rounded to BF16. MXFP4: the token's 64 payload bytes at
+ *           section + offset*64, its 4 UE8M0 bytes at section + 4096 + offset*4.
+ *           FP8: 128 E4M3 bytes at section + offset*128 with s = pow2_ceil(max(1e-10,
+ *           amax) / 448); FP32 s at section + 8192 + offset*4.
+ *  Caller contract: slots unique within one call (duplicates race).
+ *  tokens == 0 enqueues nothing.
+ */
+dsaidx_status dsaidx_store_keys(int fmt, const void *keys, int64_t tokens, int64_t k_row_stride,
+                                const float *gamma, const float *beta, float eps,
+                                const int64_t *slots, void *cache, int64_t num_pages,
+                                int64_t page_stride, void *stream);
+
+/*
+ * decode_layout -- [fp4ops] decode_layout. One workgroup; no device-to-host reads.
+ *
+ *  seq_lens, query_lens  device, int32 [num_requests] (query_lens >= 0).
+ *  query_starts device, int32 [num_requests + 1] = [0, cumsum(query_lens)].
+ *  row_ends     device, int32 [num_rows]: row r belongs to the request with
+ *               query_starts[q] <= r < query_starts[q + 1] (the last request if none);
+ *               end = max(0, seq - qlen + r - start + 1); rows at or past
+ *               query_starts[num_requests] are graph padding with end 0. With
+ *               dcp_world_size > 1 the bound is mapped to rank dcp_rank's share of keys
+ *               interleaved across ranks in runs of `interleave`.
+ *  Errors: num_rows < 0, num_requests < 0, dcp_rank outside [0, dcp_world_size) or
+ *  interleave < 1 give DSAIDX_EINVAL.
+ */
+dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
+                                   int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+                                   int32_t dcp_world_size, int32_t interleave,
+                                   int32_t *query_starts, int32_t *row_ends, void *stream);
+
+/*
+ * score_paged -- [fp4ops] score_paged (shared-key row groups, physical page strides);
+ * [idx] module text (MX scales inside the logits contraction, head weights carry only
+ * the weight scale). Scaled FP4 / FP8 MFMA.
+ *
+ *  q        device bytes: quantized query rows as written by dsaidx_quantize_queries,
+ *           row r at q + r*q_row_stride (16-byte aligned, stride a multiple of 16).
+ *  w        device, BF16 head weights [num_rows, heads] (w_out of quantize_queries),
+ *           8-byte aligned, w_row_stride a multiple of 4.
+ *  cache    device bytes, sections as for store_keys.
+ *  block_table  device, int32 [num_requests, max_blocks] with row stride max_blocks:
+ *           key p of request q lives on page block_table[q, p / 64], token p % 64.
+ *  query_starts device, int32 [num_requests + 1]; row_ends device, int32 [num_rows]
+ *           (as written by dsaidx_decode_layout).
+ *  logits   device, FP32 [num_rows, max_blocks * 64], row stride >= max_blocks * 64:
+ *           logits[r, p] = sum_h w[r, h] * max(0, dot_h(r, p)) for every row r of a
+ *           request and every p < min(row_ends[r], max_blocks * 64), where
+ *           MXFP4: dot_h = sum_g 2^(eq_g + ek_g) * sum_{i in block g} E2M1(q) * E2M1(k),
+ *           FP8:   dot_h = s_k * sum_i E4M3(q) * E4M3(k).
+ *           Entries at or past a row's bound, and rows of no request, are not written.
+ *  max_query_len  1..16: the most rows any request has.
+ *  Caller contract: query_starts nondecreasing; every request has at most
+ *  max_query_len rows (further rows are not scored); block-table entries a row's
+ *  bound reaches lie in [0, num_pages) (keys on other pages are not written).
+ *  num_rows, num_requests or max_blocks == 0 enqueues nothing.
+ */
+dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, int32_t heads,
+                                 const void *w, int64_t w_row_stride, const void *cache,
+                                 int64_t num_pages, int64_t page_stride,
+                                 const int32_t *block_table, int64_t num_requests,
+                                 int64_t max_blocks, const int32_t *query_starts,
+                                 const int32_t *row_ends, int64_t num_rows,
+                                 int32_t max_query_len, float *logits,
+                                 int64_t logits_row_stride, void *stream);
+
+/* Device workspace bytes that dsaidx_topk needs for these sizes (0: none). */
+size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k);
+
+/*
+ * topk -- per-row selection of the scored keys ([ovl] module text: the indexer path is
+ * scoring and top-k).
+ *
+ *  logits   device, FP32 [rows, >= width], row stride logits_row_stride >= width.
+ *  row_ends device, int32 [rows]: row r selects among positions [0, min(row_ends[r], width)).
+ *  indices  device, int32 [rows, >= k], row stride >= k: the positions of the k largest
+ *           logits (ties to the lower position; -0 equals +0); the order within a row is
+ *           unspecified; if fewer than k positions exist, all of them and -1 after.
+ *  workspace  device scratch of at least dsaidx_topk_workspace_bytes bytes (may be NULL
+ *           when that is 0).
+ *  Errors: k < 1, rows < 0 or width < 0 give DSAIDX_EINVAL. NaN logits are unsupported.
+ */
+dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
+                          int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
+                          int32_t *indices, int64_t indices_row_stride, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSAIDX_H_ */

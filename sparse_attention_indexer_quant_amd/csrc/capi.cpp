@@ -1,0 +1,180 @@
+// C-ABI of the indexer hot path (include/dsaidx.h): argument checks on the host, then one
+// launch per call on the caller's stream. A failing check returns before any HIP call, so
+// every error path can be exercised without a GPU.
+//
+// The checks follow the shape rules on page "vllm.models.kimi_k3.amd.ops.fp4_indexer":
+// cache_views (uint8 [pages, 64, 68] sections, physical stride >= 4352), quantize_queries
+// (contiguous 128-element heads; 16, 32 or 64 heads), store_keys (contiguous 128-element
+// keys, one slot per key), decode_layout (DCP geometry, non-negative row count) and
+// score_paged (empty outputs return at once); plus the alignments the kernels' vector
+// loads and stores need.
+#include <cmath>
+#include <cstdint>
+
+#include "dsaidx.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_fmt(int fmt) { return fmt == DSAIDX_MXFP4 || fmt == DSAIDX_FP8; }
+
+bool valid_heads(int heads) { return heads == 16 || heads == 32 || heads == 64; }
+
+int64_t section_bytes(int fmt) {
+    return fmt == DSAIDX_MXFP4 ? DSAIDX_MXFP4_SECTION_BYTES : DSAIDX_FP8_SECTION_BYTES;
+}
+
+// FP32 (heads * 128)^-1/2, nearest: 2^-6 at 32 heads; 2^-6 * sqrt(2) and 2^-7 * sqrt(2) at
+// 16 and 64 heads, written from the nearest FP32 of sqrt(2) (bits 0x3FB504F3).
+float head_weight_scale(int heads) {
+    const float sqrt2 = 1.41421353816986083984375f;
+    switch (heads) {
+        case 16: return sqrt2 * 0.015625f;
+        case 32: return 0.015625f;
+        default: return sqrt2 * 0.0078125f;
+    }
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+dsaidx_status hip_status(hipError_t e) { return e == hipSuccess ? DSAIDX_OK : DSAIDX_EHIP; }
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+}  // namespace
+
+extern "C" {
+
+const char *dsaidx_status_string(int status) {
+    switch (status) {
+        case DSAIDX_OK: return "ok";
+        case DSAIDX_EINVAL: return "invalid argument";
+        case DSAIDX_ELAYOUT: return "unsupported stride, alignment or buffer layout";
+        case DSAIDX_EUNSUPPORTED: return "unsupported shape";
+        case DSAIDX_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int64_t dsaidx_query_row_bytes(int fmt, int32_t heads) {
+    if (!valid_fmt(fmt) || !valid_heads(heads)) return 0;
+    return fmt == DSAIDX_MXFP4 ? (int64_t)heads * 68 : (int64_t)heads * 128;
+}
+
+dsaidx_status dsaidx_quantize_queries(int fmt, const void *q, int64_t rows, int32_t heads,
+                                      int64_t q_row_stride, int64_t q_head_stride,
+                                      const void *wv, int64_t wv_row_stride, void *q_out,
+                                      int64_t q_out_row_stride, void *w_out,
+                                      int64_t w_out_row_stride, void *stream) {
+    if (!valid_fmt(fmt) || rows < 0 || rows > kMaxGrid) return DSAIDX_EINVAL;
+    if (!valid_heads(heads)) return DSAIDX_EUNSUPPORTED;
+    if (rows == 0) return DSAIDX_OK;
+    if (!q || !q_out || (wv && !w_out)) return DSAIDX_EINVAL;
+    if (q_head_stride < DSAIDX_DIM || q_row_stride < (int64_t)(heads - 1) * q_head_stride + DSAIDX_DIM)
+        return DSAIDX_ELAYOUT;
+    if (!aligned(q, 16) || q_head_stride % 8 || q_row_stride % 8) return DSAIDX_ELAYOUT;
+    if (!aligned(q_out, 16) || q_out_row_stride % 16 ||
+        q_out_row_stride < dsaidx_query_row_bytes(fmt, heads))
+        return DSAIDX_ELAYOUT;
+    if (wv && (wv_row_stride < heads || w_out_row_stride < heads || !aligned(wv, 2) ||
+               !aligned(w_out, 2)))
+        return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_quantize_queries(
+        fmt, q, rows, heads, q_row_stride, q_head_stride, wv, wv_row_stride, q_out,
+        q_out_row_stride, wv ? w_out : nullptr, w_out_row_stride, head_weight_scale(heads),
+        as_stream(stream)));
+}
+
+dsaidx_status dsaidx_store_keys(int fmt, const void *keys, int64_t tokens, int64_t k_row_stride,
+                                const float *gamma, const float *beta, float eps,
+                                const int64_t *slots, void *cache, int64_t num_pages,
+                                int64_t page_stride, void *stream) {
+    if (!valid_fmt(fmt) || tokens < 0 || (tokens + 3) / 4 > kMaxGrid || num_pages < 0)
+        return DSAIDX_EINVAL;
+    if (!std::isfinite(eps) || eps < 0.0f) return DSAIDX_EINVAL;
+    if (tokens == 0) return DSAIDX_OK;
+    if (!keys || !gamma || !beta || !slots || !cache) return DSAIDX_EINVAL;
+    if (k_row_stride < DSAIDX_DIM || k_row_stride % 2 || !aligned(keys, 4)) return DSAIDX_ELAYOUT;
+    if (!aligned(gamma, 8) || !aligned(beta, 8) || !aligned(slots, 8)) return DSAIDX_ELAYOUT;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_store_keys(fmt, keys, tokens, k_row_stride, gamma, beta, eps,
+                                                slots, cache, num_pages, page_stride,
+                                                as_stream(stream)));
+}
+
+dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
+                                   int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+                                   int32_t dcp_world_size, int32_t interleave,
+                                   int32_t *query_starts, int32_t *row_ends, void *stream) {
+    if (!(0 <= dcp_rank && dcp_rank < dcp_world_size) || interleave < 1 || num_rows < 0 ||
+        num_requests < 0 || num_requests > kMaxGrid || num_rows > kMaxGrid)
+        return DSAIDX_EINVAL;
+    if (!query_starts || (num_rows > 0 && !row_ends) ||
+        (num_requests > 0 && (!seq_lens || !query_lens)))
+        return DSAIDX_EINVAL;
+    if (!aligned(query_starts, 4) || (row_ends && !aligned(row_ends, 4))) return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests, num_rows,
+                                                   dcp_rank, dcp_world_size, interleave,
+                                                   query_starts, row_ends, as_stream(stream)));
+}
+
+dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, int32_t heads,
+                                 const void *w, int64_t w_row_stride, const void *cache,
+                                 int64_t num_pages, int64_t page_stride,
+                                 const int32_t *block_table, int64_t num_requests,
+                                 int64_t max_blocks, const int32_t *query_starts,
+                                 const int32_t *row_ends, int64_t num_rows,
+                                 int32_t max_query_len, float *logits,
+                                 int64_t logits_row_stride, void *stream) {
+    if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0)
+        return DSAIDX_EINVAL;
+    if (!valid_heads(heads) || max_query_len < 1 || max_query_len > DSAIDX_MAX_QUERY_LEN)
+        return DSAIDX_EUNSUPPORTED;
+    if (num_rows == 0 || num_requests == 0 || max_blocks == 0) return DSAIDX_OK;
+    if (!q || !w || !cache || !block_table || !query_starts || !row_ends || !logits)
+        return DSAIDX_EINVAL;
+    if (!aligned(q, 16) || q_row_stride % 16 || q_row_stride < dsaidx_query_row_bytes(fmt, heads))
+        return DSAIDX_ELAYOUT;
+    if (!aligned(w, 8) || w_row_stride % 4 || w_row_stride < heads) return DSAIDX_ELAYOUT;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS ||
+        logits_row_stride < max_blocks * DSAIDX_PAGE_TOKENS || !aligned(logits, 4))
+        return DSAIDX_ELAYOUT;
+    const int pages_per_wg = fmt == DSAIDX_MXFP4 ? 16 : 8;
+    const int64_t chunks = (max_blocks + pages_per_wg - 1) / pages_per_wg;
+    if (chunks * num_requests > kMaxGrid) return DSAIDX_EUNSUPPORTED;
+    dsaidx::ScoreArgs a{fmt,         q,          q_row_stride, heads,         w,
+                        w_row_stride, cache,     num_pages,    page_stride,   block_table,
+                        num_requests, max_blocks, query_starts, row_ends,     num_rows,
+                        max_query_len, logits,    logits_row_stride};
+    return hip_status(dsaidx::launch_score_paged(a, as_stream(stream)));
+}
+
+size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k) {
+    if (rows < 0 || width < 0 || k < 1) return 0;
+    return dsaidx::topk_workspace_bytes(rows, width, k);
+}
+
+dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
+                          int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
+                          int32_t *indices, int64_t indices_row_stride, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (rows < 0 || rows > kMaxGrid || width < 0 || width > INT32_MAX || k < 1)
+        return DSAIDX_EINVAL;
+    if (rows == 0) return DSAIDX_OK;
+    if (!row_ends || !indices || (width > 0 && !logits)) return DSAIDX_EINVAL;
+    if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||
+        !aligned(indices, 4))
+        return DSAIDX_ELAYOUT;
+    const size_t need = dsaidx::topk_workspace_bytes(rows, width, k);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return DSAIDX_EINVAL;
+    return hip_status(dsaidx::launch_topk(logits, rows, width, logits_row_stride, row_ends, k,
+                                          indices, indices_row_stride, workspace,
+                                          workspace_bytes, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device helpers of the gfx950 indexer kernels: BF16 conversion, the E2M1 / E4M3 encoders,
+// UE8M0 and power-of-two scale exponents from FP32 bit fields, and wavefront reductions.
+//
+// Format definitions: page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index"
+// (module text: MXFP4 = one UE8M0 scale per 32 values, E2M1 round to nearest even with
+// saturation; e2m1x2; mxfp4_scale; DsaIndex.fp8_query).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+constexpr int kDim = 128;
+constexpr int kPageTokens = 64;
+constexpr int kMxfp4Section = 64 * 64 + 64 * 4;   // 4352
+constexpr int kFp8Section = 64 * 128 + 64 * 4;    // 8448
+constexpr int kFmtMxfp4 = 0;
+constexpr int kFmtFp8 = 1;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// FP32 -> BF16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(bf16_bits_rne(f) << 16); }
+
+// E2M1 code of an FP32 value (grid 0, .5, 1, 1.5, 2, 3, 4, 6): each comparison crosses one
+// midpoint between neighbouring grid values; at a midpoint the even code wins, so the
+// comparison is strict where the lower neighbour is even and inclusive where the upper one
+// is. Magnitudes above 5 all give 6 (saturation). Bit 3 is the input's sign bit.
+__device__ __forceinline__ uint32_t e2m1_code(float s) {
+    const float m = fabsf(s);
+    uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                 (m >= 3.5f) + (m > 5.0f);
+    return c | ((__float_as_uint(s) >> 28) & 8u);
+}
+
+// E4M3FN code of an FP32 value, round to nearest even, saturating to 448 (finite inputs).
+// Normal range: round the FP32 mantissa to 3 bits in the integer domain (a carry moves into
+// the exponent) and rebias 127 -> 7. Below 2^-6: the value in units of 2^-9, rounded to
+// nearest even (8 units is the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t e4m3_code(float s) {
+    const uint32_t b = __float_as_uint(s);
+    const uint32_t m = b & 0x7FFFFFFFu;
+    uint32_t c;
+    if (m >= 0x43E00000u) {            // >= 448
+        c = 0x7Eu;
+    } else if (m < 0x3C800000u) {      // < 2^-6
+        c = (uint32_t)__builtin_rintf(__uint_as_float(m) * 512.0f);
+    } else {
+        const uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);
+        c = (r >> 20) - (120u << 3);
+    }
+    return c | ((b >> 24) & 0x80u);
+}
+
+// UE8M0 exponent e of an MXFP4 block: the smallest integer with 6 * 2^e >= max(amax,
+// 6 * 2^-126). For amax = M * 2^E (M in [1, 2)) that is E - 2 when M <= 1.5 and E - 1 when
+// M > 1.5; every amax below 6 * 2^-126 (bits 0x01C00000) gives -126.
+__device__ __forceinline__ int ue8m0_exponent(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (b < 0x01C00000u) return -126;
+    return (int)(b >> 23) - 129 + ((b & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+}
+
+// 2^-e for e in [-126, 126], built from its exponent field.
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Smallest power of two >= x (x positive and normal).
+__device__ __forceinline__ float pow2_ceil(float x) {
+    uint32_t b = __float_as_uint(x);
+    if (b & 0x7FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+    return __uint_as_float(b);
+}
+
+// Correctly rounded FP32 square root of a positive normal value. The hardware estimate y is
+// within one ulp, so the answer is y or a neighbour y' = y -+ 1 ulp. For neighbours a < b the
+// midpoint satisfies mid^2 = a*b + (b - a)^2 / 4, and x - a*b is an exact multiple of
+// (b - a)^2 (both x and a*b are), so sqrt(x) < mid exactly when x - a*b <= 0. One fused
+// multiply-add gives the sign of x - a*b exactly, which picks the rounding.
+__device__ __forceinline__ float sqrt_rn(float x) {
+    float y = __builtin_amdgcn_sqrtf(x);
+    const float below = __uint_as_float(__float_as_uint(y) - 1u);
+    const float above = __uint_as_float(__float_as_uint(y) + 1u);
+    if (__builtin_fmaf(-below, y, x) <= 0.0f) y = below;
+    else if (__builtin_fmaf(-y, above, x) > 0.0f) y = above;
+    return y;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int lanes) {
+    for (int m = 1; m < lanes; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+}  // namespace dsaidx

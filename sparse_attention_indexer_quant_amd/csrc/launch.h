@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels. The C-ABI layer (capi.cpp) validates every
+// argument first and only then calls these; each returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,
+                                   int64_t q_row_stride, int64_t q_head_stride, const void *wv,
+                                   int64_t wv_row_stride, void *q_out, int64_t q_out_row_stride,
+                                   void *w_out, int64_t w_out_row_stride, float c_h,
+                                   hipStream_t stream);
+
+hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t k_row_stride,
+                             const float *gamma, const float *beta, float eps,
+                             const int64_t *slots, void *cache, int64_t num_pages,
+                             int64_t page_stride, hipStream_t stream);
+
+hipError_t launch_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
+                                int64_t num_requests, int64_t num_rows, int dcp_rank,
+                                int dcp_world_size, int interleave, int32_t *query_starts,
+                                int32_t *row_ends, hipStream_t stream);
+
+struct ScoreArgs {
+    int fmt;
+    const void *q;
+    int64_t q_row_stride;
+    int heads;
+    const void *w;
+    int64_t w_row_stride;
+    const void *cache;
+    int64_t num_pages;
+    int64_t page_stride;
+    const int32_t *block_table;
+    int64_t num_requests;
+    int64_t max_blocks;
+    const int32_t *query_starts;
+    const int32_t *row_ends;
+    int64_t num_rows;
+    int max_query_len;
+    float *logits;
+    int64_t logits_row_stride;
+};
+
+hipError_t launch_score_paged(const ScoreArgs &args, hipStream_t stream);
+
+size_t topk_workspace_bytes(int64_t rows, int64_t width, int k);
+
+hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t logits_row_stride,
+                       const int32_t *row_ends, int k, int32_t *indices,
+                       int64_t indices_row_stride, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+}  // namespace dsaidx

@@ -1,0 +1,175 @@
+// Query quantization and key LayerNorm + quantization + paged insert for gfx950.
+//
+// quantize_queries: page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index",
+//   quantize_fp4_query (MXFP4 of one head; scales after all payload bytes) and
+//   DsaIndex.fp8_query (FP8 with one power-of-two scale per head folded into the weight);
+//   page "vllm.models.kimi_k3.amd.ops.fp4_indexer", quantize_queries (shape rules).
+// store_keys: same index page, insert_key (FP32 LayerNorm, BF16, then the cache writer) and
+//   insert_fp4_key (payload at token * 64, four UE8M0 bytes at 64 * 64 + token * 4);
+//   fp4_indexer page, store_keys (negative slots are padding) and cache_views (sections
+//   inside merged pages, addressed by the physical page stride).
+//
+// Every float operation that decides a stored byte is a single IEEE RN operation written
+// with the __f*_rn intrinsics, so the bytes do not depend on contraction choices.
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsaidx {
+
+// One workgroup (256 lanes = 4 wavefronts) per query row. Lane t owns 8 consecutive
+// columns (one 16-byte load) of head (t / 16) + 16 * pass: 16 lanes per head, 4 lanes per
+// 32-value MX block.
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_queries_kernel(
+    const uint16_t *__restrict__ q, int heads, int64_t q_row_stride, int64_t q_head_stride,
+    const uint16_t *__restrict__ wv, int64_t wv_row_stride, uint8_t *__restrict__ q_out,
+    int64_t q_out_row_stride, uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int part = tid & 15;
+    uint8_t *out_row = q_out + row * q_out_row_stride;
+    for (int head = tid >> 4; head < heads; head += 16) {
+        const uint16_t *src = q + row * q_row_stride + (int64_t)head * q_head_stride + part * 8;
+        const uint4 raw = *reinterpret_cast<const uint4 *>(src);
+        float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                      bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+        if constexpr (FMT == kFmtMxfp4) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = wave_max_xor(amax, 4);  // the 4 lanes of one 32-value block
+            const int e = ue8m0_exponent(amax);
+            const float inv = pow2_neg(e);
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) word |= e2m1_code(__fmul_rn(v[i], inv)) << (4 * i);
+            *reinterpret_cast<uint32_t *>(out_row + head * 64 + part * 4) = word;
+            // UE8M0 bytes of blocks 0..3 live in lanes part = 0, 4, 8, 12 of the head.
+            const uint32_t byte = (uint32_t)(e + 127);
+            const uint32_t b1 = __shfl_down(byte, 4, 16), b2 = __shfl_down(byte, 8, 16),
+                           b3 = __shfl_down(byte, 12, 16);
+            if (part == 0) {
+                *reinterpret_cast<uint32_t *>(out_row + heads * 64 + head * 4) =
+                    byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                if (wv) {
+                    const float w = bf16_val(wv[row * wv_row_stride + head]);
+                    w_out[row * w_out_row_stride + head] = (uint16_t)bf16_bits_rne(__fmul_rn(w, c_h));
+                }
+            }
+        } else {
+            float amax = 1e-10f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = wave_max_xor(amax, 16);  // the 16 lanes of the head
+            const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
+            const float inv = __fdiv_rn(1.0f, s);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= e4m3_code(__fmul_rn(v[i], inv)) << (8 * i);
+                hi |= e4m3_code(__fmul_rn(v[4 + i], inv)) << (8 * i);
+            }
+            *reinterpret_cast<uint2 *>(out_row + head * 128 + part * 8) = make_uint2(lo, hi);
+            if (part == 0 && wv) {
+                const float w = bf16_val(wv[row * wv_row_stride + head]);
+                w_out[row * w_out_row_stride + head] =
+                    (uint16_t)bf16_bits_rne(__fmul_rn(__fmul_rn(w, s), c_h));
+            }
+        }
+    }
+}
+
+// One wavefront per key: lane l owns columns 2l and 2l+1 (one 4-byte load). The LayerNorm
+// sums run as the pairwise tree "adjacent pair, then fold 32, 16, 8, 4, 2, 1 apart", which
+// the xor butterfly below computes in every lane.
+template <int FMT>
+__global__ __launch_bounds__(256) void store_keys_kernel(
+    const uint16_t *__restrict__ keys, int64_t tokens, int64_t k_row_stride,
+    const float *__restrict__ gamma, const float *__restrict__ beta, float eps,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
+    int64_t page_stride) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= tokens) return;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_pages * kPageTokens) return;  // padding / out of range
+    const uint32_t pair = *reinterpret_cast<const uint32_t *>(keys + t * k_row_stride + 2 * lane);
+    const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+
+    float sum = __fadd_rn(x0, x1);
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) sum = __fadd_rn(sum, __shfl_xor(sum, h));
+    const float mean = __fmul_rn(sum, 0.0078125f);
+    const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
+    float sq = __fadd_rn(__fmul_rn(d0, d0), __fmul_rn(d1, d1));
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) sq = __fadd_rn(sq, __shfl_xor(sq, h));
+    const float var = __fmul_rn(sq, 0.0078125f);
+    const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
+    const float2 g = *reinterpret_cast<const float2 *>(gamma + 2 * lane);
+    const float2 b = *reinterpret_cast<const float2 *>(beta + 2 * lane);
+    const float n0 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d0, rstd), g.x), b.x));
+    const float n1 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d1, rstd), g.y), b.y));
+
+    uint8_t *sec = cache + (slot >> 6) * page_stride;
+    const int off = (int)(slot & 63);
+    if constexpr (FMT == kFmtMxfp4) {
+        const float amax = wave_max_xor(fmaxf(fabsf(n0), fabsf(n1)), 16);  // 16 lanes = 32 columns
+        const int e = ue8m0_exponent(amax);
+        const float inv = pow2_neg(e);
+        const uint32_t byte = e2m1_code(__fmul_rn(n0, inv)) | (e2m1_code(__fmul_rn(n1, inv)) << 4);
+        const uint32_t word = byte | (__shfl_down(byte, 1) << 8) | (__shfl_down(byte, 2) << 16) |
+                              (__shfl_down(byte, 3) << 24);
+        if ((lane & 3) == 0) *reinterpret_cast<uint32_t *>(sec + off * 64 + lane) = word;
+        const uint32_t sb = (uint32_t)(e + 127);
+        const uint32_t scales = sb | (__shfl(sb, 16) << 8) | (__shfl(sb, 32) << 16) | (__shfl(sb, 48) << 24);
+        if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
+    } else {
+        const float amax = wave_max_xor(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))), 64);
+        const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
+        const float inv = __fdiv_rn(1.0f, s);
+        const uint32_t two = e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8);
+        const uint32_t word = two | (__shfl_down(two, 1) << 16);
+        if ((lane & 1) == 0) *reinterpret_cast<uint32_t *>(sec + off * 128 + 2 * lane) = word;
+        if (lane == 0) *reinterpret_cast<float *>(sec + 64 * 128 + off * 4) = s;
+    }
+}
+
+hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,
+                                   int64_t q_row_stride, int64_t q_head_stride, const void *wv,
+                                   int64_t wv_row_stride, void *q_out, int64_t q_out_row_stride,
+                                   void *w_out, int64_t w_out_row_stride, float c_h,
+                                   hipStream_t stream) {
+    const dim3 grid((unsigned)rows), block(256);
+    auto *qq = static_cast<const uint16_t *>(q);
+    auto *ww = static_cast<const uint16_t *>(wv);
+    auto *qo = static_cast<uint8_t *>(q_out);
+    auto *wo = static_cast<uint16_t *>(w_out);
+    if (fmt == kFmtMxfp4)
+        hipLaunchKernelGGL(quantize_queries_kernel<kFmtMxfp4>, grid, block, 0, stream, qq, heads,
+                           q_row_stride, q_head_stride, ww, wv_row_stride, qo, q_out_row_stride,
+                           wo, w_out_row_stride, c_h);
+    else
+        hipLaunchKernelGGL(quantize_queries_kernel<kFmtFp8>, grid, block, 0, stream, qq, heads,
+                           q_row_stride, q_head_stride, ww, wv_row_stride, qo, q_out_row_stride,
+                           wo, w_out_row_stride, c_h);
+    return hipGetLastError();
+}
+
+hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t k_row_stride,
+                             const float *gamma, const float *beta, float eps,
+                             const int64_t *slots, void *cache, int64_t num_pages,
+                             int64_t page_stride, hipStream_t stream) {
+    const dim3 grid((unsigned)((tokens + 3) / 4)), block(256);
+    auto *kk = static_cast<const uint16_t *>(keys);
+    auto *cc = static_cast<uint8_t *>(cache);
+    if (fmt == kFmtMxfp4)
+        hipLaunchKernelGGL(store_keys_kernel<kFmtMxfp4>, grid, block, 0, stream, kk, tokens,
+                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+    else
+        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8>, grid, block, 0, stream, kk, tokens,
+                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+    return hipGetLastError();
+}
+
+}  // namespace dsaidx

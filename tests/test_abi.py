@@ -1,0 +1,176 @@
+"""The C-ABI library on the host: it loads, exports every entry point include/dsaidx.h
+declares, and every argument check fails before anything is enqueued (no GPU needed; the
+pointers passed here are never dereferenced because each call returns at its check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_quant_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsaidx.h")
+
+OK, EINVAL, ELAYOUT, EUNSUP = 0, 1, 2, 3
+P = 0x10000  # a 64 KiB-aligned stand-in pointer: every check below fails before any use
+MX, FP8 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIBRARY):
+        pytest.skip("libdsaidx.so not built (run __graft_entry__.build())")
+    return dsa.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsaidx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dsaidx_quantize_queries", "dsaidx_store_keys", "dsaidx_score_paged", "dsaidx_topk",
+              "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
+              "dsaidx_query_row_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(dsa.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings_and_row_bytes(lib):
+    assert lib.dsaidx_status_string(0) == b"ok"
+    assert lib.dsaidx_status_string(99) == b"unknown status"
+    assert lib.dsaidx_query_row_bytes(MX, 32) == 2176
+    assert lib.dsaidx_query_row_bytes(MX, 64) == 4352
+    assert lib.dsaidx_query_row_bytes(FP8, 32) == 4096
+    assert lib.dsaidx_query_row_bytes(MX, 48) == 0
+    assert lib.dsaidx_query_row_bytes(7, 32) == 0
+
+
+def quant(lib, **kw):
+    a = dict(fmt=MX, q=P, rows=4, heads=32, rs=32 * 128, hs=128, wv=P, wvs=32, out=P, outs=2176,
+             wo=P, wos=32)
+    a.update(kw)
+    return lib.dsaidx_quantize_queries(a["fmt"], a["q"], a["rows"], a["heads"], a["rs"], a["hs"],
+                                       a["wv"], a["wvs"], a["out"], a["outs"], a["wo"], a["wos"], None)
+
+
+def test_quantize_queries_checks(lib):
+    assert quant(lib, fmt=5) == EINVAL
+    assert quant(lib, rows=-1) == EINVAL
+    assert quant(lib, heads=48) == EUNSUP            # fp4_indexer quantize_queries: 16, 32 or 64
+    assert quant(lib, rows=0, q=None, out=None) == OK  # empty: nothing enqueued
+    assert quant(lib, q=None) == EINVAL
+    assert quant(lib, wo=None) == EINVAL             # weights without an output
+    assert quant(lib, hs=64) == ELAYOUT              # heads overlap
+    assert quant(lib, rs=31 * 128) == ELAYOUT        # rows overlap
+    assert quant(lib, q=P + 2) == ELAYOUT            # 16-byte loads
+    assert quant(lib, hs=132, rs=32 * 132) == ELAYOUT
+    assert quant(lib, outs=2160) == ELAYOUT          # stride below the row size
+    assert quant(lib, outs=2184) == ELAYOUT          # stride not a multiple of 16
+    assert quant(lib, fmt=FP8, outs=2176) == ELAYOUT  # FP8 rows are 4096 B
+    assert quant(lib, wvs=16) == ELAYOUT
+
+
+def store(lib, **kw):
+    a = dict(fmt=MX, keys=P, t=8, ks=128, g=P, b=P, eps=1e-6, slots=P, cache=P, pages=4, ps=4352)
+    a.update(kw)
+    return lib.dsaidx_store_keys(a["fmt"], a["keys"], a["t"], a["ks"], a["g"], a["b"], a["eps"],
+                                 a["slots"], a["cache"], a["pages"], a["ps"], None)
+
+
+def test_store_keys_checks(lib):
+    assert store(lib, fmt=-1) == EINVAL
+    assert store(lib, t=-2) == EINVAL
+    assert store(lib, eps=float("nan")) == EINVAL
+    assert store(lib, eps=-1.0) == EINVAL
+    assert store(lib, t=0, keys=None) == OK
+    assert store(lib, slots=None) == EINVAL
+    assert store(lib, ks=127) == ELAYOUT            # contiguous 128-element rows
+    assert store(lib, ks=129) == ELAYOUT
+    assert store(lib, ps=4351) == ELAYOUT           # cache_views: stride >= 4352
+    assert store(lib, ps=4360) == ELAYOUT           # 16-byte aligned sections
+    assert store(lib, fmt=FP8, ps=4352) == ELAYOUT  # FP8 sections are 8448 B
+    assert store(lib, cache=P + 8) == ELAYOUT
+    assert store(lib, g=P + 4) == ELAYOUT
+
+
+def layout(lib, **kw):
+    a = dict(seq=P, ql=P, r=4, rows=8, rank=0, world=1, il=1, starts=P, ends=P)
+    a.update(kw)
+    return lib.dsaidx_decode_layout(a["seq"], a["ql"], a["r"], a["rows"], a["rank"], a["world"],
+                                    a["il"], a["starts"], a["ends"], None)
+
+
+def test_decode_layout_checks(lib):
+    # fp4_indexer decode_layout: invalid DCP geometry or query row count
+    assert layout(lib, rank=1, world=1) == EINVAL
+    assert layout(lib, rank=-1) == EINVAL
+    assert layout(lib, il=0) == EINVAL
+    assert layout(lib, rows=-1) == EINVAL
+    assert layout(lib, r=-1) == EINVAL
+    assert layout(lib, starts=None) == EINVAL
+    assert layout(lib, ends=None) == EINVAL
+    assert layout(lib, seq=None) == EINVAL
+    assert layout(lib, starts=P + 2) == ELAYOUT
+
+
+def score(lib, **kw):
+    a = dict(fmt=MX, q=P, qs=2176, heads=32, w=P, ws=32, cache=P, pages=8, ps=4352, bt=P, r=2,
+             mb=4, starts=P, ends=P, rows=2, mql=1, out=P, os=256)
+    a.update(kw)
+    return lib.dsaidx_score_paged(a["fmt"], a["q"], a["qs"], a["heads"], a["w"], a["ws"], a["cache"],
+                                  a["pages"], a["ps"], a["bt"], a["r"], a["mb"], a["starts"],
+                                  a["ends"], a["rows"], a["mql"], a["out"], a["os"], None)
+
+
+def test_score_paged_checks(lib):
+    assert score(lib, fmt=3) == EINVAL
+    assert score(lib, rows=-1) == EINVAL
+    assert score(lib, heads=8) == EUNSUP
+    assert score(lib, mql=0) == EUNSUP
+    assert score(lib, mql=17) == EUNSUP
+    assert score(lib, rows=0, q=None) == OK          # fp4_indexer score_paged: empty output
+    assert score(lib, r=0, q=None) == OK
+    assert score(lib, mb=0, q=None) == OK
+    assert score(lib, bt=None) == EINVAL
+    assert score(lib, qs=2160) == ELAYOUT
+    assert score(lib, q=P + 4) == ELAYOUT
+    assert score(lib, ws=30) == ELAYOUT
+    assert score(lib, ps=4000) == ELAYOUT
+    assert score(lib, fmt=FP8, qs=4096, ps=4352) == ELAYOUT
+    assert score(lib, os=255) == ELAYOUT
+
+
+def topk(lib, **kw):
+    a = dict(lg=P, rows=2, width=256, ls=256, ends=P, k=16, out=P, os=16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.dsaidx_topk(a["lg"], a["rows"], a["width"], a["ls"], a["ends"], a["k"], a["out"],
+                           a["os"], a["ws"], a["wsb"], None)
+
+
+def test_topk_checks(lib):
+    assert topk(lib, k=0) == EINVAL
+    assert topk(lib, rows=-1) == EINVAL
+    assert topk(lib, width=-1) == EINVAL
+    assert topk(lib, rows=0, lg=None) == OK
+    assert topk(lib, ends=None) == EINVAL
+    assert topk(lib, ls=255) == ELAYOUT
+    assert topk(lib, os=15) == ELAYOUT
+    assert topk(lib, lg=P + 2) == ELAYOUT
+    assert lib.dsaidx_topk_workspace_bytes(4, 1024, 0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        dsa.quantize_queries(torch.zeros((1, 32, 128), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        dsa.topk(torch.zeros((1, 8)), torch.zeros(1, dtype=torch.int32), 2)

@@ -1,0 +1,114 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration bench.py times:
+the whole cache, every quantized query byte and every row bound bit-exact; logits of
+sampled rows within 1e-5 * max |logit| of the oracle; top-k sets equal on identical
+(oracle) logits; and end-to-end top-k differing only by boundary swaps within tolerance."""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_indexer_quant_amd as dsa
+from gpu_util import DeviceWorkload, assert_logits_close, assert_topk_sets, bf16_host, dev, oracle_cache
+from sparse_attention_indexer_quant_amd.workloads import CONFIG_NAMES, config
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(wl, starts, ends, n=4):
+    live = [r for r in range(wl.num_rows) if ends[r] > 0]
+    rng = np.random.default_rng(wl.seed)
+    pick = {live[0], live[-1]}
+    # every row of one multi-row request, if there is one
+    for q in range(wl.num_requests):
+        if starts[q + 1] - starts[q] >= 3:
+            pick.update(range(starts[q], starts[q + 1]))
+            break
+    pick.update(rng.choice(live, size=min(n, len(live)), replace=False).tolist())
+    return sorted(int(r) for r in pick)
+
+
+@pytest.fixture(scope="module", params=CONFIG_NAMES)
+def run(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.library()
+    name = request.param
+    print(f"\n[config {name}] building inputs", flush=True)
+    wl = config(name)
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, ends = dw.layout()
+    logits = dw.score(q_rows, w, starts, ends)
+    idx = dsa.topk(logits, ends, wl.topk)
+    torch.cuda.synchronize()
+    print(f"[config {name}] GPU path done; oracle", flush=True)
+    ocache = oracle_cache(wl)
+    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+    os_, oe = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+    rows = _sample_rows(wl, os_, oe)
+    ref = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
+                             os_, oe, wl.fmt, wl.section_offset, rows_subset=rows)
+    ctx = dict(name=name, wl=wl, dw=dw, q_rows=q_rows, w=w, starts=starts, ends=ends,
+               logits=logits, idx=idx, ocache=ocache, oq=oq, ow=ow, os=os_, oe=oe, rows=rows, ref=ref)
+    yield ctx
+    del ctx, dw, logits, idx
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_cache_bit_exact(run):
+    assert np.array_equal(run["dw"].cache.cpu().numpy(), run["ocache"])
+
+
+def test_queries_and_weights_bit_exact(run):
+    assert np.array_equal(run["q_rows"].cpu().numpy(), run["oq"])
+    assert np.array_equal(bf16_host(run["w"]), run["ow"])
+
+
+def test_row_bounds_exact(run):
+    assert np.array_equal(run["starts"].cpu().numpy(), run["os"])
+    assert np.array_equal(run["ends"].cpu().numpy(), run["oe"])
+
+
+def test_sampled_logits_within_tolerance(run):
+    got = run["logits"][run["rows"]].cpu().numpy()
+    ref = run["ref"][run["rows"]]
+    ends = run["oe"][run["rows"]]
+    assert_logits_close(got, ref, ends, range(len(run["rows"])), run["name"])
+
+
+def test_topk_on_identical_logits(run):
+    # both sides select from the oracle's logits of the sampled rows
+    wl, rows = run["wl"], run["rows"]
+    lg = np.nan_to_num(run["ref"][rows], nan=0.0).astype(np.float32)
+    ends = run["oe"][rows].astype(np.int32)
+    want = oracle.topk(lg, ends, wl.topk)
+    got = dsa.topk(dev(lg), dev(ends), wl.topk).cpu().numpy()
+    assert_topk_sets(got, want, range(len(rows)), run["name"])
+
+
+def test_topk_end_to_end_boundary_swaps_only(run):
+    # GPU logits -> GPU top-k against oracle logits -> oracle top-k: any index in one set but
+    # not the other must have an oracle logit within the logit tolerance of the k-th value.
+    wl, rows = run["wl"], run["rows"]
+    ref = run["ref"][rows]
+    ends = run["oe"][rows].astype(np.int32)
+    want = oracle.topk(np.nan_to_num(ref, nan=0.0).astype(np.float32), ends, wl.topk)
+    got = run["idx"][rows].cpu().numpy()
+    swaps = 0
+    for i in range(len(rows)):
+        n = int(ends[i])
+        if n == 0:
+            assert np.all(got[i] == -1)
+            continue
+        diff = np.setxor1d(got[i], want[i])
+        swaps += diff.size // 2
+        if diff.size:
+            tol = 1e-5 * float(np.max(np.abs(ref[i, :n])))
+            kth = np.sort(ref[i, :n])[::-1][min(wl.topk, n) - 1]
+            assert np.all(diff >= 0) and np.all(np.abs(ref[i, diff] - kth) <= 2 * tol), run["name"]
+    print(f"[config {run['name']}] end-to-end top-k boundary swaps: {swaps}", file=sys.stderr)

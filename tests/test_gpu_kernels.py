@@ -1,0 +1,276 @@
+"""GPU parity of each HIP kernel against the oracle on small seeded inputs that still span
+several tiles and ragged tails, plus the edge cases: empty inputs, padding slots and rows,
+bounds that are zero, below k, or not a multiple of 64, every head count, FP8, and the
+placement invariances. Bit-exact on bytes, scales, weights and index sets; logits within
+1e-5 * max |logit| per row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_indexer_quant_amd as dsa
+from gpu_util import (DeviceWorkload, assert_logits_close, assert_topk_sets, bf16_dev, bf16_host,
+                      dev, oracle_cache)
+from sparse_attention_indexer_quant_amd.workloads import bf16_bits, bf16_to_f32, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.library()  # fail loudly if the HIP library is missing
+
+
+# ---- quantize_queries -----------------------------------------------------------------------
+
+def _query_cases():
+    rng = np.random.default_rng(100)
+    cases = {}
+    for heads in (16, 32, 64):
+        cases[f"normal_h{heads}"] = rng.standard_normal((37, heads, 128)).astype(np.float32)
+    q = rng.standard_normal((9, 32, 128)).astype(np.float32)
+    q[0] = 0.0                                       # all-zero rows (scale floor)
+    q[1, :, :] *= 1e-38                              # tiny values around the subnormal range
+    q[2, :, ::3] *= 1e30                             # huge values
+    q[3] = np.where(rng.random((32, 128)) < 0.01, q[3] * 20, q[3])   # outliers x20
+    q[4, :, :] = -0.0                                # negative zeros
+    q[5] = np.round(q[5] * 4) / 4                    # many exact E2M1 midpoints after scaling
+    q[6] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], size=(32, 128)) * \
+        rng.choice([-1, 1], size=(32, 128))          # midpoints with amax 6 -> scale 1
+    cases["edges"] = q
+    return cases
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("case", list(_query_cases().keys()))
+def test_quantize_queries_bit_exact(fmt, case):
+    q = _query_cases()[case]
+    qb = bf16_bits(q)
+    wvb = bf16_bits(np.random.default_rng(3).standard_normal(q.shape[:2]).astype(np.float32) * 3)
+    want_q, want_w = oracle.quantize_queries(qb, wvb, fmt)
+    got_q, got_w = dsa.quantize_queries(bf16_dev(qb), bf16_dev(wvb), fmt)
+    assert np.array_equal(got_q.cpu().numpy(), want_q)
+    assert np.array_equal(bf16_host(got_w), want_w)
+
+
+def test_quantize_queries_strided_input_and_no_weights():
+    rng = np.random.default_rng(5)
+    full = bf16_bits(rng.standard_normal((6, 40, 136)).astype(np.float32))
+    view = bf16_dev(full)[:, 2:34, 8:136]  # head stride 136, row stride 40*136
+    want, _ = oracle.quantize_queries(full[:, 2:34, 8:136], None, "mxfp4")
+    out = torch.full((6, 2304), 7, dtype=torch.uint8, device="cuda")
+    got, w = dsa.quantize_queries(view, None, "mxfp4", out=out)
+    assert w is None
+    assert np.array_equal(got.cpu().numpy()[:, :2176], want)
+    assert np.all(got.cpu().numpy()[:, 2176:] == 7)  # row padding untouched
+
+
+def test_quantize_queries_empty():
+    got, w = dsa.quantize_queries(torch.empty((0, 32, 128), dtype=torch.bfloat16, device="cuda"),
+                                  torch.empty((0, 32), dtype=torch.bfloat16, device="cuda"))
+    assert got.shape == (0, 2176)
+
+
+# ---- store_keys -----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,stride,offset", [("mxfp4", 4352, 0), ("mxfp4", 8192, 3840),
+                                               ("mxfp4", 8192, 0), ("fp8", 8448, 0),
+                                               ("fp8", 12288, 1024)])
+def test_store_keys_bit_exact(fmt, stride, offset):
+    rng = np.random.default_rng(7)
+    pages = 9
+    wl = make_workload("st", fmt=fmt, heads=16, seq_lens=[64 * pages - 5], query_lens=[1], topk=4,
+                       seed=8, page_stride=stride, section_offset=offset)
+    keys = wl.key_bits.copy()
+    keys[3] = bf16_bits(np.full(128, 2.5, np.float32))              # constant key -> beta
+    keys[4] = bf16_bits(np.zeros(128, np.float32))
+    keys[5] = bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e4)
+    keys[6] = bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e-4)
+    slots = wl.key_slots.copy()
+    slots[10] = -1                                                   # padding
+    slots[11] = -12345
+    slots[12] = 64 * pages + 3                                       # beyond the cache
+    slots[13] = 1 << 40
+    want = np.full(wl.cache_bytes, 0xA5, np.uint8)
+    oracle.store_keys(keys, wl.gamma, wl.beta, wl.eps, slots, want, wl.num_pages, stride, offset, fmt)
+    got = torch.full((wl.cache_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    dsa.store_keys(bf16_dev(keys), dev(wl.gamma), dev(wl.beta), wl.eps, dev(slots), got, wl.num_pages,
+                   stride, fmt, offset)
+    got = got.cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_store_keys_bulk_layernorm_bit_exact(fmt):
+    # 300k keys spanning 2^-20 .. 2^20 in scale and offset: every LayerNorm rounding step
+    # (tree sums, correctly rounded sqrt and divide, BF16) must match; FP8's finer grid
+    # exposes a one-ulp rstd difference far more often than E2M1 does.
+    rng = np.random.default_rng(21)
+    T = 300_000
+    scale = np.exp2(rng.uniform(-20, 20, size=(T, 1))).astype(np.float32)
+    shift = (rng.standard_normal((T, 1)) * np.exp2(rng.uniform(-20, 20, size=(T, 1)))).astype(np.float32)
+    keys = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32) * scale + shift)
+    pages = (T + 63) // 64
+    section = 4352 if fmt == "mxfp4" else 8448
+    slots = rng.permutation(pages * 64)[:T].astype(np.int64)
+    gamma = bf16_to_f32(bf16_bits(1 + 0.1 * rng.standard_normal(128).astype(np.float32)))
+    beta = bf16_to_f32(bf16_bits(0.1 * rng.standard_normal(128).astype(np.float32)))
+    want = np.zeros(pages * section, np.uint8)
+    oracle.store_keys(keys, gamma, beta, 1e-6, slots, want, pages, section, 0, fmt)
+    got = torch.zeros(pages * section, dtype=torch.uint8, device="cuda")
+    dsa.store_keys(bf16_dev(keys), dev(gamma), dev(beta), 1e-6, dev(slots), got, pages, section, fmt)
+    got = got.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:4]}"
+
+
+def test_store_keys_empty_and_all_padding():
+    cache = torch.full((4352,), 0x5A, dtype=torch.uint8, device="cuda")
+    g = torch.ones(128, device="cuda")
+    b = torch.zeros(128, device="cuda")
+    dsa.store_keys(torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"), g, b, 1e-6,
+                   torch.empty(0, dtype=torch.int64, device="cuda"), cache, 1, 4352)
+    dsa.store_keys(torch.ones((5, 128), dtype=torch.bfloat16, device="cuda"), g, b, 1e-6,
+                   torch.full((5,), -1, dtype=torch.int64, device="cuda"), cache, 1, 4352)
+    assert torch.all(cache == 0x5A)
+
+
+# ---- decode_layout --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seq,ql,rows,dcp", [
+    ([10, 20, 5], [1, 3, 2], 8, (0, 1, 1)), ([1], [3], 3, (0, 1, 1)), ([], [], 4, (0, 1, 1)),
+    ([7], [1], 0, (0, 1, 1)), ([100], [1], 1, (0, 4, 8)), ([100], [1], 1, (3, 4, 8)),
+    ([45], [1], 1, (1, 2, 4)), ([9, 9], [2, 0], 3, (0, 1, 1))])
+def test_decode_layout_small(seq, ql, rows, dcp):
+    s_want, e_want = oracle.decode_layout(seq, ql, rows, *dcp)
+    s, e = dsa.decode_layout(dev(np.array(seq, np.int32)), dev(np.array(ql, np.int32)), rows, *dcp)
+    assert np.array_equal(s.cpu().numpy(), s_want) and np.array_equal(e.cpu().numpy(), e_want)
+
+
+def test_decode_layout_large_random():
+    rng = np.random.default_rng(9)
+    for R, rows in [(3000, 9000), (128, 512), (1, 1)]:
+        ql = rng.integers(0, 5, R).astype(np.int32)
+        seq = (ql + rng.integers(0, 70000, R)).astype(np.int32)
+        rows = max(rows, int(ql.sum()))
+        for dcp in [(0, 1, 1), (2, 4, 16)]:
+            s_want, e_want = oracle.decode_layout(seq, ql, rows, *dcp)
+            s, e = dsa.decode_layout(dev(seq), dev(ql), rows, *dcp)
+            assert np.array_equal(s.cpu().numpy(), s_want)
+            assert np.array_equal(e.cpu().numpy(), e_want)
+
+
+# ---- score_paged ----------------------------------------------------------------------------
+
+SCORE_CASES = {
+    # name: make_workload kwargs
+    "fp4_h32_ragged": dict(fmt="mxfp4", heads=32, seq_lens=[1000, 64, 1, 777, 130], query_lens=[1, 1, 1, 1, 1]),
+    "fp4_h16_verify": dict(fmt="mxfp4", heads=16, seq_lens=[300, 1200, 7, 64], query_lens=[4, 2, 3, 1],
+                           num_rows=16),
+    "fp4_h64_merged": dict(fmt="mxfp4", heads=64, seq_lens=[2100, 513], query_lens=[1, 3],
+                           page_stride=8192, section_offset=3840),
+    "fp4_h32_qlen16": dict(fmt="mxfp4", heads=32, seq_lens=[600, 40], query_lens=[16, 5], num_rows=24),
+    "fp8_h32": dict(fmt="fp8", heads=32, seq_lens=[1500, 65, 300], query_lens=[1, 2, 1],
+                    outlier_frac=0.01, outlier_gain=20.0),
+    "fp8_h64_verify": dict(fmt="fp8", heads=64, seq_lens=[500, 129], query_lens=[3, 4], num_rows=9,
+                           page_stride=9216, section_offset=512),
+    "fp4_h32_scaled_heads": dict(fmt="mxfp4", heads=32, seq_lens=[900], query_lens=[2], head_log2_scale=4.0),
+}
+
+
+def _run_score(name, seed=11):
+    kw = dict(SCORE_CASES[name])
+    wl = make_workload(name, topk=64, seed=seed, extra_pages=3, **kw)
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    ocache = oracle_cache(wl)
+    assert np.array_equal(dw.cache.cpu().numpy(), ocache)
+    q_rows, w = dw.quantize()
+    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+    assert np.array_equal(q_rows.cpu().numpy(), oq) and np.array_equal(bf16_host(w), ow)
+    starts, ends = dw.layout()
+    os_, oe = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+    assert np.array_equal(starts.cpu().numpy(), os_) and np.array_equal(ends.cpu().numpy(), oe)
+    logits = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    dsa.score_paged(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride, dw.block_table,
+                    starts, ends, wl.max_query_len, wl.fmt, wl.section_offset, out=logits)
+    ref = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
+                             os_, oe, wl.fmt, wl.section_offset)
+    return wl, dw, logits.cpu().numpy(), ref, oe, (q_rows, w, starts, ends)
+
+
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+def test_score_paged_matches_oracle(name):
+    wl, _, got, ref, ends, _ = _run_score(name)
+    # written exactly where the oracle writes (bounds respected, padding rows untouched)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert_logits_close(got, ref, ends, range(wl.num_rows), name)
+
+
+def test_score_paged_placement_invariance_and_determinism():
+    outs = []
+    for permute, stride, offset in [(True, 4352, 0), (False, 4352, 0), (True, 8192, 3840)]:
+        wl = make_workload("inv", fmt="mxfp4", heads=32, seq_lens=[700, 129], query_lens=[2, 1],
+                           topk=8, seed=12, permute_pages=permute, page_stride=stride,
+                           section_offset=offset, extra_pages=2)
+        dw = DeviceWorkload(wl)
+        dw.fill_cache()
+        q_rows, w = dw.quantize()
+        starts, ends = dw.layout()
+        for _ in range(2):
+            outs.append(dw.score(q_rows, w, starts, ends).cpu().numpy())
+    e = ends.cpu().numpy()
+    for r in range(3):
+        for o in outs[1:]:
+            assert np.array_equal(o[r, :e[r]], outs[0][r, :e[r]])
+
+
+def test_score_paged_zero_bounds_write_nothing():
+    wl = make_workload("zero", fmt="mxfp4", heads=32, seq_lens=[200, 64], query_lens=[1, 1], topk=8,
+                       seed=13)
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, _ = dw.layout()
+    ends = dev(np.array([0, 0], np.int32))
+    out = torch.full((2, wl.width), 3.0, device="cuda")
+    dsa.score_paged(q_rows, 32, w, dw.cache, wl.num_pages, wl.page_stride, dw.block_table, starts,
+                    ends, 1, out=out)
+    assert torch.all(out == 3.0)
+
+
+# ---- topk -----------------------------------------------------------------------------------
+
+def _topk_inputs(seed):
+    rng = np.random.default_rng(seed)
+    rows, width = 12, 5000
+    lg = rng.standard_normal((rows, width)).astype(np.float32)
+    lg[1] = 1.0                                        # all equal
+    lg[2, :] = np.round(lg[2, :] * 2) / 2              # heavy ties
+    lg[3, ::2] = -0.0
+    lg[3, 1::2] = 0.0                                  # signed zeros are equal
+    lg[4] = -np.abs(lg[4])                             # all negative
+    lg[5, 100:] = lg[5, 99]                            # ties spanning the boundary
+    lg[6] *= 1e30
+    lg[7] = np.arange(width, dtype=np.float32)         # strictly increasing
+    ends = np.array([5000, 5000, 4999, 5000, 3333, 5000, 64, 5000, 0, 1, 2047, 2049], np.int32)
+    return lg, ends
+
+
+@pytest.mark.parametrize("k", [1, 64, 2048, 4999, 6000])
+def test_topk_sets_match_oracle(k):
+    lg, ends = _topk_inputs(14)
+    want = oracle.topk(lg, ends, k)
+    got = dsa.topk(dev(lg), dev(ends), k).cpu().numpy()
+    assert_topk_sets(got, want, range(lg.shape[0]), f"k={k}")
+
+
+def test_topk_strided_rows():
+    lg, ends = _topk_inputs(15)
+    wide = np.full((lg.shape[0], lg.shape[1] + 120), 1e38, np.float32)
+    wide[:, :lg.shape[1]] = lg
+    want = oracle.topk(lg, ends, 100)
+    got = dsa.topk(dev(wide), dev(ends), 100, width=lg.shape[1]).cpu().numpy()
+    assert_topk_sets(got, want, range(lg.shape[0]))
