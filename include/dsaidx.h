@@ -188,9 +188,12 @@ size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k);
  *  indices  device, int32 [rows, >= k], row stride >= k: the positions of the k largest
  *           logits (ties to the lower position; -0 equals +0); the order within a row is
  *           unspecified; if fewer than k positions exist, all of them and -1 after.
- *  workspace  device scratch of at least dsaidx_topk_workspace_bytes bytes (may be NULL
- *           when that is 0).
- *  Errors: k < 1, rows < 0 or width < 0 give DSAIDX_EINVAL. NaN logits are unsupported.
+ *  workspace  device scratch of at least dsaidx_topk_workspace_bytes bytes, 256-byte
+ *           aligned, zero-filled before its first use; every call returns its histograms
+ *           and counters to zero, so it stays ready for the next call. Calls that share a
+ *           workspace must be ordered (one stream).
+ *  Errors: k < 1, rows < 0 or width < 0 give DSAIDX_EINVAL; a missing or short workspace
+ *  gives DSAIDX_EINVAL. NaN logits are unsupported.
  */
 dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int64_t logits_row_stride, const int32_t *row_ends, int32_t k,

@@ -34,6 +34,8 @@ def common_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
             "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix results land in VGPRs, read directly by the epilogue
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

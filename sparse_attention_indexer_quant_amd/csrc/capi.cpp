@@ -144,8 +144,7 @@ dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, i
     if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS ||
         logits_row_stride < max_blocks * DSAIDX_PAGE_TOKENS || !aligned(logits, 4))
         return DSAIDX_ELAYOUT;
-    const int pages_per_wg = fmt == DSAIDX_MXFP4 ? 16 : 8;
-    const int64_t chunks = (max_blocks + pages_per_wg - 1) / pages_per_wg;
+    const int64_t chunks = (max_blocks + 7) / 8;  // at least 2 pages per wavefront, 4 wavefronts
     if (chunks * num_requests > kMaxGrid) return DSAIDX_EUNSUPPORTED;
     dsaidx::ScoreArgs a{fmt,         q,          q_row_stride, heads,         w,
                         w_row_stride, cache,     num_pages,    page_stride,   block_table,
@@ -163,8 +162,8 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
                           int32_t *indices, int64_t indices_row_stride, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    if (rows < 0 || rows > kMaxGrid || width < 0 || width > INT32_MAX || k < 1)
-        return DSAIDX_EINVAL;
+    if (rows < 0 || width < 0 || width > INT32_MAX || k < 1) return DSAIDX_EINVAL;
+    if (rows * ((width + 4095) / 4096 + 1) > kMaxGrid) return DSAIDX_EUNSUPPORTED;
     if (rows == 0) return DSAIDX_OK;
     if (!row_ends || !indices || (width > 0 && !logits)) return DSAIDX_EINVAL;
     if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||
@@ -172,6 +171,7 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
         return DSAIDX_ELAYOUT;
     const size_t need = dsaidx::topk_workspace_bytes(rows, width, k);
     if (workspace_bytes < need || (need > 0 && !workspace)) return DSAIDX_EINVAL;
+    if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
     return hip_status(dsaidx::launch_topk(logits, rows, width, logits_row_stride, row_ends, k,
                                           indices, indices_row_stride, workspace,
                                           workspace_bytes, as_stream(stream)));

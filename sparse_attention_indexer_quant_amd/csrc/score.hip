@@ -13,8 +13,8 @@
 // B = 128 x 16 key tokens. Operand lane l holds row/column (l % 16) and the 32-value K block
 // (l / 16) -- exactly one MX block, so each lane's UE8M0 byte is its block scale. D lane l
 // holds heads 4 * (l / 16) + i, i < 4, of token (l % 16). ReLU and the head weight are
-// applied per lane, the head sum finishes with two cross-lane adds, and lane l ends up with
-// the logit of token l of the page, so each row's 64 logits go out as one 256-byte store.
+// applied per lane, the head sum finishes with three cross-row swaps, and lane l ends up
+// with the logit of token l of the page, so each row's 64 logits go out as one 256-B store.
 //
 // FP8 keys take another route: the scaled MFMA sums each 32-value FP8 block with only about
 // 13 bits below the block's largest product (448^2 + 1 comes out as 448^2), which cannot hold
@@ -23,9 +23,9 @@
 // byte permute) and contracts on v_mfma_f32_16x16x32_bf16, whose sums kept every probed case
 // exact. MXFP4 products span at most 2^7 (0.25 .. 36), so the FP4 MFMA is exact as it is.
 //
-// Work split: one workgroup of 4 wavefronts covers 4 * PPW consecutive pages of one request;
-// each wavefront loads its PPW pages into registers first (all of them in flight at once),
-// then runs the rows of the request over them in groups of RG rows.
+// Work split: a workgroup's 4 wavefronts each stream a run of consecutive pages of one
+// request through a ring of page buffers, for all rows of the request (in groups of RG
+// rows held in registers).
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,103 +82,90 @@ __device__ __forceinline__ v4f mfma_bf16_head(const uint4 qa[4], const uint4 kb[
     return c;
 }
 
-__device__ __forceinline__ float relu_dot4(const v4f &c, const float *w, float acc) {
-    acc = fmaf(w[0], fmaxf(c[0], 0.f), acc);
-    acc = fmaf(w[1], fmaxf(c[1], 0.f), acc);
-    acc = fmaf(w[2], fmaxf(c[2], 0.f), acc);
-    acc = fmaf(w[3], fmaxf(c[3], 0.f), acc);
+// max(0, x) on the bit pattern: non-negative floats compare as non-negative integers, and
+// negative floats (and -0) have the sign bit set, so an integer max with 0 returns +0 for
+// them. One integer max, and no NaN canonicalization.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// acc + sum_i w_i * max(0, c_i) for the lane's 4 heads; w holds 4 BF16 weights.
+__device__ __forceinline__ float relu_dot4(const v4f &c, const uint2 &w, float acc) {
+    acc = fmaf(bf16_lo(w.x), relu(c[0]), acc);
+    acc = fmaf(bf16_hi(w.x), relu(c[1]), acc);
+    acc = fmaf(bf16_lo(w.y), relu(c[2]), acc);
+    acc = fmaf(bf16_hi(w.y), relu(c[3]), acc);
     return acc;
 }
 
-// Sum the four lane groups (l / 16) of each tile's partials and leave tile t's token n in
-// lane 16 t + n.
-__device__ __forceinline__ float head_sum_to_token(float p0, float p1, float p2, float p3, int grp) {
-    p0 += __shfl_xor(p0, 16);
-    p1 += __shfl_xor(p1, 16);
-    p2 += __shfl_xor(p2, 16);
-    p3 += __shfl_xor(p3, 16);
-    p0 += __shfl_xor(p0, 32);
-    p1 += __shfl_xor(p1, 32);
-    p2 += __shfl_xor(p2, 32);
-    p3 += __shfl_xor(p3, 32);
-    return grp == 0 ? p0 : grp == 1 ? p1 : grp == 2 ? p2 : p3;
+// Head sum across the four lane groups (rows of 16 lanes) for the page's four token tiles,
+// leaving tile t's token n in lane 16 t + n; p_t holds each lane's partial for tile t.
+// A reduce-scatter on the cross-row swap instructions: swapping halves pairs tiles (0, 2)
+// and (1, 3) so the lower half keeps tiles 0 / 1 and the upper half tiles 2 / 3, then
+// swapping odd and even rows finishes each tile in its own row. Three swaps, three adds.
+__device__ __forceinline__ float head_sum_to_token(float p0, float p1, float p2, float p3) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+    const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows 0,1: tile 0; rows 2,3: tile 2
+    const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows 0,1: tile 1; rows 2,3: tile 3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int FMT, int H, int RG, int PPW>
-__global__ __launch_bounds__(256) void score_paged_kernel(
-    const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
-    int64_t w_row_stride, const uint8_t *__restrict__ cache, int64_t num_pages,
-    int64_t page_stride, const int32_t *__restrict__ block_table, int64_t max_blocks,
-    int64_t chunks, const int32_t *__restrict__ query_starts,
-    const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
-    float *__restrict__ logits, int64_t logits_row_stride) {
-    constexpr int HT = H / 16;  // 16-head tiles
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int l16 = lane & 15, grp = lane >> 4;
-    const int64_t req = blockIdx.x / chunks;
-    const int64_t chunk = blockIdx.x % chunks;
-    const int64_t blk0 = (chunk * kWaves + wave) * PPW;
-    const int64_t width = max_blocks * kPageTokens;
+// One page of keys held in registers: per lane, tile t (tokens 16t .. 16t+15) contributes
+// its token (l % 16), 32-value block (l / 16): 16 B for MXFP4 (plus that block's UE8M0 byte),
+// 32 B for FP8 (plus the token's FP32 scale).
+template <int FMT>
+struct PageRegs {
+    uint4 kp[4][FMT == kFmtMxfp4 ? 1 : 2];
+    uint32_t ks[4];
+};
 
-    int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
-    if (r0 < 0) return;
-    if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
-    if (r1 > num_rows) r1 = num_rows;
-    const int nrows = (int)(r1 - r0);
-    if (nrows <= 0) return;
-
-    // Keys this request needs: the largest bound over its rows.
-    int kmax = lane < nrows ? row_ends[r0 + lane] : 0;
-    for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, __shfl_xor(kmax, m));
-    kmax = __builtin_amdgcn_readfirstlane(kmax);
-    const int64_t kext = kmax < width ? kmax : width;
-    if (blk0 * kPageTokens >= kext) return;
-
-    // ---- stream this wavefront's pages into registers ----
-    bool valid[PPW];
-    uint4 kp[PPW][4][FMT == kFmtMxfp4 ? 1 : 2];
-    uint32_t ks[PPW][4];  // MXFP4: UE8M0 byte of (token, block); FP8: FP32 scale bits of token
+// Loads one page section into registers. The caller always issues the loads (an
+// out-of-range page reads a valid stand-in page instead and is not scored), so the
+// instruction stream has no conditional loads and every wait can count exactly.
+// Per-lane offsets are unsigned 32-bit so every load can address as (uniform section base in
+// scalar registers) + (lane offset in one vector register).
+template <int FMT>
+__device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec, uint32_t l16,
+                                          uint32_t grp) {
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-        const int64_t blk = blk0 + p;
-        int page = -1;
-        if (blk * kPageTokens < kext)
-            page = __builtin_amdgcn_readfirstlane(block_table[req * max_blocks + blk]);
-        valid[p] = page >= 0 && page < num_pages;
-        if (valid[p]) {
-            const uint8_t *sec = cache + (int64_t)page * page_stride;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int tok = t * 16 + l16;
-                if constexpr (FMT == kFmtMxfp4) {
-                    kp[p][t][0] = *reinterpret_cast<const uint4 *>(sec + tok * 64 + grp * 16);
-                    ks[p][t] = *reinterpret_cast<const uint32_t *>(sec + 4096 + tok * 4) >> (8 * grp);
-                } else {
-                    const uint4 *src = reinterpret_cast<const uint4 *>(sec + tok * 128 + grp * 32);
-                    kp[p][t][0] = src[0];
-                    kp[p][t][1] = src[1];
-                    ks[p][t] = *reinterpret_cast<const uint32_t *>(sec + 8192 + tok * 4);
-                }
-            }
+    for (uint32_t t = 0; t < 4; ++t) {
+        const uint32_t tok = t * 16u + l16;
+        if constexpr (FMT == kFmtMxfp4) {
+            pg.kp[t][0] = *reinterpret_cast<const uint4 *>(sec + (tok * 64u + grp * 16u));
+            // the token's 4 scale bytes, kept raw: touching a loaded value here would make
+            // the wavefront wait for this load (and every earlier one) before it can go on
+            pg.ks[t] = *reinterpret_cast<const uint32_t *>(sec + (4096u + tok * 4u));
+        } else {
+            const uint4 *src = reinterpret_cast<const uint4 *>(sec + (tok * 128u + grp * 32u));
+            pg.kp[t][0] = src[0];
+            pg.kp[t][1] = src[1];
+            pg.ks[t] = *reinterpret_cast<const uint32_t *>(sec + (8192u + tok * 4u));
         }
     }
+}
 
-    for (int rg = 0; rg < nrows; rg += RG) {
-        // ---- query operands and head weights of RG rows ----
-        uint4 qa[RG][HT][FMT == kFmtMxfp4 ? 1 : 4];
-        int qs[RG][HT];
-        float wt[RG][HT][4];
-        int rend[RG];
+// Query operands, head weights and key bounds of one group of RG rows.
+template <int FMT, int H, int RG>
+struct RowGroup {
+    static constexpr int HT = H / 16;
+    uint4 qa[RG][HT][FMT == kFmtMxfp4 ? 1 : 4];
+    int qs[RG][HT];
+    uint2 wt[RG][HT];  // 4 BF16 head weights, widened at use
+    int rend[RG];
+
+    __device__ __forceinline__ void load(const uint8_t *q, int64_t q_row_stride, const uint16_t *w,
+                                         int64_t w_row_stride, const int32_t *row_ends,
+                                         int64_t first, int64_t last, int64_t width, int l16,
+                                         int grp) {
 #pragma unroll
         for (int j = 0; j < RG; ++j) {
-            const int64_t row = r0 + rg + j;
-            const bool active = rg + j < nrows;
+            const int64_t row = first + j;
+            const bool active = row < last;
             int e = active ? row_ends[row] : 0;
             e = __builtin_amdgcn_readfirstlane(e);
             rend[j] = (int64_t)e < width ? e : (int)width;
-            const uint8_t *qrow = q + (active ? row : r0) * q_row_stride;
-            const uint16_t *wrow = w + (active ? row : r0) * w_row_stride;
+            const uint8_t *qrow = q + (active ? row : first) * q_row_stride;
+            const uint16_t *wrow = w + (active ? row : first) * w_row_stride;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const int head = ht * 16 + l16;
@@ -190,63 +177,180 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                     e4m3x32_to_bf16(src[0], src[1], qa[j][ht]);
                     qs[j][ht] = 0;
                 }
-                const uint2 wb = *reinterpret_cast<const uint2 *>(wrow + ht * 16 + grp * 4);
-                wt[j][ht][0] = bf16_lo(wb.x);
-                wt[j][ht][1] = bf16_hi(wb.x);
-                wt[j][ht][2] = bf16_lo(wb.y);
-                wt[j][ht][3] = bf16_hi(wb.y);
+                wt[j][ht] = *reinterpret_cast<const uint2 *>(wrow + ht * 16 + grp * 4);
             }
         }
+    }
 
+    // Logits of one page for the group's rows (rows past `count` are skipped). Each tile's
+    // RG x HT contractions are issued back to back into separate results before any is read,
+    // so the matrix unit pipelines them instead of waiting on each result in turn.
+    __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int64_t kbase, int count,
+                                          float *logits, int64_t first_row, int64_t logits_row_stride,
+                                          int lane, int grp) const {
+        float part[RG][4];
 #pragma unroll
-        for (int p = 0; p < PPW; ++p) {
-            if (!valid[p]) continue;
-            const int64_t kbase = (blk0 + p) * kPageTokens;
-            float part[RG][4];
+        for (int t = 0; t < 4; ++t) {
+            uint4 kb[FMT == kFmtMxfp4 ? 1 : 4];  // FP8: this tile's keys widened to BF16
+            if constexpr (FMT == kFmtFp8) e4m3x32_to_bf16(pg.kp[t][0], pg.kp[t][1], kb);
+            v4f c[RG][HT];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint4 kb[FMT == kFmtMxfp4 ? 1 : 4];  // FP8: this tile's keys widened to BF16
-                if constexpr (FMT == kFmtFp8) e4m3x32_to_bf16(kp[p][t][0], kp[p][t][1], kb);
+            for (int j = 0; j < RG; ++j) {
 #pragma unroll
-                for (int j = 0; j < RG; ++j) {
-                    float acc = 0.f;
-                    if (rg + j < nrows && kbase < rend[j]) {
-#pragma unroll
-                        for (int ht = 0; ht < HT; ++ht) {
-                            v4f c;
-                            if constexpr (FMT == kFmtMxfp4)
-                                c = mfma_fp4(qa[j][ht][0], kp[p][t][0], qs[j][ht], (int)ks[p][t]);
-                            else
-                                c = mfma_bf16_head(qa[j][ht], kb);
-                            acc = relu_dot4(c, wt[j][ht], acc);
-                        }
-                        if constexpr (FMT == kFmtFp8) acc *= __uint_as_float(ks[p][t]);  // s_k > 0
-                    }
-                    part[j][t] = acc;
+                for (int ht = 0; ht < HT; ++ht) {
+                    if constexpr (FMT == kFmtMxfp4)
+                        c[j][ht] = mfma_fp4(qa[j][ht][0], pg.kp[t][0], qs[j][ht],
+                                            (int)(pg.ks[t] >> (8 * grp)));
+                    else
+                        c[j][ht] = mfma_bf16_head(qa[j][ht], kb);
                 }
             }
 #pragma unroll
             for (int j = 0; j < RG; ++j) {
-                if (rg + j >= nrows || kbase >= rend[j]) continue;
-                const float out = head_sum_to_token(part[j][0], part[j][1], part[j][2], part[j][3], grp);
-                const int64_t key = kbase + lane;
-                if (key < rend[j]) logits[(r0 + rg + j) * logits_row_stride + key] = out;
+                float acc = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) acc = relu_dot4(c[j][ht], wt[j][ht], acc);
+                if constexpr (FMT == kFmtFp8) acc *= __uint_as_float(pg.ks[t]);  // s_k > 0
+                part[j][t] = acc;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RG; ++j) {
+            if (j >= count || kbase >= rend[j]) continue;
+            const float out = head_sum_to_token(part[j][0], part[j][1], part[j][2], part[j][3]);
+            const int64_t key = kbase + lane;
+            if (key < rend[j]) logits[(first_row + j) * logits_row_stride + key] = out;
+        }
+    }
+};
+
+// Grid: requests x chunks; a workgroup's 4 wavefronts take consecutive runs of PW pages of
+// the request. Each wavefront streams its run through a ring of NB page buffers: the next
+// NB - 1 pages' loads are in flight while one page is scored. Every prefetch is issued
+// unconditionally (pages past the run read a stand-in page and are not scored), so the
+// loop carries the same loads across its back edge on every path and the hardware wait
+// counts stay exact; conditional prefetches made the compiler wait for all loads there.
+template <int FMT, int H, int RG, int NB>
+__global__ __launch_bounds__(256) void score_paged_kernel(
+    const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
+    int64_t w_row_stride, const uint8_t *__restrict__ cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *__restrict__ block_table, int64_t max_blocks,
+    int64_t chunks, int pages_per_wave, const int32_t *__restrict__ query_starts,
+    const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
+    float *__restrict__ logits, int64_t logits_row_stride) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int64_t req = blockIdx.x / chunks;
+    const int64_t chunk = blockIdx.x % chunks;
+    const int64_t width = max_blocks * kPageTokens;
+    const int PW = pages_per_wave;
+    const int64_t blk_begin = (chunk * kWaves + wave) * (int64_t)PW;
+    if (blk_begin >= max_blocks) return;
+    // This wavefront's slice of the block table, one entry per lane, loaded before the row
+    // bounds are known (every entry below max_blocks is in bounds).
+    const int32_t *bt = block_table + req * max_blocks;
+    const int bt_lane = lane < PW && blk_begin + lane < max_blocks ? bt[blk_begin + lane] : -1;
+
+    int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
+    if (r0 < 0) return;
+    if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
+    if (r1 > num_rows) r1 = num_rows;
+    const int nrows = (int)(r1 - r0);
+    if (nrows <= 0) return;
+
+    // Query operands of the first row group, in flight together with the row bounds.
+    const int ngroups = (nrows + RG - 1) / RG;
+    RowGroup<FMT, H, RG> rows;
+    rows.load(q, q_row_stride, w, w_row_stride, row_ends, r0, r1, width, l16, grp);
+
+    // Keys this request needs: the largest bound over its rows.
+    int kmax = lane < nrows ? row_ends[r0 + lane] : 0;
+    for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, __shfl_xor(kmax, m));
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    const int64_t kext = kmax < width ? kmax : width;
+    const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
+    const int64_t blk_end = blk_begin + PW < nblk ? blk_begin + PW : nblk;
+    if (blk_begin >= blk_end) return;
+
+    // A page outside [0, num_pages) or past the run's end is not scored; its loads read the
+    // run's first valid page instead, so every prefetch is issued unconditionally.
+    auto page_at = [&](int p) -> int {  // uniform; -1 when not to be scored
+        if (blk_begin + p >= blk_end) return -1;
+        const int pg = __builtin_amdgcn_readlane(bt_lane, p);
+        return pg >= 0 && pg < num_pages ? pg : -1;
+    };
+    int fallback = -1;
+    for (int p = 0; p < PW && fallback < 0; ++p) fallback = page_at(p);
+    if (fallback < 0) return;  // nothing valid to score
+    auto section = [&](int p) {
+        const int pg = p < PW ? page_at(p) : -1;
+        return cache + (int64_t)(pg >= 0 ? pg : fallback) * page_stride;
+    };
+    const int run = (int)(blk_end - blk_begin);
+
+    // Requests with more rows than one register group stream their pages once per group
+    // (the second and later passes mostly hit the L2).
+    for (int g = 0; g < ngroups; ++g) {
+        const int64_t first = r0 + (int64_t)g * RG;
+        if (g > 0) rows.load(q, q_row_stride, w, w_row_stride, row_ends, first, r1, width, l16, grp);
+        const int count = (int)(r1 - first);
+        PageRegs<FMT> buf[NB];
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p), l16, grp);
+        for (int base = 0; base < run; base += NB) {
+#pragma unroll
+            for (int slot = 0; slot < NB; ++slot) {
+                // keep the ring as written: without this compiler-only fence (it emits
+                // nothing) later pages' loads get hoisted, which costs the registers a second
+                // wavefront per SIMD needs to overlap one wavefront's math with another's loads
+                asm volatile("" ::: "memory");
+                const int p = base + slot;
+                load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1), l16, grp);
+                if (p < run && page_at(p) >= 0)
+                    rows.score(buf[slot], (blk_begin + p) * kPageTokens, count, logits, first,
+                               logits_row_stride, lane, grp);
             }
         }
     }
 }
 
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Pages per wavefront: enough work to stream through the ring, with about one round of
+// eight wavefronts per compute unit over the whole (request x block) space (multiple of 4).
+int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
+    const int64_t target_waves = (int64_t)device_cus() * 8;
+    int64_t ppw = (num_requests * max_blocks + target_waves - 1) / target_waves;
+    ppw = (ppw + 3) / 4 * 4;
+    return (int)(ppw < 4 ? 4 : (ppw > 16 ? 16 : ppw));
+}
+
 template <int FMT, int H, int RG>
 static hipError_t launch_score_rg(const ScoreArgs &a, hipStream_t stream) {
-    constexpr int PPW = FMT == kFmtMxfp4 ? 4 : 2;
-    const int64_t pages_per_wg = (int64_t)kWaves * PPW;
+    const int ppw = score_pages_per_wave(a.num_requests, a.max_blocks);
+    const int64_t pages_per_wg = (int64_t)kWaves * ppw;
     const int64_t chunks = (a.max_blocks + pages_per_wg - 1) / pages_per_wg;
     const dim3 grid((unsigned)(chunks * a.num_requests)), block(256);
-    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, PPW>), grid, block, 0, stream,
+    // page buffers per wavefront: 4 for MXFP4 with up to 2 rows per group, else 2 (FP8 pages
+    // and 4-row query groups take the registers a deeper ring would need)
+    constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 4 : 2;
+    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB>), grid, block, 0, stream,
                        static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride,
                        static_cast<const uint8_t *>(a.cache), a.num_pages, a.page_stride,
-                       a.block_table, a.max_blocks, chunks, a.query_starts, a.row_ends,
+                       a.block_table, a.max_blocks, chunks, ppw, a.query_starts, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride);
     return hipGetLastError();
 }

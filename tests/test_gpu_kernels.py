@@ -274,3 +274,20 @@ def test_topk_strided_rows():
     want = oracle.topk(lg, ends, 100)
     got = dsa.topk(dev(wide), dev(ends), 100, width=lg.shape[1]).cpu().numpy()
     assert_topk_sets(got, want, range(lg.shape[0]))
+
+
+def test_topk_candidate_overflow_and_workspace_reuse():
+    # A threshold bin holding more keys than the candidate list keeps (20000 equal logits)
+    # selects from the row itself; one workspace serves several calls in a row, since every
+    # call returns its histograms and counters to zero.
+    rng = np.random.default_rng(16)
+    lg = np.full((3, 20000), 0.5, np.float32)
+    lg[0, 7777] = 2.0
+    lg[1] = rng.standard_normal(20000).astype(np.float32)
+    lg[2, ::3] = 0.25
+    ends = np.array([20000, 20000, 19999], np.int32)
+    ws = torch.zeros(dsa.topk_workspace_bytes(3, 20000, 100), dtype=torch.uint8, device="cuda")
+    for k in (100, 5000, 1, 100, 2047):
+        want = oracle.topk(lg, ends, k)
+        got = dsa.topk(dev(lg), dev(ends), k, workspace=ws).cpu().numpy()
+        assert_topk_sets(got, want, range(3), f"k={k}")
