@@ -112,7 +112,7 @@ class Setup:
         self.logits = torch.empty((wl.num_rows, wl.width), dtype=torch.float32, device=dev)
         self.idx = torch.empty((wl.num_rows, wl.topk), dtype=torch.int32, device=dev)
         wsb = dsa.topk_workspace_bytes(wl.num_rows, wl.width, wl.topk)
-        self.ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)  # zero between calls
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
         self.quant = Prepared(lib.dsaidx_quantize_queries, fmt, self.q.data_ptr(), wl.num_rows,
                               wl.heads, self.q.stride(0), self.q.stride(1), self.wv.data_ptr(),

@@ -56,6 +56,7 @@ typedef enum {
 #define DSAIDX_MXFP4_SECTION_BYTES 4352 /* [64 x 64 B E2M1 | 64 x 4 B UE8M0] */
 #define DSAIDX_FP8_SECTION_BYTES 8448   /* [64 x 128 B E4M3 | 64 x 4 B FP32 scale] */
 #define DSAIDX_MAX_QUERY_LEN 16        /* query rows per request that score_paged accepts */
+#define DSAIDX_TOPK_MAX_WIDTH 33554432 /* 2^25: keys per row that topk accepts */
 
 /* Text of a status code (static storage; never NULL). */
 const char *dsaidx_status_string(int status);
@@ -189,11 +190,12 @@ size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k);
  *           logits (ties to the lower position; -0 equals +0); the order within a row is
  *           unspecified; if fewer than k positions exist, all of them and -1 after.
  *  workspace  device scratch of at least dsaidx_topk_workspace_bytes bytes, 256-byte
- *           aligned, zero-filled before its first use; every call returns its histograms
- *           and counters to zero, so it stays ready for the next call. Calls that share a
- *           workspace must be ordered (one stream).
- *  Errors: k < 1, rows < 0 or width < 0 give DSAIDX_EINVAL; a missing or short workspace
- *  gives DSAIDX_EINVAL. NaN logits are unsupported.
+ *           aligned, owned by the caller; no initialisation is needed (each call writes
+ *           every field before reading it). Calls that share a workspace must be ordered
+ *           (one stream).
+ *  Errors: k < 1, rows < 0 or width < 0 give DSAIDX_EINVAL; width above
+ *  DSAIDX_TOPK_MAX_WIDTH gives DSAIDX_EUNSUPPORTED; a missing or short workspace gives
+ *  DSAIDX_EINVAL. NaN logits are unsupported.
  */
 dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int64_t logits_row_stride, const int32_t *row_ends, int32_t k,

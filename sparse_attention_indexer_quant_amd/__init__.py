@@ -221,8 +221,7 @@ def topk(logits, row_ends, k, width=None, out=None, workspace=None):
     _dev(out, "out", torch.int32)
     need = topk_workspace_bytes(rows, width, k)
     if workspace is None and need > 0:
-        # zero-filled before first use; each call returns its histograms and counters to zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=logits.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     st = library().dsaidx_topk(
         logits.data_ptr(), rows, width, logits.stride(0), row_ends.data_ptr(), int(k),
         out.data_ptr(), out.stride(0), None if workspace is None else workspace.data_ptr(),

@@ -42,6 +42,7 @@ hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 dsaidx_status hip_status(hipError_t e) { return e == hipSuccess ? DSAIDX_OK : DSAIDX_EHIP; }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+static_assert(dsaidx::kTopkMaxWidth == DSAIDX_TOPK_MAX_WIDTH, "one top-k width limit");
 
 }  // namespace
 
@@ -133,7 +134,7 @@ dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, i
         return DSAIDX_EINVAL;
     if (!valid_heads(heads) || max_query_len < 1 || max_query_len > DSAIDX_MAX_QUERY_LEN)
         return DSAIDX_EUNSUPPORTED;
-    if (num_rows == 0 || num_requests == 0 || max_blocks == 0) return DSAIDX_OK;
+    if (num_rows == 0 || num_requests == 0 || max_blocks == 0 || num_pages == 0) return DSAIDX_OK;
     if (!q || !w || !cache || !block_table || !query_starts || !row_ends || !logits)
         return DSAIDX_EINVAL;
     if (!aligned(q, 16) || q_row_stride % 16 || q_row_stride < dsaidx_query_row_bytes(fmt, heads))
@@ -154,7 +155,7 @@ dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, i
 }
 
 size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k) {
-    if (rows < 0 || width < 0 || k < 1) return 0;
+    if (rows < 0 || width < 0 || width > DSAIDX_TOPK_MAX_WIDTH || k < 1) return 0;
     return dsaidx::topk_workspace_bytes(rows, width, k);
 }
 
@@ -162,8 +163,9 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
                           int32_t *indices, int64_t indices_row_stride, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    if (rows < 0 || width < 0 || width > INT32_MAX || k < 1) return DSAIDX_EINVAL;
-    if (rows * ((width + 4095) / 4096 + 1) > kMaxGrid) return DSAIDX_EUNSUPPORTED;
+    if (rows < 0 || width < 0 || k < 1) return DSAIDX_EINVAL;
+    if (width > DSAIDX_TOPK_MAX_WIDTH || rows * ((width + 4095) / 4096 + 1) > kMaxGrid)
+        return DSAIDX_EUNSUPPORTED;
     if (rows == 0) return DSAIDX_OK;
     if (!row_ends || !indices || (width > 0 && !logits)) return DSAIDX_EINVAL;
     if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||

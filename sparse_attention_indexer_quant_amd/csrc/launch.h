@@ -7,6 +7,8 @@
 
 namespace dsaidx {
 
+constexpr int64_t kTopkMaxWidth = int64_t(1) << 25;  // keys per row that topk accepts
+
 hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,
                                    int64_t q_row_stride, int64_t q_head_stride, const void *wv,
                                    int64_t wv_row_stride, void *q_out, int64_t q_out_row_stride,

@@ -35,6 +35,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
+constexpr int kMaxPagesPerWave = 16;
 
 __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, int sa, int sb) {
     const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -119,27 +120,35 @@ struct PageRegs {
     uint32_t ks[4];
 };
 
-// Loads one page section into registers. The caller always issues the loads (an
-// out-of-range page reads a valid stand-in page instead and is not scored), so the
-// instruction stream has no conditional loads and every wait can count exactly.
-// Per-lane offsets are unsigned 32-bit so every load can address as (uniform section base in
-// scalar registers) + (lane offset in one vector register).
+// Loads one page section into registers. The caller always issues the loads (a page that
+// is not scored reads a valid stand-in page instead), so the instruction stream has no
+// conditional loads and every wait can count exactly. Each load addresses as (uniform base
+// in scalar registers: section + tile offset) + (the lane's unsigned 32-bit offset), which
+// keeps the address arithmetic off the vector ALUs.
 template <int FMT>
-__device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec, uint32_t l16,
-                                          uint32_t grp) {
+struct LaneOffsets {
+    uint32_t key;    // the lane's token row (l % 16) and K block (l / 16) within a tile
+    uint32_t scale;  // the lane's scale byte (MXFP4) or its token's FP32 scale (FP8)
+    __device__ __forceinline__ LaneOffsets(uint32_t l16, uint32_t grp)
+        : key(FMT == kFmtMxfp4 ? l16 * 64u + grp * 16u : l16 * 128u + grp * 32u),
+          scale(FMT == kFmtMxfp4 ? 4096u + l16 * 4u + grp : 8192u + l16 * 4u) {}
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec,
+                                          const LaneOffsets<FMT> &off) {
 #pragma unroll
     for (uint32_t t = 0; t < 4; ++t) {
-        const uint32_t tok = t * 16u + l16;
         if constexpr (FMT == kFmtMxfp4) {
-            pg.kp[t][0] = *reinterpret_cast<const uint4 *>(sec + (tok * 64u + grp * 16u));
-            // the token's 4 scale bytes, kept raw: touching a loaded value here would make
-            // the wavefront wait for this load (and every earlier one) before it can go on
-            pg.ks[t] = *reinterpret_cast<const uint32_t *>(sec + (4096u + tok * 4u));
+            const uint8_t *tile = sec + t * 1024u;         // 16 tokens x 64 B
+            pg.kp[t][0] = *reinterpret_cast<const uint4 *>(tile + off.key);
+            // the lane's own UE8M0 byte (its token, its 32-value block), used as loaded
+            pg.ks[t] = (sec + t * 64u)[off.scale];
         } else {
-            const uint4 *src = reinterpret_cast<const uint4 *>(sec + (tok * 128u + grp * 32u));
-            pg.kp[t][0] = src[0];
-            pg.kp[t][1] = src[1];
-            pg.ks[t] = *reinterpret_cast<const uint32_t *>(sec + (8192u + tok * 4u));
+            const uint8_t *tile = sec + t * 2048u;         // 16 tokens x 128 B
+            pg.kp[t][0] = *reinterpret_cast<const uint4 *>(tile + off.key);
+            pg.kp[t][1] = *reinterpret_cast<const uint4 *>(tile + off.key + 16u);
+            pg.ks[t] = *reinterpret_cast<const uint32_t *>((sec + t * 64u) + off.scale);
         }
     }
 }
@@ -185,9 +194,9 @@ struct RowGroup {
     // Logits of one page for the group's rows (rows past `count` are skipped). Each tile's
     // RG x HT contractions are issued back to back into separate results before any is read,
     // so the matrix unit pipelines them instead of waiting on each result in turn.
-    __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int64_t kbase, int count,
-                                          float *logits, int64_t first_row, int64_t logits_row_stride,
-                                          int lane, int grp) const {
+    __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
+                                          float *logits, int64_t first_row,
+                                          int64_t logits_row_stride, int lane, int grp) const {
         float part[RG][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -199,8 +208,7 @@ struct RowGroup {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
                     if constexpr (FMT == kFmtMxfp4)
-                        c[j][ht] = mfma_fp4(qa[j][ht][0], pg.kp[t][0], qs[j][ht],
-                                            (int)(pg.ks[t] >> (8 * grp)));
+                        c[j][ht] = mfma_fp4(qa[j][ht][0], pg.kp[t][0], qs[j][ht], (int)pg.ks[t]);
                     else
                         c[j][ht] = mfma_bf16_head(qa[j][ht], kb);
                 }
@@ -218,8 +226,8 @@ struct RowGroup {
         for (int j = 0; j < RG; ++j) {
             if (j >= count || kbase >= rend[j]) continue;
             const float out = head_sum_to_token(part[j][0], part[j][1], part[j][2], part[j][3]);
-            const int64_t key = kbase + lane;
-            if (key < rend[j]) logits[(first_row + j) * logits_row_stride + key] = out;
+            float *row = logits + (first_row + j) * logits_row_stride + kbase;
+            if (kbase + lane < rend[j]) row[lane] = out;
         }
     }
 };
@@ -227,9 +235,10 @@ struct RowGroup {
 // Grid: requests x chunks; a workgroup's 4 wavefronts take consecutive runs of PW pages of
 // the request. Each wavefront streams its run through a ring of NB page buffers: the next
 // NB - 1 pages' loads are in flight while one page is scored. Every prefetch is issued
-// unconditionally (pages past the run read a stand-in page and are not scored), so the
-// loop carries the same loads across its back edge on every path and the hardware wait
-// counts stay exact; conditional prefetches made the compiler wait for all loads there.
+// unconditionally (a page that is not scored reads page 0 instead), so the loop carries the
+// same loads across its back edge on every path and the hardware wait counts stay exact;
+// conditional prefetches made the compiler wait for all loads there. The first NB - 1 loads
+// go out as soon as the block table slice arrives, while the row bounds are still in flight.
 template <int FMT, int H, int RG, int NB>
 __global__ __launch_bounds__(256) void score_paged_kernel(
     const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
@@ -239,7 +248,9 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
     float *__restrict__ logits, int64_t logits_row_stride) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // uniform across the wavefront; said explicitly so that all page and bound arithmetic
+    // below stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
     const int64_t req = blockIdx.x / chunks;
     const int64_t chunk = blockIdx.x % chunks;
@@ -247,12 +258,31 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const int PW = pages_per_wave;
     const int64_t blk_begin = (chunk * kWaves + wave) * (int64_t)PW;
     if (blk_begin >= max_blocks) return;
-    // This wavefront's slice of the block table, one entry per lane, loaded before the row
-    // bounds are known (every entry below max_blocks is in bounds).
+    // This wavefront's slice of the block table, one entry per lane (every entry below
+    // max_blocks is in bounds).
     const int32_t *bt = block_table + req * max_blocks;
     const int bt_lane = lane < PW && blk_begin + lane < max_blocks ? bt[blk_begin + lane] : -1;
-
     int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
+
+    // Table entry of run page p (uniform), or -1 if it names no page of the cache.
+    const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
+    auto table_page = [&](int p) -> int {
+        const int pg = __builtin_amdgcn_readlane(bt_lane, p);
+        return (uint32_t)pg < npages ? pg : -1;
+    };
+    // Section that run page p's loads read: the page itself, or page 0 as a stand-in for a
+    // page that is not scored (past `limit`, or not a page of the cache).
+    auto section = [&](int p, int limit) {
+        const int pg = p < limit ? table_page(p) : -1;
+        return cache + (int64_t)(pg >= 0 ? pg : 0) * page_stride;
+    };
+
+    const LaneOffsets<FMT> off(l16, grp);
+    PageRegs<FMT> buf[NB];
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
+    asm volatile("" ::: "memory");  // issue these before waiting on the row bounds
+
     if (r0 < 0) return;
     if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
     if (r1 > num_rows) r1 = num_rows;
@@ -272,32 +302,18 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
     const int64_t blk_end = blk_begin + PW < nblk ? blk_begin + PW : nblk;
     if (blk_begin >= blk_end) return;
-
-    // A page outside [0, num_pages) or past the run's end is not scored; its loads read the
-    // run's first valid page instead, so every prefetch is issued unconditionally.
-    auto page_at = [&](int p) -> int {  // uniform; -1 when not to be scored
-        if (blk_begin + p >= blk_end) return -1;
-        const int pg = __builtin_amdgcn_readlane(bt_lane, p);
-        return pg >= 0 && pg < num_pages ? pg : -1;
-    };
-    int fallback = -1;
-    for (int p = 0; p < PW && fallback < 0; ++p) fallback = page_at(p);
-    if (fallback < 0) return;  // nothing valid to score
-    auto section = [&](int p) {
-        const int pg = p < PW ? page_at(p) : -1;
-        return cache + (int64_t)(pg >= 0 ? pg : fallback) * page_stride;
-    };
     const int run = (int)(blk_end - blk_begin);
 
     // Requests with more rows than one register group stream their pages once per group
     // (the second and later passes mostly hit the L2).
     for (int g = 0; g < ngroups; ++g) {
         const int64_t first = r0 + (int64_t)g * RG;
-        if (g > 0) rows.load(q, q_row_stride, w, w_row_stride, row_ends, first, r1, width, l16, grp);
-        const int count = (int)(r1 - first);
-        PageRegs<FMT> buf[NB];
+        if (g > 0) {
+            rows.load(q, q_row_stride, w, w_row_stride, row_ends, first, r1, width, l16, grp);
 #pragma unroll
-        for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p), l16, grp);
+            for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, run), off);
+        }
+        const int count = (int)(r1 - first);
         for (int base = 0; base < run; base += NB) {
 #pragma unroll
             for (int slot = 0; slot < NB; ++slot) {
@@ -306,10 +322,10 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 // wavefront per SIMD needs to overlap one wavefront's math with another's loads
                 asm volatile("" ::: "memory");
                 const int p = base + slot;
-                load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1), l16, grp);
-                if (p < run && page_at(p) >= 0)
-                    rows.score(buf[slot], (blk_begin + p) * kPageTokens, count, logits, first,
-                               logits_row_stride, lane, grp);
+                load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
+                if (p < run && table_page(p) >= 0)
+                    rows.score(buf[slot], (int)((blk_begin + p) * kPageTokens), count, logits,
+                               first, logits_row_stride, lane, grp);
             }
         }
     }
@@ -334,7 +350,7 @@ int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
     const int64_t target_waves = (int64_t)device_cus() * 8;
     int64_t ppw = (num_requests * max_blocks + target_waves - 1) / target_waves;
     ppw = (ppw + 3) / 4 * 4;
-    return (int)(ppw < 4 ? 4 : (ppw > 16 ? 16 : ppw));
+    return (int)(ppw < 4 ? 4 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
 }
 
 template <int FMT, int H, int RG>

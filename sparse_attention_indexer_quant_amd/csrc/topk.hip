@@ -5,55 +5,63 @@
 // of [0, row_end) with ties going to the lower key position (-0 counts as +0); fewer than
 // k keys give all of them and -1 after. The order within a row is not specified.
 //
-// Logits map to order-preserving 32-bit keys u. Many workgroups share each row:
+// Logits map to order-preserving 32-bit keys u. Four kernels, which communicate only
+// through the workspace across kernel boundaries (handing work to a last-arriving workgroup
+// needs a device-scope fence per workgroup, an L2 write-back on every XCD, and atomics on a
+// row's shared counters serialize; both measured slower than the selection itself):
 //
-//   1. topk_hist: every workgroup histograms the top 12 bits of its segment of the row in
-//      LDS and stores it (16-bit counts) in the workspace. The last workgroup of the row to
-//      finish (an arrival counter) sums the row's segment histograms, finds the bin b that
-//      holds the k-th largest key and records how many keys lie above it. (Merging with
-//      global atomics instead costs one L2 atomic per non-zero bin per segment, which
-//      measured slower than the whole selection.)
-//   2. topk_collect: every workgroup writes the positions of its keys above bin b straight
-//      into the output (one atomic per 4096 keys) and appends the positions of keys inside
-//      bin b to the row's candidate list. The last workgroup to finish selects the missing
-//      `remaining` keys among the candidates: a radix select over the composite
-//      (low 20 key bits inverted, position), smallest first, which is unique per key, so
-//      exactly the keys with the largest values -- ties to the lower position -- are taken.
-//      If the bin overflows the candidate list it selects from the row itself instead.
+//   1. topk_hist (rows x segments): each workgroup histograms the top 12 key bits of its
+//      segment in LDS and stores the counts (16-bit) in the workspace. Rows with
+//      row_end <= k are written here directly.
+//   2. topk_threshold (one workgroup per row): sums the row's segment histograms, finds the
+//      bin b holding the k-th largest key, then counts each segment's keys above b and
+//      inside b and stores their exclusive prefix sums over the segments: every segment's
+//      first output slot and first candidate slot.
+//   3. topk_collect (rows x segments): writes the positions of keys above bin b to the
+//      output and the (key, position) pairs of keys inside bin b to the row's candidate
+//      list, at the offsets from step 2 plus an in-workgroup prefix sum -- no atomics, and
+//      the positions above b come out in ascending order.
+//   4. topk_select (one workgroup per row): loads the candidates into LDS as the composite
+//      (low 20 key bits inverted, position), unique per key, and radix-selects the
+//      `remaining` smallest, so exactly the keys with the largest values -- ties to the
+//      lower position -- are taken. A bin that overflowed the candidate list is selected
+//      from the row itself instead.
 //
 // Segments are 4096 keys, doubled (up to 32768) until rows x segments is at most 2048
-// workgroups. Rows with row_end <= k are written directly. The workspace's counters are
-// zero when a call starts and each call returns them to zero (histograms, candidate lists
-// and the per-row threshold fields are rewritten before every use).
+// workgroups and a row has at most 1024 segments (rows hold at most 2^25 keys). Every
+// workspace field is written before it is read within a call, so the workspace needs no
+// initialisation; calls sharing one must be ordered.
 #include "device_common.h"
 #include "launch.h"
 
 namespace dsaidx {
 
 constexpr int kTopkThreads = 256;
+constexpr int kRowThreads = 1024;        // threshold: one workgroup per row
 constexpr int kMinSegment = 4096;        // keys per workgroup (doubled for many rows)
 constexpr int kMaxSegment = 32768;       // 16-bit segment histogram counts stay exact
+constexpr int kMaxRowSegments = kTopkMaxWidth / kMaxSegment;
 constexpr int kMaxWorkgroups = 2048;
 constexpr int kBins = 4096;              // top 12 key bits
 constexpr int kBinShift = 20;
-constexpr int kCandCap = 8192;           // candidate positions kept per row
-constexpr int kSelectThreads = 256;
+constexpr int kCandCap = 8192;           // candidate (key, position) pairs kept per row
+constexpr int kSelectThreads = 512;
+constexpr int kRadixBits = 11;
+constexpr int kRadixBins = 1 << kRadixBits;
+static_assert(kMaxRowSegments <= kRowThreads, "one thread per segment in the offset scan");
 
 struct RowState {
     uint32_t bin;          // threshold bin
     int32_t above;         // keys above the threshold bin
     int32_t remaining;     // keys still to take from inside the bin
-    uint32_t arrive_hist;
-    uint32_t arrive_collect;
-    uint32_t n_above;      // positions written so far (collect)
-    uint32_t n_cand;       // candidates appended so far (collect)
-    uint32_t pad;
+    uint32_t n_cand;       // keys inside the bin
 };
 
 struct TopkWorkspace {
     RowState *state;
     uint16_t *seghist;  // [rows][nseg][kBins]
-    int32_t *cand;      // [rows][kCandCap]
+    uint2 *segoff;      // [rows][nseg]: first output slot, first candidate slot
+    uint2 *cand;        // [rows][kCandCap]: order key, position
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -61,7 +69,9 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 // Keys per segment for this call's shape (the same rule sizes the workspace).
 inline int64_t topk_segment(int64_t rows, int64_t width) {
     int64_t seg = kMinSegment;
-    while (seg < kMaxSegment && rows * ((width + seg - 1) / seg) > kMaxWorkgroups) seg *= 2;
+    while (seg < kMaxSegment && (rows * ((width + seg - 1) / seg) > kMaxWorkgroups ||
+                                 (width + seg - 1) / seg > kMaxRowSegments))
+        seg *= 2;
     return seg;
 }
 
@@ -74,7 +84,9 @@ __host__ __device__ inline TopkWorkspace carve(void *ws, int64_t rows, int64_t n
     p += align256(sizeof(RowState) * rows);
     w.seghist = reinterpret_cast<uint16_t *>(p);
     p += align256(sizeof(uint16_t) * kBins * nseg * rows);
-    w.cand = reinterpret_cast<int32_t *>(p);
+    w.segoff = reinterpret_cast<uint2 *>(p);
+    p += align256(sizeof(uint2) * nseg * rows);
+    w.cand = reinterpret_cast<uint2 *>(p);
     return w;
 }
 
@@ -84,12 +96,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t load_relaxed(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Inclusive prefix sum over a 256-lane workgroup; `partials` holds 4 ints.
-__device__ __forceinline__ int scan256(int v, int *partials) {
+// Inclusive prefix sum over an NT-lane workgroup; `partials` holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int scan_block(int v, int *partials) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -100,7 +109,7 @@ __device__ __forceinline__ int scan256(int v, int *partials) {
     __syncthreads();
     int before = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) before += w < wave ? partials[w] : 0;
+    for (int w = 0; w < NT / 64; ++w) before += w < wave ? partials[w] : 0;
     __syncthreads();
     return v + before;
 }
@@ -142,8 +151,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
     int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
     __shared__ uint32_t hist[kBins];
-    __shared__ int partials[4];
-    __shared__ int last;
     const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t n = row_bound(row_ends, row, width);
     if (n <= k) {
@@ -153,7 +160,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     const int64_t lo = seg * seg_len;
     if (lo >= n) return;  // only the segments that hold keys take part below
     const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
-    const uint32_t row_segments = (uint32_t)((n + seg_len - 1) / seg_len);
     const float *x = logits + row * logits_row_stride;
 
     for (int b = threadIdx.x; b < kBins; b += kTopkThreads) hist[b] = 0;
@@ -162,269 +168,355 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
         atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
     });
     __syncthreads();
-    // store this segment's histogram: lane t writes bins [16t, 16t+16) as 16-bit counts
-    uint16_t *rowhist = ws.seghist + row * nseg * kBins;
-    {
-        uint32_t c[8];
+    // lane t stores bins [16t, 16t+16) as 16-bit counts
+    uint32_t c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            c[j] = hist[16 * threadIdx.x + 2 * j] | (hist[16 * threadIdx.x + 2 * j + 1] << 16);
-        uint4 *dst = reinterpret_cast<uint4 *>(rowhist + seg * kBins + 16 * threadIdx.x);
-        dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
-        dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-    }
-    __threadfence();
-    __syncthreads();
-    RowState &st = ws.state[row];
-    if (threadIdx.x == 0) last = atomicAdd(&st.arrive_hist, 1u) == row_segments - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+    for (int j = 0; j < 8; ++j)
+        c[j] = hist[16 * threadIdx.x + 2 * j] | (hist[16 * threadIdx.x + 2 * j + 1] << 16);
+    uint4 *dst = reinterpret_cast<uint4 *>(ws.seghist + (row * nseg + seg) * kBins +
+                                           16 * threadIdx.x);
+    dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+    dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+}
 
-    // Last workgroup of the row: sum the segment histograms and find the bin holding the
-    // k-th largest key. Lane t owns the 16 bins of block 255 - t, walked from the top down.
-    constexpr int per = kBins / kTopkThreads;
-    static_assert(per == 16, "16 bins per lane");
-    uint32_t mine[per];
-#pragma unroll
-    for (int j = 0; j < per; ++j) mine[j] = 0;
-    const int block = kTopkThreads - 1 - threadIdx.x;
-    for (uint32_t sgi = 0; sgi < row_segments; ++sgi) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(rowhist + sgi * kBins + 16 * block);
-        const uint4 lo4 = src[0], hi4 = src[1];
-        const uint32_t w[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mine[15 - e] += (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+// One workgroup per row: the threshold bin and every segment's output offsets.
+__global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
+    const int32_t *__restrict__ row_ends, int64_t width, int k, TopkWorkspace ws, int64_t nseg,
+    int64_t seg_len) {
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t seg_above[kMaxRowSegments];
+    __shared__ int partials[kRowThreads / 64];
+    __shared__ uint32_t found_bin, found_count, top_bin;
+    __shared__ int found_above;
+    const int64_t row = blockIdx.x;
+    const int64_t n = row_bound(row_ends, row, width);
+    if (n <= k) return;
+    const int row_segments = (int)((n + seg_len - 1) / seg_len);
+    const uint16_t *rowhist = ws.seghist + row * nseg * kBins;
+    const int t = threadIdx.x;
+
+    // (a) Thread t sums bins [16 (t % 256), +16) over the segments s = t / 256 (mod 4),
+    // four segments' loads in flight at a time, then merges into the LDS histogram.
+    for (int b = t; b < kBins; b += kRowThreads) hist[b] = 0;
+    if (t == 0) {
+        found_bin = kBins;  // kept only if the counts do not reach k (they always do)
+        found_above = k;
+        found_count = 0;
+        top_bin = 0;
     }
+    {
+        const int blk = t & 255, sg0 = t >> 8;
+        uint32_t sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // bin pairs, 16 bits each
+        uint32_t hi16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int s = sg0;
+        for (; s + 12 < row_segments; s += 16) {
+            uint4 v[4][2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(rowhist + (int64_t)(s + 4 * u) * kBins + 16 * blk);
+                v[u][0] = src[0];
+                v[u][1] = src[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t w[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                                       v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sum[e] += w[e] & 0xFFFFu;
+                    hi16[e] += w[e] >> 16;
+                }
+            }
+        }
+        for (; s < row_segments; s += 4) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(rowhist + (int64_t)s * kBins + 16 * blk);
+            const uint4 a = src[0], b = src[1];
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sum[e] += w[e] & 0xFFFFu;
+                hi16[e] += w[e] >> 16;
+            }
+        }
+        __syncthreads();  // histogram cleared
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (sum[e]) atomicAdd(&hist[16 * blk + 2 * e], sum[e]);
+            if (hi16[e]) atomicAdd(&hist[16 * blk + 2 * e + 1], hi16[e]);
+        }
+    }
+    __syncthreads();
+
+    // (b) Thread t owns bins 4095 - 4t - j, j < 4 (descending): the bin holding the k-th
+    // largest key, the keys above it, and the highest non-empty bin.
+    uint32_t mine[4];
     int own = 0;
 #pragma unroll
-    for (int j = 0; j < per; ++j) own += (int)mine[j];
-    const int incl = scan256(own, partials);
+    for (int j = 0; j < 4; ++j) {
+        mine[j] = hist[kBins - 1 - 4 * t - j];
+        own += (int)mine[j];
+    }
+    if (own) {
+#pragma unroll
+        for (int j = 3; j >= 0; --j)
+            if (mine[j]) atomicMax(&top_bin, (uint32_t)(kBins - 1 - 4 * t - j));
+    }
+    const int incl = scan_block<kRowThreads>(own, partials);
     int before = incl - own;
 #pragma unroll
-    for (int j = 0; j < per; ++j) {
+    for (int j = 0; j < 4; ++j) {
         const int c = (int)mine[j];
         if (before < k && before + c >= k) {
-            st.bin = (uint32_t)(kBins - 1 - (threadIdx.x * per + j));
-            st.above = before;
-            st.remaining = k - before;
+            found_bin = (uint32_t)(kBins - 1 - 4 * t - j);
+            found_above = before;
+            found_count = (uint32_t)c;
         }
         before += c;
     }
-    if (threadIdx.x == 0) {
-        st.arrive_hist = 0;
-        st.arrive_collect = 0;
-        st.n_above = 0;
-        st.n_cand = 0;
-    }
-}
-
-// Radix select of the `r` smallest composites c(i) = (~u(i) & 0xFFFFF) << pos_bits | i over
-// a source of positions (i < 2^pos_bits), then writes them to out[0..r). `bits` =
-// 20 + pos_bits significant composite bits.
-template <typename Source>
-__device__ void select_smallest(const Source &src, int r, int bits, int32_t *out,
-                                uint32_t *hist, int *partials, uint64_t *sel_prefix,
-                                int *sel_below, uint32_t *n_out) {
-    uint64_t prefix = 0;
-    int done_bits = 0;  // high composite bits already fixed in `prefix`
-    const int top = bits;
-    while (done_bits < top) {
-        const int digit = top - done_bits >= 11 ? 11 : top - done_bits;
-        const int shift = top - done_bits - digit;
-        const int nb = 1 << digit;
-        for (int b = threadIdx.x; b < 2048; b += kSelectThreads) hist[b] = 0;
-        __syncthreads();
-        src.for_each([&](uint64_t c) {
-            if ((c >> (shift + digit)) == (prefix >> (shift + digit)))
-                atomicAdd(&hist[(c >> shift) & (uint64_t)(nb - 1)], 1u);
-        });
-        __syncthreads();
-        // ascending: lane t owns bins 8t .. 8t+7
-        constexpr int per = 2048 / kSelectThreads;
-        int own = 0;
-        uint32_t mine[per];
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            const int b = threadIdx.x * per + j;
-            mine[j] = b < nb ? hist[b] : 0u;
-            own += (int)mine[j];
-        }
-        const int incl = scan256(own, partials);
-        int before = incl - own;
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            const int c = (int)mine[j];
-            if (before < r && before + c >= r) {
-                *sel_prefix = prefix | ((uint64_t)(threadIdx.x * per + j) << shift);
-                *sel_below = before;
-            }
-            before += c;
-        }
-        __syncthreads();
-        prefix = *sel_prefix;
-        r -= *sel_below;
-        done_bits += digit;
-        __syncthreads();
-    }
-    // `prefix` is the r0-th smallest composite; composites are unique, so exactly r0 of them
-    // are <= prefix.
-    if (threadIdx.x == 0) *n_out = 0;
+    for (int sgi = t; sgi < row_segments; sgi += kRowThreads) seg_above[sgi] = 0;
     __syncthreads();
-    const uint64_t T = prefix;
-    src.for_each_pos([&](uint64_t c, int64_t pos) {
-        if (c <= T) out[atomicAdd(n_out, 1u)] = (int32_t)pos;
-    });
+    const uint32_t bin = found_bin, top = top_bin;
+
+    // (c) Per-segment keys above the bin: the bins (bin, top] of every segment, spread
+    // over all threads, summed into LDS per segment.
+    if (bin < (uint32_t)kBins && top > bin) {
+        const int span = (int)(top - bin);
+        const int64_t total = (int64_t)row_segments * span;
+        for (int64_t idx = t; idx < total; idx += kRowThreads) {
+            const int sgi = (int)(idx / span);
+            const int b = (int)(bin + 1 + idx % span);
+            const uint32_t c = rowhist[(int64_t)sgi * kBins + b];
+            if (c) atomicAdd(&seg_above[sgi], c);
+        }
+    }
+    __syncthreads();
+
+    // (d) Exclusive prefix sums over the segments (one per thread): output and candidate
+    // offsets of every segment.
+    const uint32_t my_above = t < row_segments ? seg_above[t] : 0u;
+    const uint32_t my_in =
+        t < row_segments && bin < (uint32_t)kBins ? (uint32_t)rowhist[(int64_t)t * kBins + bin] : 0u;
+    const int ia = scan_block<kRowThreads>((int)my_above, partials);
+    const int ic = scan_block<kRowThreads>((int)my_in, partials);
+    if (t < row_segments)
+        ws.segoff[row * nseg + t] = make_uint2((uint32_t)ia - my_above, (uint32_t)ic - my_in);
+    if (t == 0) {
+        RowState &st = ws.state[row];
+        st.bin = bin;
+        st.above = found_above;
+        st.remaining = k - found_above;
+        st.n_cand = found_count;
+    }
 }
-
-struct CandidateSource {
-    const float *x;
-    const int32_t *cand;
-    int m;
-    int pos_bits;
-    template <typename F>
-    __device__ void for_each(F &&f) const {
-        for (int j = threadIdx.x; j < m; j += kSelectThreads) {
-            const int32_t i = cand[j];
-            f(((uint64_t)(~order_key(x[i]) & 0xFFFFFu) << pos_bits) | (uint32_t)i);
-        }
-    }
-    template <typename F>
-    __device__ void for_each_pos(F &&f) const {
-        for (int j = threadIdx.x; j < m; j += kSelectThreads) {
-            const int32_t i = cand[j];
-            f(((uint64_t)(~order_key(x[i]) & 0xFFFFFu) << pos_bits) | (uint32_t)i, (int64_t)i);
-        }
-    }
-};
-
-struct RowBinSource {  // every key of the row inside the threshold bin
-    const float *x;
-    int64_t n;
-    uint32_t bin;
-    int pos_bits;
-    template <typename F>
-    __device__ void for_each(F &&f) const {
-        for (int64_t i = threadIdx.x; i < n; i += kSelectThreads) {
-            const uint32_t u = order_key(x[i]);
-            if ((u >> kBinShift) == bin) f(((uint64_t)(~u & 0xFFFFFu) << pos_bits) | (uint32_t)i);
-        }
-    }
-    template <typename F>
-    __device__ void for_each_pos(F &&f) const {
-        for (int64_t i = threadIdx.x; i < n; i += kSelectThreads) {
-            const uint32_t u = order_key(x[i]);
-            if ((u >> kBinShift) == bin) f(((uint64_t)(~u & 0xFFFFFu) << pos_bits) | (uint32_t)i, i);
-        }
-    }
-};
 
 template <int VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
     const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
     const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
     int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
-    __shared__ uint32_t hist[2048];
-    __shared__ int partials[4];
-    __shared__ int last;
-    __shared__ uint64_t sel_prefix;
-    __shared__ int sel_below;
-    __shared__ uint32_t n_out;
-    __shared__ uint32_t chunk_base[2];
+    __shared__ int partials[kTopkThreads / 64];
     const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t n = row_bound(row_ends, row, width);
     if (n <= k) return;
     const int64_t lo = seg * seg_len;
     if (lo >= n) return;
     const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
-    const uint32_t row_segments = (uint32_t)((n + seg_len - 1) / seg_len);
     const float *x = logits + row * logits_row_stride;
     int32_t *out = indices + row * indices_row_stride;
-    RowState &st = ws.state[row];
-    const uint32_t bin = st.bin;
-    int32_t *cand = ws.cand + row * kCandCap;
+    const RowState &st = ws.state[row];
+    const uint32_t bin = st.bin, above = (uint32_t)st.above;
+    const uint2 off = ws.segoff[row * nseg + seg];
+    uint2 *cand = ws.cand + row * kCandCap;
 
-    // Chunks of 4096 keys (16 per lane, in registers): lane counts, a workgroup prefix sum,
-    // and one atomic per counter per chunk reserve the output and candidate slots. (Atomics
-    // per wavefront on the row's two shared counters serialize in L2.)
+    // Chunks of 4096 keys (16 per lane, in registers): lane counts and a workgroup prefix
+    // sum place every key after the segment's offsets and the earlier chunks' keys.
     constexpr int kPer = 16, kChunk = kPer * kTopkThreads;
+    uint32_t base_above = off.x, base_in = off.y;
     for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
-        uint32_t d[kPer];
-        int n_above = 0, n_in = 0;
+        uint32_t u[kPer];
         const int64_t first = cbase + (int64_t)threadIdx.x * kPer;
         if (VEC == 4 && first + kPer <= hi) {
 #pragma unroll
             for (int j = 0; j < kPer; j += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(x + first + j);
-                d[j] = order_key(v.x) >> kBinShift;
-                d[j + 1] = order_key(v.y) >> kBinShift;
-                d[j + 2] = order_key(v.z) >> kBinShift;
-                d[j + 3] = order_key(v.w) >> kBinShift;
+                u[j] = order_key(v.x);
+                u[j + 1] = order_key(v.y);
+                u[j + 2] = order_key(v.z);
+                u[j + 3] = order_key(v.w);
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) d[j] = first + j < hi ? order_key(x[first + j]) >> kBinShift : 0u;
+            for (int j = 0; j < kPer; ++j) u[j] = first + j < hi ? order_key(x[first + j]) : 0u;
         }
+        int n_above = 0, n_in = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            n_above += first + j < hi && d[j] > bin;
-            n_in += first + j < hi && d[j] == bin;
+            const uint32_t d = u[j] >> kBinShift;
+            n_above += first + j < hi && d > bin;
+            n_in += first + j < hi && d == bin;
         }
         const int mine = n_above | (n_in << 16);
-        const int incl = scan256(mine, partials);
-        if (threadIdx.x == kTopkThreads - 1) {
-            const int tot_above = incl & 0xFFFF, tot_in = incl >> 16;
-            chunk_base[0] = tot_above ? atomicAdd(&st.n_above, (uint32_t)tot_above) : 0u;
-            chunk_base[1] = tot_in ? atomicAdd(&st.n_cand, (uint32_t)tot_in) : 0u;
-        }
-        __syncthreads();
-        uint32_t pa = chunk_base[0] + ((incl - mine) & 0xFFFF);
-        uint32_t pc = chunk_base[1] + ((incl - mine) >> 16);
+        const int incl = scan_block<kTopkThreads>(mine, partials);
+        uint32_t pa = base_above + ((incl - mine) & 0xFFFF);
+        uint32_t pc = base_in + ((incl - mine) >> 16);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int64_t i = cbase + (int64_t)threadIdx.x * kPer + j;
+            const int64_t i = first + j;
             if (i >= hi) break;
-            if (d[j] > bin) {
-                out[pa++] = (int32_t)i;
-            } else if (d[j] == bin) {
-                if (pc < (uint32_t)kCandCap) cand[pc] = (int32_t)i;
+            const uint32_t d = u[j] >> kBinShift;
+            if (d > bin) {
+                if (pa < above) out[pa] = (int32_t)i;
+                ++pa;
+            } else if (d == bin) {
+                if (pc < (uint32_t)kCandCap) cand[pc] = make_uint2(u[j], (uint32_t)i);
                 ++pc;
             }
         }
+        // the chunk's totals are the sum of the wave totals the scan left in `partials`
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkThreads / 64; ++w) tot += partials[w];
+        base_above += (uint32_t)(tot & 0xFFFF);
+        base_in += (uint32_t)(tot >> 16);
         __syncthreads();
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(&st.arrive_collect, 1u) == row_segments - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
 
-    const int above = st.above, remaining = st.remaining;
-    const uint32_t ncand = load_relaxed(&st.n_cand);
+// Composite of a key inside the threshold bin: smaller for a larger value, and for equal
+// values smaller for the lower position; unique per position.
+__device__ __forceinline__ uint64_t composite(uint32_t u, uint32_t pos, int pos_bits) {
+    return ((uint64_t)(~u & 0xFFFFFu) << pos_bits) | pos;
+}
+
+struct LdsCandidates {  // composites already in LDS
+    const uint64_t *c;
+    int m;
+    template <typename F>
+    __device__ __forceinline__ void for_each(F &&f) const {
+        for (int j = threadIdx.x; j < m; j += kSelectThreads) f(c[j]);
+    }
+};
+
+struct RowBin {  // every key of the row inside the threshold bin, read from the logits
+    const float *x;
+    int64_t n;
+    uint32_t bin;
+    int pos_bits;
+    template <typename F>
+    __device__ __forceinline__ void for_each(F &&f) const {
+        for (int64_t i = threadIdx.x; i < n; i += kSelectThreads) {
+            const uint32_t u = order_key(x[i]);
+            if ((u >> kBinShift) == bin) f(composite(u, (uint32_t)i, pos_bits));
+        }
+    }
+};
+
+struct SelectShared {
+    uint32_t hist[kRadixBins];
+    int partials[kSelectThreads / 64];
+    uint64_t prefix;
+    int below;
+    int count;
+    uint32_t n_out;
+};
+
+// Writes the positions of the r smallest composites (of `bits` significant bits) that
+// `src` yields to out[0..r), by a most-significant-digit radix select in LDS.
+template <typename Source>
+__device__ void select_smallest(const Source &src, int r, int bits, int pos_bits, int32_t *out,
+                                SelectShared &sh) {
+    const int r0 = r;
+    uint64_t prefix = 0;
+    int done = 0;  // high composite bits fixed in `prefix`
+    uint64_t threshold = ~(uint64_t)0;
+    while (done < bits) {
+        const int digit = bits - done >= kRadixBits ? kRadixBits : bits - done;
+        const int shift = bits - done - digit;
+        for (int b = threadIdx.x; b < kRadixBins; b += kSelectThreads) sh.hist[b] = 0;
+        __syncthreads();
+        const uint64_t want = prefix >> (shift + digit);
+        src.for_each([&](uint64_t c) {
+            if ((c >> (shift + digit)) == want)
+                atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)((1 << digit) - 1)], 1u);
+        });
+        __syncthreads();
+        constexpr int per = kRadixBins / kSelectThreads;  // ascending: lane t owns per*t ..
+        int own = 0;
+        uint32_t mine[per];
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            mine[j] = sh.hist[threadIdx.x * per + j];
+            own += (int)mine[j];
+        }
+        const int incl = scan_block<kSelectThreads>(own, sh.partials);
+        int before = incl - own;
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            const int c = (int)mine[j];
+            if (before < r && before + c >= r) {
+                sh.prefix = prefix | ((uint64_t)(threadIdx.x * per + j) << shift);
+                sh.below = before;
+                sh.count = c;
+            }
+            before += c;
+        }
+        __syncthreads();
+        prefix = sh.prefix;
+        done += digit;
+        if (sh.below + sh.count == r) {  // the whole digit bin is taken: stop early
+            threshold = prefix | (((uint64_t)1 << shift) - 1);
+            break;
+        }
+        r -= sh.below;
+        threshold = prefix;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sh.n_out = 0;
+    __syncthreads();
+    const uint64_t pos_mask = ((uint64_t)1 << pos_bits) - 1;
+    src.for_each([&](uint64_t c) {
+        if (c <= threshold) {
+            const uint32_t slot = atomicAdd(&sh.n_out, 1u);
+            if (slot < (uint32_t)r0) out[slot] = (int32_t)(c & pos_mask);
+        }
+    });
+}
+
+__global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
+    const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
+    const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
+    int64_t indices_row_stride, TopkWorkspace ws) {
+    __shared__ uint64_t cands[kCandCap];
+    __shared__ SelectShared sh;
+    const int64_t row = blockIdx.x;
+    const int64_t n = row_bound(row_ends, row, width);
+    if (n <= k) return;
+    const float *x = logits + row * logits_row_stride;
+    const RowState &st = ws.state[row];
+    const uint32_t bin = st.bin, ncand = st.n_cand;
+    const int remaining = st.remaining;
+    if (remaining <= 0 || remaining > k) return;
+    int32_t *out = indices + row * indices_row_stride + st.above;
     int pos_bits = 1;
     while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
     const int bits = 20 + pos_bits;
     if (ncand <= (uint32_t)kCandCap) {
-        CandidateSource src{x, cand, (int)ncand, pos_bits};
-        select_smallest(src, remaining, bits, out + above, hist, partials, &sel_prefix,
-                        &sel_below, &n_out);
+        const uint2 *cand = ws.cand + row * kCandCap;
+        for (int j = threadIdx.x; j < (int)ncand; j += kSelectThreads) {
+            const uint2 e = cand[j];
+            cands[j] = composite(e.x, e.y, pos_bits);
+        }
+        __syncthreads();
+        select_smallest(LdsCandidates{cands, (int)ncand}, remaining, bits, pos_bits, out, sh);
     } else {
-        RowBinSource src{x, n, bin, pos_bits};
-        select_smallest(src, remaining, bits, out + above, hist, partials, &sel_prefix,
-                        &sel_below, &n_out);
-    }
-    if (threadIdx.x == 0) {
-        st.arrive_collect = 0;
-        st.n_above = 0;
-        st.n_cand = 0;
+        select_smallest(RowBin{x, n, bin, pos_bits}, remaining, bits, pos_bits, out, sh);
     }
 }
 
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int) {
     const int64_t nseg = topk_nseg(width, topk_segment(rows, width));
     return align256(sizeof(RowState) * rows) + align256(sizeof(uint16_t) * kBins * nseg * rows) +
-           align256(sizeof(int32_t) * (size_t)kCandCap * rows);
+           align256(sizeof(uint2) * nseg * rows) + align256(sizeof(uint2) * (size_t)kCandCap * rows);
 }
 
 hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t logits_row_stride,
@@ -435,17 +527,27 @@ hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t
     const TopkWorkspace ws = carve(workspace, rows, nseg);
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
-    if (vec) {
+    if (vec)
         hipLaunchKernelGGL(topk_hist_kernel<4>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg, seg_len);
-        hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg, seg_len);
-    } else {
+                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
+                           seg_len);
+    else
         hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg, seg_len);
+                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
+                           seg_len);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
+                       row_ends, width, k, ws, nseg, seg_len);
+    if (vec)
+        hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits, width,
+                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
+                           seg_len);
+    else
         hipLaunchKernelGGL(topk_collect_kernel<1>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg, seg_len);
-    }
+                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
+                           seg_len);
+    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads), 0, stream,
+                       logits, width, logits_row_stride, row_ends, k, indices, indices_row_stride,
+                       ws);
     return hipGetLastError();
 }
 

@@ -166,6 +166,10 @@ def test_topk_checks(lib):
     assert topk(lib, os=15) == ELAYOUT
     assert topk(lib, lg=P + 2) == ELAYOUT
     assert lib.dsaidx_topk_workspace_bytes(4, 1024, 0) == 0
+    # rows hold at most 2^25 keys
+    assert topk(lib, width=(1 << 25) + 1, ls=(1 << 25) + 1) == EUNSUP
+    assert lib.dsaidx_topk_workspace_bytes(1, (1 << 25) + 1, 8) == 0
+    assert lib.dsaidx_topk_workspace_bytes(1, 1 << 25, 8) > 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -278,16 +278,31 @@ def test_topk_strided_rows():
 
 def test_topk_candidate_overflow_and_workspace_reuse():
     # A threshold bin holding more keys than the candidate list keeps (20000 equal logits)
-    # selects from the row itself; one workspace serves several calls in a row, since every
-    # call returns its histograms and counters to zero.
+    # selects from the row itself; the workspace needs no initialisation (it starts as
+    # arbitrary bytes here) and one workspace serves several calls in a row.
     rng = np.random.default_rng(16)
     lg = np.full((3, 20000), 0.5, np.float32)
     lg[0, 7777] = 2.0
     lg[1] = rng.standard_normal(20000).astype(np.float32)
     lg[2, ::3] = 0.25
     ends = np.array([20000, 20000, 19999], np.int32)
-    ws = torch.zeros(dsa.topk_workspace_bytes(3, 20000, 100), dtype=torch.uint8, device="cuda")
+    ws = torch.full((dsa.topk_workspace_bytes(3, 20000, 100),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
     for k in (100, 5000, 1, 100, 2047):
         want = oracle.topk(lg, ends, k)
         got = dsa.topk(dev(lg), dev(ends), k, workspace=ws).cpu().numpy()
         assert_topk_sets(got, want, range(3), f"k={k}")
+
+
+@pytest.mark.parametrize("rows,width,k", [(1, 3_000_000, 2048), (40, 300_000, 2048), (3, 70_000, 1)])
+def test_topk_wide_rows(rows, width, k):
+    # hundreds of segments per row (733 for the 3M-key row); 40 rows double the segment
+    # length to 8192 keys; a row whose top bin holds everything but the first few keys
+    rng = np.random.default_rng(17)
+    lg = rng.standard_normal((rows, width)).astype(np.float32)
+    lg[-1, 5:] = 3.0
+    ends = np.full(rows, width, np.int32)
+    ends[0] = width - 1
+    want = oracle.topk(lg, ends, k)
+    got = dsa.topk(dev(lg), dev(ends), k).cpu().numpy()
+    assert_topk_sets(got, want, range(rows), f"{rows}x{width}")
