@@ -96,15 +96,25 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inclusive prefix sum over an NT-lane workgroup; `partials` holds NT / 64 ints.
+// Inclusive prefix sum over the wavefront on the data-parallel primitives (DPP): shifts by
+// 1, 2, 4 and 8 lanes within each row of 16, then row 0's and row 1's totals broadcast
+// into the rows above them. All in registers, no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
+// Inclusive prefix sum over an NT-lane workgroup; `partials` holds NT / 64 ints. On return
+// partials[w] is wavefront w's total (valid until the next call).
 template <int NT>
 __device__ __forceinline__ int scan_block(int v, int *partials) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int n = __shfl_up(v, d);
-        if (lane >= d) v += n;
-    }
+    v = wave_incl_scan(v);
     if (lane == 63) partials[wave] = v;
     __syncthreads();
     int before = 0;
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
     const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
     int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
-    __shared__ uint32_t hist[kBins];
+    __shared__ __align__(16) uint32_t hist[kBins];
     const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t n = row_bound(row_ends, row, width);
     if (n <= k) {
@@ -170,9 +180,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     __syncthreads();
     // lane t stores bins [16t, 16t+16) as 16-bit counts
     uint32_t c[8];
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + 4 * threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        c[j] = hist[16 * threadIdx.x + 2 * j] | (hist[16 * threadIdx.x + 2 * j + 1] << 16);
+    for (int v = 0; v < 4; ++v) {
+        const uint4 q = h4[v];
+        c[2 * v] = q.x | (q.y << 16);
+        c[2 * v + 1] = q.z | (q.w << 16);
+    }
     uint4 *dst = reinterpret_cast<uint4 *>(ws.seghist + (row * nseg + seg) * kBins +
                                            16 * threadIdx.x);
     dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
 __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const int32_t *__restrict__ row_ends, int64_t width, int k, TopkWorkspace ws, int64_t nseg,
     int64_t seg_len) {
-    __shared__ uint32_t hist[kBins];
+    __shared__ __align__(16) uint32_t part_hist[kRowThreads / 256][kBins];  // per segment group
     __shared__ uint32_t seg_above[kMaxRowSegments];
     __shared__ int partials[kRowThreads / 64];
     __shared__ uint32_t found_bin, found_count, top_bin;
@@ -196,8 +210,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const int t = threadIdx.x;
 
     // (a) Thread t sums bins [16 (t % 256), +16) over the segments s = t / 256 (mod 4),
-    // four segments' loads in flight at a time, then merges into the LDS histogram.
-    for (int b = t; b < kBins; b += kRowThreads) hist[b] = 0;
+    // four segments' loads in flight at a time, and stores the sums for its segment group
+    // (plain vector stores: every entry is written, nothing to clear, no atomics).
     if (t == 0) {
         found_bin = kBins;  // kept only if the counts do not reach k (they always do)
         found_above = k;
@@ -238,34 +252,33 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
                 hi16[e] += w[e] >> 16;
             }
         }
-        __syncthreads();  // histogram cleared
+        uint4 *dst = reinterpret_cast<uint4 *>(&part_hist[sg0][16 * blk]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (sum[e]) atomicAdd(&hist[16 * blk + 2 * e], sum[e]);
-            if (hi16[e]) atomicAdd(&hist[16 * blk + 2 * e + 1], hi16[e]);
-        }
+        for (int v = 0; v < 4; ++v)
+            dst[v] = make_uint4(sum[2 * v], hi16[2 * v], sum[2 * v + 1], hi16[2 * v + 1]);
     }
     __syncthreads();
 
     // (b) Thread t owns bins 4095 - 4t - j, j < 4 (descending): the bin holding the k-th
-    // largest key, the keys above it, and the highest non-empty bin.
-    uint32_t mine[4];
-    int own = 0;
+    // largest key, the keys above it, and the highest non-empty bin (the one where the
+    // descending count first leaves zero; a single thread sees that).
+    uint4 m4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        mine[j] = hist[kBins - 1 - 4 * t - j];
-        own += (int)mine[j];
+    for (int g = 0; g < kRowThreads / 256; ++g) {
+        const uint4 v = reinterpret_cast<const uint4 *>(part_hist[g])[kBins / 4 - 1 - t];
+        m4.x += v.x;
+        m4.y += v.y;
+        m4.z += v.z;
+        m4.w += v.w;
     }
-    if (own) {
-#pragma unroll
-        for (int j = 3; j >= 0; --j)
-            if (mine[j]) atomicMax(&top_bin, (uint32_t)(kBins - 1 - 4 * t - j));
-    }
+    const uint32_t mine[4] = {m4.w, m4.z, m4.y, m4.x};
+    const int own = (int)(m4.x + m4.y + m4.z + m4.w);
     const int incl = scan_block<kRowThreads>(own, partials);
     int before = incl - own;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = (int)mine[j];
+        if (before == 0 && c > 0) top_bin = (uint32_t)(kBins - 1 - 4 * t - j);
         if (before < k && before + c >= k) {
             found_bin = (uint32_t)(kBins - 1 - 4 * t - j);
             found_above = before;
@@ -362,12 +375,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int64_t i = first + j;
-            if (i >= hi) break;
             const uint32_t d = u[j] >> kBinShift;
-            if (d > bin) {
+            const bool live = i < hi;
+            if (live && d > bin) {
                 if (pa < above) out[pa] = (int32_t)i;
                 ++pa;
-            } else if (d == bin) {
+            } else if (live && d == bin) {
                 if (pc < (uint32_t)kCandCap) cand[pc] = make_uint2(u[j], (uint32_t)i);
                 ++pc;
             }
