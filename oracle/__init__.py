@@ -178,6 +178,25 @@ def store_keys(key_bits: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: f
     _check(st, "store_keys")
 
 
+def index_inputs(projected_bits: np.ndarray, key_col: int, weight_col: int, q_bits: np.ndarray,
+                 gamma: np.ndarray, beta: np.ndarray, eps: float, slots: np.ndarray,
+                 cache: np.ndarray, num_pages: int, page_stride: int, section_offset: int = 0,
+                 fmt="mxfp4"):
+    """The indexer inputs of one step, per token (page
+    "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex): the token's
+    query ``q_bits[t]`` (uint16 BF16 [tokens, heads, 128]) quantized as ``quantize_queries``
+    does, with the raw head weights read from the packed projection row ``projected_bits[t]``
+    (uint16 BF16 [tokens, >= cols]) at columns [weight_col, weight_col + heads), and the key
+    at columns [key_col, key_col + 128) of the same row inserted at ``slots[t]`` as
+    ``store_keys`` does. Returns (q_out, w_out); ``cache`` is modified in place."""
+    proj = np.ascontiguousarray(projected_bits, dtype=np.uint16)
+    heads = q_bits.shape[1]
+    q_out, w_out = quantize_queries(q_bits, proj[:, weight_col:weight_col + heads], fmt)
+    store_keys(proj[:, key_col:key_col + 128], gamma, beta, eps, slots, cache, num_pages,
+               page_stride, section_offset, fmt)
+    return q_out, w_out
+
+
 def decode_layout(seq_lens, query_lens, num_rows: int, dcp_rank: int = 0,
                   dcp_world_size: int = 1, interleave: int = 1):
     seq = np.ascontiguousarray(seq_lens, dtype=np.int32)

@@ -171,6 +171,75 @@ def test_store_keys_fp8_zero_key_scale_floor():
     assert scale == 2.0 ** -42 and np.all(vals == 0)
 
 
+# ---- index_inputs (page "...cutedsl.dsa.index", DsaIndex: per token, query quant + head
+#      weights from the packed projection row + key LayerNorm and insert) ------------------
+
+def _packed_rows(tokens, cols, key_col, weight_col, keys, wv, rng):
+    # filler columns hold NaN/Inf and huge BF16 patterns: nothing outside the key and weight
+    # columns may reach any output
+    filler = rng.choice(np.array([0x7FC0, 0xFF80, 0x7F80, 0x7F7F, 0xFF7F], np.uint16),
+                        size=(tokens, cols))
+    proj = filler.copy()
+    proj[:, key_col:key_col + 128] = bf16_bits(keys)
+    proj[:, weight_col:weight_col + wv.shape[1]] = bf16_bits(wv)
+    return proj
+
+
+@pytest.mark.parametrize("fmt,heads,key_col,weight_col,stride,offset",
+                         [("mxfp4", 32, 4096, 4224, 4352, 0), ("mxfp4", 64, 0, 200, 8192, 3840),
+                          ("fp8", 32, 130, 2, 8448, 0)])
+def test_index_inputs_columns_and_layout(fmt, heads, key_col, weight_col, stride, offset):
+    # Lossless queries, constant pre-norm keys (normalize to beta exactly) with lossless betas,
+    # and head weights that scale exactly: every output decodes back to its input, and only
+    # the key and weight columns of the packed row are read.
+    rng = np.random.default_rng(21)
+    tokens, pages = 4, 3
+    if fmt == "mxfp4":
+        q = _lossless_fp4_queries(tokens, heads, 22)
+    else:
+        codes = rng.integers(0, 0x7F, size=(tokens, heads, 128))
+        q = npdecode.e4m3(codes)
+        q[:, :, 7] = 448.0
+        q = q.astype(np.float32)
+    beta = _lossless_beta(fmt, rng)
+    keys = np.repeat(np.arange(tokens, dtype=np.float32)[:, None] - 1.5, 128, axis=1)
+    wv = (2.0 ** rng.integers(-4, 4, size=(tokens, heads))).astype(np.float32)
+    cols = max(key_col + 128, weight_col + heads) + 7
+    proj = _packed_rows(tokens, cols, key_col, weight_col, keys, wv, rng)
+    slots = np.array([5, -1, 64 * 2 + 17, 64], np.int64)
+    section = 4352 if fmt == "mxfp4" else 8448
+    cache = np.full(offset + (pages - 1) * stride + section, 0xA5, np.uint8)
+    q_out, w_out = oracle.index_inputs(proj, key_col, weight_col, bf16_bits(q), np.ones(128, np.float32),
+                                       beta, 1e-6, slots, cache, pages, stride, offset, fmt)
+    # head weights: BF16(wv * c_H) (FP8: times s = 1, since every head's amax is 448)
+    c = np.float32(oracle.head_weight_scale(heads))
+    want_w = torch.from_numpy(wv * c).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(bf16_to_f32(w_out), want_w)
+    if fmt == "mxfp4":
+        assert np.array_equal(npdecode.mxfp4_query_rows(q_out, heads), q.astype(np.float64))
+    else:
+        assert np.array_equal(npdecode.fp8_query_rows(q_out, heads), q.astype(np.float64))
+    for t, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        page, off = divmod(int(sl), 64)
+        if fmt == "mxfp4":
+            got = npdecode.mxfp4_key(cache, page, off, stride, offset)
+        else:
+            got, _ = npdecode.fp8_key(cache, page, off, stride, offset)
+        assert np.array_equal(got, beta.astype(np.float64)), (t, sl)
+    # padding token 1 wrote nothing: its would-be slot region still holds filler elsewhere
+    untouched = np.ones(cache.size, bool)
+    for sl in slots[slots >= 0]:
+        page, off = divmod(int(sl), 64)
+        base = offset + page * stride
+        w = 64 if fmt == "mxfp4" else 128
+        untouched[base + off * w: base + off * w + w] = False
+        sb = base + (4096 if fmt == "mxfp4" else 8192) + off * 4
+        untouched[sb:sb + 4] = False
+    assert np.all(cache[untouched] == 0xA5)
+
+
 # ---- decode_layout (page "...amd.ops.fp4_indexer", decode_layout) -------------------------
 
 def _parse_layout(line):
