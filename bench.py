@@ -1,8 +1,8 @@
 """Benchmark of the DSA lightning-indexer hot path on one MI355X.
 
 One step = one pass of the whole path over one decode batch, inputs resident in HBM:
-quantize_queries (all rows), store_keys (the step's new keys), decode_layout,
-score_paged, topk. Prints ONE JSON line: scored (row, key) pairs per second of the whole
+index_inputs (one launch: every row's query quantized with its head weights, and the step's
+new keys normalized, quantized and inserted), decode_layout, score_paged, topk. Prints ONE JSON line: scored (row, key) pairs per second of the whole
 step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
 launch stream around every score launch in the timed region), and the CPU oracle timed on
 a bounded sample of the same workload.
@@ -64,6 +64,19 @@ class Prepared:
             raise RuntimeError(f"{self.fn.__name__} returned status {st}")
 
 
+def packed_rows(wl):
+    """Packed projection rows of a step's tokens, one per query row, [key 128 | weights H]
+    BF16 bits, and each row's key slot (-1 for graph padding rows)."""
+    sk = wl.step_key_index()
+    live = sk.size
+    proj = np.zeros((wl.num_rows, 128 + wl.heads), np.uint16)
+    proj[:live, :128] = wl.key_bits[sk]
+    proj[:, 128:] = wl.wv_bits
+    slots = np.full(wl.num_rows, -1, np.int64)
+    slots[:live] = wl.key_slots[sk]
+    return proj, slots
+
+
 class Setup:
     """Device buffers of one workload, the cache replicas, and the prepared step calls."""
 
@@ -102,6 +115,11 @@ class Setup:
         sk = wl.step_key_index()
         self.new_keys = bf16(wl.key_bits[sk])
         self.new_slots = up(wl.key_slots[sk])
+        # packed projection rows of the step's tokens, one per query row: [key 128 | weights H]
+        # (padding rows carry no key: slot -1)
+        self.proj_np, self.row_slots_np = packed_rows(wl)
+        self.projected = bf16(self.proj_np)
+        self.row_slots = up(self.row_slots_np)
         self.seq_lens, self.query_lens = up(wl.seq_lens), up(wl.query_lens)
         self.block_table = up(wl.block_table)
         rb = dsa.query_row_bytes(fmt, wl.heads)
@@ -124,9 +142,16 @@ class Setup:
         self.topk = Prepared(lib.dsaidx_topk, self.logits.data_ptr(), wl.num_rows, wl.width,
                              self.logits.stride(0), self.ends.data_ptr(), wl.topk,
                              self.idx.data_ptr(), self.idx.stride(0), self.ws.data_ptr(), wsb, sp)
-        self.store, self.score = [], []
+        self.store, self.score, self.inputs = [], [], []
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
+            self.inputs.append(Prepared(
+                lib.dsaidx_index_inputs, fmt, self.projected.data_ptr(), wl.num_rows,
+                self.projected.stride(0), 0, 128, self.q.data_ptr(), wl.heads, self.q.stride(0),
+                self.q.stride(1), self.gamma.data_ptr(), self.beta.data_ptr(), ctypes.c_float(wl.eps),
+                self.row_slots.data_ptr(), base, wl.num_pages, wl.page_stride,
+                self.q_rows.data_ptr(), self.q_rows.stride(0), self.w_out.data_ptr(),
+                self.w_out.stride(0), sp))
             self.store.append(Prepared(
                 lib.dsaidx_store_keys, fmt, self.new_keys.data_ptr(), self.new_keys.shape[0],
                 self.new_keys.stride(0), self.gamma.data_ptr(), self.beta.data_ptr(),
@@ -151,8 +176,7 @@ class Setup:
         self.score_flops = 2 * wl.heads * 128 * self.pairs
 
     def step(self, i, ev=None):
-        self.quant()
-        self.store[i % len(self.caches)]()
+        self.inputs[i % len(self.caches)]()
         self.layout()
         if ev is not None:
             ev[0].record(self.stream)
@@ -183,7 +207,8 @@ def kernel_times(s: Setup, reps: int = 30):
     """Per-kernel HIP-event times (ms, median) of each stage launched alone."""
     import torch
     out = {}
-    stages = [("quantize_queries", lambda i: s.quant()),
+    stages = [("index_inputs", lambda i: s.inputs[i % len(s.caches)]()),
+              ("quantize_queries", lambda i: s.quant()),
               ("store_keys", lambda i: s.store[i % len(s.caches)]()),
               ("decode_layout", lambda i: s.layout()),
               ("score_paged", lambda i: s.score[i % len(s.caches)]()),
@@ -212,14 +237,13 @@ def cpu_baseline(s: Setup, budget_s: float):
     starts, ends = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
     live = [r for r in range(wl.num_rows) if ends[r] > 0]
     # probe one row to size the sample to the budget
-    t0 = time.perf_counter()
-    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
-    sk = wl.step_key_index()
     scratch = ocache.copy()
-    oracle.store_keys(wl.key_bits[sk], wl.gamma, wl.beta, wl.eps, wl.key_slots[sk], scratch,
-                      wl.num_pages, wl.page_stride, wl.section_offset, wl.fmt)
-    del scratch
+    t0 = time.perf_counter()
+    oq, ow = oracle.index_inputs(s.proj_np, 0, 128, wl.q_bits, wl.gamma, wl.beta, wl.eps,
+                                 s.row_slots_np, scratch, wl.num_pages, wl.page_stride,
+                                 wl.section_offset, wl.fmt)
     fixed = time.perf_counter() - t0
+    del scratch
     t0 = time.perf_counter()
     lg = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
                             starts, ends, wl.fmt, wl.section_offset, rows_subset=[live[0]])
@@ -238,9 +262,9 @@ def cpu_baseline(s: Setup, budget_s: float):
     return {"value": s.pairs / step_s, "unit": "pairs/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{wl.name}: score_paged + topk of {len(rows)} of {len(live)} live rows "
-                      f"({pairs} pairs, {el:.2f} s), plus quantize_queries of all {wl.num_rows} "
-                      f"rows and store_keys of the step's {sk.size} keys ({fixed:.2f} s), scaled "
-                      f"to the whole step",
+                      f"({pairs} pairs, {el:.2f} s), plus index_inputs of all {wl.num_rows} rows "
+                      f"and the step's {int((s.row_slots_np >= 0).sum())} keys ({fixed:.2f} s), "
+                      f"scaled to the whole step",
             "score_topk_pairs_per_s": pairs / el,
             "cpu_model": cpu_model()}
 

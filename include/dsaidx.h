@@ -124,6 +124,35 @@ dsaidx_status dsaidx_store_keys(int fmt, const void *keys, int64_t tokens, int64
                                 int64_t page_stride, void *stream);
 
 /*
+ * index_inputs -- [idx] DsaIndex: the indexer inputs of one step in one launch, one
+ * workgroup per token. For token t it does what dsaidx_quantize_queries does for row t of
+ * q (with the raw head weights taken from the packed projection row) and what
+ * dsaidx_store_keys does for the key held in the same packed row; the results are
+ * bit-identical to those two calls.
+ *
+ *  projected  device, BF16 packed projection rows [tokens, >= proj_row_stride]: row t at
+ *           projected + t*proj_row_stride (4-byte aligned, stride even); the token's
+ *           pre-norm key is columns [key_col, key_col + 128) (key_col even) and its raw
+ *           head weights columns [weight_col, weight_col + heads). Both ranges must lie
+ *           inside the row stride. No other column is read.
+ *  q, heads, q_row_stride, q_head_stride, q_out, q_out_row_stride  as in
+ *           dsaidx_quantize_queries, one row per token.
+ *  w_out    device, BF16 [tokens, heads] (required), as in dsaidx_quantize_queries.
+ *  gamma, beta, eps, slots, cache, num_pages, page_stride  as in dsaidx_store_keys, one
+ *           slot per token (negative: padding, no insert).
+ *  Errors: as the two calls it combines; key_col or weight_col < 0 gives DSAIDX_EINVAL.
+ *  tokens == 0 enqueues nothing.
+ */
+dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens,
+                                  int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+                                  const void *q, int32_t heads, int64_t q_row_stride,
+                                  int64_t q_head_stride, const float *gamma, const float *beta,
+                                  float eps, const int64_t *slots, void *cache,
+                                  int64_t num_pages, int64_t page_stride, void *q_out,
+                                  int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride,
+                                  void *stream);
+
+/*
  * decode_layout -- [fp4ops] decode_layout. One workgroup; no device-to-host reads.
  *
  *  seq_lens, query_lens  device, int32 [num_requests] (query_lens >= 0).

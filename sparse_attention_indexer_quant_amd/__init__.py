@@ -7,9 +7,12 @@ runs in Python. The library is loaded on first use and a missing build raises
 
 Calls (names follow the pages' problem statement: page
 "vllm.models.kimi_k3.amd.ops.fp4_indexer" quantize_queries / store_keys /
-score_paged / decode_layout, plus the per-row top-k):
+score_paged / decode_layout, plus the per-row top-k and the fused per-token inputs of
+page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex):
 
   quantize_queries(q, wv, fmt)            -> (q_rows uint8, w_out bf16)
+  index_inputs(projected, key_col, weight_col, q, gamma, beta, eps, slots, cache, ...)
+                                          -> (q_rows uint8, w_out bf16); keys inserted
   store_keys(keys, gamma, beta, eps, slots, cache, num_pages, page_stride, fmt)
   decode_layout(seq_lens, query_lens, num_rows, dcp_rank, dcp_world_size, interleave)
   score_paged(q_rows, heads, weights, cache, ..., block_table, query_starts, row_ends, max_query_len)
@@ -54,6 +57,8 @@ def library():
             "dsaidx_query_row_bytes": (I64, [I32, I32]),
             "dsaidx_quantize_queries": (I32, [I32, P, I64, I32, I64, I64, P, I64, P, I64, P, I64, P]),
             "dsaidx_store_keys": (I32, [I32, P, I64, I64, P, P, F32, P, P, I64, I64, P]),
+            "dsaidx_index_inputs": (I32, [I32, P, I64, I64, I64, I64, P, I32, I64, I64, P, P, F32,
+                                          P, P, I64, I64, P, I64, P, I64, P]),
             "dsaidx_decode_layout": (I32, [P, P, I64, I64, I32, I32, I32, P, P, P]),
             "dsaidx_score_paged": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64, P, P,
                                          I64, I32, P, I64, P]),
@@ -147,6 +152,45 @@ def store_keys(keys, gamma, beta, eps, slots, cache, num_pages, page_stride, fmt
         beta.data_ptr(), float(eps), slots.data_ptr(), cache.data_ptr() + int(section_offset),
         int(num_pages), int(page_stride), _stream(keys))
     _check("store_keys", st)
+
+
+def index_inputs(projected, key_col, weight_col, q, gamma, beta, eps, slots, cache, num_pages,
+                 page_stride, fmt="mxfp4", section_offset=0, out=None, w_out=None):
+    """The indexer inputs of one step in one launch, one workgroup per token: the query
+    q [tokens, heads, 128] (bf16) quantized with the raw head weights read from the packed
+    projection rows projected [tokens, >= cols] (bf16) at columns weight_col.., and the key
+    at columns key_col..key_col+128 of the same rows inserted at slots (int64 [tokens]).
+    Returns (q_rows uint8 [tokens, row_bytes], w_out bf16 [tokens, heads])."""
+    import torch
+    _dev(projected, "projected", torch.bfloat16)
+    if projected.dim() != 2 or projected.stride(1) != 1:
+        raise ValueError("index_inputs: projected must be [tokens, cols] with unit column stride")
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != 128 or q.stride(2) != 1 or q.shape[0] != projected.shape[0]:
+        raise ValueError("index_inputs: q must be [tokens, heads, 128] with contiguous heads")
+    _dev(slots, "slots", torch.int64)
+    if slots.dim() != 1 or slots.numel() != q.shape[0] or slots.stride(0) != 1:
+        raise ValueError("index_inputs: one contiguous slot per token")
+    _dev(gamma, "gamma", torch.float32)
+    _dev(beta, "beta", torch.float32)
+    _dev(cache, "cache", torch.uint8)
+    tokens, heads = q.shape[0], q.shape[1]
+    f = _fmt(fmt)
+    if out is None:
+        out = torch.empty((tokens, query_row_bytes(f, heads) or heads * 128), dtype=torch.uint8,
+                          device=q.device)
+    if w_out is None:
+        w_out = torch.empty((tokens, heads), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", torch.uint8)
+    _dev(w_out, "w_out", torch.bfloat16)
+    st = library().dsaidx_index_inputs(
+        f, projected.data_ptr(), tokens, projected.stride(0), int(key_col), int(weight_col),
+        q.data_ptr(), heads, q.stride(0), q.stride(1), gamma.data_ptr(), beta.data_ptr(),
+        float(eps), slots.data_ptr(), cache.data_ptr() + int(section_offset), int(num_pages),
+        int(page_stride), out.data_ptr(), out.stride(0), w_out.data_ptr(), w_out.stride(0),
+        _stream(q))
+    _check("index_inputs", st)
+    return out, w_out
 
 
 def decode_layout(seq_lens, query_lens, num_rows, dcp_rank=0, dcp_world_size=1, interleave=1,

@@ -106,6 +106,43 @@ dsaidx_status dsaidx_store_keys(int fmt, const void *keys, int64_t tokens, int64
                                                 as_stream(stream)));
 }
 
+dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens,
+                                  int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+                                  const void *q, int32_t heads, int64_t q_row_stride,
+                                  int64_t q_head_stride, const float *gamma, const float *beta,
+                                  float eps, const int64_t *slots, void *cache,
+                                  int64_t num_pages, int64_t page_stride, void *q_out,
+                                  int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride,
+                                  void *stream) {
+    if (!valid_fmt(fmt) || tokens < 0 || tokens > kMaxGrid || num_pages < 0 || key_col < 0 ||
+        weight_col < 0)
+        return DSAIDX_EINVAL;
+    if (!std::isfinite(eps) || eps < 0.0f) return DSAIDX_EINVAL;
+    if (!valid_heads(heads)) return DSAIDX_EUNSUPPORTED;
+    if (tokens == 0) return DSAIDX_OK;
+    if (!projected || !q || !gamma || !beta || !slots || !cache || !q_out || !w_out)
+        return DSAIDX_EINVAL;
+    // packed row: the key's 128 columns and the H weight columns lie inside each row; the key
+    // is read as 4-byte column pairs
+    if (proj_row_stride < key_col + DSAIDX_DIM || proj_row_stride < weight_col + heads ||
+        !aligned(projected, 4) || proj_row_stride % 2 || key_col % 2)
+        return DSAIDX_ELAYOUT;
+    if (q_head_stride < DSAIDX_DIM || q_row_stride < (int64_t)(heads - 1) * q_head_stride + DSAIDX_DIM)
+        return DSAIDX_ELAYOUT;
+    if (!aligned(q, 16) || q_head_stride % 8 || q_row_stride % 8) return DSAIDX_ELAYOUT;
+    if (!aligned(q_out, 16) || q_out_row_stride % 16 ||
+        q_out_row_stride < dsaidx_query_row_bytes(fmt, heads))
+        return DSAIDX_ELAYOUT;
+    if (w_out_row_stride < heads || !aligned(w_out, 2)) return DSAIDX_ELAYOUT;
+    if (!aligned(gamma, 8) || !aligned(beta, 8) || !aligned(slots, 8)) return DSAIDX_ELAYOUT;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_index_inputs(
+        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
+        q_out_row_stride, w_out, w_out_row_stride, head_weight_scale(heads), as_stream(stream)));
+}
+
 dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
                                    int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
                                    int32_t dcp_world_size, int32_t interleave,

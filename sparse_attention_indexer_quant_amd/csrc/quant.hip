@@ -4,6 +4,8 @@
 //   quantize_fp4_query (MXFP4 of one head; scales after all payload bytes) and
 //   DsaIndex.fp8_query (FP8 with one power-of-two scale per head folded into the weight);
 //   page "vllm.models.kimi_k3.amd.ops.fp4_indexer", quantize_queries (shape rules).
+// index_inputs: same index page, DsaIndex (both of the above for one token per workgroup,
+//   reading the head weights and the key from the packed projection row).
 // store_keys: same index page, insert_key (FP32 LayerNorm, BF16, then the cache writer) and
 //   insert_fp4_key (payload at token * 64, four UE8M0 bytes at 64 * 64 + token * 4);
 //   fp4_indexer page, store_keys (negative slots are padding) and cache_views (sections
@@ -16,20 +18,19 @@
 
 namespace dsaidx {
 
-// One workgroup (256 lanes = 4 wavefronts) per query row. Lane t owns 8 consecutive
+// One query row on a workgroup of 256 lanes (4 wavefronts). Lane t owns 8 consecutive
 // columns (one 16-byte load) of head (t / 16) + 16 * pass: 16 lanes per head, 4 lanes per
-// 32-value MX block.
+// 32-value MX block. `wv_row` (raw head weights, unit head stride) may be null.
 template <int FMT>
-__global__ __launch_bounds__(256) void quantize_queries_kernel(
-    const uint16_t *__restrict__ q, int heads, int64_t q_row_stride, int64_t q_head_stride,
-    const uint16_t *__restrict__ wv, int64_t wv_row_stride, uint8_t *__restrict__ q_out,
-    int64_t q_out_row_stride, uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ q_row, int heads,
+                                                   int64_t q_head_stride,
+                                                   const uint16_t *__restrict__ wv_row,
+                                                   uint8_t *__restrict__ out_row,
+                                                   uint16_t *__restrict__ w_out_row, float c_h,
+                                                   int tid) {
     const int part = tid & 15;
-    uint8_t *out_row = q_out + row * q_out_row_stride;
     for (int head = tid >> 4; head < heads; head += 16) {
-        const uint16_t *src = q + row * q_row_stride + (int64_t)head * q_head_stride + part * 8;
+        const uint16_t *src = q_row + (int64_t)head * q_head_stride + part * 8;
         const uint4 raw = *reinterpret_cast<const uint4 *>(src);
         float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
@@ -51,9 +52,9 @@ __global__ __launch_bounds__(256) void quantize_queries_kernel(
             if (part == 0) {
                 *reinterpret_cast<uint32_t *>(out_row + heads * 64 + head * 4) =
                     byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-                if (wv) {
-                    const float w = bf16_val(wv[row * wv_row_stride + head]);
-                    w_out[row * w_out_row_stride + head] = (uint16_t)bf16_bits_rne(__fmul_rn(w, c_h));
+                if (wv_row) {
+                    const float w = bf16_val(wv_row[head]);
+                    w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(w, c_h));
                 }
             }
         } else {
@@ -70,30 +71,26 @@ __global__ __launch_bounds__(256) void quantize_queries_kernel(
                 hi |= e4m3_code(__fmul_rn(v[4 + i], inv)) << (8 * i);
             }
             *reinterpret_cast<uint2 *>(out_row + head * 128 + part * 8) = make_uint2(lo, hi);
-            if (part == 0 && wv) {
-                const float w = bf16_val(wv[row * wv_row_stride + head]);
-                w_out[row * w_out_row_stride + head] =
-                    (uint16_t)bf16_bits_rne(__fmul_rn(__fmul_rn(w, s), c_h));
+            if (part == 0 && wv_row) {
+                const float w = bf16_val(wv_row[head]);
+                w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(__fmul_rn(w, s), c_h));
             }
         }
     }
 }
 
-// One wavefront per key: lane l owns columns 2l and 2l+1 (one 4-byte load). The LayerNorm
+// One key on one wavefront: lane l owns columns 2l and 2l+1 (one 4-byte load). The LayerNorm
 // sums run as the pairwise tree "adjacent pair, then fold 32, 16, 8, 4, 2, 1 apart", which
-// the xor butterfly below computes in every lane.
+// the xor butterfly below computes in every lane. Slots outside [0, num_pages * 64) (negative
+// slots are padding) write nothing.
 template <int FMT>
-__global__ __launch_bounds__(256) void store_keys_kernel(
-    const uint16_t *__restrict__ keys, int64_t tokens, int64_t k_row_stride,
-    const float *__restrict__ gamma, const float *__restrict__ beta, float eps,
-    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
-    int64_t page_stride) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= tokens) return;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_pages * kPageTokens) return;  // padding / out of range
-    const uint32_t pair = *reinterpret_cast<const uint32_t *>(keys + t * k_row_stride + 2 * lane);
+__device__ __forceinline__ void store_key(const uint16_t *__restrict__ key,
+                                          const float *__restrict__ gamma,
+                                          const float *__restrict__ beta, float eps, int64_t slot,
+                                          uint8_t *__restrict__ cache, int64_t num_pages,
+                                          int64_t page_stride, int lane) {
+    if (slot < 0 || slot >= num_pages * kPageTokens) return;
+    const uint32_t pair = *reinterpret_cast<const uint32_t *>(key + 2 * lane);
     const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
 
     float sum = __fadd_rn(x0, x1);
@@ -135,6 +132,54 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
     }
 }
 
+// One workgroup per query row.
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_queries_kernel(
+    const uint16_t *__restrict__ q, int heads, int64_t q_row_stride, int64_t q_head_stride,
+    const uint16_t *__restrict__ wv, int64_t wv_row_stride, uint8_t *__restrict__ q_out,
+    int64_t q_out_row_stride, uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
+    const int64_t row = blockIdx.x;
+    quantize_query_row<FMT>(q + row * q_row_stride, heads, q_head_stride,
+                            wv ? wv + row * wv_row_stride : nullptr, q_out + row * q_out_row_stride,
+                            w_out ? w_out + row * w_out_row_stride : nullptr, c_h, threadIdx.x);
+}
+
+// One wavefront per key, four keys per workgroup.
+template <int FMT>
+__global__ __launch_bounds__(256) void store_keys_kernel(
+    const uint16_t *__restrict__ keys, int64_t tokens, int64_t k_row_stride,
+    const float *__restrict__ gamma, const float *__restrict__ beta, float eps,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
+    int64_t page_stride) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= tokens) return;
+    store_key<FMT>(keys + t * k_row_stride, gamma, beta, eps, slots[t], cache, num_pages,
+                   page_stride, threadIdx.x & 63);
+}
+
+// The indexer inputs of one step in one launch (page
+// "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex): one workgroup
+// per token quantizes the token's query with the head weights read from the packed projection
+// row, and its last wavefront then normalizes, quantizes and inserts the key held in the same
+// row (at H = 16, 32, 64 every wavefront quantizes the same number of heads).
+template <int FMT>
+__global__ __launch_bounds__(256) void index_inputs_kernel(
+    const uint16_t *__restrict__ projected, int64_t proj_row_stride, int64_t key_col,
+    int64_t weight_col, const uint16_t *__restrict__ q, int heads, int64_t q_row_stride,
+    int64_t q_head_stride, const float *__restrict__ gamma, const float *__restrict__ beta,
+    float eps, const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
+    int64_t page_stride, uint8_t *__restrict__ q_out, int64_t q_out_row_stride,
+    uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
+    const int64_t token = blockIdx.x;
+    const uint16_t *prow = projected + token * proj_row_stride;
+    quantize_query_row<FMT>(q + token * q_row_stride, heads, q_head_stride, prow + weight_col,
+                            q_out + token * q_out_row_stride, w_out + token * w_out_row_stride, c_h,
+                            threadIdx.x);
+    if ((threadIdx.x >> 6) == 3)
+        store_key<FMT>(prow + key_col, gamma, beta, eps, slots[token], cache, num_pages,
+                       page_stride, threadIdx.x & 63);
+}
+
 hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,
                                    int64_t q_row_stride, int64_t q_head_stride, const void *wv,
                                    int64_t wv_row_stride, void *q_out, int64_t q_out_row_stride,
@@ -169,6 +214,33 @@ hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t 
     else
         hipLaunchKernelGGL(store_keys_kernel<kFmtFp8>, grid, block, 0, stream, kk, tokens,
                            k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
+                               int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+                               const void *q, int heads, int64_t q_row_stride,
+                               int64_t q_head_stride, const float *gamma, const float *beta,
+                               float eps, const int64_t *slots, void *cache, int64_t num_pages,
+                               int64_t page_stride, void *q_out, int64_t q_out_row_stride,
+                               void *w_out, int64_t w_out_row_stride, float c_h,
+                               hipStream_t stream) {
+    const dim3 grid((unsigned)tokens), block(256);
+    auto *pp = static_cast<const uint16_t *>(projected);
+    auto *qq = static_cast<const uint16_t *>(q);
+    auto *cc = static_cast<uint8_t *>(cache);
+    auto *qo = static_cast<uint8_t *>(q_out);
+    auto *wo = static_cast<uint16_t *>(w_out);
+    if (fmt == kFmtMxfp4)
+        hipLaunchKernelGGL(index_inputs_kernel<kFmtMxfp4>, grid, block, 0, stream, pp,
+                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
+                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
+                           q_out_row_stride, wo, w_out_row_stride, c_h);
+    else
+        hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8>, grid, block, 0, stream, pp,
+                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
+                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
+                           q_out_row_stride, wo, w_out_row_stride, c_h);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsaidx_quantize_queries", "dsaidx_store_keys", "dsaidx_score_paged", "dsaidx_topk",
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
-              "dsaidx_query_row_bytes"):
+              "dsaidx_query_row_bytes", "dsaidx_index_inputs"):
         assert n in names
 
 
@@ -100,6 +100,38 @@ def test_store_keys_checks(lib):
     assert store(lib, fmt=FP8, ps=4352) == ELAYOUT  # FP8 sections are 8448 B
     assert store(lib, cache=P + 8) == ELAYOUT
     assert store(lib, g=P + 4) == ELAYOUT
+
+
+def inputs(lib, **kw):
+    a = dict(fmt=MX, proj=P, t=4, ps=4352, kc=4096, wc=4224, q=P, h=32, qs=4096, qh=128, g=P,
+             b=P, eps=1e-6, slots=P, cache=P, pages=4, cs=4352, qo=P, qos=2176, wo=P, wos=32)
+    a.update(kw)
+    return lib.dsaidx_index_inputs(a["fmt"], a["proj"], a["t"], a["ps"], a["kc"], a["wc"], a["q"],
+                                   a["h"], a["qs"], a["qh"], a["g"], a["b"], a["eps"], a["slots"],
+                                   a["cache"], a["pages"], a["cs"], a["qo"], a["qos"], a["wo"],
+                                   a["wos"], None)
+
+
+def test_index_inputs_checks(lib):
+    assert inputs(lib, fmt=2) == EINVAL
+    assert inputs(lib, t=-1) == EINVAL
+    assert inputs(lib, kc=-2) == EINVAL
+    assert inputs(lib, wc=-1) == EINVAL
+    assert inputs(lib, eps=float("inf")) == EINVAL
+    assert inputs(lib, h=48) == EUNSUP
+    assert inputs(lib, t=0, proj=None, q=None) == OK
+    assert inputs(lib, wo=None) == EINVAL               # head weights are always written
+    assert inputs(lib, slots=None) == EINVAL
+    assert inputs(lib, ps=4223) == ELAYOUT              # key columns outside the row
+    assert inputs(lib, ps=4240) == ELAYOUT              # weight columns outside the row
+    assert inputs(lib, kc=4095) == ELAYOUT              # key read as column pairs
+    assert inputs(lib, ps=4353) == ELAYOUT
+    assert inputs(lib, proj=P + 2) == ELAYOUT
+    assert inputs(lib, qh=127) == ELAYOUT               # contiguous 128-element heads
+    assert inputs(lib, q=P + 8) == ELAYOUT
+    assert inputs(lib, qos=2175) == ELAYOUT
+    assert inputs(lib, cs=4351) == ELAYOUT              # cache_views: stride >= 4352
+    assert inputs(lib, fmt=FP8, qos=4096, cs=4352) == ELAYOUT
 
 
 def layout(lib, **kw):

@@ -137,6 +137,73 @@ def test_store_keys_empty_and_all_padding():
     assert torch.all(cache == 0x5A)
 
 
+# ---- index_inputs (fused per-token query quant + weights + key insert) ---------------------
+
+@pytest.mark.parametrize("fmt,heads,stride,offset,key_col,weight_col",
+                         [("mxfp4", 32, 4352, 0, 4096, 4224), ("mxfp4", 64, 8192, 3840, 0, 130),
+                          ("mxfp4", 16, 4352, 0, 2, 1), ("fp8", 32, 8448, 0, 200, 4),
+                          ("fp8", 64, 9216, 512, 8192, 0)])
+def test_index_inputs_bit_exact(fmt, heads, stride, offset, key_col, weight_col):
+    # queries with the same edge rows as the quantize tests, keys with extreme scales, padding
+    # and out-of-range slots, and packed rows whose other columns hold NaN / Inf patterns
+    rng = np.random.default_rng(30 + heads)
+    pages = 7
+    tokens = 45
+    q = rng.standard_normal((tokens, heads, 128)).astype(np.float32)
+    q[0] = 0.0
+    q[1] *= 1e-38
+    q[2, :, ::3] *= 1e30
+    q[3] = -0.0
+    keys = rng.standard_normal((tokens, 128)).astype(np.float32)
+    keys[4] = 2.5
+    keys[5] *= 1e4
+    keys[6] *= 1e-4
+    wv = (rng.standard_normal((tokens, heads)) * 3).astype(np.float32)
+    cols = max(key_col + 128, weight_col + heads) + 6
+    proj = rng.choice(np.array([0x7FC0, 0xFF80, 0x7F80, 0x3F80], np.uint16), size=(tokens, cols))
+    proj[:, key_col:key_col + 128] = bf16_bits(keys)
+    proj[:, weight_col:weight_col + heads] = bf16_bits(wv)
+    slots = rng.permutation(pages * 64)[:tokens].astype(np.int64)
+    slots[7] = -1
+    slots[8] = 64 * pages + 1
+    gamma = bf16_to_f32(bf16_bits(1 + 0.1 * rng.standard_normal(128).astype(np.float32)))
+    beta = bf16_to_f32(bf16_bits(0.1 * rng.standard_normal(128).astype(np.float32)))
+    section = 4352 if fmt == "mxfp4" else 8448
+    nbytes = offset + (pages - 1) * stride + section
+    want_cache = np.full(nbytes, 0xA5, np.uint8)
+    want_q, want_w = oracle.index_inputs(proj, key_col, weight_col, bf16_bits(q), gamma, beta, 1e-6,
+                                         slots, want_cache, pages, stride, offset, fmt)
+    got_cache = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    proj_dev = bf16_dev(proj)
+    got_q, got_w = dsa.index_inputs(proj_dev, key_col, weight_col, bf16_dev(bf16_bits(q)), dev(gamma),
+                                    dev(beta), 1e-6, dev(slots), got_cache, pages, stride, fmt,
+                                    offset)
+    assert np.array_equal(got_q.cpu().numpy(), want_q)
+    assert np.array_equal(bf16_host(got_w), want_w)
+    assert np.array_equal(got_cache.cpu().numpy(), want_cache)
+
+
+def test_index_inputs_matches_separate_calls_and_empty():
+    # one launch gives the same bytes as quantize_queries + store_keys on the extracted columns
+    rng = np.random.default_rng(44)
+    tokens, heads, pages = 20, 32, 3
+    proj = bf16_bits(rng.standard_normal((tokens, 300)).astype(np.float32))
+    q = bf16_bits(rng.standard_normal((tokens, heads, 128)).astype(np.float32))
+    slots = rng.permutation(pages * 64)[:tokens].astype(np.int64)
+    g, b = dev(np.ones(128, np.float32)), dev(np.zeros(128, np.float32))
+    c1 = torch.zeros(pages * 4352, dtype=torch.uint8, device="cuda")
+    c2 = torch.zeros(pages * 4352, dtype=torch.uint8, device="cuda")
+    proj_dev = bf16_dev(proj)
+    q1, w1 = dsa.index_inputs(proj_dev, 10, 160, bf16_dev(q), g, b, 1e-6, dev(slots), c1, pages, 4352)
+    q2, w2 = dsa.quantize_queries(bf16_dev(q), proj_dev[:, 160:160 + heads].contiguous())
+    dsa.store_keys(proj_dev[:, 10:138].contiguous(), g, b, 1e-6, dev(slots), c2, pages, 4352)
+    assert torch.equal(q1, q2) and torch.equal(w1, w2) and torch.equal(c1, c2)
+    # no tokens: nothing enqueued, nothing written
+    c3 = torch.full((4352,), 0x5A, dtype=torch.uint8, device="cuda")
+    dsa.index_inputs(proj_dev[:0], 10, 160, bf16_dev(q)[:0], g, b, 1e-6, dev(slots)[:0], c3, 1, 4352)
+    assert torch.all(c3 == 0x5A)
+
+
 # ---- decode_layout --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seq,ql,rows,dcp", [
