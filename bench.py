@@ -2,7 +2,9 @@
 
 One step = one pass of the whole path over one decode batch, inputs resident in HBM:
 index_inputs (one launch: every row's query quantized with its head weights, and the step's
-new keys normalized, quantized and inserted), decode_layout, score_paged, topk. Prints ONE JSON line: scored (row, key) pairs per second of the whole
+new keys normalized, quantized and inserted), decode_layout, score_paged_hist (scoring that
+also writes the top-k segment histograms) and topk_scored. The same step with the separate
+score_paged + topk is timed too (per_config ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of the whole
 step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
 launch stream around every score launch in the timed region), and the CPU oracle timed on
 a bounded sample of the same workload.
@@ -77,6 +79,17 @@ def packed_rows(wl):
     return proj, slots
 
 
+def hist_segment_keys(wl):
+    """Keys per scoring workgroup (the top-k segment score_paged_hist writes histograms for):
+    4 wavefronts x pages per wavefront x 64, with the scorer's pages-per-wavefront rule."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    target = cus * 8
+    ppw = (wl.num_requests * wl.max_blocks + target - 1) // target
+    ppw = min(16, max(4, (ppw + 3) // 4 * 4))
+    return 4 * ppw * 64
+
+
 class Setup:
     """Device buffers of one workload, the cache replicas, and the prepared step calls."""
 
@@ -131,6 +144,8 @@ class Setup:
         self.idx = torch.empty((wl.num_rows, wl.topk), dtype=torch.int32, device=dev)
         wsb = dsa.topk_workspace_bytes(wl.num_rows, wl.width, wl.topk)
         self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        hwsb = dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows)
+        self.hws = torch.empty(max(hwsb, 1), dtype=torch.uint8, device=dev)
 
         self.quant = Prepared(lib.dsaidx_quantize_queries, fmt, self.q.data_ptr(), wl.num_rows,
                               wl.heads, self.q.stride(0), self.q.stride(1), self.wv.data_ptr(),
@@ -142,7 +157,11 @@ class Setup:
         self.topk = Prepared(lib.dsaidx_topk, self.logits.data_ptr(), wl.num_rows, wl.width,
                              self.logits.stride(0), self.ends.data_ptr(), wl.topk,
                              self.idx.data_ptr(), self.idx.stride(0), self.ws.data_ptr(), wsb, sp)
-        self.store, self.score, self.inputs = [], [], []
+        self.topk_scored = Prepared(lib.dsaidx_topk_scored, self.logits.data_ptr(), wl.num_rows,
+                                    self.logits.stride(0), self.ends.data_ptr(), wl.topk,
+                                    self.idx.data_ptr(), self.idx.stride(0), wl.num_requests,
+                                    wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
+        self.store, self.score, self.inputs, self.score_hist = [], [], [], []
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(
@@ -163,6 +182,12 @@ class Setup:
                 wl.page_stride, self.block_table.data_ptr(), wl.num_requests, wl.max_blocks,
                 self.starts.data_ptr(), self.ends.data_ptr(), wl.num_rows, wl.max_query_len,
                 self.logits.data_ptr(), self.logits.stride(0), sp))
+            self.score_hist.append(Prepared(
+                lib.dsaidx_score_paged_hist, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
+                wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
+                wl.page_stride, self.block_table.data_ptr(), wl.num_requests, wl.max_blocks,
+                self.starts.data_ptr(), self.ends.data_ptr(), wl.num_rows, wl.max_query_len,
+                self.logits.data_ptr(), self.logits.stride(0), self.hws.data_ptr(), hwsb, sp))
         self.layout()
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
@@ -174,8 +199,25 @@ class Setup:
         per_row_q = rb + 2 * wl.heads
         self.score_bytes = wl.key_bytes() + 4 * self.pairs + wl.num_rows * per_row_q
         self.score_flops = 2 * wl.heads * 128 * self.pairs
+        # score_paged_hist also writes one 8 KB histogram per (row, scoring workgroup) that
+        # holds keys of the row
+        seg = hist_segment_keys(wl)
+        self.hist_bytes = int(sum(8192 * ((int(e) + seg - 1) // seg) for e in ends))
+        self.score_hist_bytes = self.score_bytes + self.hist_bytes
 
     def step(self, i, ev=None):
+        """index_inputs, decode_layout, score_paged_hist (timed), topk_scored."""
+        self.inputs[i % len(self.caches)]()
+        self.layout()
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.score_hist[i % len(self.caches)]()
+        if ev is not None:
+            ev[1].record(self.stream)
+        self.topk_scored()
+
+    def step_unfused(self, i, ev=None):
+        """index_inputs, decode_layout, score_paged (timed), topk."""
         self.inputs[i % len(self.caches)]()
         self.layout()
         if ev is not None:
@@ -186,17 +228,18 @@ class Setup:
         self.topk()
 
 
-def time_steps(s: Setup, steps: int, warmup: int):
+def time_steps(s: Setup, steps: int, warmup: int, fused: bool = True):
     import torch
+    step = s.step if fused else s.step_unfused
     for i in range(warmup):
-        s.step(i)
+        step(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        s.step(warmup + i, evs[i])
+        step(warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     score_ms = np.array([a.elapsed_time(b) for a, b in evs])
@@ -212,7 +255,9 @@ def kernel_times(s: Setup, reps: int = 30):
               ("store_keys", lambda i: s.store[i % len(s.caches)]()),
               ("decode_layout", lambda i: s.layout()),
               ("score_paged", lambda i: s.score[i % len(s.caches)]()),
-              ("topk", lambda i: s.topk())]
+              ("topk", lambda i: s.topk()),
+              ("score_paged_hist", lambda i: s.score_hist[i % len(s.caches)]()),
+              ("topk_scored", lambda i: s.topk_scored())]
     for name, fn in stages:
         ts = []
         for i in range(reps):
@@ -304,9 +349,11 @@ def measured_traffic(score_bytes):
 def run_config(name, args, steps, warmup, cpu_budget):
     import torch
     s = Setup(name, args.min_rotation_mb)
-    wall, score_ms = time_steps(s, steps, warmup)
+    wall_u, score_ms_u = time_steps(s, steps, warmup, fused=False)
+    wall, score_ms = time_steps(s, steps, warmup, fused=True)
     ms_step = wall / steps * 1e3
     score_us = float(score_ms.mean() * 1e3)
+    score_us_u = float(score_ms_u.mean() * 1e3)
     res = {
         "workload": name,
         "fmt": s.wl.fmt, "heads": s.wl.heads, "rows": s.wl.num_rows, "requests": s.wl.num_requests,
@@ -318,8 +365,14 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "score_us_p10_p50_p90": [float(np.percentile(score_ms, p) * 1e3) for p in (10, 50, 90)],
         "score_pairs_per_s": s.pairs / (score_us / 1e6),
         "score_key_GBps": s.wl.key_bytes() / (score_us / 1e6) / 1e9,
-        "score_algorithmic_GBps": s.score_bytes / (score_us / 1e6) / 1e9,
-        "score_algorithmic_bytes": s.score_bytes,
+        "score_algorithmic_GBps": s.score_hist_bytes / (score_us / 1e6) / 1e9,
+        "score_algorithmic_bytes": s.score_hist_bytes,
+        "score_histogram_bytes": s.hist_bytes,
+        "score_kernel": "score_paged_hist",
+        "ms_per_step_unfused": wall_u / steps * 1e3,
+        "step_pairs_per_s_unfused": s.pairs / (wall_u / steps),
+        "score_paged_us_mean_unfused": score_us_u,
+        "score_paged_algorithmic_GBps_unfused": s.score_bytes / (score_us_u / 1e6) / 1e9,
         "score_TFLOPs": s.score_flops / (score_us / 1e6) / 1e12,
         "cache_replicas": len(s.caches),
         "kernel_us_alone": {k: v * 1e3 for k, v in kernel_times(s).items()},
@@ -392,7 +445,8 @@ def main():
         "key_cache_frac_of_peak": m["score_key_frac_of_peak"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "score_paged", "bytes_per_launch": m["score_algorithmic_bytes"],
+                     "kernel": "score_paged_hist",
+                     "bytes_per_launch": m["score_algorithmic_bytes"],
                      "launch_us_mean": m["score_us_mean"]},
         "cpu_baseline": m.get("cpu_baseline"),
         "per_config": per_config,

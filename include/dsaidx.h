@@ -206,6 +206,55 @@ dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, i
                                  int32_t max_query_len, float *logits,
                                  int64_t logits_row_stride, void *stream);
 
+/*
+ * Scoring and selection with one pass fewer over the logits ([ovl] module text: the indexer
+ * path is scoring and then top-k; [fp4ops] decode_tile_size sizes logits plus selection
+ * scratch together). dsaidx_score_paged_hist scores exactly as dsaidx_score_paged does (the
+ * same logits, bit for bit) and also counts every written logit into a histogram per
+ * (row, scoring workgroup) inside a top-k workspace; dsaidx_topk_scored then selects as
+ * dsaidx_topk does (the same index sets) without its own histogram pass.
+ *
+ * dsaidx_score_topk_workspace_bytes: device workspace bytes for these sizes on the current
+ * device (the segment geometry depends on its compute-unit count); 0 if the sizes are
+ * invalid or a row would span more than 1024 scoring workgroups (more than 4,194,304 keys).
+ */
+size_t dsaidx_score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks,
+                                         int64_t num_rows);
+
+/*
+ * score_paged_hist -- dsaidx_score_paged plus the top-k segment histograms.
+ *  All arguments as dsaidx_score_paged, and
+ *  workspace  device, >= dsaidx_score_topk_workspace_bytes(num_requests, max_blocks,
+ *           num_rows) bytes, 256-byte aligned, caller-owned, no initialisation needed.
+ *  Errors: as dsaidx_score_paged; a missing or short workspace gives DSAIDX_EINVAL; more
+ *  than 1024 scoring workgroups per row gives DSAIDX_EUNSUPPORTED.
+ */
+dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stride,
+                                      int32_t heads, const void *w, int64_t w_row_stride,
+                                      const void *cache, int64_t num_pages, int64_t page_stride,
+                                      const int32_t *block_table, int64_t num_requests,
+                                      int64_t max_blocks, const int32_t *query_starts,
+                                      const int32_t *row_ends, int64_t num_rows,
+                                      int32_t max_query_len, float *logits,
+                                      int64_t logits_row_stride, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
+ * topk_scored -- the per-row top-k of logits that dsaidx_score_paged_hist has just written,
+ * using its histograms. Rows, bounds and output as dsaidx_topk with width = max_blocks * 64.
+ *  num_requests, max_blocks, workspace  exactly as passed to the dsaidx_score_paged_hist call
+ *           that wrote the logits and histograms (same stream, ordered after it; the same
+ *           device). A row whose keys that call did not score (a row beyond max_query_len
+ *           of its request) gets unspecified positions, as its logits are unwritten.
+ *  Errors: k < 1 or negative sizes give DSAIDX_EINVAL, as do num_requests or max_blocks of
+ *  0 with rows to select; a short workspace gives DSAIDX_EINVAL.
+ */
+dsaidx_status dsaidx_topk_scored(const float *logits, int64_t num_rows, int64_t logits_row_stride,
+                                 const int32_t *row_ends, int32_t k, int32_t *indices,
+                                 int64_t indices_row_stride, int64_t num_requests,
+                                 int64_t max_blocks, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Device workspace bytes that dsaidx_topk needs for these sizes (0: none). */
 size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k);
 

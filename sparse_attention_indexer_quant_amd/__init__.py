@@ -17,6 +17,7 @@ page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex
   decode_layout(seq_lens, query_lens, num_rows, dcp_rank, dcp_world_size, interleave)
   score_paged(q_rows, heads, weights, cache, ..., block_table, query_starts, row_ends, max_query_len)
   topk(logits, row_ends, k)
+  score_topk(...)  = score_paged + topk with the scorer writing the selection's histograms
 """
 from __future__ import annotations
 
@@ -63,6 +64,10 @@ def library():
             "dsaidx_score_paged": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64, P, P,
                                          I64, I32, P, I64, P]),
             "dsaidx_topk_workspace_bytes": (SZ, [I64, I64, I32]),
+            "dsaidx_score_topk_workspace_bytes": (SZ, [I64, I64, I64]),
+            "dsaidx_score_paged_hist": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
+                                              P, P, I64, I32, P, I64, P, SZ, P]),
+            "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
@@ -245,6 +250,51 @@ def score_paged(q_rows, heads, weights, cache, num_pages, page_stride, block_tab
         out.data_ptr(), out.stride(0), _stream(q_rows))
     _check("score_paged", st)
     return out
+
+
+def score_topk_workspace_bytes(num_requests, max_blocks, num_rows) -> int:
+    return int(library().dsaidx_score_topk_workspace_bytes(int(num_requests), int(max_blocks),
+                                                           int(num_rows)))
+
+
+def score_topk(q_rows, heads, weights, cache, num_pages, page_stride, block_table, query_starts,
+               row_ends, max_query_len, k, fmt="mxfp4", section_offset=0, out=None, indices=None,
+               workspace=None):
+    """score_paged followed by topk with one pass fewer over the logits: the scorer writes the
+    selection's histograms. Returns (logits FP32 [rows, max_blocks*64], indices int32 [rows, k])."""
+    import torch
+    _dev(q_rows, "q_rows", torch.uint8)
+    _dev(weights, "weights", torch.bfloat16)
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(query_starts, "query_starts", torch.int32)
+    _dev(row_ends, "row_ends", torch.int32)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("score_topk: block_table must be [requests, max_blocks], row-major")
+    num_rows = row_ends.numel()
+    R, mb = block_table.shape
+    if out is None:
+        out = torch.empty((num_rows, mb * PAGE_TOKENS), dtype=torch.float32, device=q_rows.device)
+    if indices is None:
+        indices = torch.empty((num_rows, int(k)), dtype=torch.int32, device=q_rows.device)
+    _dev(out, "out", torch.float32)
+    _dev(indices, "indices", torch.int32)
+    need = score_topk_workspace_bytes(R, mb, num_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_rows.device)
+    lib = library()
+    st = lib.dsaidx_score_paged_hist(
+        _fmt(fmt), q_rows.data_ptr(), q_rows.stride(0), int(heads), weights.data_ptr(),
+        weights.stride(0), cache.data_ptr() + int(section_offset), int(num_pages),
+        int(page_stride), block_table.data_ptr(), R, block_table.stride(0),
+        query_starts.data_ptr(), row_ends.data_ptr(), num_rows, int(max_query_len),
+        out.data_ptr(), out.stride(0), workspace.data_ptr(), workspace.numel(), _stream(q_rows))
+    _check("score_paged_hist", st)
+    st = lib.dsaidx_topk_scored(out.data_ptr(), num_rows, out.stride(0), row_ends.data_ptr(),
+                                int(k), indices.data_ptr(), indices.stride(0), R, mb,
+                                workspace.data_ptr(), workspace.numel(), _stream(q_rows))
+    _check("topk_scored", st)
+    return out, indices
 
 
 def topk_workspace_bytes(rows, width, k) -> int:

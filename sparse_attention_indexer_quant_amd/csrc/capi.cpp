@@ -13,6 +13,7 @@
 
 #include "dsaidx.h"
 #include "launch.h"
+#include "topk_layout.h"
 
 namespace {
 
@@ -189,6 +190,77 @@ dsaidx_status dsaidx_score_paged(int fmt, const void *q, int64_t q_row_stride, i
                         num_requests, max_blocks, query_starts, row_ends,     num_rows,
                         max_query_len, logits,    logits_row_stride};
     return hip_status(dsaidx::launch_score_paged(a, as_stream(stream)));
+}
+
+size_t dsaidx_score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks,
+                                         int64_t num_rows) {
+    if (num_requests < 1 || max_blocks < 1 || num_rows < 0 || max_blocks > (int64_t)INT32_MAX / 64)
+        return 0;
+    if (dsaidx::score_geometry(num_requests, max_blocks).chunks > dsaidx::kMaxRowSegments) return 0;
+    return dsaidx::score_topk_workspace_bytes(num_requests, max_blocks, num_rows);
+}
+
+dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stride,
+                                      int32_t heads, const void *w, int64_t w_row_stride,
+                                      const void *cache, int64_t num_pages, int64_t page_stride,
+                                      const int32_t *block_table, int64_t num_requests,
+                                      int64_t max_blocks, const int32_t *query_starts,
+                                      const int32_t *row_ends, int64_t num_rows,
+                                      int32_t max_query_len, float *logits,
+                                      int64_t logits_row_stride, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    // the argument rules of score_paged first (a dry run: launch nothing yet)
+    if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0)
+        return DSAIDX_EINVAL;
+    if (!valid_heads(heads) || max_query_len < 1 || max_query_len > DSAIDX_MAX_QUERY_LEN)
+        return DSAIDX_EUNSUPPORTED;
+    if (num_rows == 0 || num_requests == 0 || max_blocks == 0 || num_pages == 0) return DSAIDX_OK;
+    if (!q || !w || !cache || !block_table || !query_starts || !row_ends || !logits)
+        return DSAIDX_EINVAL;
+    if (!aligned(q, 16) || q_row_stride % 16 || q_row_stride < dsaidx_query_row_bytes(fmt, heads))
+        return DSAIDX_ELAYOUT;
+    if (!aligned(w, 8) || w_row_stride % 4 || w_row_stride < heads) return DSAIDX_ELAYOUT;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS ||
+        logits_row_stride < max_blocks * DSAIDX_PAGE_TOKENS || !aligned(logits, 4))
+        return DSAIDX_ELAYOUT;
+    const dsaidx::ScoreGeometry geo = dsaidx::score_geometry(num_requests, max_blocks);
+    if (geo.chunks * num_requests > kMaxGrid || geo.chunks > dsaidx::kMaxRowSegments)
+        return DSAIDX_EUNSUPPORTED;
+    const size_t need = dsaidx::score_topk_workspace_bytes(num_requests, max_blocks, num_rows);
+    if (!workspace || workspace_bytes < need) return DSAIDX_EINVAL;
+    if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
+    dsaidx::ScoreArgs a{fmt,         q,          q_row_stride, heads,         w,
+                        w_row_stride, cache,     num_pages,    page_stride,   block_table,
+                        num_requests, max_blocks, query_starts, row_ends,     num_rows,
+                        max_query_len, logits,    logits_row_stride};
+    return hip_status(dsaidx::launch_score_paged_hist(a, workspace, as_stream(stream)));
+}
+
+dsaidx_status dsaidx_topk_scored(const float *logits, int64_t num_rows, int64_t logits_row_stride,
+                                 const int32_t *row_ends, int32_t k, int32_t *indices,
+                                 int64_t indices_row_stride, int64_t num_requests,
+                                 int64_t max_blocks, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    if (num_rows < 0 || num_requests < 0 || max_blocks < 0 || k < 1) return DSAIDX_EINVAL;
+    if (num_rows == 0) return DSAIDX_OK;
+    if (num_requests == 0 || max_blocks == 0) return DSAIDX_EINVAL;  // no scoring geometry
+    if (!row_ends || !indices || !logits || !workspace) return DSAIDX_EINVAL;
+    if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS) return DSAIDX_ELAYOUT;
+    const int64_t width = max_blocks * DSAIDX_PAGE_TOKENS;
+    if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||
+        !aligned(indices, 4))
+        return DSAIDX_ELAYOUT;
+    const dsaidx::ScoreGeometry geo = dsaidx::score_geometry(num_requests, max_blocks);
+    if (geo.chunks > dsaidx::kMaxRowSegments || num_rows * (geo.chunks + 1) > kMaxGrid)
+        return DSAIDX_EUNSUPPORTED;
+    if (workspace_bytes < dsaidx::score_topk_workspace_bytes(num_requests, max_blocks, num_rows))
+        return DSAIDX_EINVAL;
+    if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_topk_after_histograms(
+        logits, num_rows, width, logits_row_stride, row_ends, k, indices, indices_row_stride,
+        workspace, geo.chunks, geo.segment_keys, as_stream(stream)));
 }
 
 size_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t width, int32_t k) {

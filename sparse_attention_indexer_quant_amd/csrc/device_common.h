@@ -98,4 +98,12 @@ __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
     return v;
 }
 
+// Order-preserving 32-bit key of a logit for the top-k selection: unsigned comparison of
+// keys is the float order, with -0 mapped to +0 so the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t b = __float_as_uint(f);
+    if (b == 0x80000000u) b = 0;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 }  // namespace dsaidx

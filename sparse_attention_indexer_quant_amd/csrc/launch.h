@@ -57,7 +57,27 @@ struct ScoreArgs {
 
 hipError_t launch_score_paged(const ScoreArgs &args, hipStream_t stream);
 
+// How score_paged splits a request's pages: pages per wavefront, workgroups ("chunks") per
+// request, and the keys one workgroup covers (the top-k segment when the scorer writes the
+// selection's histograms). Depends on the current device's compute-unit count.
+struct ScoreGeometry {
+    int pages_per_wave;
+    int64_t chunks;
+    int64_t segment_keys;
+};
+ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks);
+
+// Scoring that also writes the top-k segment histograms into a top-k workspace laid out for
+// (num_rows, chunks) segments; then launch_topk_after_histograms finishes the selection.
+size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t num_rows);
+hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream);
+
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int k);
+hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64_t width,
+                                        int64_t logits_row_stride, const int32_t *row_ends, int k,
+                                        int32_t *indices, int64_t indices_row_stride,
+                                        void *workspace, int64_t nseg, int64_t seg_len,
+                                        hipStream_t stream);
 
 hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t logits_row_stride,
                        const int32_t *row_ends, int k, int32_t *indices,

@@ -26,8 +26,14 @@
 // Work split: a workgroup's 4 wavefronts each stream a run of consecutive pages of one
 // request through a ring of page buffers, for all rows of the request (in groups of RG
 // rows held in registers).
+//
+// With HIST, the kernel also feeds the top-k selection: each workgroup counts its logits per
+// row into an LDS histogram of the top 12 order-key bits (two 16-bit counts per word) and
+// writes it as the (row, segment) histogram of a top-k workspace, segment = the workgroup's
+// run of keys. The selection then skips its own pass over the logits.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_layout.h"
 
 namespace dsaidx {
 
@@ -196,7 +202,8 @@ struct RowGroup {
     // so the matrix unit pipelines them instead of waiting on each result in turn.
     __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
                                           float *logits, int64_t first_row,
-                                          int64_t logits_row_stride, int lane, int grp) const {
+                                          int64_t logits_row_stride, int lane, int grp,
+                                          uint32_t *hist) const {
         float part[RG][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -227,7 +234,13 @@ struct RowGroup {
             if (j >= count || kbase >= rend[j]) continue;
             const float out = head_sum_to_token(part[j][0], part[j][1], part[j][2], part[j][3]);
             float *row = logits + (first_row + j) * logits_row_stride + kbase;
-            if (kbase + lane < rend[j]) row[lane] = out;
+            if (kbase + lane < rend[j]) {
+                row[lane] = out;
+                if (hist) {
+                    const uint32_t bin = order_key(out) >> kBinShift;
+                    atomicAdd(&hist[j * (kBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
+                }
+            }
         }
     }
 };
@@ -239,14 +252,17 @@ struct RowGroup {
 // same loads across its back edge on every path and the hardware wait counts stay exact;
 // conditional prefetches made the compiler wait for all loads there. The first NB - 1 loads
 // go out as soon as the block table slice arrives, while the row bounds are still in flight.
-template <int FMT, int H, int RG, int NB>
+template <int FMT, int H, int RG, int NB, bool HIST>
 __global__ __launch_bounds__(256) void score_paged_kernel(
     const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
     int64_t w_row_stride, const uint8_t *__restrict__ cache, int64_t num_pages,
     int64_t page_stride, const int32_t *__restrict__ block_table, int64_t max_blocks,
     int64_t chunks, int pages_per_wave, const int32_t *__restrict__ query_starts,
     const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
-    float *__restrict__ logits, int64_t logits_row_stride) {
+    float *__restrict__ logits, int64_t logits_row_stride, uint16_t *__restrict__ seghist) {
+    // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
+    // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
+    __shared__ __align__(16) uint32_t hist[HIST ? RG * (kBins / 2) : 1];
     const int lane = threadIdx.x & 63;
     // uniform across the wavefront; said explicitly so that all page and bound arithmetic
     // below stays in scalar registers
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const int64_t width = max_blocks * kPageTokens;
     const int PW = pages_per_wave;
     const int64_t blk_begin = (chunk * kWaves + wave) * (int64_t)PW;
-    if (blk_begin >= max_blocks) return;
+    if (!HIST && blk_begin >= max_blocks) return;
     // This wavefront's slice of the block table, one entry per lane (every entry below
     // max_blocks is in bounds).
     const int32_t *bt = block_table + req * max_blocks;
@@ -301,8 +317,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const int64_t kext = kmax < width ? kmax : width;
     const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
     const int64_t blk_end = blk_begin + PW < nblk ? blk_begin + PW : nblk;
-    if (blk_begin >= blk_end) return;
-    const int run = (int)(blk_end - blk_begin);
+    if (!HIST && blk_begin >= blk_end) return;
+    const int run = blk_begin < blk_end ? (int)(blk_end - blk_begin) : 0;
 
     // Requests with more rows than one register group stream their pages once per group
     // (the second and later passes mostly hit the L2).
@@ -314,6 +330,11 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
             for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, run), off);
         }
         const int count = (int)(r1 - first);
+        if constexpr (HIST) {
+            __syncthreads();  // the previous group's histograms are written out
+            for (int i = threadIdx.x; i < RG * (kBins / 2); i += 256) hist[i] = 0;
+            __syncthreads();
+        }
         for (int base = 0; base < run; base += NB) {
 #pragma unroll
             for (int slot = 0; slot < NB; ++slot) {
@@ -325,7 +346,20 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
                 if (p < run && table_page(p) >= 0)
                     rows.score(buf[slot], (int)((blk_begin + p) * kPageTokens), count, logits,
-                               first, logits_row_stride, lane, grp);
+                               first, logits_row_stride, lane, grp, HIST ? hist : nullptr);
+            }
+        }
+        if constexpr (HIST) {
+            // (row, segment = chunk) histograms of the rows whose keys reach this chunk; the
+            // packed 16-bit counts are already the workspace's layout
+            __syncthreads();
+            const int64_t seg_begin = chunk * kWaves * (int64_t)PW * kPageTokens;
+#pragma unroll
+            for (int j = 0; j < RG; ++j) {  // unrolled: a runtime index would put `rows` in scratch
+                if (j >= count || seg_begin >= rows.rend[j]) continue;
+                uint4 *dst = reinterpret_cast<uint4 *>(seghist + ((first + j) * chunks + chunk) * kBins);
+                const uint4 *src = reinterpret_cast<const uint4 *>(hist + j * (kBins / 2));
+                for (int i = threadIdx.x; i < kBins / 8; i += 256) dst[i] = src[i];
             }
         }
     }
@@ -353,48 +387,67 @@ int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
     return (int)(ppw < 4 ? 4 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
 }
 
-template <int FMT, int H, int RG>
-static hipError_t launch_score_rg(const ScoreArgs &a, hipStream_t stream) {
-    const int ppw = score_pages_per_wave(a.num_requests, a.max_blocks);
-    const int64_t pages_per_wg = (int64_t)kWaves * ppw;
-    const int64_t chunks = (a.max_blocks + pages_per_wg - 1) / pages_per_wg;
-    const dim3 grid((unsigned)(chunks * a.num_requests)), block(256);
+ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
+    ScoreGeometry g;
+    g.pages_per_wave = score_pages_per_wave(num_requests, max_blocks);
+    const int64_t pages_per_wg = (int64_t)kWaves * g.pages_per_wave;
+    g.chunks = (max_blocks + pages_per_wg - 1) / pages_per_wg;
+    g.segment_keys = pages_per_wg * kPageTokens;
+    return g;
+}
+
+template <int FMT, int H, int RG, bool HIST>
+static hipError_t launch_score_rg(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
+    const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
+    const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
     // page buffers per wavefront: 4 for MXFP4 with up to 2 rows per group, else 2 (FP8 pages
     // and 4-row query groups take the registers a deeper ring would need)
     constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 4 : 2;
-    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB>), grid, block, 0, stream,
+    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST>), grid, block, 0, stream,
                        static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride,
                        static_cast<const uint8_t *>(a.cache), a.num_pages, a.page_stride,
-                       a.block_table, a.max_blocks, chunks, ppw, a.query_starts, a.row_ends,
-                       a.num_rows, a.max_query_len, a.logits, a.logits_row_stride);
+                       a.block_table, a.max_blocks, geo.chunks, geo.pages_per_wave,
+                       a.query_starts, a.row_ends, a.num_rows, a.max_query_len, a.logits,
+                       a.logits_row_stride, seghist);
     return hipGetLastError();
 }
 
-template <int FMT, int H>
-static hipError_t launch_score_h(const ScoreArgs &a, hipStream_t stream) {
-    if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1>(a, stream);
+template <int FMT, int H, bool HIST>
+static hipError_t launch_score_h(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
+    if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, HIST>(a, seghist, stream);
     if constexpr (FMT == kFmtFp8) {
         // FP8 queries occupy 4x the registers once widened to BF16: at most 2 rows per group
-        return launch_score_rg<FMT, H, 2>(a, stream);
+        return launch_score_rg<FMT, H, 2, HIST>(a, seghist, stream);
     } else {
-        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2>(a, stream);
-        return launch_score_rg<FMT, H, 4>(a, stream);
+        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, HIST>(a, seghist, stream);
+        return launch_score_rg<FMT, H, 4, HIST>(a, seghist, stream);
     }
 }
 
-template <int FMT>
-static hipError_t launch_score_fmt(const ScoreArgs &a, hipStream_t stream) {
+template <int FMT, bool HIST>
+static hipError_t launch_score_fmt(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
     switch (a.heads) {
-        case 16: return launch_score_h<FMT, 16>(a, stream);
-        case 32: return launch_score_h<FMT, 32>(a, stream);
-        default: return launch_score_h<FMT, 64>(a, stream);
+        case 16: return launch_score_h<FMT, 16, HIST>(a, seghist, stream);
+        case 32: return launch_score_h<FMT, 32, HIST>(a, seghist, stream);
+        default: return launch_score_h<FMT, 64, HIST>(a, seghist, stream);
     }
 }
 
 hipError_t launch_score_paged(const ScoreArgs &a, hipStream_t stream) {
-    return a.fmt == kFmtMxfp4 ? launch_score_fmt<kFmtMxfp4>(a, stream)
-                              : launch_score_fmt<kFmtFp8>(a, stream);
+    return a.fmt == kFmtMxfp4 ? launch_score_fmt<kFmtMxfp4, false>(a, nullptr, stream)
+                              : launch_score_fmt<kFmtFp8, false>(a, nullptr, stream);
+}
+
+size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t num_rows) {
+    return topk_layout_bytes(num_rows, score_geometry(num_requests, max_blocks).chunks);
+}
+
+hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream) {
+    const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
+    uint16_t *seghist = carve(workspace, a.num_rows, geo.chunks).seghist;
+    return a.fmt == kFmtMxfp4 ? launch_score_fmt<kFmtMxfp4, true>(a, seghist, stream)
+                              : launch_score_fmt<kFmtFp8, true>(a, seghist, stream);
 }
 
 }  // namespace dsaidx

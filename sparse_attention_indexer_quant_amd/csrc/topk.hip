@@ -11,12 +11,14 @@
 // row's shared counters serialize; both measured slower than the selection itself):
 //
 //   1. topk_hist (rows x segments): each workgroup histograms the top 12 key bits of its
-//      segment in LDS and stores the counts (16-bit) in the workspace. Rows with
-//      row_end <= k are written here directly.
-//   2. topk_threshold (one workgroup per row): sums the row's segment histograms, finds the
-//      bin b holding the k-th largest key, then counts each segment's keys above b and
-//      inside b and stores their exclusive prefix sums over the segments: every segment's
-//      first output slot and first candidate slot.
+//      segment in LDS and stores the counts (16-bit) in the workspace. (The scorer can write
+//      these histograms itself, segment = one scoring workgroup's keys; then the selection
+//      starts at step 2.)
+//   2. topk_threshold (one workgroup per row): rows with row_end <= k are written here
+//      directly. Otherwise it sums the row's segment histograms, finds the bin b holding the
+//      k-th largest key, then counts each segment's keys above b and inside b and stores
+//      their exclusive prefix sums over the segments: every segment's first output slot and
+//      first candidate slot.
 //   3. topk_collect (rows x segments): writes the positions of keys above bin b to the
 //      output and the (key, position) pairs of keys inside bin b to the row's candidate
 //      list, at the offsets from step 2 plus an in-workgroup prefix sum -- no atomics, and
@@ -27,12 +29,13 @@
 //      lower position -- are taken. A bin that overflowed the candidate list is selected
 //      from the row itself instead.
 //
-// Segments are 4096 keys, doubled (up to 32768) until rows x segments is at most 2048
-// workgroups and a row has at most 1024 segments (rows hold at most 2^25 keys). Every
+// Standalone segments are 4096 keys, doubled (up to 32768) until rows x segments is at most
+// 2048 workgroups and a row has at most 1024 segments (rows hold at most 2^25 keys). Every
 // workspace field is written before it is read within a call, so the workspace needs no
 // initialisation; calls sharing one must be ordered.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_layout.h"
 
 namespace dsaidx {
 
@@ -40,31 +43,12 @@ constexpr int kTopkThreads = 256;
 constexpr int kRowThreads = 1024;        // threshold: one workgroup per row
 constexpr int kMinSegment = 4096;        // keys per workgroup (doubled for many rows)
 constexpr int kMaxSegment = 32768;       // 16-bit segment histogram counts stay exact
-constexpr int kMaxRowSegments = kTopkMaxWidth / kMaxSegment;
 constexpr int kMaxWorkgroups = 2048;
-constexpr int kBins = 4096;              // top 12 key bits
-constexpr int kBinShift = 20;
-constexpr int kCandCap = 8192;           // candidate (key, position) pairs kept per row
 constexpr int kSelectThreads = 512;
 constexpr int kRadixBits = 11;
 constexpr int kRadixBins = 1 << kRadixBits;
+static_assert(kTopkMaxWidth / kMaxSegment <= kMaxRowSegments, "a row fits the threshold kernel");
 static_assert(kMaxRowSegments <= kRowThreads, "one thread per segment in the offset scan");
-
-struct RowState {
-    uint32_t bin;          // threshold bin
-    int32_t above;         // keys above the threshold bin
-    int32_t remaining;     // keys still to take from inside the bin
-    uint32_t n_cand;       // keys inside the bin
-};
-
-struct TopkWorkspace {
-    RowState *state;
-    uint16_t *seghist;  // [rows][nseg][kBins]
-    uint2 *segoff;      // [rows][nseg]: first output slot, first candidate slot
-    uint2 *cand;        // [rows][kCandCap]: order key, position
-};
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Keys per segment for this call's shape (the same rule sizes the workspace).
 inline int64_t topk_segment(int64_t rows, int64_t width) {
@@ -76,25 +60,6 @@ inline int64_t topk_segment(int64_t rows, int64_t width) {
 }
 
 inline int64_t topk_nseg(int64_t width, int64_t seg) { return width > 0 ? (width + seg - 1) / seg : 1; }
-
-__host__ __device__ inline TopkWorkspace carve(void *ws, int64_t rows, int64_t nseg) {
-    char *p = static_cast<char *>(ws);
-    TopkWorkspace w;
-    w.state = reinterpret_cast<RowState *>(p);
-    p += align256(sizeof(RowState) * rows);
-    w.seghist = reinterpret_cast<uint16_t *>(p);
-    p += align256(sizeof(uint16_t) * kBins * nseg * rows);
-    w.segoff = reinterpret_cast<uint2 *>(p);
-    p += align256(sizeof(uint2) * nseg * rows);
-    w.cand = reinterpret_cast<uint2 *>(p);
-    return w;
-}
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t b = __float_as_uint(f);
-    if (b == 0x80000000u) b = 0;  // -0 == +0
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
 
 // Inclusive prefix sum over the wavefront on the data-parallel primitives (DPP): shifts by
 // 1, 2, 4 and 8 lanes within each row of 16, then row 0's and row 1's totals broadcast
@@ -129,15 +94,6 @@ __device__ __forceinline__ int64_t row_bound(const int32_t *row_ends, int64_t ro
     return n < 0 ? 0 : (n > width ? width : n);
 }
 
-// Rows with at most k keys: all positions, then -1. Segment s writes [s*seg_len, ...) of
-// the k outputs; the last segment also writes whatever lies past the row width.
-__device__ __forceinline__ void write_short_row(int32_t *out, int64_t n, int k, int64_t seg,
-                                                int64_t nseg, int64_t seg_len) {
-    const int64_t lo = seg * seg_len;
-    const int64_t hi = seg == nseg - 1 ? (int64_t)k : (lo + seg_len < k ? lo + seg_len : k);
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kTopkThreads) out[i] = i < n ? (int32_t)i : -1;
-}
-
 template <int VEC, typename F>
 __device__ __forceinline__ void for_segment(const float *x, int64_t lo, int64_t hi, F &&fn) {
     if constexpr (VEC == 4) {
@@ -158,15 +114,12 @@ __device__ __forceinline__ void for_segment(const float *x, int64_t lo, int64_t 
 template <int VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
-    const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
-    int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
+    const int32_t *__restrict__ row_ends, int k, TopkWorkspace ws, int64_t nseg,
+    int64_t seg_len) {
     __shared__ __align__(16) uint32_t hist[kBins];
     const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t n = row_bound(row_ends, row, width);
-    if (n <= k) {
-        write_short_row(indices + row * indices_row_stride, n, k, seg, nseg, seg_len);
-        return;
-    }
+    if (n <= k) return;   // written by the threshold kernel
     const int64_t lo = seg * seg_len;
     if (lo >= n) return;  // only the segments that hold keys take part below
     const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
@@ -193,10 +146,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
     dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
 }
 
-// One workgroup per row: the threshold bin and every segment's output offsets.
+// One workgroup per row: a row with at most k keys is written whole (all positions, then
+// -1); otherwise the threshold bin and every segment's output offsets.
 __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
-    const int32_t *__restrict__ row_ends, int64_t width, int k, TopkWorkspace ws, int64_t nseg,
-    int64_t seg_len) {
+    const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
+    int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
     __shared__ __align__(16) uint32_t part_hist[kRowThreads / 256][kBins];  // per segment group
     __shared__ uint32_t seg_above[kMaxRowSegments];
     __shared__ int partials[kRowThreads / 64];
@@ -204,7 +158,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     __shared__ int found_above;
     const int64_t row = blockIdx.x;
     const int64_t n = row_bound(row_ends, row, width);
-    if (n <= k) return;
+    if (n <= k) {
+        int32_t *out = indices + row * indices_row_stride;
+        for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
+        return;
+    }
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
     const uint16_t *rowhist = ws.seghist + row * nseg * kBins;
     const int t = threadIdx.x;
@@ -527,29 +485,20 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
 }
 
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int) {
-    const int64_t nseg = topk_nseg(width, topk_segment(rows, width));
-    return align256(sizeof(RowState) * rows) + align256(sizeof(uint16_t) * kBins * nseg * rows) +
-           align256(sizeof(uint2) * nseg * rows) + align256(sizeof(uint2) * (size_t)kCandCap * rows);
+    return topk_layout_bytes(rows, topk_nseg(width, topk_segment(rows, width)));
 }
 
-hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t logits_row_stride,
-                       const int32_t *row_ends, int k, int32_t *indices,
-                       int64_t indices_row_stride, void *workspace, size_t, hipStream_t stream) {
-    const int64_t seg_len = topk_segment(rows, width);
-    const int64_t nseg = topk_nseg(width, seg_len);
+// Steps 2-4 of the selection, on segment histograms already in the workspace.
+hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64_t width,
+                                        int64_t logits_row_stride, const int32_t *row_ends, int k,
+                                        int32_t *indices, int64_t indices_row_stride,
+                                        void *workspace, int64_t nseg, int64_t seg_len,
+                                        hipStream_t stream) {
     const TopkWorkspace ws = carve(workspace, rows, nseg);
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
-    if (vec)
-        hipLaunchKernelGGL(topk_hist_kernel<4>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
-                           seg_len);
-    else
-        hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
-                           seg_len);
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
-                       row_ends, width, k, ws, nseg, seg_len);
+                       row_ends, width, k, indices, indices_row_stride, ws, nseg, seg_len);
     if (vec)
         hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits, width,
                            logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
@@ -562,6 +511,25 @@ hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t
                        logits, width, logits_row_stride, row_ends, k, indices, indices_row_stride,
                        ws);
     return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t logits_row_stride,
+                       const int32_t *row_ends, int k, int32_t *indices,
+                       int64_t indices_row_stride, void *workspace, size_t, hipStream_t stream) {
+    const int64_t seg_len = topk_segment(rows, width);
+    const int64_t nseg = topk_nseg(width, seg_len);
+    const TopkWorkspace ws = carve(workspace, rows, nseg);
+    const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
+    const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
+    if (vec)
+        hipLaunchKernelGGL(topk_hist_kernel<4>, grid, block, 0, stream, logits, width,
+                           logits_row_stride, row_ends, k, ws, nseg, seg_len);
+    else
+        hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, logits, width,
+                           logits_row_stride, row_ends, k, ws, nseg, seg_len);
+    return launch_topk_after_histograms(logits, rows, width, logits_row_stride, row_ends, k,
+                                        indices, indices_row_stride, workspace, nseg, seg_len,
+                                        stream);
 }
 
 }  // namespace dsaidx

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsaidx_quantize_queries", "dsaidx_store_keys", "dsaidx_score_paged", "dsaidx_topk",
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
-              "dsaidx_query_row_bytes", "dsaidx_index_inputs"):
+              "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
+              "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes"):
         assert n in names
 
 
@@ -202,6 +203,52 @@ def test_topk_checks(lib):
     assert topk(lib, width=(1 << 25) + 1, ls=(1 << 25) + 1) == EUNSUP
     assert lib.dsaidx_topk_workspace_bytes(1, (1 << 25) + 1, 8) == 0
     assert lib.dsaidx_topk_workspace_bytes(1, 1 << 25, 8) > 0
+
+
+def score_hist(lib, **kw):
+    a = dict(fmt=MX, q=P, qs=2176, h=32, w=P, ws=32, cache=P, pages=8, ps=4352, bt=P, r=2, mb=4,
+             starts=P, ends=P, rows=2, mq=1, lg=P, ls=256, wk=P, wkb=1 << 30)
+    a.update(kw)
+    return lib.dsaidx_score_paged_hist(a["fmt"], a["q"], a["qs"], a["h"], a["w"], a["ws"],
+                                       a["cache"], a["pages"], a["ps"], a["bt"], a["r"], a["mb"],
+                                       a["starts"], a["ends"], a["rows"], a["mq"], a["lg"],
+                                       a["ls"], a["wk"], a["wkb"], None)
+
+
+def test_score_paged_hist_checks(lib):
+    assert score_hist(lib, fmt=3) == EINVAL
+    assert score_hist(lib, h=20) == EUNSUP
+    assert score_hist(lib, mq=17) == EUNSUP
+    assert score_hist(lib, rows=0, q=None) == OK
+    assert score_hist(lib, wk=None) == EINVAL
+    assert score_hist(lib, wkb=16) == EINVAL
+    assert score_hist(lib, wk=P + 16) == ELAYOUT
+    assert score_hist(lib, ls=255) == ELAYOUT
+    assert score_hist(lib, ps=4350) == ELAYOUT
+    assert lib.dsaidx_score_topk_workspace_bytes(0, 4, 2) == 0
+    assert lib.dsaidx_score_topk_workspace_bytes(2, 4, 2) > 0
+    # more than 1024 scoring workgroups per row (> 4M keys) is refused
+    assert lib.dsaidx_score_topk_workspace_bytes(1, 70000, 1) == 0
+    assert score_hist(lib, r=1, mb=70000, ls=70000 * 64) == EUNSUP
+
+
+def topk_scored(lib, **kw):
+    a = dict(lg=P, rows=2, ls=256, ends=P, k=8, out=P, os=8, r=2, mb=4, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.dsaidx_topk_scored(a["lg"], a["rows"], a["ls"], a["ends"], a["k"], a["out"],
+                                  a["os"], a["r"], a["mb"], a["ws"], a["wsb"], None)
+
+
+def test_topk_scored_checks(lib):
+    assert topk_scored(lib, k=0) == EINVAL
+    assert topk_scored(lib, rows=-1) == EINVAL
+    assert topk_scored(lib, rows=0, lg=None) == OK
+    assert topk_scored(lib, r=0) == EINVAL
+    assert topk_scored(lib, ws=None) == EINVAL
+    assert topk_scored(lib, wsb=8) == EINVAL
+    assert topk_scored(lib, ls=255) == ELAYOUT
+    assert topk_scored(lib, os=7) == ELAYOUT
+    assert topk_scored(lib, ws=P + 8) == ELAYOUT
 
 
 def test_binding_refuses_cpu_tensors():

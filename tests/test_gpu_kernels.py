@@ -276,6 +276,25 @@ def test_score_paged_matches_oracle(name):
     assert_logits_close(got, ref, ends, range(wl.num_rows), name)
 
 
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+@pytest.mark.parametrize("k", [1, 64, 700])
+def test_score_topk_matches_separate_calls(name, k):
+    # the scorer writing the selection's histograms changes nothing: the same logits bit for
+    # bit, and index sets equal to the oracle's top-k of those logits (workspace starts as
+    # arbitrary bytes)
+    wl, dw, got, ref, ends, (q_rows, w, starts, dends) = _run_score(name)
+    logits = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    ws = torch.full((dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows),),
+                    0x5C, dtype=torch.uint8, device="cuda")
+    _, idx = dsa.score_topk(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride,
+                            dw.block_table, starts, dends, wl.max_query_len, k, wl.fmt,
+                            wl.section_offset, out=logits, workspace=ws)
+    fused = logits.cpu().numpy()
+    assert np.array_equal(fused.view(np.uint32), got.view(np.uint32))
+    want = oracle.topk(np.nan_to_num(fused, nan=0.0), ends, k)
+    assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), f"{name} k={k}")
+
+
 def test_score_paged_placement_invariance_and_determinism():
     outs = []
     for permute, stride, offset in [(True, 4352, 0), (False, 4352, 0), (True, 8192, 3840)]:
