@@ -25,8 +25,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsaidx_oracle.c")
 _LIB = os.path.join(_HERE, "libdsaidx_oracle.so")
 
-MXFP4, FP8 = 0, 1
-FORMATS = {"mxfp4": MXFP4, "fp8": FP8}
+MXFP4, FP8, FP8_MX = 0, 1, 2
+FORMATS = {"mxfp4": MXFP4, "fp8": FP8, "fp8_mx": FP8_MX}
 
 _lib = None
 

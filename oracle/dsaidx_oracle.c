@@ -28,6 +28,11 @@
 
 #define ORC_FMT_MXFP4 0
 #define ORC_FMT_FP8 1
+#define ORC_FMT_FP8_MX 2   /* FP8 keys whose power-of-two scale is stored as UE8M0 bytes */
+
+static int valid_fmt(int fmt) {
+    return fmt == ORC_FMT_MXFP4 || fmt == ORC_FMT_FP8 || fmt == ORC_FMT_FP8_MX;
+}
 
 #define ORC_OK 0
 #define ORC_EINVAL 1
@@ -267,7 +272,7 @@ int orc_quantize_queries(int fmt, const uint16_t *q, int64_t rows, int heads,
                          int64_t q_row_stride, int64_t q_head_stride, const uint16_t *wv,
                          int64_t wv_row_stride, uint8_t *q_out, int64_t q_out_row_stride,
                          uint16_t *w_out, int64_t w_out_row_stride) {
-    if ((fmt != ORC_FMT_MXFP4 && fmt != ORC_FMT_FP8) || rows < 0 || heads < 1) return ORC_EINVAL;
+    if (!valid_fmt(fmt) || rows < 0 || heads < 1) return ORC_EINVAL;
     const float c_h = orc_head_weight_scale(heads);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -299,13 +304,15 @@ int orc_quantize_queries(int fmt, const uint16_t *q, int64_t rows, int heads,
 /* Per token: LayerNorm of the BF16 pre-norm key, BF16, then MXFP4 into the
  * 4352-byte section [64 x 64 B E2M1 | 64 x 4 B UE8M0] of page slot / 64 at
  * token offset slot % 64, or FP8 into the 8448-byte section
- * [64 x 128 B E4M3 | 64 x 4 B FP32 scale]. Section p starts at
+ * [64 x 128 B E4M3 | 64 x 4 B scale]: the FP32 scale, or for FP8_MX the
+ * scale's exponent e (the scale is 2^e) as four equal UE8M0 bytes e + 127
+ * ([idx] module text and insert_key, mx). Section p starts at
  * cache + p * page_stride. A negative slot is padding and writes nothing;
  * a slot at or beyond num_pages * 64 writes nothing either. */
 int orc_store_keys(int fmt, const uint16_t *keys, int64_t tokens, int64_t k_row_stride,
                    const float *gamma, const float *beta, float eps, const int64_t *slots,
                    uint8_t *cache, int64_t num_pages, int64_t page_stride) {
-    if ((fmt != ORC_FMT_MXFP4 && fmt != ORC_FMT_FP8) || tokens < 0) return ORC_EINVAL;
+    if (!valid_fmt(fmt) || tokens < 0) return ORC_EINVAL;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < tokens; ++t) {
         int64_t slot = slots[t];
@@ -317,9 +324,15 @@ int orc_store_keys(int fmt, const uint16_t *keys, int64_t tokens, int64_t k_row_
         orc_layernorm128(x, gamma, beta, eps, n);
         if (fmt == ORC_FMT_MXFP4) {
             mxfp4_of_128(n, sec + off * 64, sec + 64 * 64 + off * 4);
-        } else {
+        } else if (fmt == ORC_FMT_FP8) {
             float s = fp8_of_128(n, sec + off * DIM);
             memcpy(sec + 64 * DIM + off * 4, &s, 4);
+        } else {
+            float s = fp8_of_128(n, sec + off * DIM);
+            int ex;
+            frexpf(s, &ex);  /* s = 0.5 * 2^ex exactly, so s = 2^(ex - 1) */
+            uint8_t b = (uint8_t)(ex - 1 + 127);
+            for (int i = 0; i < 4; ++i) sec[64 * DIM + off * 4 + i] = b;
         }
     }
     return ORC_OK;
@@ -378,7 +391,8 @@ static int nibble(const uint8_t *bytes, int col) {
 
 /* One head's dot product q_h . k, exact: MXFP4 as integer block sums of
  * (2 E2M1) x (2 E2M1) scaled by 2^(eq + ek - 2); FP8 as the double sum of
- * exact E4M3 products times the key's FP32 scale. */
+ * exact E4M3 products times the key's scale (FP32, or 2^(byte - 127) from the
+ * first of its four UE8M0 bytes for FP8_MX). */
 static double head_dot(int fmt, const uint8_t *qrow, int heads, int h, const uint8_t *sec,
                        int64_t off) {
     if (fmt == ORC_FMT_MXFP4) {
@@ -398,11 +412,17 @@ static double head_dot(int fmt, const uint8_t *qrow, int heads, int h, const uin
         return dot;
     } else {
         const uint8_t *qp = qrow + (int64_t)h * DIM, *kp = sec + off * DIM;
-        float ks;
-        memcpy(&ks, sec + 64 * DIM + off * 4, 4);
+        double ks;
+        if (fmt == ORC_FMT_FP8) {
+            float f;
+            memcpy(&f, sec + 64 * DIM + off * 4, 4);
+            ks = (double)f;
+        } else {
+            ks = ldexp(1.0, (int)sec[64 * DIM + off * 4] - 127);
+        }
         double dot = 0.0;
         for (int i = 0; i < DIM; ++i) dot += orc_e4m3_value(qp[i]) * orc_e4m3_value(kp[i]);
-        return dot * (double)ks;
+        return dot * ks;
     }
 }
 
@@ -418,7 +438,7 @@ int orc_score_paged(int fmt, const uint8_t *q, int64_t q_row_stride, int heads,
                     int64_t num_requests, int64_t max_blocks, const int32_t *query_starts,
                     const int32_t *row_ends, int64_t num_rows, float *logits,
                     int64_t logits_row_stride, const int64_t *row_subset, int64_t n_subset) {
-    if ((fmt != ORC_FMT_MXFP4 && fmt != ORC_FMT_FP8) || heads < 1) return ORC_EINVAL;
+    if (!valid_fmt(fmt) || heads < 1) return ORC_EINVAL;
     if (!e4m3_ready) e4m3_fill();
     int64_t width = max_blocks * PAGE_TOKENS;
     for (int64_t req = 0; req < num_requests; ++req) {

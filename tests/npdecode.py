@@ -6,6 +6,7 @@ text and insert_fp4_key; page "vllm.models.kimi_k3.amd.ops.fp4_indexer", cache_v
   MXFP4 query row  [H x 64 B E2M1 | H x 4 B UE8M0]
   MXFP4 key section [64 tokens x 64 B E2M1 | 64 tokens x 4 B UE8M0]   (4352 B)
   FP8 key section   [64 tokens x 128 B E4M3 | 64 tokens x 4 B FP32]    (8448 B)
+  FP8 mx section    [64 tokens x 128 B E4M3 | 64 tokens x 4 equal UE8M0 bytes]
 Byte j of a 128-value vector holds column 2j in its low nibble, 2j+1 in its high nibble;
 scale byte g covers columns [32g, 32g + 32).
 """
@@ -73,6 +74,16 @@ def fp8_key(cache: np.ndarray, page: int, slot: int, page_stride: int, offset: i
     scale = np.frombuffer(cache[base + 8192 + slot * 4: base + 8192 + slot * 4 + 4].tobytes(),
                           dtype="<f4")[0]
     return vals * float(scale), float(scale)
+
+
+def fp8_mx_key(cache: np.ndarray, page: int, slot: int, page_stride: int, offset: int = 0):
+    """FP8 key whose scale 2^e is stored as four UE8M0 bytes e + 127; returns (values,
+    scale, the four bytes)."""
+    base = offset + page * page_stride
+    vals = e4m3(cache[base + slot * 128: base + slot * 128 + 128])
+    sb = cache[base + 8192 + slot * 4: base + 8192 + slot * 4 + 4].astype(np.int64)
+    scale = float(np.exp2(sb[0] - 127.0))
+    return vals * scale, scale, sb
 
 
 def bf16(bits) -> np.ndarray:

@@ -162,6 +162,41 @@ def test_store_keys_layout_padding_and_filler(fmt, stride, offset):
     assert np.all(cache[~touched] == 0xA5)
 
 
+@pytest.mark.parametrize("k", [-10, 0, 7])
+def test_store_keys_fp8_mx_scale_bytes(k):
+    # the mx variant ([idx] module text and insert_key, mx): a key normalizing to E4M3 values
+    # with amax 448 * 2^k has scale 2^k, stored as four equal UE8M0 bytes k + 127, and the
+    # same payload bytes as the FP32-scale variant
+    rng = np.random.default_rng(40 + k)
+    v = npdecode.e4m3(rng.integers(0, 0xFF, size=128) & 0xF7)
+    v[9] = -448.0
+    beta = (v * 2.0 ** k).astype(np.float32)
+    key = bf16_bits(np.full((1, 128), 3.0, np.float32))        # normalizes to beta exactly
+    caches = {}
+    for fmt in ("fp8", "fp8_mx"):
+        c = np.full(8448 * 2, 0xA5, np.uint8)
+        oracle.store_keys(key, np.ones(128, np.float32), beta, 1e-6, np.array([64 + 5]), c, 2,
+                          8448, 0, fmt)
+        caches[fmt] = c
+    vals, scale, sb = npdecode.fp8_mx_key(caches["fp8_mx"], 1, 5, 8448)
+    assert np.all(sb == k + 127) and scale == 2.0 ** k
+    assert np.array_equal(vals, beta.astype(np.float64))
+    payload = slice(8448 + 5 * 128, 8448 + 6 * 128)
+    assert np.array_equal(caches["fp8"][payload], caches["fp8_mx"][payload])
+    # nothing else differs between the two layouts
+    diff = np.nonzero(caches["fp8"] != caches["fp8_mx"])[0]
+    assert np.all((diff >= 8448 + 8192 + 5 * 4) & (diff < 8448 + 8192 + 6 * 4))
+
+
+def test_store_keys_fp8_mx_zero_key_scale_floor():
+    # an all-zero normalized key: amax floored at FP32(1e-10), scale 2^-42, bytes 85
+    cache = np.zeros(8448, np.uint8)
+    oracle.store_keys(bf16_bits(np.ones((1, 128), np.float32)), np.ones(128, np.float32),
+                      np.zeros(128, np.float32), 1e-6, np.array([9]), cache, 1, 8448, 0, "fp8_mx")
+    vals, scale, sb = npdecode.fp8_mx_key(cache, 0, 9, 8448)
+    assert scale == 2.0 ** -42 and np.all(sb == 85) and np.all(vals == 0)
+
+
 def test_store_keys_fp8_zero_key_scale_floor():
     # an all-zero normalized key: amax floored at FP32(1e-10) gives s = 2^-42 and zero codes
     cache = np.zeros(8448, np.uint8)
@@ -362,6 +397,8 @@ def _brute_force(wl, qrows, w_bits, cache, starts, ends):
                 page = wl.block_table[q, p // 64]
                 if wl.fmt == "mxfp4":
                     keys[p] = npdecode.mxfp4_key(cache, page, p % 64, wl.page_stride, wl.section_offset)
+                elif wl.fmt == "fp8_mx":
+                    keys[p] = npdecode.fp8_mx_key(cache, page, p % 64, wl.page_stride, wl.section_offset)[0]
                 else:
                     keys[p] = npdecode.fp8_key(cache, page, p % 64, wl.page_stride, wl.section_offset)[0]
             dots = qv[r] @ keys.T  # [H, n]
@@ -370,7 +407,8 @@ def _brute_force(wl, qrows, w_bits, cache, starts, ends):
 
 
 @pytest.mark.parametrize("fmt,heads,stride,offset", [("mxfp4", 32, 4352, 0), ("mxfp4", 16, 8192, 3840),
-                                                     ("mxfp4", 64, 4352, 0), ("fp8", 32, 8448, 0)])
+                                                     ("mxfp4", 64, 4352, 0), ("fp8", 32, 8448, 0),
+                                                     ("fp8_mx", 32, 9216, 512)])
 def test_score_matches_fp64_brute_force(fmt, heads, stride, offset):
     wl = make_workload("tiny", fmt=fmt, heads=heads, seq_lens=[70, 200, 3], query_lens=[1, 3, 2],
                        num_rows=8, topk=8, seed=heads, page_stride=stride, section_offset=offset,
@@ -393,6 +431,22 @@ def test_score_matches_fp64_brute_force(fmt, heads, stride, offset):
     assert np.all(np.abs(got - want) <= ulp)
     # ReLU actually clips: some head dots are negative in this workload
     assert (lg[valid] > 0).any() and (lg[valid] < 0).any()
+
+
+def test_score_fp8_mx_equals_fp8():
+    # the key scale is a power of two either way: storing it as UE8M0 bytes changes no logit
+    wls = {f: make_workload("mx", fmt=f, heads=32, seq_lens=[300, 65], query_lens=[2, 1], topk=8,
+                            seed=12, outlier_frac=0.01, outlier_gain=20.0) for f in ("fp8", "fp8_mx")}
+    out = {}
+    for f, wl in wls.items():
+        cache = np.full(wl.cache_bytes, 0xA5, np.uint8)
+        oracle.store_keys(wl.key_bits, wl.gamma, wl.beta, wl.eps, wl.key_slots, cache,
+                          wl.num_pages, wl.page_stride, 0, f)
+        qrows, w_out = oracle.quantize_queries(wl.q_bits, wl.wv_bits, f)
+        starts, ends = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+        out[f] = oracle.score_paged(qrows, 32, w_out, cache, wl.num_pages, wl.page_stride,
+                                    wl.block_table, starts, ends, f, 0)
+    assert np.array_equal(out["fp8"], out["fp8_mx"], equal_nan=True)
 
 
 def test_score_invariant_to_page_placement():
