@@ -111,7 +111,7 @@ class Setup:
         def bf16(bits):
             return up(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
 
-        fmt = dsa.MXFP4 if wl.fmt == "mxfp4" else dsa.FP8
+        fmt = dsa._FORMATS[wl.fmt]
         self.gamma, self.beta = up(wl.gamma), up(wl.beta)
         cache0 = torch.full((wl.cache_bytes,), 0xA5, dtype=torch.uint8, device=dev)
         chunk = 1 << 21

@@ -48,13 +48,15 @@ typedef enum {
 
 typedef enum {
     DSAIDX_MXFP4 = 0,       /* E2M1 payload + UE8M0 scale per 32 values */
-    DSAIDX_FP8 = 1          /* E4M3FN payload + one power-of-two scale per 128 values */
+    DSAIDX_FP8 = 1,         /* E4M3FN payload + one power-of-two scale per 128 values */
+    DSAIDX_FP8_MX = 2       /* as DSAIDX_FP8, the key scale stored as 4 equal UE8M0 bytes
+                               ([idx] module text, insert_key with mx); queries as FP8 */
 } dsaidx_format;
 
 #define DSAIDX_DIM 128                 /* values per head and per key */
 #define DSAIDX_PAGE_TOKENS 64          /* tokens per cache page */
 #define DSAIDX_MXFP4_SECTION_BYTES 4352 /* [64 x 64 B E2M1 | 64 x 4 B UE8M0] */
-#define DSAIDX_FP8_SECTION_BYTES 8448   /* [64 x 128 B E4M3 | 64 x 4 B FP32 scale] */
+#define DSAIDX_FP8_SECTION_BYTES 8448   /* [64 x 128 B E4M3 | 64 x 4 B scale] (also mx) */
 #define DSAIDX_MAX_QUERY_LEN 16        /* query rows per request that score_paged accepts */
 #define DSAIDX_TOPK_MAX_WIDTH 33554432 /* 2^25: keys per row that topk accepts */
 
@@ -114,7 +116,8 @@ dsaidx_status dsaidx_quantize_queries(int fmt, const void *q, int64_t rows, int3
  *           gamma + beta, then rounded to BF16. MXFP4: the token's 64 payload bytes at
  *           section + offset*64, its 4 UE8M0 bytes at section + 4096 + offset*4.
  *           FP8: 128 E4M3 bytes at section + offset*128 with s = pow2_ceil(max(1e-10,
- *           amax) / 448); FP32 s at section + 8192 + offset*4.
+ *           amax) / 448); FP32 s at section + 8192 + offset*4 (DSAIDX_FP8_MX: the four
+ *           bytes there each hold log2(s) + 127).
  *  Caller contract: slots unique within one call (duplicates race).
  *  tokens == 0 enqueues nothing.
  */

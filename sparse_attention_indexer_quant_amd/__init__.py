@@ -27,9 +27,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libdsaidx.so")
 
-MXFP4, FP8 = 0, 1
-_FORMATS = {"mxfp4": MXFP4, "fp8": FP8}
-SECTION_BYTES = {MXFP4: 4352, FP8: 8448}
+MXFP4, FP8, FP8_MX = 0, 1, 2
+_FORMATS = {"mxfp4": MXFP4, "fp8": FP8, "fp8_mx": FP8_MX}
+SECTION_BYTES = {MXFP4: 4352, FP8: 8448, FP8_MX: 8448}
 PAGE_TOKENS = 64
 
 _lib = None

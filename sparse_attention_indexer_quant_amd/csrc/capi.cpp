@@ -19,7 +19,7 @@ namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool valid_fmt(int fmt) { return fmt == DSAIDX_MXFP4 || fmt == DSAIDX_FP8; }
+bool valid_fmt(int fmt) { return fmt == DSAIDX_MXFP4 || fmt == DSAIDX_FP8 || fmt == DSAIDX_FP8_MX; }
 
 bool valid_heads(int heads) { return heads == 16 || heads == 32 || heads == 64; }
 

@@ -17,6 +17,8 @@ constexpr int kMxfp4Section = 64 * 64 + 64 * 4;   // 4352
 constexpr int kFp8Section = 64 * 128 + 64 * 4;    // 8448
 constexpr int kFmtMxfp4 = 0;
 constexpr int kFmtFp8 = 1;
+constexpr int kFmtFp8Mx = 2;  // FP8 keys, scale stored as four equal UE8M0 bytes
+constexpr bool is_fp8(int fmt) { return fmt != kFmtMxfp4; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }

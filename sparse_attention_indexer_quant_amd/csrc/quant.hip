@@ -6,8 +6,9 @@
 //   page "vllm.models.kimi_k3.amd.ops.fp4_indexer", quantize_queries (shape rules).
 // index_inputs: same index page, DsaIndex (both of the above for one token per workgroup,
 //   reading the head weights and the key from the packed projection row).
-// store_keys: same index page, insert_key (FP32 LayerNorm, BF16, then the cache writer) and
-//   insert_fp4_key (payload at token * 64, four UE8M0 bytes at 64 * 64 + token * 4);
+// store_keys: same index page, insert_key (FP32 LayerNorm, BF16, then the cache writer; with
+//   mx the FP8 scale's exponent as four equal UE8M0 bytes) and insert_fp4_key (payload at
+//   token * 64, four UE8M0 bytes at 64 * 64 + token * 4);
 //   fp4_indexer page, store_keys (negative slots are padding) and cache_views (sections
 //   inside merged pages, addressed by the physical page stride).
 //
@@ -128,7 +129,15 @@ __device__ __forceinline__ void store_key(const uint16_t *__restrict__ key,
         const uint32_t two = e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8);
         const uint32_t word = two | (__shfl_down(two, 1) << 16);
         if ((lane & 1) == 0) *reinterpret_cast<uint32_t *>(sec + off * 128 + 2 * lane) = word;
-        if (lane == 0) *reinterpret_cast<float *>(sec + 64 * 128 + off * 4) = s;
+        if (lane == 0) {
+            if constexpr (FMT == kFmtFp8Mx) {
+                // s = 2^e is a normal FP32 (2^-42 <= s <= 2^120): its exponent field is e + 127
+                const uint32_t b = __float_as_uint(s) >> 23;
+                *reinterpret_cast<uint32_t *>(sec + 64 * 128 + off * 4) = b * 0x01010101u;
+            } else {
+                *reinterpret_cast<float *>(sec + 64 * 128 + off * 4) = s;
+            }
+        }
     }
 }
 
@@ -190,6 +199,7 @@ hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int hea
     auto *ww = static_cast<const uint16_t *>(wv);
     auto *qo = static_cast<uint8_t *>(q_out);
     auto *wo = static_cast<uint16_t *>(w_out);
+    // the FP8 query is the same for both FP8 key layouts
     if (fmt == kFmtMxfp4)
         hipLaunchKernelGGL(quantize_queries_kernel<kFmtMxfp4>, grid, block, 0, stream, qq, heads,
                            q_row_stride, q_head_stride, ww, wv_row_stride, qo, q_out_row_stride,
@@ -211,8 +221,11 @@ hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t 
     if (fmt == kFmtMxfp4)
         hipLaunchKernelGGL(store_keys_kernel<kFmtMxfp4>, grid, block, 0, stream, kk, tokens,
                            k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
-    else
+    else if (fmt == kFmtFp8)
         hipLaunchKernelGGL(store_keys_kernel<kFmtFp8>, grid, block, 0, stream, kk, tokens,
+                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+    else
+        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8Mx>, grid, block, 0, stream, kk, tokens,
                            k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
     return hipGetLastError();
 }
@@ -236,8 +249,13 @@ hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
                            proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
                            q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
                            q_out_row_stride, wo, w_out_row_stride, c_h);
-    else
+    else if (fmt == kFmtFp8)
         hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8>, grid, block, 0, stream, pp,
+                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
+                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
+                           q_out_row_stride, wo, w_out_row_stride, c_h);
+    else
+        hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8Mx>, grid, block, 0, stream, pp,
                            proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
                            q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
                            q_out_row_stride, wo, w_out_row_stride, c_h);

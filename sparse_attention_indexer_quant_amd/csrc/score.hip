@@ -16,7 +16,8 @@
 // applied per lane, the head sum finishes with three cross-row swaps, and lane l ends up
 // with the logit of token l of the page, so each row's 64 logits go out as one 256-B store.
 //
-// FP8 keys take another route: the scaled MFMA sums each 32-value FP8 block with only about
+// FP8 keys (scale stored as FP32, or with mx as its UE8M0 exponent byte; the scale is a power
+// of two either way) take another route: the scaled MFMA sums each 32-value FP8 block with only about
 // 13 bits below the block's largest product (448^2 + 1 comes out as 448^2), which cannot hold
 // the 1e-5 logit tolerance once a head has outliers. E4M3 values are exactly representable in
 // BF16, so the FP8 path widens both operands to BF16 in registers (v_cvt_pk_f32_fp8 plus a
@@ -208,7 +209,7 @@ struct RowGroup {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             uint4 kb[FMT == kFmtMxfp4 ? 1 : 4];  // FP8: this tile's keys widened to BF16
-            if constexpr (FMT == kFmtFp8) e4m3x32_to_bf16(pg.kp[t][0], pg.kp[t][1], kb);
+            if constexpr (is_fp8(FMT)) e4m3x32_to_bf16(pg.kp[t][0], pg.kp[t][1], kb);
             v4f c[RG][HT];
 #pragma unroll
             for (int j = 0; j < RG; ++j) {
@@ -225,7 +226,9 @@ struct RowGroup {
                 float acc = 0.f;
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) acc = relu_dot4(c[j][ht], wt[j][ht], acc);
-                if constexpr (FMT == kFmtFp8) acc *= __uint_as_float(pg.ks[t]);  // s_k > 0
+                // the token's scale s_k > 0 (a power of two): FP32, or its UE8M0 exponent byte
+                if constexpr (FMT == kFmtFp8) acc *= __uint_as_float(pg.ks[t]);
+                if constexpr (FMT == kFmtFp8Mx) acc *= __uint_as_float((pg.ks[t] & 0xFFu) << 23);
                 part[j][t] = acc;
             }
         }
@@ -416,7 +419,7 @@ static hipError_t launch_score_rg(const ScoreArgs &a, uint16_t *seghist, hipStre
 template <int FMT, int H, bool HIST>
 static hipError_t launch_score_h(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
     if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, HIST>(a, seghist, stream);
-    if constexpr (FMT == kFmtFp8) {
+    if constexpr (is_fp8(FMT)) {
         // FP8 queries occupy 4x the registers once widened to BF16: at most 2 rows per group
         return launch_score_rg<FMT, H, 2, HIST>(a, seghist, stream);
     } else {
@@ -435,8 +438,11 @@ static hipError_t launch_score_fmt(const ScoreArgs &a, uint16_t *seghist, hipStr
 }
 
 hipError_t launch_score_paged(const ScoreArgs &a, hipStream_t stream) {
-    return a.fmt == kFmtMxfp4 ? launch_score_fmt<kFmtMxfp4, false>(a, nullptr, stream)
-                              : launch_score_fmt<kFmtFp8, false>(a, nullptr, stream);
+    switch (a.fmt) {
+        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, false>(a, nullptr, stream);
+        case kFmtFp8: return launch_score_fmt<kFmtFp8, false>(a, nullptr, stream);
+        default: return launch_score_fmt<kFmtFp8Mx, false>(a, nullptr, stream);
+    }
 }
 
 size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t num_rows) {
@@ -446,8 +452,11 @@ size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int6
 hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     uint16_t *seghist = carve(workspace, a.num_rows, geo.chunks).seghist;
-    return a.fmt == kFmtMxfp4 ? launch_score_fmt<kFmtMxfp4, true>(a, seghist, stream)
-                              : launch_score_fmt<kFmtFp8, true>(a, seghist, stream);
+    switch (a.fmt) {
+        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, true>(a, seghist, stream);
+        case kFmtFp8: return launch_score_fmt<kFmtFp8, true>(a, seghist, stream);
+        default: return launch_score_fmt<kFmtFp8Mx, true>(a, seghist, stream);
+    }
 }
 
 }  // namespace dsaidx

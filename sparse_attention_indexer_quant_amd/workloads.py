@@ -33,7 +33,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 @dataclass
 class Workload:
     name: str
-    fmt: str                    # "mxfp4" or "fp8"
+    fmt: str                    # "mxfp4", "fp8" or "fp8_mx" (FP8 keys, UE8M0 scale bytes)
     heads: int
     topk: int
     seed: int

@@ -99,6 +99,8 @@ def test_store_keys_checks(lib):
     assert store(lib, ps=4351) == ELAYOUT           # cache_views: stride >= 4352
     assert store(lib, ps=4360) == ELAYOUT           # 16-byte aligned sections
     assert store(lib, fmt=FP8, ps=4352) == ELAYOUT  # FP8 sections are 8448 B
+    assert store(lib, fmt=2, ps=4352) == ELAYOUT    # so are FP8 sections with UE8M0 scales
+    assert store(lib, fmt=3) == EINVAL
     assert store(lib, cache=P + 8) == ELAYOUT
     assert store(lib, g=P + 4) == ELAYOUT
 
@@ -114,7 +116,7 @@ def inputs(lib, **kw):
 
 
 def test_index_inputs_checks(lib):
-    assert inputs(lib, fmt=2) == EINVAL
+    assert inputs(lib, fmt=3) == EINVAL
     assert inputs(lib, t=-1) == EINVAL
     assert inputs(lib, kc=-2) == EINVAL
     assert inputs(lib, wc=-1) == EINVAL

@@ -43,7 +43,7 @@ def _query_cases():
     return cases
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "fp8_mx"])
 @pytest.mark.parametrize("case", list(_query_cases().keys()))
 def test_quantize_queries_bit_exact(fmt, case):
     q = _query_cases()[case]
@@ -77,7 +77,8 @@ def test_quantize_queries_empty():
 
 @pytest.mark.parametrize("fmt,stride,offset", [("mxfp4", 4352, 0), ("mxfp4", 8192, 3840),
                                                ("mxfp4", 8192, 0), ("fp8", 8448, 0),
-                                               ("fp8", 12288, 1024)])
+                                               ("fp8", 12288, 1024), ("fp8_mx", 8448, 0),
+                                               ("fp8_mx", 9216, 512)])
 def test_store_keys_bit_exact(fmt, stride, offset):
     rng = np.random.default_rng(7)
     pages = 9
@@ -102,7 +103,7 @@ def test_store_keys_bit_exact(fmt, stride, offset):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "fp8_mx"])
 def test_store_keys_bulk_layernorm_bit_exact(fmt):
     # 300k keys spanning 2^-20 .. 2^20 in scale and offset: every LayerNorm rounding step
     # (tree sums, correctly rounded sqrt and divide, BF16) must match; FP8's finer grid
@@ -142,6 +143,7 @@ def test_store_keys_empty_and_all_padding():
 @pytest.mark.parametrize("fmt,heads,stride,offset,key_col,weight_col",
                          [("mxfp4", 32, 4352, 0, 4096, 4224), ("mxfp4", 64, 8192, 3840, 0, 130),
                           ("mxfp4", 16, 4352, 0, 2, 1), ("fp8", 32, 8448, 0, 200, 4),
+                          ("fp8_mx", 16, 8448, 0, 64, 300),
                           ("fp8", 64, 9216, 512, 8192, 0)])
 def test_index_inputs_bit_exact(fmt, heads, stride, offset, key_col, weight_col):
     # queries with the same edge rows as the quantize tests, keys with extreme scales, padding
@@ -244,6 +246,8 @@ SCORE_CASES = {
     "fp8_h64_verify": dict(fmt="fp8", heads=64, seq_lens=[500, 129], query_lens=[3, 4], num_rows=9,
                            page_stride=9216, section_offset=512),
     "fp4_h32_scaled_heads": dict(fmt="mxfp4", heads=32, seq_lens=[900], query_lens=[2], head_log2_scale=4.0),
+    "fp8mx_h32_verify": dict(fmt="fp8_mx", heads=32, seq_lens=[700, 130, 5], query_lens=[2, 1, 1],
+                             num_rows=6, outlier_frac=0.01, outlier_gain=20.0),
 }
 
 
