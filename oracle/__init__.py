@@ -248,5 +248,69 @@ def topk(logits: np.ndarray, row_ends: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+# ---- decode context parallelism: rank-local keys and the top-k merge -------------------------
+# Page "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_layout: keys are dealt to the ranks in
+# runs of `interleave`; page "...cutedsl.dsa.overlap", module text: under DCP the indexer path
+# ends in a top-k merge and the local slots.
+
+def dcp_owner(position, world: int, interleave: int):
+    """(rank, rank-local position) of global key position(s): run j = position // interleave
+    goes to rank j % world as that rank's run j // world."""
+    g = np.asarray(position, dtype=np.int64)
+    run = g // interleave
+    return run % world, (run // world) * interleave + g % interleave
+
+
+def dcp_global_position(local, rank: int, world: int, interleave: int):
+    """Global key position of rank-local position(s) on `rank` (inverse of dcp_owner)."""
+    l = np.asarray(local, dtype=np.int64)
+    return (l // interleave) * (world * interleave) + rank * interleave + l % interleave
+
+
+def dcp_candidates(logits: np.ndarray, indices: np.ndarray, rank: int, world: int,
+                   interleave: int):
+    """One rank's merge candidates from its local top-k: (values FP32 [rows, k], global
+    positions int64 [rows, k]); an index of -1 gives value -inf and position -1."""
+    idx = np.asarray(indices, dtype=np.int64)
+    lg = np.asarray(logits, dtype=np.float32)
+    rows = np.arange(idx.shape[0])[:, None]
+    ok = idx >= 0
+    vals = np.where(ok, lg[rows, np.where(ok, idx, 0)], -np.inf).astype(np.float32)
+    pos = np.where(ok, dcp_global_position(np.where(ok, idx, 0), rank, world, interleave), -1)
+    return vals, pos
+
+
+def dcp_merge(values: np.ndarray, positions: np.ndarray, k: int):
+    """Global top-k of every row from all ranks' candidates (values / global positions
+    [world, rows, kc], position -1 = none): the k largest values, ties to the lower global
+    position (-0 equals +0), -1 padded. Returns int32 [rows, k] global positions."""
+    v = np.asarray(values, dtype=np.float32)
+    p = np.asarray(positions, dtype=np.int64)
+    world, rows, kc = v.shape
+    out = np.full((rows, k), -1, np.int32)
+    for r in range(rows):
+        vv = v[:, r, :].reshape(-1).astype(np.float64)
+        pp = p[:, r, :].reshape(-1)
+        keep = pp >= 0
+        vv, pp = vv[keep] + 0.0, pp[keep]          # + 0.0 turns -0 into +0
+        order = np.lexsort((pp, -vv))               # value descending, then position ascending
+        sel = pp[order[:k]]
+        out[r, :sel.size] = sel
+    return out
+
+
+def dcp_local_slots(merged: np.ndarray, rank: int, world: int, interleave: int):
+    """The rank-local positions of the merged global top-k that `rank` owns, in the merged
+    order, -1 padded: int32 [rows, k]."""
+    m = np.asarray(merged, dtype=np.int64)
+    out = np.full(m.shape, -1, np.int32)
+    for r in range(m.shape[0]):
+        g = m[r][m[r] >= 0]
+        owner, local = dcp_owner(g, world, interleave)
+        mine = local[owner == rank]
+        out[r, :mine.size] = mine
+    return out
+
+
 def num_threads() -> int:
     return _load().orc_num_threads()
