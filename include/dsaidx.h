@@ -283,6 +283,51 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int32_t *indices, int64_t indices_row_stride, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * Decode context parallelism (DCP): [fp4ops] decode_layout deals a request's keys to W ranks
+ * in runs of `interleave` (run j to rank j % W as that rank's run j / W; rank-local key
+ * positions keep the global order); each rank scores and selects over its own keys with the
+ * rank-local bounds dsaidx_decode_layout writes for it. [ovl] module text: the indexer path
+ * then ends in a top-k merge and the local slots. The exchange between ranks (an all-gather of
+ * the candidates) is the caller's; these two calls are the per-GPU parts around it.
+ *
+ * dcp_candidates -- one rank's merge candidates from its local top-k.
+ *  logits, rows, width, logits_row_stride  the rank's local logits (as for dsaidx_topk).
+ *  indices  device, int32 [rows, >= k]: the rank's local top-k positions (-1 = none).
+ *  values   device, FP32 [rows, k] contiguous: logits[row, indices[row, j]] (-inf for none).
+ *  positions device, int32 [rows, k] contiguous: the global key position of each candidate
+ *           (-1 for none). The two outputs are this rank's slice of the gathered buffers.
+ *  Errors: rows < 0, width < 0, k < 1, interleave < 1, or dcp_rank outside
+ *  [0, dcp_world_size) give DSAIDX_EINVAL; global positions beyond INT32_MAX give
+ *  DSAIDX_EUNSUPPORTED.
+ */
+dsaidx_status dsaidx_dcp_candidates(const float *logits, int64_t rows, int64_t width,
+                                    int64_t logits_row_stride, const int32_t *indices, int32_t k,
+                                    int64_t indices_row_stride, int32_t dcp_rank,
+                                    int32_t dcp_world_size, int32_t interleave, float *values,
+                                    int32_t *positions, void *stream);
+
+/*
+ * dcp_merge -- the global top-k of every row from all ranks' candidates.
+ *  values, positions  device, FP32 / int32 [dcp_world_size, rows, kc] contiguous (every
+ *           rank's dsaidx_dcp_candidates output, gathered; position -1 = none). Positions
+ *           must be distinct within a row.
+ *  merged   device, int32 [rows, >= k]: the global positions of the k largest values, ties
+ *           to the lower global position (-0 equals +0); fewer than k candidates give all of
+ *           them and -1 after; order within a row unspecified. When each rank's candidates
+ *           are its local top-k (k each), this is the top-k over the whole row.
+ *  local_slots  device, int32 [rows, >= k], or NULL: the rank-local positions of the merged
+ *           keys that rank dcp_rank owns, -1 after (order unspecified).
+ *  Errors: rows < 0, kc < 1, k < 1, interleave < 1, or (with local_slots) dcp_rank outside
+ *  [0, dcp_world_size) give DSAIDX_EINVAL; dcp_world_size * kc > 16384 gives
+ *  DSAIDX_EUNSUPPORTED.
+ */
+dsaidx_status dsaidx_dcp_merge(const float *values, const int32_t *positions,
+                               int32_t dcp_world_size, int64_t rows, int32_t kc, int32_t k,
+                               int32_t *merged, int64_t merged_row_stride, int32_t dcp_rank,
+                               int32_t interleave, int32_t *local_slots,
+                               int64_t local_row_stride, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,8 @@ def library():
                                               P, P, I64, I32, P, I64, P, SZ, P]),
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
+            "dsaidx_dcp_candidates": (I32, [P, I64, I64, I64, P, I32, I64, I32, I32, I32, P, P, P]),
+            "dsaidx_dcp_merge": (I32, [P, P, I32, I64, I32, I32, P, I64, I32, I32, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -322,3 +324,49 @@ def topk(logits, row_ends, k, width=None, out=None, workspace=None):
         0 if workspace is None else workspace.numel(), _stream(logits))
     _check("topk", st)
     return out
+
+
+def dcp_candidates(logits, indices, rank, world, interleave, width=None, values=None,
+                   positions=None):
+    """One DCP rank's merge candidates from its local top-k: (values FP32 [rows, k], global
+    positions int32 [rows, k]); pass slices of the gathered [world, rows, k] buffers as
+    values / positions to write in place."""
+    import torch
+    _dev(logits, "logits", torch.float32)
+    _dev(indices, "indices", torch.int32)
+    rows, k = indices.shape
+    width = logits.shape[1] if width is None else int(width)
+    if values is None:
+        values = torch.empty((rows, k), dtype=torch.float32, device=logits.device)
+    if positions is None:
+        positions = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    if not (values.is_contiguous() and positions.is_contiguous()):
+        raise ValueError("dcp_candidates: values and positions must be contiguous [rows, k]")
+    st = library().dsaidx_dcp_candidates(
+        logits.data_ptr(), rows, width, logits.stride(0), indices.data_ptr(), k,
+        indices.stride(0), int(rank), int(world), int(interleave), values.data_ptr(),
+        positions.data_ptr(), _stream(logits))
+    _check("dcp_candidates", st)
+    return values, positions
+
+
+def dcp_merge(values, positions, k, rank=None, interleave=1):
+    """Global top-k of every row from all ranks' candidates (values / positions
+    [world, rows, kc]). Returns merged global positions int32 [rows, k], and with `rank` also
+    that rank's local slots int32 [rows, k]."""
+    import torch
+    _dev(values, "values", torch.float32)
+    _dev(positions, "positions", torch.int32)
+    if values.dim() != 3 or values.shape != positions.shape or not values.is_contiguous() \
+            or not positions.is_contiguous():
+        raise ValueError("dcp_merge: values and positions must be contiguous [world, rows, kc]")
+    world, rows, kc = values.shape
+    merged = torch.empty((rows, int(k)), dtype=torch.int32, device=values.device)
+    local = None if rank is None else torch.empty_like(merged)
+    st = library().dsaidx_dcp_merge(
+        values.data_ptr(), positions.data_ptr(), world, rows, kc, int(k), merged.data_ptr(),
+        merged.stride(0), -1 if rank is None else int(rank), int(interleave),
+        None if local is None else local.data_ptr(), 0 if local is None else local.stride(0),
+        _stream(values))
+    _check("dcp_merge", st)
+    return merged if local is None else (merged, local)

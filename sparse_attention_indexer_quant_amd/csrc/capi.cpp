@@ -288,4 +288,44 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                                           workspace_bytes, as_stream(stream)));
 }
 
+dsaidx_status dsaidx_dcp_candidates(const float *logits, int64_t rows, int64_t width,
+                                    int64_t logits_row_stride, const int32_t *indices, int32_t k,
+                                    int64_t indices_row_stride, int32_t dcp_rank,
+                                    int32_t dcp_world_size, int32_t interleave, float *values,
+                                    int32_t *positions, void *stream) {
+    if (rows < 0 || width < 0 || k < 1 || interleave < 1 || dcp_world_size < 1 ||
+        !(0 <= dcp_rank && dcp_rank < dcp_world_size))
+        return DSAIDX_EINVAL;
+    if ((width + interleave) * (int64_t)dcp_world_size > INT32_MAX || rows * ((k + 255) / 256) > kMaxGrid)
+        return DSAIDX_EUNSUPPORTED;
+    if (rows == 0) return DSAIDX_OK;
+    if (!indices || !values || !positions || (width > 0 && !logits)) return DSAIDX_EINVAL;
+    if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||
+        !aligned(indices, 4) || !aligned(values, 4) || !aligned(positions, 4))
+        return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_dcp_candidates(logits, rows, width, logits_row_stride,
+                                                    indices, k, indices_row_stride, dcp_rank,
+                                                    dcp_world_size, interleave, values, positions,
+                                                    as_stream(stream)));
+}
+
+dsaidx_status dsaidx_dcp_merge(const float *values, const int32_t *positions,
+                               int32_t dcp_world_size, int64_t rows, int32_t kc, int32_t k,
+                               int32_t *merged, int64_t merged_row_stride, int32_t dcp_rank,
+                               int32_t interleave, int32_t *local_slots,
+                               int64_t local_row_stride, void *stream) {
+    if (rows < 0 || kc < 1 || k < 1 || dcp_world_size < 1 || interleave < 1 || rows > kMaxGrid)
+        return DSAIDX_EINVAL;
+    if (local_slots && !(0 <= dcp_rank && dcp_rank < dcp_world_size)) return DSAIDX_EINVAL;
+    if ((int64_t)dcp_world_size * kc > dsaidx::kDcpMergeCap) return DSAIDX_EUNSUPPORTED;
+    if (rows == 0) return DSAIDX_OK;
+    if (!values || !positions || !merged) return DSAIDX_EINVAL;
+    if (merged_row_stride < k || (local_slots && local_row_stride < k) || !aligned(values, 4) ||
+        !aligned(positions, 4) || !aligned(merged, 4) || !aligned(local_slots, 4))
+        return DSAIDX_ELAYOUT;
+    return hip_status(dsaidx::launch_dcp_merge(values, positions, dcp_world_size, rows, kc, k,
+                                               merged, merged_row_stride, dcp_rank, interleave,
+                                               local_slots, local_row_stride, as_stream(stream)));
+}
+
 }  // extern "C"

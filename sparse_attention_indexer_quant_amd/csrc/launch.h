@@ -72,6 +72,17 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks);
 size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t num_rows);
 hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream);
 
+// Decode context parallelism: one rank's merge candidates, and the merge.
+constexpr int kDcpMergeCap = 16384;  // world * candidates per rank, per row
+hipError_t launch_dcp_candidates(const float *logits, int64_t rows, int64_t width,
+                                 int64_t logits_row_stride, const int32_t *indices, int k,
+                                 int64_t indices_row_stride, int rank, int world, int interleave,
+                                 float *values, int32_t *positions, hipStream_t stream);
+hipError_t launch_dcp_merge(const float *values, const int32_t *positions, int world,
+                            int64_t rows, int kc, int k, int32_t *merged,
+                            int64_t merged_row_stride, int rank, int interleave,
+                            int32_t *local_slots, int64_t local_row_stride, hipStream_t stream);
+
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int k);
 hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64_t width,
                                         int64_t logits_row_stride, const int32_t *row_ends, int k,

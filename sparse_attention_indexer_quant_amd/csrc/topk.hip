@@ -35,6 +35,7 @@
 // initialisation; calls sharing one must be ordered.
 #include "device_common.h"
 #include "launch.h"
+#include "select.h"
 #include "topk_layout.h"
 
 namespace dsaidx {
@@ -44,9 +45,6 @@ constexpr int kRowThreads = 1024;        // threshold: one workgroup per row
 constexpr int kMinSegment = 4096;        // keys per workgroup (doubled for many rows)
 constexpr int kMaxSegment = 32768;       // 16-bit segment histogram counts stay exact
 constexpr int kMaxWorkgroups = 2048;
-constexpr int kSelectThreads = 512;
-constexpr int kRadixBits = 11;
-constexpr int kRadixBins = 1 << kRadixBits;
 static_assert(kTopkMaxWidth / kMaxSegment <= kMaxRowSegments, "a row fits the threshold kernel");
 static_assert(kMaxRowSegments <= kRowThreads, "one thread per segment in the offset scan");
 
@@ -60,34 +58,6 @@ inline int64_t topk_segment(int64_t rows, int64_t width) {
 }
 
 inline int64_t topk_nseg(int64_t width, int64_t seg) { return width > 0 ? (width + seg - 1) / seg : 1; }
-
-// Inclusive prefix sum over the wavefront on the data-parallel primitives (DPP): shifts by
-// 1, 2, 4 and 8 lanes within each row of 16, then row 0's and row 1's totals broadcast
-// into the rows above them. All in registers, no LDS round trips.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return x;
-}
-
-// Inclusive prefix sum over an NT-lane workgroup; `partials` holds NT / 64 ints. On return
-// partials[w] is wavefront w's total (valid until the next call).
-template <int NT>
-__device__ __forceinline__ int scan_block(int v, int *partials) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_incl_scan(v);
-    if (lane == 63) partials[wave] = v;
-    __syncthreads();
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) before += w < wave ? partials[w] : 0;
-    __syncthreads();
-    return v + before;
-}
 
 __device__ __forceinline__ int64_t row_bound(const int32_t *row_ends, int64_t row, int64_t width) {
     int64_t n = row_ends[row];
@@ -359,15 +329,6 @@ __device__ __forceinline__ uint64_t composite(uint32_t u, uint32_t pos, int pos_
     return ((uint64_t)(~u & 0xFFFFFu) << pos_bits) | pos;
 }
 
-struct LdsCandidates {  // composites already in LDS
-    const uint64_t *c;
-    int m;
-    template <typename F>
-    __device__ __forceinline__ void for_each(F &&f) const {
-        for (int j = threadIdx.x; j < m; j += kSelectThreads) f(c[j]);
-    }
-};
-
 struct RowBin {  // every key of the row inside the threshold bin, read from the logits
     const float *x;
     int64_t n;
@@ -381,77 +342,6 @@ struct RowBin {  // every key of the row inside the threshold bin, read from the
         }
     }
 };
-
-struct SelectShared {
-    uint32_t hist[kRadixBins];
-    int partials[kSelectThreads / 64];
-    uint64_t prefix;
-    int below;
-    int count;
-    uint32_t n_out;
-};
-
-// Writes the positions of the r smallest composites (of `bits` significant bits) that
-// `src` yields to out[0..r), by a most-significant-digit radix select in LDS.
-template <typename Source>
-__device__ void select_smallest(const Source &src, int r, int bits, int pos_bits, int32_t *out,
-                                SelectShared &sh) {
-    const int r0 = r;
-    uint64_t prefix = 0;
-    int done = 0;  // high composite bits fixed in `prefix`
-    uint64_t threshold = ~(uint64_t)0;
-    while (done < bits) {
-        const int digit = bits - done >= kRadixBits ? kRadixBits : bits - done;
-        const int shift = bits - done - digit;
-        for (int b = threadIdx.x; b < kRadixBins; b += kSelectThreads) sh.hist[b] = 0;
-        __syncthreads();
-        const uint64_t want = prefix >> (shift + digit);
-        src.for_each([&](uint64_t c) {
-            if ((c >> (shift + digit)) == want)
-                atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)((1 << digit) - 1)], 1u);
-        });
-        __syncthreads();
-        constexpr int per = kRadixBins / kSelectThreads;  // ascending: lane t owns per*t ..
-        int own = 0;
-        uint32_t mine[per];
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            mine[j] = sh.hist[threadIdx.x * per + j];
-            own += (int)mine[j];
-        }
-        const int incl = scan_block<kSelectThreads>(own, sh.partials);
-        int before = incl - own;
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            const int c = (int)mine[j];
-            if (before < r && before + c >= r) {
-                sh.prefix = prefix | ((uint64_t)(threadIdx.x * per + j) << shift);
-                sh.below = before;
-                sh.count = c;
-            }
-            before += c;
-        }
-        __syncthreads();
-        prefix = sh.prefix;
-        done += digit;
-        if (sh.below + sh.count == r) {  // the whole digit bin is taken: stop early
-            threshold = prefix | (((uint64_t)1 << shift) - 1);
-            break;
-        }
-        r -= sh.below;
-        threshold = prefix;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) sh.n_out = 0;
-    __syncthreads();
-    const uint64_t pos_mask = ((uint64_t)1 << pos_bits) - 1;
-    src.for_each([&](uint64_t c) {
-        if (c <= threshold) {
-            const uint32_t slot = atomicAdd(&sh.n_out, 1u);
-            if (slot < (uint32_t)r0) out[slot] = (int32_t)(c & pos_mask);
-        }
-    });
-}
 
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,

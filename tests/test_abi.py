@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("dsaidx_quantize_queries", "dsaidx_store_keys", "dsaidx_score_paged", "dsaidx_topk",
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
-              "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes"):
+              "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
+              "dsaidx_dcp_merge"):
         assert n in names
 
 
@@ -251,6 +252,40 @@ def test_topk_scored_checks(lib):
     assert topk_scored(lib, ls=255) == ELAYOUT
     assert topk_scored(lib, os=7) == ELAYOUT
     assert topk_scored(lib, ws=P + 8) == ELAYOUT
+
+
+def cand(lib, **kw):
+    a = dict(lg=P, rows=4, width=1000, ls=1000, idx=P, k=64, istr=64, rank=1, world=4, il=64,
+             v=P, p=P)
+    a.update(kw)
+    return lib.dsaidx_dcp_candidates(a["lg"], a["rows"], a["width"], a["ls"], a["idx"], a["k"],
+                                     a["istr"], a["rank"], a["world"], a["il"], a["v"], a["p"], None)
+
+
+def merge(lib, **kw):
+    a = dict(v=P, p=P, world=4, rows=4, kc=64, k=64, out=P, os=64, rank=0, il=64, loc=None, lstr=0)
+    a.update(kw)
+    return lib.dsaidx_dcp_merge(a["v"], a["p"], a["world"], a["rows"], a["kc"], a["k"], a["out"],
+                                a["os"], a["rank"], a["il"], a["loc"], a["lstr"], None)
+
+
+def test_dcp_checks(lib):
+    assert cand(lib, k=0) == EINVAL
+    assert cand(lib, rank=4) == EINVAL
+    assert cand(lib, rank=-1) == EINVAL
+    assert cand(lib, il=0) == EINVAL
+    assert cand(lib, rows=0, lg=None) == OK
+    assert cand(lib, width=1 << 30, ls=1 << 30) == EUNSUP   # global positions past INT32_MAX
+    assert cand(lib, istr=63) == ELAYOUT
+    assert cand(lib, v=P + 2) == ELAYOUT
+    assert merge(lib, kc=0) == EINVAL
+    assert merge(lib, k=0) == EINVAL
+    assert merge(lib, loc=P, lstr=64, rank=4) == EINVAL
+    assert merge(lib, world=8, kc=4096) == EUNSUP           # 32768 candidates per row
+    assert merge(lib, rows=0, v=None) == OK
+    assert merge(lib, out=None) == EINVAL
+    assert merge(lib, os=63) == ELAYOUT
+    assert merge(lib, loc=P, lstr=10) == ELAYOUT
 
 
 def test_binding_refuses_cpu_tensors():
