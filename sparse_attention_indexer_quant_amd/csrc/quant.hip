@@ -30,9 +30,24 @@ __device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ 
                                                    uint16_t *__restrict__ w_out_row, float c_h,
                                                    int tid) {
     const int part = tid & 15;
-    for (int head = tid >> 4; head < heads; head += 16) {
-        const uint16_t *src = q_row + (int64_t)head * q_head_stride + part * 8;
-        const uint4 raw = *reinterpret_cast<const uint4 *>(src);
+    // every pass's 16-byte load (and head weight) is issued before any is used, so the row
+    // costs one memory round trip instead of one per pass (heads <= 64: at most 4 passes)
+    constexpr int kMaxPasses = 4;
+    uint4 raws[kMaxPasses];
+    uint16_t wraw[kMaxPasses];
+#pragma unroll
+    for (int pass = 0; pass < kMaxPasses; ++pass) {
+        const int head = (tid >> 4) + 16 * pass;
+        if (head < heads) {
+            raws[pass] = *reinterpret_cast<const uint4 *>(q_row + (int64_t)head * q_head_stride + part * 8);
+            wraw[pass] = wv_row && part == 0 ? wv_row[head] : (uint16_t)0;
+        }
+    }
+#pragma unroll
+    for (int pass = 0; pass < kMaxPasses; ++pass) {
+        const int head = (tid >> 4) + 16 * pass;
+        if (head >= heads) continue;
+        const uint4 raw = raws[pass];
         float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
         if constexpr (FMT == kFmtMxfp4) {
@@ -54,7 +69,7 @@ __device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ 
                 *reinterpret_cast<uint32_t *>(out_row + heads * 64 + head * 4) =
                     byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
                 if (wv_row) {
-                    const float w = bf16_val(wv_row[head]);
+                    const float w = bf16_val(wraw[pass]);
                     w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(w, c_h));
                 }
             }
@@ -73,26 +88,43 @@ __device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ 
             }
             *reinterpret_cast<uint2 *>(out_row + head * 128 + part * 8) = make_uint2(lo, hi);
             if (part == 0 && wv_row) {
-                const float w = bf16_val(wv_row[head]);
+                const float w = bf16_val(wraw[pass]);
                 w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(__fmul_rn(w, s), c_h));
             }
         }
     }
 }
 
-// One key on one wavefront: lane l owns columns 2l and 2l+1 (one 4-byte load). The LayerNorm
-// sums run as the pairwise tree "adjacent pair, then fold 32, 16, 8, 4, 2, 1 apart", which
-// the xor butterfly below computes in every lane. Slots outside [0, num_pages * 64) (negative
-// slots are padding) write nothing.
+// One key's inputs as one lane of its wavefront holds them: columns 2l and 2l+1 (one 4-byte
+// load), their LayerNorm weights and biases, and the key's slot.
+struct KeyLane {
+    uint32_t pair;
+    float2 g, b;
+    int64_t slot;
+};
+
+__device__ __forceinline__ KeyLane load_key(const uint16_t *__restrict__ key,
+                                            const float *__restrict__ gamma,
+                                            const float *__restrict__ beta,
+                                            const int64_t *__restrict__ slot, int lane) {
+    KeyLane k;
+    k.pair = *reinterpret_cast<const uint32_t *>(key + 2 * lane);
+    k.g = *reinterpret_cast<const float2 *>(gamma + 2 * lane);
+    k.b = *reinterpret_cast<const float2 *>(beta + 2 * lane);
+    k.slot = *slot;
+    return k;
+}
+
+// One key on one wavefront. The LayerNorm sums run as the pairwise tree "adjacent pair, then
+// fold 32, 16, 8, 4, 2, 1 apart", which the xor butterfly below computes in every lane. Slots
+// outside [0, num_pages * 64) (negative slots are padding) write nothing.
 template <int FMT>
-__device__ __forceinline__ void store_key(const uint16_t *__restrict__ key,
-                                          const float *__restrict__ gamma,
-                                          const float *__restrict__ beta, float eps, int64_t slot,
+__device__ __forceinline__ void store_key(const KeyLane &in, float eps,
                                           uint8_t *__restrict__ cache, int64_t num_pages,
                                           int64_t page_stride, int lane) {
+    const int64_t slot = in.slot;
     if (slot < 0 || slot >= num_pages * kPageTokens) return;
-    const uint32_t pair = *reinterpret_cast<const uint32_t *>(key + 2 * lane);
-    const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+    const float x0 = bf16_lo(in.pair), x1 = bf16_hi(in.pair);
 
     float sum = __fadd_rn(x0, x1);
 #pragma unroll
@@ -104,8 +136,7 @@ __device__ __forceinline__ void store_key(const uint16_t *__restrict__ key,
     for (int h = 32; h >= 1; h >>= 1) sq = __fadd_rn(sq, __shfl_xor(sq, h));
     const float var = __fmul_rn(sq, 0.0078125f);
     const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
-    const float2 g = *reinterpret_cast<const float2 *>(gamma + 2 * lane);
-    const float2 b = *reinterpret_cast<const float2 *>(beta + 2 * lane);
+    const float2 g = in.g, b = in.b;
     const float n0 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d0, rstd), g.x), b.x));
     const float n1 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d1, rstd), g.y), b.y));
 
@@ -162,8 +193,9 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
     int64_t page_stride) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= tokens) return;
-    store_key<FMT>(keys + t * k_row_stride, gamma, beta, eps, slots[t], cache, num_pages,
-                   page_stride, threadIdx.x & 63);
+    const int lane = threadIdx.x & 63;
+    store_key<FMT>(load_key(keys + t * k_row_stride, gamma, beta, slots + t, lane), eps, cache,
+                   num_pages, page_stride, lane);
 }
 
 // The indexer inputs of one step in one launch (page
@@ -181,12 +213,14 @@ __global__ __launch_bounds__(256) void index_inputs_kernel(
     uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
     const int64_t token = blockIdx.x;
     const uint16_t *prow = projected + token * proj_row_stride;
+    const int lane = threadIdx.x & 63;
+    const bool key_wave = (threadIdx.x >> 6) == 3;
+    KeyLane key{};
+    if (key_wave) key = load_key(prow + key_col, gamma, beta, slots + token, lane);  // in flight
     quantize_query_row<FMT>(q + token * q_row_stride, heads, q_head_stride, prow + weight_col,
                             q_out + token * q_out_row_stride, w_out + token * w_out_row_stride, c_h,
                             threadIdx.x);
-    if ((threadIdx.x >> 6) == 3)
-        store_key<FMT>(prow + key_col, gamma, beta, eps, slots[token], cache, num_pages,
-                       page_stride, threadIdx.x & 63);
+    if (key_wave) store_key<FMT>(key, eps, cache, num_pages, page_stride, lane);
 }
 
 hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,

@@ -262,7 +262,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     int64_t page_stride, const int32_t *__restrict__ block_table, int64_t max_blocks,
     int64_t chunks, int pages_per_wave, const int32_t *__restrict__ query_starts,
     const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
-    float *__restrict__ logits, int64_t logits_row_stride, uint16_t *__restrict__ seghist) {
+    float *__restrict__ logits, int64_t logits_row_stride, uint16_t *__restrict__ seghist,
+    uint16_t *__restrict__ coarse) {
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
     __shared__ __align__(16) uint32_t hist[HIST ? RG * (kBins / 2) : 1];
@@ -360,9 +361,23 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 #pragma unroll
             for (int j = 0; j < RG; ++j) {  // unrolled: a runtime index would put `rows` in scratch
                 if (j >= count || seg_begin >= rows.rend[j]) continue;
-                uint4 *dst = reinterpret_cast<uint4 *>(seghist + ((first + j) * chunks + chunk) * kBins);
-                const uint4 *src = reinterpret_cast<const uint4 *>(hist + j * (kBins / 2));
-                for (int i = threadIdx.x; i < kBins / 8; i += 256) dst[i] = src[i];
+                // lane t copies fine bins [16 t, 16 t + 16) and, with lanes 4c..4c+3, forms
+                // coarse bin c (fine bins [64 c, 64 c + 64))
+                const int64_t at = (first + j) * chunks + chunk;
+                uint4 *dst = reinterpret_cast<uint4 *>(seghist + at * kBins) + 2 * threadIdx.x;
+                const uint4 *src = reinterpret_cast<const uint4 *>(hist + j * (kBins / 2)) +
+                                   2 * threadIdx.x;
+                const uint4 a = src[0], b = src[1];
+                dst[0] = a;
+                dst[1] = b;
+                uint32_t s16 = 0;
+                const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s16 += (w8[e] & 0xFFFFu) + (w8[e] >> 16);
+                s16 += __shfl_xor(s16, 1);
+                s16 += __shfl_xor(s16, 2);
+                if ((threadIdx.x & 3) == 0)
+                    coarse[at * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)s16;
             }
         }
     }
@@ -400,7 +415,7 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
 }
 
 template <int FMT, int H, int RG, bool HIST>
-static hipError_t launch_score_rg(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
+static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
     // page buffers per wavefront: 4 for MXFP4 with up to 2 rows per group, else 2 (FP8 pages
@@ -412,36 +427,36 @@ static hipError_t launch_score_rg(const ScoreArgs &a, uint16_t *seghist, hipStre
                        static_cast<const uint8_t *>(a.cache), a.num_pages, a.page_stride,
                        a.block_table, a.max_blocks, geo.chunks, geo.pages_per_wave,
                        a.query_starts, a.row_ends, a.num_rows, a.max_query_len, a.logits,
-                       a.logits_row_stride, seghist);
+                       a.logits_row_stride, ws.seghist, ws.coarse);
     return hipGetLastError();
 }
 
 template <int FMT, int H, bool HIST>
-static hipError_t launch_score_h(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
-    if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, HIST>(a, seghist, stream);
+static hipError_t launch_score_h(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
+    if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, HIST>(a, ws, stream);
     if constexpr (is_fp8(FMT)) {
         // FP8 queries occupy 4x the registers once widened to BF16: at most 2 rows per group
-        return launch_score_rg<FMT, H, 2, HIST>(a, seghist, stream);
+        return launch_score_rg<FMT, H, 2, HIST>(a, ws, stream);
     } else {
-        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, HIST>(a, seghist, stream);
-        return launch_score_rg<FMT, H, 4, HIST>(a, seghist, stream);
+        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, HIST>(a, ws, stream);
+        return launch_score_rg<FMT, H, 4, HIST>(a, ws, stream);
     }
 }
 
 template <int FMT, bool HIST>
-static hipError_t launch_score_fmt(const ScoreArgs &a, uint16_t *seghist, hipStream_t stream) {
+static hipError_t launch_score_fmt(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
     switch (a.heads) {
-        case 16: return launch_score_h<FMT, 16, HIST>(a, seghist, stream);
-        case 32: return launch_score_h<FMT, 32, HIST>(a, seghist, stream);
-        default: return launch_score_h<FMT, 64, HIST>(a, seghist, stream);
+        case 16: return launch_score_h<FMT, 16, HIST>(a, ws, stream);
+        case 32: return launch_score_h<FMT, 32, HIST>(a, ws, stream);
+        default: return launch_score_h<FMT, 64, HIST>(a, ws, stream);
     }
 }
 
 hipError_t launch_score_paged(const ScoreArgs &a, hipStream_t stream) {
     switch (a.fmt) {
-        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, false>(a, nullptr, stream);
-        case kFmtFp8: return launch_score_fmt<kFmtFp8, false>(a, nullptr, stream);
-        default: return launch_score_fmt<kFmtFp8Mx, false>(a, nullptr, stream);
+        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, false>(a, TopkWorkspace{}, stream);
+        case kFmtFp8: return launch_score_fmt<kFmtFp8, false>(a, TopkWorkspace{}, stream);
+        default: return launch_score_fmt<kFmtFp8Mx, false>(a, TopkWorkspace{}, stream);
     }
 }
 
@@ -451,11 +466,11 @@ size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int6
 
 hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
-    uint16_t *seghist = carve(workspace, a.num_rows, geo.chunks).seghist;
+    const TopkWorkspace ws = carve(workspace, a.num_rows, geo.chunks);
     switch (a.fmt) {
-        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, true>(a, seghist, stream);
-        case kFmtFp8: return launch_score_fmt<kFmtFp8, true>(a, seghist, stream);
-        default: return launch_score_fmt<kFmtFp8Mx, true>(a, seghist, stream);
+        case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, true>(a, ws, stream);
+        case kFmtFp8: return launch_score_fmt<kFmtFp8, true>(a, ws, stream);
+        default: return launch_score_fmt<kFmtFp8Mx, true>(a, ws, stream);
     }
 }
 

@@ -101,152 +101,215 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
         atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
     });
     __syncthreads();
-    // lane t stores bins [16t, 16t+16) as 16-bit counts
+    // lane t stores bins [16t, 16t+16) as 16-bit counts, and lanes 4c..4c+3 together coarse
+    // bin c (fine bins [64c, 64c+64))
     uint32_t c[8];
+    uint32_t sum16 = 0;
     const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + 4 * threadIdx.x;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const uint4 q = h4[v];
         c[2 * v] = q.x | (q.y << 16);
         c[2 * v + 1] = q.z | (q.w << 16);
+        sum16 += q.x + q.y + q.z + q.w;
     }
     uint4 *dst = reinterpret_cast<uint4 *>(ws.seghist + (row * nseg + seg) * kBins +
                                            16 * threadIdx.x);
     dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
     dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    sum16 += __shfl_xor(sum16, 1);
+    sum16 += __shfl_xor(sum16, 2);
+    if ((threadIdx.x & 3) == 0)
+        ws.coarse[(row * nseg + seg) * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)sum16;
 }
 
 // One workgroup per row: a row with at most k keys is written whole (all positions, then
-// -1); otherwise the threshold bin and every segment's output offsets.
+// -1); otherwise the threshold bin and every segment's output offsets, in two levels:
+//   (a) the 64-bin coarse histograms of all segments give the coarse bin B holding the k-th
+//       largest key and the count above B;
+//   (b) the 64 fine bins inside B, per segment, give the fine bin b and the count above b;
+//   (c) per segment: keys above b = its coarse bins above B + its fine bins in B above b,
+//       keys in b = its fine bin b; their exclusive prefix sums are the segment offsets.
+// Lane t covers 8 bins (one 16-byte word) t % 8 of segments t / 8 + 128 i. Rows of up to
+// 128 segments (every workload here) keep the words of their one block in registers and read
+// 256 B per segment once; longer rows read their further blocks again in step (c) (from L2).
+constexpr int kSegBlock = kRowThreads / 8;  // segments per block
+
+__device__ __forceinline__ uint32_t sum8(const uint4 &w) {
+    return (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
+           (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
+}
+
+// 16-bit count i (0..7) of a word of 8 counts
+__device__ __forceinline__ uint32_t count8(const uint4 &w, int i) {
+    const uint32_t d = i < 2 ? w.x : i < 4 ? w.y : i < 6 ? w.z : w.w;
+    return (i & 1) ? d >> 16 : d & 0xFFFFu;
+}
+
+// Sum over the lanes of a wavefront that share t % 8 (lanes t % 8 + 8 j), in every one of
+// them, in registers: a DPP rotate by 8 within each row of 16, then the cross-row swaps
+// (with the value as both operands, each swap pairs rows 0-1 / 2-3, then halves).
+__device__ __forceinline__ uint32_t sum_over_segments_in_wave(uint32_t v) {
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);  // row_ror:8
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = r[0] + r[1];
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return h[0] + h[1];
+}
+
+// Sum over the 8 consecutive lanes of one segment, in all of them: DPP quad permutes (xor 1,
+// xor 2), then the mirror within each half row.
+__device__ __forceinline__ uint32_t sum_over_parts(uint32_t v) {
+    v += __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    return v;
+}
+
+// The bin (0..63, counted from the top) holding the k-th largest of 64 descending counts held
+// one per lane of wavefront 0, with the count above it; run by wavefront 0 only.
+__device__ __forceinline__ void find_in_64(uint32_t c, int k, uint32_t *bin, int *above,
+                                           uint32_t *count) {
+    const int lane = threadIdx.x & 63;
+    const int incl = wave_incl_scan((int)c);
+    const int before = incl - (int)c;
+    if (before < k && incl >= k) {
+        *bin = (uint32_t)lane;
+        *above = before;
+        *count = c;
+    }
+}
+
 __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
     int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
-    __shared__ __align__(16) uint32_t part_hist[kRowThreads / 256][kBins];  // per segment group
-    __shared__ uint32_t seg_above[kMaxRowSegments];
+    __shared__ uint32_t part[kRowThreads / 64][64];
+    __shared__ uint32_t seg_above[kMaxRowSegments], seg_in[kMaxRowSegments];
     __shared__ int partials[kRowThreads / 64];
-    __shared__ uint32_t found_bin, found_count, top_bin;
-    __shared__ int found_above;
+    __shared__ uint32_t found_c, found_f, count_c, count_f;
+    __shared__ int above_c, above_f;
     const int64_t row = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int p8 = t & 7, s0 = t >> 3;
+    // the coarse word of this lane's first segment, issued before the row bound is known
+    // (every segment < nseg lies in the workspace; those past the row's keys are masked below)
+    const uint4 *coarse = reinterpret_cast<const uint4 *>(ws.coarse + row * nseg * kCoarseBins);
+    const uint4 *fine = reinterpret_cast<const uint4 *>(ws.seghist + row * nseg * kBins);
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    uint4 cw0 = s0 < nseg ? coarse[s0 * (kCoarseBins / 8) + p8] : zero4;
     const int64_t n = row_bound(row_ends, row, width);
     if (n <= k) {
         int32_t *out = indices + row * indices_row_stride;
-        for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
+        for (int i = t; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
         return;
     }
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
-    const uint16_t *rowhist = ws.seghist + row * nseg * kBins;
-    const int t = threadIdx.x;
-
-    // (a) Thread t sums bins [16 (t % 256), +16) over the segments s = t / 256 (mod 4),
-    // four segments' loads in flight at a time, and stores the sums for its segment group
-    // (plain vector stores: every entry is written, nothing to clear, no atomics).
+    const int blocks = (row_segments + kSegBlock - 1) / kSegBlock;
+    if (s0 >= row_segments) cw0 = zero4;
     if (t == 0) {
-        found_bin = kBins;  // kept only if the counts do not reach k (they always do)
-        found_above = k;
-        found_count = 0;
-        top_bin = 0;
+        found_c = 0;  // kept only if the counts do not reach k (they always do)
+        above_c = 0;
+        count_c = 0;
     }
-    {
-        const int blk = t & 255, sg0 = t >> 8;
-        uint32_t sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // bin pairs, 16 bits each
-        uint32_t hi16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int s = sg0;
-        for (; s + 12 < row_segments; s += 16) {
-            uint4 v[4][2];
+
+    // (a) coarse totals: bins [8 p8, 8 p8 + 8) summed over this lane's segments, then over the
+    // lanes sharing p8 (in the wavefront by shuffles, across wavefronts in LDS)
+    uint32_t csum[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(rowhist + (int64_t)(s + 4 * u) * kBins + 16 * blk);
-                v[u][0] = src[0];
-                v[u][1] = src[1];
-            }
+    for (int e = 0; e < 8; ++e) csum[e] = count8(cw0, e);
+    for (int i = 1; i < blocks; ++i) {
+        const int sg = s0 + i * kSegBlock;
+        const uint4 w = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t w[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
-                                       v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+        for (int e = 0; e < 8; ++e) csum[e] += count8(w, e);
+    }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sum[e] += w[e] & 0xFFFFu;
-                    hi16[e] += w[e] >> 16;
-                }
-            }
-        }
-        for (; s < row_segments; s += 4) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(rowhist + (int64_t)s * kBins + 16 * blk);
-            const uint4 a = src[0], b = src[1];
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    for (int e = 0; e < 8; ++e) csum[e] = sum_over_segments_in_wave(csum[e]);
+    if (lane < 8) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sum[e] += w[e] & 0xFFFFu;
-                hi16[e] += w[e] >> 16;
-            }
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(&part_hist[sg0][16 * blk]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            dst[v] = make_uint4(sum[2 * v], hi16[2 * v], sum[2 * v + 1], hi16[2 * v + 1]);
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = csum[e];
     }
     __syncthreads();
-
-    // (b) Thread t owns bins 4095 - 4t - j, j < 4 (descending): the bin holding the k-th
-    // largest key, the keys above it, and the highest non-empty bin (the one where the
-    // descending count first leaves zero; a single thread sees that).
-    uint4 m4 = make_uint4(0, 0, 0, 0);
+    if (wave == 0) {  // lane l holds coarse bin 63 - l (descending)
+        uint32_t c = 0;
 #pragma unroll
-    for (int g = 0; g < kRowThreads / 256; ++g) {
-        const uint4 v = reinterpret_cast<const uint4 *>(part_hist[g])[kBins / 4 - 1 - t];
-        m4.x += v.x;
-        m4.y += v.y;
-        m4.z += v.z;
-        m4.w += v.w;
-    }
-    const uint32_t mine[4] = {m4.w, m4.z, m4.y, m4.x};
-    const int own = (int)(m4.x + m4.y + m4.z + m4.w);
-    const int incl = scan_block<kRowThreads>(own, partials);
-    int before = incl - own;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = (int)mine[j];
-        if (before == 0 && c > 0) top_bin = (uint32_t)(kBins - 1 - 4 * t - j);
-        if (before < k && before + c >= k) {
-            found_bin = (uint32_t)(kBins - 1 - 4 * t - j);
-            found_above = before;
-            found_count = (uint32_t)c;
-        }
-        before += c;
-    }
-    for (int sgi = t; sgi < row_segments; sgi += kRowThreads) seg_above[sgi] = 0;
-    __syncthreads();
-    const uint32_t bin = found_bin, top = top_bin;
-
-    // (c) Per-segment keys above the bin: the bins (bin, top] of every segment, spread
-    // over all threads, summed into LDS per segment.
-    if (bin < (uint32_t)kBins && top > bin) {
-        const int span = (int)(top - bin);
-        const int64_t total = (int64_t)row_segments * span;
-        for (int64_t idx = t; idx < total; idx += kRowThreads) {
-            const int sgi = (int)(idx / span);
-            const int b = (int)(bin + 1 + idx % span);
-            const uint32_t c = rowhist[(int64_t)sgi * kBins + b];
-            if (c) atomicAdd(&seg_above[sgi], c);
-        }
+        for (int w = 0; w < kRowThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k, &found_c, &above_c, &count_c);
     }
     __syncthreads();
+    const uint32_t B = 63u - found_c;  // coarse bin, in ascending order
 
-    // (d) Exclusive prefix sums over the segments (one per thread): output and candidate
-    // offsets of every segment.
+    // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
+    const uint4 fw0 = s0 < row_segments ? fine[(int64_t)s0 * (kBins / 8) + B * 8 + p8] : zero4;
+    uint32_t fsum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fsum[e] = count8(fw0, e);
+    for (int i = 1; i < blocks; ++i) {
+        const int sg = s0 + i * kSegBlock;
+        const uint4 w = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fsum[e] += count8(w, e);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(fsum[e]);
+    if (t == 0) {
+        found_f = 0;
+        above_f = 0;
+        count_f = 0;
+    }
+    __syncthreads();  // part[] is rewritten below
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = fsum[e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kRowThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k - above_c, &found_f, &above_f, &count_f);
+    }
+    __syncthreads();
+    const uint32_t f = 63u - found_f;          // fine bin inside B, ascending
+    const uint32_t bin = B * 64 + f;           // threshold bin of the 4096
+
+    // (c) per segment: coarse bins above B, fine bins in B above f, and fine bin f
+    for (int i = 0; i < blocks; ++i) {
+        const int sg = s0 + i * kSegBlock;
+        uint4 cw = cw0, fw = fw0;
+        if (i > 0) {
+            cw = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
+            fw = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+        }
+        uint32_t up = 0, in = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b8 = 8u * p8 + e;
+            up += b8 > B ? count8(cw, e) : 0u;
+            up += b8 > f ? count8(fw, e) : 0u;
+            in += b8 == f ? count8(fw, e) : 0u;
+        }
+        up = sum_over_parts(up);
+        in = sum_over_parts(in);
+        if (p8 == 0 && sg < row_segments) {
+            seg_above[sg] = up;
+            seg_in[sg] = in;
+        }
+    }
+    __syncthreads();
     const uint32_t my_above = t < row_segments ? seg_above[t] : 0u;
-    const uint32_t my_in =
-        t < row_segments && bin < (uint32_t)kBins ? (uint32_t)rowhist[(int64_t)t * kBins + bin] : 0u;
+    const uint32_t my_in = t < row_segments ? seg_in[t] : 0u;
     const int ia = scan_block<kRowThreads>((int)my_above, partials);
     const int ic = scan_block<kRowThreads>((int)my_in, partials);
     if (t < row_segments)
         ws.segoff[row * nseg + t] = make_uint2((uint32_t)ia - my_above, (uint32_t)ic - my_in);
     if (t == 0) {
+        const int above = above_c + above_f;
         RowState &st = ws.state[row];
         st.bin = bin;
-        st.above = found_above;
-        st.remaining = k - found_above;
-        st.n_cand = found_count;
+        st.above = above;
+        st.remaining = k - above;
+        st.n_cand = count_f;
     }
 }
 

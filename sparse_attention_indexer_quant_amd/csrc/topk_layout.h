@@ -1,7 +1,7 @@
 // Workspace layout shared by the top-k kernels and the scorer that can fill its histograms.
 //
 // The selection works on segments of a row's keys: a histogram of the top 12 order-key bits
-// per (row, segment), then per-row threshold state, per-segment output offsets and a
+// per (row, segment) and its 64-bin coarse sums, then per-row threshold state, per-segment output offsets and a
 // candidate list per row. Either the standalone histogram kernel (segments of 4096..32768
 // keys) or the scorer (segments = one scoring workgroup's run of pages) writes the
 // histograms; the rest of the selection only needs the segment count and length.
@@ -14,6 +14,7 @@ namespace dsaidx {
 
 constexpr int kBins = 4096;              // top 12 order-key bits
 constexpr int kBinShift = 20;
+constexpr int kCoarseBins = 64;          // top 6 order-key bits: fine bins [64 c, 64 c + 64)
 constexpr int kCandCap = 8192;           // candidate (key, position) pairs kept per row
 constexpr int kMaxRowSegments = 1024;    // segments per row the threshold kernel handles
 
@@ -27,6 +28,7 @@ struct RowState {
 struct TopkWorkspace {
     RowState *state;
     uint16_t *seghist;  // [rows][nseg][kBins]
+    uint16_t *coarse;   // [rows][nseg][kCoarseBins]: sums of 64 consecutive fine bins
     uint2 *segoff;      // [rows][nseg]: first output slot, first candidate slot
     uint2 *cand;        // [rows][kCandCap]: order key, position
 };
@@ -40,6 +42,8 @@ __host__ __device__ inline TopkWorkspace carve(void *ws, int64_t rows, int64_t n
     p += align256(sizeof(RowState) * rows);
     w.seghist = reinterpret_cast<uint16_t *>(p);
     p += align256(sizeof(uint16_t) * kBins * nseg * rows);
+    w.coarse = reinterpret_cast<uint16_t *>(p);
+    p += align256(sizeof(uint16_t) * kCoarseBins * nseg * rows);
     w.segoff = reinterpret_cast<uint2 *>(p);
     p += align256(sizeof(uint2) * nseg * rows);
     w.cand = reinterpret_cast<uint2 *>(p);
@@ -48,6 +52,7 @@ __host__ __device__ inline TopkWorkspace carve(void *ws, int64_t rows, int64_t n
 
 inline size_t topk_layout_bytes(int64_t rows, int64_t nseg) {
     return align256(sizeof(RowState) * rows) + align256(sizeof(uint16_t) * kBins * nseg * rows) +
+           align256(sizeof(uint16_t) * kCoarseBins * nseg * rows) +
            align256(sizeof(uint2) * nseg * rows) + align256(sizeof(uint2) * (size_t)kCandCap * rows);
 }
 
