@@ -199,10 +199,10 @@ class Setup:
         per_row_q = rb + 2 * wl.heads
         self.score_bytes = wl.key_bytes() + 4 * self.pairs + wl.num_rows * per_row_q
         self.score_flops = 2 * wl.heads * 128 * self.pairs
-        # score_paged_hist also writes one 8 KB histogram per (row, scoring workgroup) that
-        # holds keys of the row
+        # score_paged_hist also writes, per (row, scoring workgroup) holding keys of the row, an
+        # 8 KB histogram and its 128 B of coarse sums
         seg = hist_segment_keys(wl)
-        self.hist_bytes = int(sum(8192 * ((int(e) + seg - 1) // seg) for e in ends))
+        self.hist_bytes = int(sum((8192 + 128) * ((int(e) + seg - 1) // seg) for e in ends))
         self.score_hist_bytes = self.score_bytes + self.hist_bytes
 
     def step(self, i, ev=None):
