@@ -47,6 +47,7 @@ constexpr int kMaxSegment = 32768;       // 16-bit segment histogram counts stay
 constexpr int kMaxWorkgroups = 2048;
 static_assert(kTopkMaxWidth / kMaxSegment <= kMaxRowSegments, "a row fits the threshold kernel");
 static_assert(kMaxRowSegments <= kRowThreads, "one thread per segment in the offset scan");
+static_assert(4 * kSelectThreads <= kCandCap, "speculative candidate loads stay in the list");
 
 // Keys per segment for this call's shape (the same rule sizes the workspace).
 inline int64_t topk_segment(int64_t rows, int64_t width) {
@@ -413,6 +414,13 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     __shared__ uint64_t cands[kCandCap];
     __shared__ SelectShared sh;
     const int64_t row = blockIdx.x;
+    // the first kSpec candidates, loaded before their count is known (the list always has
+    // kCandCap slots; slots past the count are ignored)
+    constexpr int kSpec = 4;
+    const uint2 *cand = ws.cand + row * kCandCap;
+    uint2 pre[kSpec];
+#pragma unroll
+    for (int i = 0; i < kSpec; ++i) pre[i] = cand[threadIdx.x + i * kSelectThreads];
     const int64_t n = row_bound(row_ends, row, width);
     if (n <= k) return;
     const float *x = logits + row * logits_row_stride;
@@ -425,8 +433,12 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
     const int bits = 20 + pos_bits;
     if (ncand <= (uint32_t)kCandCap) {
-        const uint2 *cand = ws.cand + row * kCandCap;
-        for (int j = threadIdx.x; j < (int)ncand; j += kSelectThreads) {
+#pragma unroll
+        for (int i = 0; i < kSpec; ++i) {
+            const int j = threadIdx.x + i * kSelectThreads;
+            if (j < (int)ncand) cands[j] = composite(pre[i].x, pre[i].y, pos_bits);
+        }
+        for (int j = threadIdx.x + kSpec * kSelectThreads; j < (int)ncand; j += kSelectThreads) {
             const uint2 e = cand[j];
             cands[j] = composite(e.x, e.y, pos_bits);
         }
