@@ -1,9 +1,9 @@
 """Benchmark of the DSA lightning-indexer hot path on one MI355X.
 
 One step = one pass of the whole path over one decode batch, inputs resident in HBM:
-index_inputs (one launch: every row's query quantized with its head weights, and the step's
-new keys normalized, quantized and inserted), decode_layout, score_paged_hist (scoring that
-also writes the top-k segment histograms) and topk_scored. The same step with the separate
+index_inputs_layout (one launch: every row's query quantized with its head weights, the step's
+new keys normalized, quantized and inserted, and the decode_layout row bounds),
+score_paged_hist (scoring that also writes the top-k segment histograms) and topk_scored. The same step with the separate
 score_paged + topk is timed too (per_config ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of the whole
 step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
 launch stream around every score launch in the timed region), and the CPU oracle timed on
@@ -163,6 +163,7 @@ class Setup:
                                     self.idx.data_ptr(), self.idx.stride(0), wl.num_requests,
                                     wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
         self.store, self.score, self.inputs, self.score_hist = [], [], [], []
+        self.inputs_layout = []
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(
@@ -172,6 +173,15 @@ class Setup:
                 self.row_slots.data_ptr(), base, wl.num_pages, wl.page_stride,
                 self.q_rows.data_ptr(), self.q_rows.stride(0), self.w_out.data_ptr(),
                 self.w_out.stride(0), sp))
+            self.inputs_layout.append(Prepared(
+                lib.dsaidx_index_inputs_layout, fmt, self.projected.data_ptr(), wl.num_rows,
+                self.projected.stride(0), 0, 128, self.q.data_ptr(), wl.heads, self.q.stride(0),
+                self.q.stride(1), self.gamma.data_ptr(), self.beta.data_ptr(), ctypes.c_float(wl.eps),
+                self.row_slots.data_ptr(), base, wl.num_pages, wl.page_stride,
+                self.q_rows.data_ptr(), self.q_rows.stride(0), self.w_out.data_ptr(),
+                self.w_out.stride(0), self.seq_lens.data_ptr(), self.query_lens.data_ptr(),
+                wl.num_requests, wl.num_rows, 0, 1, 1, self.starts.data_ptr(),
+                self.ends.data_ptr(), sp))
             self.store.append(Prepared(
                 lib.dsaidx_store_keys, fmt, self.new_keys.data_ptr(), self.new_keys.shape[0],
                 self.new_keys.stride(0), self.gamma.data_ptr(), self.beta.data_ptr(),
@@ -207,11 +217,10 @@ class Setup:
         self.score_hist_bytes = self.score_bytes + self.hist_bytes
 
     def prologue(self, i):
-        """index_inputs and decode_layout, in line on one stream. (Running decode_layout on a
-        second stream beside index_inputs measured 20-40 us slower per step: the cross-stream
-        waits cost more than the kernel they would hide.)"""
-        self.inputs[i % len(self.caches)]()
-        self.layout()
+        """index_inputs and decode_layout in one launch (index_inputs_layout). (Running
+        decode_layout on a second stream beside index_inputs measured 20-40 us slower per step:
+        the cross-stream waits cost more than the kernel they would hide.)"""
+        self.inputs_layout[i % len(self.caches)]()
 
     def step(self, i, ev=None):
         """index_inputs, decode_layout, score_paged_hist (timed), topk_scored."""
@@ -256,7 +265,8 @@ def kernel_times(s: Setup, reps: int = 30):
     """Per-kernel HIP-event times (ms, median) of each stage launched alone."""
     import torch
     out = {}
-    stages = [("index_inputs", lambda i: s.inputs[i % len(s.caches)]()),
+    stages = [("index_inputs_layout", lambda i: s.inputs_layout[i % len(s.caches)]()),
+              ("index_inputs", lambda i: s.inputs[i % len(s.caches)]()),
               ("quantize_queries", lambda i: s.quant()),
               ("store_keys", lambda i: s.store[i % len(s.caches)]()),
               ("decode_layout", lambda i: s.layout()),

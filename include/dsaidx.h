@@ -156,6 +156,22 @@ dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens
                                   void *stream);
 
 /*
+ * index_inputs_layout -- dsaidx_index_inputs and dsaidx_decode_layout in one launch (one more
+ * workgroup computes the row bounds): the step's query / weight / key inputs and its row
+ * bounds, bit-identical to the two calls. All arguments as in those two calls; the layout
+ * runs even when tokens == 0. Errors: as either call.
+ */
+dsaidx_status dsaidx_index_inputs_layout(
+    int fmt, const void *projected, int64_t tokens, int64_t proj_row_stride, int64_t key_col,
+    int64_t weight_col, const void *q, int32_t heads, int64_t q_row_stride,
+    int64_t q_head_stride, const float *gamma, const float *beta, float eps,
+    const int64_t *slots, void *cache, int64_t num_pages, int64_t page_stride, void *q_out,
+    int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride, const int32_t *seq_lens,
+    const int32_t *query_lens, int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+    int32_t dcp_world_size, int32_t interleave, int32_t *query_starts, int32_t *row_ends,
+    void *stream);
+
+/*
  * decode_layout -- [fp4ops] decode_layout. One workgroup; no device-to-host reads.
  *
  *  seq_lens, query_lens  device, int32 [num_requests] (query_lens >= 0).

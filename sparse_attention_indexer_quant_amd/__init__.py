@@ -60,6 +60,9 @@ def library():
             "dsaidx_store_keys": (I32, [I32, P, I64, I64, P, P, F32, P, P, I64, I64, P]),
             "dsaidx_index_inputs": (I32, [I32, P, I64, I64, I64, I64, P, I32, I64, I64, P, P, F32,
                                           P, P, I64, I64, P, I64, P, I64, P]),
+            "dsaidx_index_inputs_layout": (I32, [I32, P, I64, I64, I64, I64, P, I32, I64, I64, P, P,
+                                                 F32, P, P, I64, I64, P, I64, P, I64, P, P, I64,
+                                                 I64, I32, I32, I32, P, P, P]),
             "dsaidx_decode_layout": (I32, [P, P, I64, I64, I32, I32, I32, P, P, P]),
             "dsaidx_score_paged": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64, P, P,
                                          I64, I32, P, I64, P]),
@@ -198,6 +201,40 @@ def index_inputs(projected, key_col, weight_col, q, gamma, beta, eps, slots, cac
         _stream(q))
     _check("index_inputs", st)
     return out, w_out
+
+
+def index_inputs_layout(projected, key_col, weight_col, q, gamma, beta, eps, slots, cache,
+                        num_pages, page_stride, seq_lens, query_lens, num_rows, fmt="mxfp4",
+                        section_offset=0, dcp_rank=0, dcp_world_size=1, interleave=1):
+    """index_inputs and decode_layout in one launch. Returns (q_rows, w_out, query_starts,
+    row_ends)."""
+    import torch
+    _dev(projected, "projected", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    _dev(slots, "slots", torch.int64)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(query_lens, "query_lens", torch.int32)
+    if projected.dim() != 2 or projected.stride(1) != 1 or q.dim() != 3 or q.stride(2) != 1 \
+            or q.shape[0] != projected.shape[0] or slots.numel() != q.shape[0]:
+        raise ValueError("index_inputs_layout: projected [tokens, cols], q [tokens, heads, 128], "
+                         "one slot per token")
+    tokens, heads = q.shape[0], q.shape[1]
+    f = _fmt(fmt)
+    out = torch.empty((tokens, query_row_bytes(f, heads)), dtype=torch.uint8, device=q.device)
+    w_out = torch.empty((tokens, heads), dtype=torch.bfloat16, device=q.device)
+    R = query_lens.numel()
+    starts = torch.empty(R + 1, dtype=torch.int32, device=q.device)
+    ends = torch.empty(max(int(num_rows), 0), dtype=torch.int32, device=q.device)
+    st = library().dsaidx_index_inputs_layout(
+        f, projected.data_ptr(), tokens, projected.stride(0), int(key_col), int(weight_col),
+        q.data_ptr(), heads, q.stride(0), q.stride(1), gamma.data_ptr(), beta.data_ptr(),
+        float(eps), slots.data_ptr(), cache.data_ptr() + int(section_offset), int(num_pages),
+        int(page_stride), out.data_ptr(), out.stride(0), w_out.data_ptr(), w_out.stride(0),
+        seq_lens.contiguous().data_ptr(), query_lens.contiguous().data_ptr(), R, int(num_rows),
+        int(dcp_rank), int(dcp_world_size), int(interleave), starts.data_ptr(), ends.data_ptr(),
+        _stream(q))
+    _check("index_inputs_layout", st)
+    return out, w_out, starts, ends
 
 
 def decode_layout(seq_lens, query_lens, num_rows, dcp_rank=0, dcp_world_size=1, interleave=1,

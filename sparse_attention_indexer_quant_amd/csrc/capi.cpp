@@ -13,6 +13,7 @@
 
 #include "dsaidx.h"
 #include "launch.h"
+#include "layout.h"
 #include "topk_layout.h"
 
 namespace {
@@ -107,20 +108,28 @@ dsaidx_status dsaidx_store_keys(int fmt, const void *keys, int64_t tokens, int64
                                                 as_stream(stream)));
 }
 
-dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens,
-                                  int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
-                                  const void *q, int32_t heads, int64_t q_row_stride,
-                                  int64_t q_head_stride, const float *gamma, const float *beta,
-                                  float eps, const int64_t *slots, void *cache,
-                                  int64_t num_pages, int64_t page_stride, void *q_out,
-                                  int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride,
-                                  void *stream) {
-    if (!valid_fmt(fmt) || tokens < 0 || tokens > kMaxGrid || num_pages < 0 || key_col < 0 ||
+}  // extern "C"
+
+namespace {
+
+// Argument rules of index_inputs; *empty = true when there are no tokens (nothing to launch).
+dsaidx_status check_index_inputs(int fmt, const void *projected, int64_t tokens,
+                                 int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+                                 const void *q, int32_t heads, int64_t q_row_stride,
+                                 int64_t q_head_stride, const float *gamma, const float *beta,
+                                 float eps, const int64_t *slots, void *cache, int64_t num_pages,
+                                 int64_t page_stride, void *q_out, int64_t q_out_row_stride,
+                                 void *w_out, int64_t w_out_row_stride, bool *empty) {
+    *empty = false;
+    if (!valid_fmt(fmt) || tokens < 0 || tokens > kMaxGrid - 1 || num_pages < 0 || key_col < 0 ||
         weight_col < 0)
         return DSAIDX_EINVAL;
     if (!std::isfinite(eps) || eps < 0.0f) return DSAIDX_EINVAL;
     if (!valid_heads(heads)) return DSAIDX_EUNSUPPORTED;
-    if (tokens == 0) return DSAIDX_OK;
+    if (tokens == 0) {
+        *empty = true;
+        return DSAIDX_OK;
+    }
     if (!projected || !q || !gamma || !beta || !slots || !cache || !q_out || !w_out)
         return DSAIDX_EINVAL;
     // packed row: the key's 128 columns and the H weight columns lie inside each row; the key
@@ -138,16 +147,14 @@ dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens
     if (!aligned(gamma, 8) || !aligned(beta, 8) || !aligned(slots, 8)) return DSAIDX_ELAYOUT;
     if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
         return DSAIDX_ELAYOUT;
-    return hip_status(dsaidx::launch_index_inputs(
-        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
-        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
-        q_out_row_stride, w_out, w_out_row_stride, head_weight_scale(heads), as_stream(stream)));
+    return DSAIDX_OK;
 }
 
-dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
-                                   int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
-                                   int32_t dcp_world_size, int32_t interleave,
-                                   int32_t *query_starts, int32_t *row_ends, void *stream) {
+// Argument rules of decode_layout.
+dsaidx_status check_layout(const int32_t *seq_lens, const int32_t *query_lens,
+                           int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+                           int32_t dcp_world_size, int32_t interleave, int32_t *query_starts,
+                           int32_t *row_ends) {
     if (!(0 <= dcp_rank && dcp_rank < dcp_world_size) || interleave < 1 || num_rows < 0 ||
         num_requests < 0 || num_requests > kMaxGrid || num_rows > kMaxGrid)
         return DSAIDX_EINVAL;
@@ -155,6 +162,68 @@ dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query
         (num_requests > 0 && (!seq_lens || !query_lens)))
         return DSAIDX_EINVAL;
     if (!aligned(query_starts, 4) || (row_ends && !aligned(row_ends, 4))) return DSAIDX_ELAYOUT;
+    return DSAIDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsaidx_status dsaidx_index_inputs(int fmt, const void *projected, int64_t tokens,
+                                  int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+                                  const void *q, int32_t heads, int64_t q_row_stride,
+                                  int64_t q_head_stride, const float *gamma, const float *beta,
+                                  float eps, const int64_t *slots, void *cache,
+                                  int64_t num_pages, int64_t page_stride, void *q_out,
+                                  int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride,
+                                  void *stream) {
+    bool empty = false;
+    const dsaidx_status st = check_index_inputs(
+        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
+        q_out_row_stride, w_out, w_out_row_stride, &empty);
+    if (st != DSAIDX_OK || empty) return st;
+    return hip_status(dsaidx::launch_index_inputs(
+        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
+        q_out_row_stride, w_out, w_out_row_stride, head_weight_scale(heads), nullptr,
+        as_stream(stream)));
+}
+
+dsaidx_status dsaidx_index_inputs_layout(
+    int fmt, const void *projected, int64_t tokens, int64_t proj_row_stride, int64_t key_col,
+    int64_t weight_col, const void *q, int32_t heads, int64_t q_row_stride,
+    int64_t q_head_stride, const float *gamma, const float *beta, float eps,
+    const int64_t *slots, void *cache, int64_t num_pages, int64_t page_stride, void *q_out,
+    int64_t q_out_row_stride, void *w_out, int64_t w_out_row_stride, const int32_t *seq_lens,
+    const int32_t *query_lens, int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+    int32_t dcp_world_size, int32_t interleave, int32_t *query_starts, int32_t *row_ends,
+    void *stream) {
+    bool empty = false;
+    dsaidx_status st = check_index_inputs(
+        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
+        q_out_row_stride, w_out, w_out_row_stride, &empty);
+    if (st != DSAIDX_OK) return st;
+    st = check_layout(seq_lens, query_lens, num_requests, num_rows, dcp_rank, dcp_world_size,
+                      interleave, query_starts, row_ends);
+    if (st != DSAIDX_OK) return st;
+    const dsaidx::LayoutArgs la{seq_lens, query_lens, num_requests, num_rows, dcp_rank,
+                                dcp_world_size, interleave, query_starts, row_ends};
+    return hip_status(dsaidx::launch_index_inputs(
+        fmt, projected, tokens, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, slots, cache, num_pages, page_stride, q_out,
+        q_out_row_stride, w_out, w_out_row_stride, head_weight_scale(heads), &la,
+        as_stream(stream)));
+}
+
+dsaidx_status dsaidx_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
+                                   int64_t num_requests, int64_t num_rows, int32_t dcp_rank,
+                                   int32_t dcp_world_size, int32_t interleave,
+                                   int32_t *query_starts, int32_t *row_ends, void *stream) {
+    const dsaidx_status st = check_layout(seq_lens, query_lens, num_requests, num_rows, dcp_rank,
+                                          dcp_world_size, interleave, query_starts, row_ends);
+    if (st != DSAIDX_OK) return st;
     return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests, num_rows,
                                                    dcp_rank, dcp_world_size, interleave,
                                                    query_starts, row_ends, as_stream(stream)));

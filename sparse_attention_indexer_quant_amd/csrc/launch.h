@@ -20,6 +20,8 @@ hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t 
                              const int64_t *slots, void *cache, int64_t num_pages,
                              int64_t page_stride, hipStream_t stream);
 
+struct LayoutArgs;
+// `layout` (may be null): also compute decode_layout in the same launch (one more workgroup).
 hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
                                int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
                                const void *q, int heads, int64_t q_row_stride,
@@ -27,7 +29,7 @@ hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
                                float eps, const int64_t *slots, void *cache, int64_t num_pages,
                                int64_t page_stride, void *q_out, int64_t q_out_row_stride,
                                void *w_out, int64_t w_out_row_stride, float c_h,
-                               hipStream_t stream);
+                               const LayoutArgs *layout, hipStream_t stream);
 
 hipError_t launch_decode_layout(const int32_t *seq_lens, const int32_t *query_lens,
                                 int64_t num_requests, int64_t num_rows, int dcp_rank,

@@ -16,6 +16,7 @@
 // with the __f*_rn intrinsics, so the bytes do not depend on contraction choices.
 #include "device_common.h"
 #include "launch.h"
+#include "layout.h"
 
 namespace dsaidx {
 
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
 // "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex): one workgroup
 // per token quantizes the token's query with the head weights read from the packed projection
 // row, and its last wavefront then normalizes, quantizes and inserts the key held in the same
-// row (at H = 16, 32, 64 every wavefront quantizes the same number of heads).
+// row (at H = 16, 32, 64 every wavefront quantizes the same number of heads). With a layout,
+// one more workgroup computes the row bounds (decode_layout) in the same launch.
 template <int FMT>
 __global__ __launch_bounds__(256) void index_inputs_kernel(
     const uint16_t *__restrict__ projected, int64_t proj_row_stride, int64_t key_col,
@@ -210,8 +212,13 @@ __global__ __launch_bounds__(256) void index_inputs_kernel(
     int64_t q_head_stride, const float *__restrict__ gamma, const float *__restrict__ beta,
     float eps, const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
     int64_t page_stride, uint8_t *__restrict__ q_out, int64_t q_out_row_stride,
-    uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
+    uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h, int64_t tokens,
+    LayoutArgs layout) {
     const int64_t token = blockIdx.x;
+    if (token == tokens) {  // the extra workgroup of the combined call: the row bounds
+        decode_layout_body<256>(layout);
+        return;
+    }
     const uint16_t *prow = projected + token * proj_row_stride;
     const int lane = threadIdx.x & 63;
     const bool key_wave = (threadIdx.x >> 6) == 3;
@@ -271,28 +278,29 @@ hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
                                float eps, const int64_t *slots, void *cache, int64_t num_pages,
                                int64_t page_stride, void *q_out, int64_t q_out_row_stride,
                                void *w_out, int64_t w_out_row_stride, float c_h,
-                               hipStream_t stream) {
-    const dim3 grid((unsigned)tokens), block(256);
+                               const LayoutArgs *layout, hipStream_t stream) {
+    const dim3 grid((unsigned)(tokens + (layout ? 1 : 0))), block(256);
     auto *pp = static_cast<const uint16_t *>(projected);
     auto *qq = static_cast<const uint16_t *>(q);
     auto *cc = static_cast<uint8_t *>(cache);
     auto *qo = static_cast<uint8_t *>(q_out);
     auto *wo = static_cast<uint16_t *>(w_out);
+    const LayoutArgs la = layout ? *layout : LayoutArgs{};
     if (fmt == kFmtMxfp4)
         hipLaunchKernelGGL(index_inputs_kernel<kFmtMxfp4>, grid, block, 0, stream, pp,
                            proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
                            q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h);
+                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
     else if (fmt == kFmtFp8)
         hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8>, grid, block, 0, stream, pp,
                            proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
                            q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h);
+                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
     else
         hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8Mx>, grid, block, 0, stream, pp,
                            proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
                            q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h);
+                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
-              "dsaidx_dcp_merge"):
+              "dsaidx_dcp_merge", "dsaidx_index_inputs_layout"):
         assert n in names
 
 

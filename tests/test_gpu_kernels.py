@@ -185,6 +185,36 @@ def test_index_inputs_bit_exact(fmt, heads, stride, offset, key_col, weight_col)
     assert np.array_equal(got_cache.cpu().numpy(), want_cache)
 
 
+@pytest.mark.parametrize("dcp", [(0, 1, 1), (1, 4, 64)])
+def test_index_inputs_layout_matches_separate_calls(dcp):
+    # one launch: the fused inputs plus the row bounds, bit-identical to the two calls
+    rng = np.random.default_rng(45)
+    tokens, heads, pages = 10, 32, 30
+    proj = bf16_bits(rng.standard_normal((tokens, 200)).astype(np.float32))
+    q = bf16_bits(rng.standard_normal((tokens, heads, 128)).astype(np.float32))
+    slots = rng.permutation(pages * 64)[:tokens].astype(np.int64)
+    slots[3] = -1
+    seq = rng.integers(1, 1500, size=7).astype(np.int32)
+    ql = np.array([1, 2, 0, 3, 1, 1, 2], np.int32)
+    g, b = dev(np.ones(128, np.float32)), dev(np.zeros(128, np.float32))
+    c1 = torch.zeros(pages * 4352, dtype=torch.uint8, device="cuda")
+    c2 = torch.zeros(pages * 4352, dtype=torch.uint8, device="cuda")
+    pd = bf16_dev(proj)
+    q1, w1, s1, e1 = dsa.index_inputs_layout(pd, 8, 140, bf16_dev(q), g, b, 1e-6, dev(slots), c1,
+                                             pages, 4352, dev(seq), dev(ql), 13, "mxfp4", 0, *dcp)
+    q2, w2 = dsa.index_inputs(pd, 8, 140, bf16_dev(q), g, b, 1e-6, dev(slots), c2, pages, 4352)
+    s2, e2 = dsa.decode_layout(dev(seq), dev(ql), 13, *dcp)
+    assert torch.equal(q1, q2) and torch.equal(w1, w2) and torch.equal(c1, c2)
+    assert torch.equal(s1, s2) and torch.equal(e1, e2)
+    os_, oe = oracle.decode_layout(seq, ql, 13, *dcp)
+    assert np.array_equal(s1.cpu().numpy(), os_) and np.array_equal(e1.cpu().numpy(), oe)
+    # no tokens: only the layout
+    _, _, s3, e3 = dsa.index_inputs_layout(pd[:0], 8, 140, bf16_dev(q)[:0], g, b, 1e-6,
+                                           dev(slots)[:0], c1, pages, 4352, dev(seq), dev(ql), 13,
+                                           "mxfp4", 0, *dcp)
+    assert torch.equal(s3, s2) and torch.equal(e3, e2)
+
+
 def test_index_inputs_matches_separate_calls_and_empty():
     # one launch gives the same bytes as quantize_queries + store_keys on the extracted columns
     rng = np.random.default_rng(44)
