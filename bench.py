@@ -6,7 +6,8 @@ new keys normalized, quantized and inserted, and the decode_layout row bounds),
 score_paged_hist (scoring that also writes the top-k segment histograms) and topk_scored. The same step with the separate
 score_paged + topk is timed too (per_config ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of the whole
 step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
-launch stream around every score launch in the timed region), and the CPU oracle timed on
+launch stream around every score launch in the timed region, created without the
+system-scope cache fence a default event's record adds), and the CPU oracle timed on
 a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config long_mxfp4] [--configs all|none|a,b]
@@ -54,6 +55,54 @@ def parse():
     return ap.parse_args()
 
 
+def _hip_runtime():
+    """The HIP runtime this process already uses (the one torch loaded), by its mapped path."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in os.path.basename(path):
+                return ctypes.CDLL(path)
+    return ctypes.CDLL("libamdhip64.so")
+
+
+class TimingEvent:
+    """A HIP event created with hipEventDisableSystemFence (0x20000000). A default event's
+    record writes back and invalidates the caches at system scope, which adds that cost to the
+    interval it closes; this flag, documented for timing-only events, leaves it out. Recorded
+    on the stream the kernels run on."""
+
+    _hip = None
+    FLAGS = 0x20000000
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            TimingEvent._hip = _hip_runtime()
+        self.ev = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                       ctypes.c_uint(self.FLAGS))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        """Milliseconds from this event to `end` (waits for `end`)."""
+        hip = TimingEvent._hip
+        if hip.hipEventSynchronize(end.ev) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.ev:
+            TimingEvent._hip.hipEventDestroy(self.ev)
+
+
 class Prepared:
     """A C-ABI call with its argument tuple marshalled once (plain integers and pointers)."""
 
@@ -80,14 +129,9 @@ def packed_rows(wl):
 
 
 def hist_segment_keys(wl):
-    """Keys per scoring workgroup (the top-k segment score_paged_hist writes histograms for):
-    4 wavefronts x pages per wavefront x 64, with the scorer's pages-per-wavefront rule."""
-    import torch
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    target = cus * 8
-    ppw = (wl.num_requests * wl.max_blocks + target - 1) // target
-    ppw = min(16, max(4, (ppw + 3) // 4 * 4))
-    return 4 * ppw * 64
+    """Keys per scoring workgroup (the top-k segment score_paged_hist writes histograms for)."""
+    import sparse_attention_indexer_quant_amd as dsa
+    return dsa.score_segment_keys(wl.num_requests, wl.max_blocks)
 
 
 class Setup:
@@ -249,8 +293,7 @@ def time_steps(s: Setup, steps: int, warmup: int, fused: bool = True):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -277,11 +320,10 @@ def kernel_times(s: Setup, reps: int = 30):
     for name, fn in stages:
         ts = []
         for i in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record(s.stream)
             fn(i)
             b.record(s.stream)
-            b.synchronize()
             ts.append(a.elapsed_time(b))
         out[name] = float(np.median(ts))
     return out

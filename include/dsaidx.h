@@ -241,6 +241,13 @@ size_t dsaidx_score_topk_workspace_bytes(int64_t num_requests, int64_t max_block
                                          int64_t num_rows);
 
 /*
+ * dsaidx_score_segment_keys: keys per segment of those histograms (the keys one scoring
+ * workgroup covers: segment s of a row holds key positions [s * n, (s + 1) * n)) for these
+ * sizes on the current device; 0 if the sizes are invalid.
+ */
+int64_t dsaidx_score_segment_keys(int64_t num_requests, int64_t max_blocks);
+
+/*
  * score_paged_hist -- dsaidx_score_paged plus the top-k segment histograms.
  *  All arguments as dsaidx_score_paged, and
  *  workspace  device, >= dsaidx_score_topk_workspace_bytes(num_requests, max_blocks,

@@ -68,6 +68,7 @@ def library():
                                          I64, I32, P, I64, P]),
             "dsaidx_topk_workspace_bytes": (SZ, [I64, I64, I32]),
             "dsaidx_score_topk_workspace_bytes": (SZ, [I64, I64, I64]),
+            "dsaidx_score_segment_keys": (I64, [I64, I64]),
             "dsaidx_score_paged_hist": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
                                               P, P, I64, I32, P, I64, P, SZ, P]),
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
@@ -294,6 +295,11 @@ def score_paged(q_rows, heads, weights, cache, num_pages, page_stride, block_tab
 def score_topk_workspace_bytes(num_requests, max_blocks, num_rows) -> int:
     return int(library().dsaidx_score_topk_workspace_bytes(int(num_requests), int(max_blocks),
                                                            int(num_rows)))
+
+
+def score_segment_keys(num_requests, max_blocks) -> int:
+    """Keys per top-k histogram segment (one scoring workgroup's keys) for these sizes."""
+    return int(library().dsaidx_score_segment_keys(int(num_requests), int(max_blocks)))
 
 
 def score_topk(q_rows, heads, weights, cache, num_pages, page_stride, block_table, query_starts,

@@ -36,6 +36,9 @@ def common_flags() -> list[str]:
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # matrix results land in VGPRs, read directly by the epilogue
             "-mllvm", "-amdgpu-mfma-vgpr-form",
+            # the leading kernel arguments arrive in scalar registers at wave launch instead of
+            # being loaded from memory (the code object keeps a fallback that loads them)
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -269,6 +269,11 @@ size_t dsaidx_score_topk_workspace_bytes(int64_t num_requests, int64_t max_block
     return dsaidx::score_topk_workspace_bytes(num_requests, max_blocks, num_rows);
 }
 
+int64_t dsaidx_score_segment_keys(int64_t num_requests, int64_t max_blocks) {
+    if (num_requests < 1 || max_blocks < 1 || max_blocks > (int64_t)INT32_MAX / 64) return 0;
+    return dsaidx::score_geometry(num_requests, max_blocks).segment_keys;
+}
+
 dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stride,
                                       int32_t heads, const void *w, int64_t w_row_stride,
                                       const void *cache, int64_t num_pages, int64_t page_stride,

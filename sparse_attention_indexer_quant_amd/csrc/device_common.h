@@ -100,6 +100,18 @@ __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
     return v;
 }
 
+// Kernel arguments are read from memory, and the compiler loads each one next to its first use;
+// in a short kernel those loads form a chain of round trips, each waited for before the next
+// is issued. Naming the arguments here, at the kernel's entry, loads all of them at once.
+template <typename T>
+__device__ __forceinline__ void hoist_arg(const T &v) {
+    asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void hoist_args(const T &...v) {
+    (hoist_arg(v), ...);
+}
+
 // Order-preserving 32-bit key of a logit for the top-k selection: unsigned comparison of
 // keys is the float order, with -0 mapped to +0 so the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -34,6 +34,7 @@
 // run of keys. The selection then skips its own pass over the logits.
 #include "device_common.h"
 #include "launch.h"
+#include <type_traits>
 #include "topk_layout.h"
 
 namespace dsaidx {
@@ -124,7 +125,9 @@ __device__ __forceinline__ float head_sum_to_token(float p0, float p1, float p2,
 template <int FMT>
 struct PageRegs {
     uint4 kp[4][FMT == kFmtMxfp4 ? 1 : 2];
-    uint32_t ks[4];
+    // MXFP4: the byte as loaded (a 32-bit copy would be masked where it is made, which waits
+    // for the load there); FP8: the token's 32-bit scale
+    typename std::conditional<FMT == kFmtMxfp4, uint8_t, uint32_t>::type ks[4];
 };
 
 // Loads one page section into registers. The caller always issues the loads (a page that
@@ -255,15 +258,16 @@ struct RowGroup {
 // same loads across its back edge on every path and the hardware wait counts stay exact;
 // conditional prefetches made the compiler wait for all loads there. The first NB - 1 loads
 // go out as soon as the block table slice arrives, while the row bounds are still in flight.
+// The arguments the first loads need come first: the library is built to preload the leading
+// kernel arguments into scalar registers at wave launch.
 template <int FMT, int H, int RG, int NB, bool HIST>
 __global__ __launch_bounds__(256) void score_paged_kernel(
-    const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
-    int64_t w_row_stride, const uint8_t *__restrict__ cache, int64_t num_pages,
-    int64_t page_stride, const int32_t *__restrict__ block_table, int64_t max_blocks,
-    int64_t chunks, int pages_per_wave, const int32_t *__restrict__ query_starts,
-    const int32_t *__restrict__ row_ends, int64_t num_rows, int max_query_len,
-    float *__restrict__ logits, int64_t logits_row_stride, uint16_t *__restrict__ seghist,
-    uint16_t *__restrict__ coarse) {
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
+    int64_t max_blocks, int64_t chunks, int pages_per_wave, const uint8_t *__restrict__ cache,
+    int64_t page_stride, int64_t num_pages, const uint8_t *__restrict__ q, int64_t q_row_stride,
+    const uint16_t *__restrict__ w, int64_t w_row_stride, const int32_t *__restrict__ row_ends,
+    int64_t num_rows, int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
+    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse) {
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
     __shared__ __align__(16) uint32_t hist[HIST ? RG * (kBins / 2) : 1];
@@ -272,17 +276,23 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
-    const int64_t req = blockIdx.x / chunks;
-    const int64_t chunk = blockIdx.x % chunks;
+    // the grid has requests x chunks < 2^31 workgroups: 32-bit division
+    const uint32_t req32 = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)chunks);
+    const int64_t req = req32;
+    const int64_t chunk = blockIdx.x - req32 * (uint32_t)chunks;
     const int64_t width = max_blocks * kPageTokens;
     const int PW = pages_per_wave;
     const int64_t blk_begin = (chunk * kWaves + wave) * (int64_t)PW;
     if (!HIST && blk_begin >= max_blocks) return;
-    // This wavefront's slice of the block table, one entry per lane (every entry below
-    // max_blocks is in bounds).
+    // At wave launch (every operand is a preloaded argument): the request's rows (scalar loads;
+    // nothing before them in the kernel writes memory) and this wavefront's slice of the block
+    // table (one entry per lane; every entry below max_blocks is in bounds). Then every other
+    // argument at once, in the same round trip.
+    int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
     const int32_t *bt = block_table + req * max_blocks;
     const int bt_lane = lane < PW && blk_begin + lane < max_blocks ? bt[blk_begin + lane] : -1;
-    int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
+    hoist_args(num_pages, q, q_row_stride, w, w_row_stride, row_ends, num_rows, max_query_len,
+               logits, logits_row_stride, seghist, coarse);
 
     // Table entry of run page p (uniform), or -1 if it names no page of the cache.
     const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
@@ -297,12 +307,6 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
         return cache + (int64_t)(pg >= 0 ? pg : 0) * page_stride;
     };
 
-    const LaneOffsets<FMT> off(l16, grp);
-    PageRegs<FMT> buf[NB];
-#pragma unroll
-    for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
-    asm volatile("" ::: "memory");  // issue these before waiting on the row bounds
-
     if (r0 < 0) return;
     if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
     if (r1 > num_rows) r1 = num_rows;
@@ -316,6 +320,15 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 
     // Keys this request needs: the largest bound over its rows.
     int kmax = lane < nrows ? row_ends[r0 + lane] : 0;
+
+    // The first NB - 1 pages go out after the query and bound loads: loads complete in issue
+    // order, so the first page's math then waits for that page and not for the whole ring.
+    const LaneOffsets<FMT> off(l16, grp);
+    PageRegs<FMT> buf[NB];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
+    asm volatile("" ::: "memory");
     for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, __shfl_xor(kmax, m));
     kmax = __builtin_amdgcn_readfirstlane(kmax);
     const int64_t kext = kmax < width ? kmax : width;
@@ -396,10 +409,13 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Pages per wavefront: enough work to stream through the ring, with about one round of
-// eight wavefronts per compute unit over the whole (request x block) space (multiple of 4).
+// Pages per wavefront: enough work to stream through the ring, with about one wavefront per
+// SIMD (four per compute unit) over the whole (request x block) space (multiple of 4). Fewer,
+// longer wavefronts measured faster than two or more per SIMD: each wavefront's start (row
+// bounds, query operands, first pages) and histogram flush is paid fewer times, and one
+// wavefront's loads in flight already cover the memory latency.
 int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
-    const int64_t target_waves = (int64_t)device_cus() * 8;
+    const int64_t target_waves = (int64_t)device_cus() * 4;
     int64_t ppw = (num_requests * max_blocks + target_waves - 1) / target_waves;
     ppw = (ppw + 3) / 4 * 4;
     return (int)(ppw < 4 ? 4 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
@@ -418,16 +434,17 @@ template <int FMT, int H, int RG, bool HIST>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
-    // page buffers per wavefront: 4 for MXFP4 with up to 2 rows per group, else 2 (FP8 pages
-    // and 4-row query groups take the registers a deeper ring would need)
-    constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 4 : 2;
+    // page buffers per wavefront: 3 for MXFP4 with up to 2 rows per group (measured best of
+    // 2-6 on the long-context workload), else 2 (FP8 pages and 4-row query groups take the
+    // registers a deeper ring would need)
+    constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 3 : 2;
     hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST>), grid, block, 0, stream,
-                       static_cast<const uint8_t *>(a.q), a.q_row_stride,
-                       static_cast<const uint16_t *>(a.w), a.w_row_stride,
-                       static_cast<const uint8_t *>(a.cache), a.num_pages, a.page_stride,
-                       a.block_table, a.max_blocks, geo.chunks, geo.pages_per_wave,
-                       a.query_starts, a.row_ends, a.num_rows, a.max_query_len, a.logits,
-                       a.logits_row_stride, ws.seghist, ws.coarse);
+                       a.block_table, a.query_starts, a.max_blocks, geo.chunks,
+                       geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,
+                       a.num_pages, static_cast<const uint8_t *>(a.q), a.q_row_stride,
+                       static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
+                       a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
+                       ws.coarse);
     return hipGetLastError();
 }
 

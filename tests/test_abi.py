@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import sparse_attention_indexer_quant_amd as dsa
 
@@ -36,7 +37,7 @@ def test_header_declares_the_entry_points():
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
-              "dsaidx_dcp_merge", "dsaidx_index_inputs_layout"):
+              "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys"):
         assert n in names
 
 
@@ -233,6 +234,15 @@ def test_score_paged_hist_checks(lib):
     # more than 1024 scoring workgroups per row (> 4M keys) is refused
     assert lib.dsaidx_score_topk_workspace_bytes(1, 70000, 1) == 0
     assert score_hist(lib, r=1, mb=70000, ls=70000 * 64) == EUNSUP
+    # segment = one scoring workgroup: 4 wavefronts x pages per wavefront x 64 keys, pages per
+    # wavefront a multiple of 4 in [4, 16] sized for one wavefront per SIMD (256 compute units
+    # assumed where no GPU is visible)
+    lib.dsaidx_score_segment_keys.restype = ctypes.c_int64
+    assert lib.dsaidx_score_segment_keys(0, 4) == 0
+    assert lib.dsaidx_score_segment_keys(2, 4) == 4 * 4 * 64
+    if not torch.cuda.is_available():
+        assert lib.dsaidx_score_segment_keys(8, 2048) == 4 * 16 * 64
+        assert lib.dsaidx_score_segment_keys(16, 128) == 4 * 4 * 64
 
 
 def topk_scored(lib, **kw):
