@@ -112,6 +112,13 @@ __device__ __forceinline__ void hoist_args(const T &...v) {
     (hoist_arg(v), ...);
 }
 
+// A use of a loaded value that emits nothing. The compiler moves a load down into the one
+// branch that uses its value, which would put a load issued early on purpose behind the
+// checks it is meant to overlap; a use on the other branch as well keeps it where it is
+// written. The use waits for the load, so it belongs on a branch that does nothing else
+// (an early return).
+__device__ __forceinline__ void keep_loaded(uint32_t v) { asm volatile("" ::"v"(v)); }
+
 // Order-preserving 32-bit key of a logit for the top-k selection: unsigned comparison of
 // keys is the float order, with -0 mapped to +0 so the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

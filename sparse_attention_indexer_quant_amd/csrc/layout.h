@@ -23,7 +23,10 @@ struct LayoutArgs {
     int32_t *row_ends;
 };
 
-// Run by all NT lanes of one workgroup.
+// Run by all NT lanes of one workgroup. Lane i of each block of NT requests scans the query
+// lengths and then writes its own request's rows (query lengths are small: decode and verify
+// rows); the rows past the last request are padding. Each request's length and sequence
+// length are loaded together, so the whole layout costs one round trip per NT requests.
 template <int NT>
 __device__ __forceinline__ void decode_layout_body(const LayoutArgs &a) {
     __shared__ int partials[NT / 64];
@@ -38,40 +41,33 @@ __device__ __forceinline__ void decode_layout_body(const LayoutArgs &a) {
     for (int64_t base = 0; base < R; base += NT) {
         const int64_t i = base + tid;
         const int v = i < R ? a.query_lens[i] : 0;
+        const int seq = i < R ? a.seq_lens[i] : 0;
         const int incl = scan_block<NT>(v, partials);
         const int c = carry;
-        if (i < R) a.starts[i + 1] = c + incl;
+        if (i < R) {
+            a.starts[i + 1] = c + incl;
+            const int64_t start = (int64_t)c + incl - v;
+            // row start + r of this request: end = max(0, seq - qlen + r + 1)
+            for (int r = 0; r < v && start + r < a.num_rows; ++r) {
+                int64_t end = (int64_t)seq - v + r + 1;
+                if (end < 0) end = 0;
+                if (a.dcp_world > 1) {
+                    const int64_t il = a.interleave;
+                    const int64_t full = end / (a.dcp_world * il) * il;
+                    int64_t local = end - full * a.dcp_world - (int64_t)a.dcp_rank * il;
+                    local = local < 0 ? 0 : (local > il ? il : local);
+                    end = full + local;
+                }
+                a.row_ends[start + r] = (int32_t)end;
+            }
+        }
         __syncthreads();
         if (tid == NT - 1) carry = c + incl;
         __syncthreads();
     }
-    const int64_t total = carry;  // query_starts[R]
-    __threadfence_block();
-    __syncthreads();
-    for (int64_t row = tid; row < a.num_rows; row += NT) {
-        if (R == 0 || row >= total) {
-            a.row_ends[row] = 0;
-            continue;
-        }
-        // first request index j with starts[j + 1] > row
-        int64_t lo = 0, hi = R;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (a.starts[mid + 1] <= row) lo = mid + 1;
-            else hi = mid;
-        }
-        const int64_t req = lo < R - 1 ? lo : R - 1;
-        int64_t end = (int64_t)a.seq_lens[req] - a.query_lens[req] + row - a.starts[req] + 1;
-        if (end < 0) end = 0;
-        if (a.dcp_world > 1) {
-            const int64_t il = a.interleave;
-            const int64_t full = end / (a.dcp_world * il) * il;
-            int64_t local = end - full * a.dcp_world - (int64_t)a.dcp_rank * il;
-            local = local < 0 ? 0 : (local > il ? il : local);
-            end = full + local;
-        }
-        a.row_ends[row] = (int32_t)end;
-    }
+    const int64_t total = carry;  // query_starts[R]: rows from here on are graph padding
+    for (int64_t row = (total > 0 ? total : 0) + tid; row < a.num_rows; row += NT)
+        a.row_ends[row] = 0;
 }
 
 }  // namespace dsaidx

@@ -20,34 +20,47 @@
 
 namespace dsaidx {
 
-// One query row on a workgroup of 256 lanes (4 wavefronts). Lane t owns 8 consecutive
-// columns (one 16-byte load) of head (t / 16) + 16 * pass: 16 lanes per head, 4 lanes per
-// 32-value MX block. `wv_row` (raw head weights, unit head stride) may be null.
-template <int FMT>
-__device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ q_row, int heads,
-                                                   int64_t q_head_stride,
-                                                   const uint16_t *__restrict__ wv_row,
+// One query row of H heads (16, 32 or 64) on a workgroup of 256 lanes (4 wavefronts). Lane t
+// owns 8 consecutive columns (one 16-byte load) of head (t / 16) + 16 * pass: 16 lanes per
+// head, 4 lanes per 32-value MX block, every lane busy in each of the H / 16 passes.
+// The row's loads are one step and its quantization another, so a kernel can issue other
+// loads in between.
+template <int H>
+struct QueryLoads {
+    static constexpr int kPasses = H / 16;
+    uint4 raws[kPasses];
+    uint32_t wraw[kPasses];  // 32-bit: 16-bit lanes would be packed in pairs, which waits for the loads
+
+    // Every pass's 16-byte load is issued before any is used, with no branch around them: the
+    // row costs one memory round trip (the head weights, raw with unit head stride, likewise).
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ q_row, int64_t q_head_stride,
+                                         int tid) {
+        const int part = tid & 15;
+#pragma unroll
+        for (int pass = 0; pass < kPasses; ++pass) {
+            const int head = (tid >> 4) + 16 * pass;
+            raws[pass] = *reinterpret_cast<const uint4 *>(q_row + (int64_t)head * q_head_stride + part * 8);
+        }
+    }
+    __device__ __forceinline__ void load_weights(const uint16_t *__restrict__ wv_row, int tid) {
+#pragma unroll
+        for (int pass = 0; pass < kPasses; ++pass)
+            wraw[pass] = (uint32_t)wv_row[(tid >> 4) + 16 * pass];
+    }
+};
+
+template <int FMT, int H>
+__device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool has_w,
                                                    uint8_t *__restrict__ out_row,
                                                    uint16_t *__restrict__ w_out_row, float c_h,
                                                    int tid) {
+    constexpr int heads = H, kPasses = H / 16;
     const int part = tid & 15;
-    // every pass's 16-byte load (and head weight) is issued before any is used, so the row
-    // costs one memory round trip instead of one per pass (heads <= 64: at most 4 passes)
-    constexpr int kMaxPasses = 4;
-    uint4 raws[kMaxPasses];
-    uint16_t wraw[kMaxPasses];
+    const uint32_t *wraw = in.wraw;
+    const uint4 *raws = in.raws;
 #pragma unroll
-    for (int pass = 0; pass < kMaxPasses; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
         const int head = (tid >> 4) + 16 * pass;
-        if (head < heads) {
-            raws[pass] = *reinterpret_cast<const uint4 *>(q_row + (int64_t)head * q_head_stride + part * 8);
-            wraw[pass] = wv_row && part == 0 ? wv_row[head] : (uint16_t)0;
-        }
-    }
-#pragma unroll
-    for (int pass = 0; pass < kMaxPasses; ++pass) {
-        const int head = (tid >> 4) + 16 * pass;
-        if (head >= heads) continue;
         const uint4 raw = raws[pass];
         float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
@@ -69,8 +82,8 @@ __device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ 
             if (part == 0) {
                 *reinterpret_cast<uint32_t *>(out_row + heads * 64 + head * 4) =
                     byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-                if (wv_row) {
-                    const float w = bf16_val(wraw[pass]);
+                if (has_w) {
+                    const float w = bf16_val((uint16_t)wraw[pass]);
                     w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(w, c_h));
                 }
             }
@@ -88,8 +101,8 @@ __device__ __forceinline__ void quantize_query_row(const uint16_t *__restrict__ 
                 hi |= e4m3_code(__fmul_rn(v[4 + i], inv)) << (8 * i);
             }
             *reinterpret_cast<uint2 *>(out_row + head * 128 + part * 8) = make_uint2(lo, hi);
-            if (part == 0 && wv_row) {
-                const float w = bf16_val(wraw[pass]);
+            if (part == 0 && has_w) {
+                const float w = bf16_val((uint16_t)wraw[pass]);
                 w_out_row[head] = (uint16_t)bf16_bits_rne(__fmul_rn(__fmul_rn(w, s), c_h));
             }
         }
@@ -173,24 +186,29 @@ __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
     }
 }
 
+// The kernels list first the arguments their first loads need: the library is built to
+// preload the leading kernel arguments into scalar registers at wave launch.
+
 // One workgroup per query row.
-template <int FMT>
+template <int FMT, int H>
 __global__ __launch_bounds__(256) void quantize_queries_kernel(
-    const uint16_t *__restrict__ q, int heads, int64_t q_row_stride, int64_t q_head_stride,
+    const uint16_t *__restrict__ q, int64_t q_row_stride, int64_t q_head_stride,
     const uint16_t *__restrict__ wv, int64_t wv_row_stride, uint8_t *__restrict__ q_out,
     int64_t q_out_row_stride, uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h) {
     const int64_t row = blockIdx.x;
-    quantize_query_row<FMT>(q + row * q_row_stride, heads, q_head_stride,
-                            wv ? wv + row * wv_row_stride : nullptr, q_out + row * q_out_row_stride,
-                            w_out ? w_out + row * w_out_row_stride : nullptr, c_h, threadIdx.x);
+    QueryLoads<H> in;
+    in.load(q + row * q_row_stride, q_head_stride, threadIdx.x);
+    if (wv) in.load_weights(wv + row * wv_row_stride, threadIdx.x);
+    quantize_query_row<FMT, H>(in, wv != nullptr, q_out + row * q_out_row_stride,
+                               w_out ? w_out + row * w_out_row_stride : nullptr, c_h, threadIdx.x);
 }
 
 // One wavefront per key, four keys per workgroup.
 template <int FMT>
 __global__ __launch_bounds__(256) void store_keys_kernel(
-    const uint16_t *__restrict__ keys, int64_t tokens, int64_t k_row_stride,
-    const float *__restrict__ gamma, const float *__restrict__ beta, float eps,
-    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
+    const uint16_t *__restrict__ keys, int64_t k_row_stride, int64_t tokens,
+    const float *__restrict__ gamma, const float *__restrict__ beta,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, float eps, int64_t num_pages,
     int64_t page_stride) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= tokens) return;
@@ -204,30 +222,64 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
 // per token quantizes the token's query with the head weights read from the packed projection
 // row, and its last wavefront then normalizes, quantizes and inserts the key held in the same
 // row (at H = 16, 32, 64 every wavefront quantizes the same number of heads). With a layout,
-// one more workgroup computes the row bounds (decode_layout) in the same launch.
-template <int FMT>
+// one more workgroup computes the row bounds (decode_layout) in the same launch. `w_in` and
+// `key_in` point at the weight and key columns of projection row 0.
+template <int FMT, int H>
 __global__ __launch_bounds__(256) void index_inputs_kernel(
-    const uint16_t *__restrict__ projected, int64_t proj_row_stride, int64_t key_col,
-    int64_t weight_col, const uint16_t *__restrict__ q, int heads, int64_t q_row_stride,
-    int64_t q_head_stride, const float *__restrict__ gamma, const float *__restrict__ beta,
-    float eps, const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
-    int64_t page_stride, uint8_t *__restrict__ q_out, int64_t q_out_row_stride,
-    uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h, int64_t tokens,
-    LayoutArgs layout) {
+    int64_t tokens, const uint16_t *__restrict__ q, int64_t q_row_stride, int64_t q_head_stride,
+    const uint16_t *__restrict__ w_in, int64_t proj_row_stride,
+    const uint16_t *__restrict__ key_in, uint8_t *__restrict__ q_out, int64_t q_out_row_stride,
+    uint16_t *__restrict__ w_out, int64_t w_out_row_stride, float c_h,
+    const float *__restrict__ gamma, const float *__restrict__ beta, float eps,
+    const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, int64_t num_pages,
+    int64_t page_stride, LayoutArgs layout) {
     const int64_t token = blockIdx.x;
     if (token == tokens) {  // the extra workgroup of the combined call: the row bounds
         decode_layout_body<256>(layout);
         return;
     }
-    const uint16_t *prow = projected + token * proj_row_stride;
+    // Issue order: the query row and its weights (every operand a preloaded argument), every
+    // other argument in one batch, then the key (its last wavefront).
+    QueryLoads<H> in;
+    in.load(q + token * q_row_stride, q_head_stride, threadIdx.x);
+    in.load_weights(w_in + token * proj_row_stride, threadIdx.x);
+    hoist_args(q_out, q_out_row_stride, w_out, w_out_row_stride, c_h, gamma, beta, eps, slots,
+               cache, num_pages, page_stride);
     const int lane = threadIdx.x & 63;
     const bool key_wave = (threadIdx.x >> 6) == 3;
     KeyLane key{};
-    if (key_wave) key = load_key(prow + key_col, gamma, beta, slots + token, lane);  // in flight
-    quantize_query_row<FMT>(q + token * q_row_stride, heads, q_head_stride, prow + weight_col,
-                            q_out + token * q_out_row_stride, w_out + token * w_out_row_stride, c_h,
-                            threadIdx.x);
+    if (key_wave) key = load_key(key_in + token * proj_row_stride, gamma, beta, slots + token, lane);
+    quantize_query_row<FMT, H>(in, true, q_out + token * q_out_row_stride,
+                               w_out + token * w_out_row_stride, c_h, threadIdx.x);
     if (key_wave) store_key<FMT>(key, eps, cache, num_pages, page_stride, lane);
+}
+
+template <int FMT, int H>
+static void launch_quantize_h(dim3 grid, hipStream_t stream, const uint16_t *q,
+                              int64_t q_row_stride, int64_t q_head_stride, const uint16_t *wv,
+                              int64_t wv_row_stride, uint8_t *q_out, int64_t q_out_row_stride,
+                              uint16_t *w_out, int64_t w_out_row_stride, float c_h) {
+    hipLaunchKernelGGL((quantize_queries_kernel<FMT, H>), grid, dim3(256), 0, stream, q,
+                       q_row_stride, q_head_stride, wv, wv_row_stride, q_out, q_out_row_stride,
+                       w_out, w_out_row_stride, c_h);
+}
+
+template <int FMT>
+static void launch_quantize_fmt(int heads, dim3 grid, hipStream_t stream, const uint16_t *q,
+                                int64_t q_row_stride, int64_t q_head_stride, const uint16_t *wv,
+                                int64_t wv_row_stride, uint8_t *q_out, int64_t q_out_row_stride,
+                                uint16_t *w_out, int64_t w_out_row_stride, float c_h) {
+    switch (heads) {
+        case 16: return launch_quantize_h<FMT, 16>(grid, stream, q, q_row_stride, q_head_stride, wv,
+                                                   wv_row_stride, q_out, q_out_row_stride, w_out,
+                                                   w_out_row_stride, c_h);
+        case 32: return launch_quantize_h<FMT, 32>(grid, stream, q, q_row_stride, q_head_stride, wv,
+                                                   wv_row_stride, q_out, q_out_row_stride, w_out,
+                                                   w_out_row_stride, c_h);
+        default: return launch_quantize_h<FMT, 64>(grid, stream, q, q_row_stride, q_head_stride, wv,
+                                                   wv_row_stride, q_out, q_out_row_stride, w_out,
+                                                   w_out_row_stride, c_h);
+    }
 }
 
 hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int heads,
@@ -235,20 +287,20 @@ hipError_t launch_quantize_queries(int fmt, const void *q, int64_t rows, int hea
                                    int64_t wv_row_stride, void *q_out, int64_t q_out_row_stride,
                                    void *w_out, int64_t w_out_row_stride, float c_h,
                                    hipStream_t stream) {
-    const dim3 grid((unsigned)rows), block(256);
+    const dim3 grid((unsigned)rows);
     auto *qq = static_cast<const uint16_t *>(q);
     auto *ww = static_cast<const uint16_t *>(wv);
     auto *qo = static_cast<uint8_t *>(q_out);
     auto *wo = static_cast<uint16_t *>(w_out);
     // the FP8 query is the same for both FP8 key layouts
     if (fmt == kFmtMxfp4)
-        hipLaunchKernelGGL(quantize_queries_kernel<kFmtMxfp4>, grid, block, 0, stream, qq, heads,
-                           q_row_stride, q_head_stride, ww, wv_row_stride, qo, q_out_row_stride,
-                           wo, w_out_row_stride, c_h);
+        launch_quantize_fmt<kFmtMxfp4>(heads, grid, stream, qq, q_row_stride, q_head_stride, ww,
+                                       wv_row_stride, qo, q_out_row_stride, wo, w_out_row_stride,
+                                       c_h);
     else
-        hipLaunchKernelGGL(quantize_queries_kernel<kFmtFp8>, grid, block, 0, stream, qq, heads,
-                           q_row_stride, q_head_stride, ww, wv_row_stride, qo, q_out_row_stride,
-                           wo, w_out_row_stride, c_h);
+        launch_quantize_fmt<kFmtFp8>(heads, grid, stream, qq, q_row_stride, q_head_stride, ww,
+                                     wv_row_stride, qo, q_out_row_stride, wo, w_out_row_stride,
+                                     c_h);
     return hipGetLastError();
 }
 
@@ -260,15 +312,53 @@ hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t 
     auto *kk = static_cast<const uint16_t *>(keys);
     auto *cc = static_cast<uint8_t *>(cache);
     if (fmt == kFmtMxfp4)
-        hipLaunchKernelGGL(store_keys_kernel<kFmtMxfp4>, grid, block, 0, stream, kk, tokens,
-                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+        hipLaunchKernelGGL(store_keys_kernel<kFmtMxfp4>, grid, block, 0, stream, kk, k_row_stride,
+                           tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
     else if (fmt == kFmtFp8)
-        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8>, grid, block, 0, stream, kk, tokens,
-                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8>, grid, block, 0, stream, kk, k_row_stride,
+                           tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
     else
-        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8Mx>, grid, block, 0, stream, kk, tokens,
-                           k_row_stride, gamma, beta, eps, slots, cc, num_pages, page_stride);
+        hipLaunchKernelGGL(store_keys_kernel<kFmtFp8Mx>, grid, block, 0, stream, kk, k_row_stride,
+                           tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
     return hipGetLastError();
+}
+
+struct IndexInputs {
+    int64_t tokens;
+    const uint16_t *q;
+    int64_t q_row_stride, q_head_stride;
+    const uint16_t *w_in;
+    int64_t proj_row_stride;
+    const uint16_t *key_in;
+    uint8_t *q_out;
+    int64_t q_out_row_stride;
+    uint16_t *w_out;
+    int64_t w_out_row_stride;
+    float c_h;
+    const float *gamma, *beta;
+    float eps;
+    const int64_t *slots;
+    uint8_t *cache;
+    int64_t num_pages, page_stride;
+    LayoutArgs layout;
+};
+
+template <int FMT, int H>
+static void launch_index_inputs_h(const IndexInputs &a, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((index_inputs_kernel<FMT, H>), grid, dim3(256), 0, stream, a.tokens, a.q,
+                       a.q_row_stride, a.q_head_stride, a.w_in, a.proj_row_stride, a.key_in,
+                       a.q_out, a.q_out_row_stride, a.w_out, a.w_out_row_stride, a.c_h, a.gamma,
+                       a.beta, a.eps, a.slots, a.cache, a.num_pages, a.page_stride, a.layout);
+}
+
+template <int FMT>
+static void launch_index_inputs_fmt(int heads, const IndexInputs &a, dim3 grid,
+                                    hipStream_t stream) {
+    switch (heads) {
+        case 16: return launch_index_inputs_h<FMT, 16>(a, grid, stream);
+        case 32: return launch_index_inputs_h<FMT, 32>(a, grid, stream);
+        default: return launch_index_inputs_h<FMT, 64>(a, grid, stream);
+    }
 }
 
 hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
@@ -279,28 +369,17 @@ hipError_t launch_index_inputs(int fmt, const void *projected, int64_t tokens,
                                int64_t page_stride, void *q_out, int64_t q_out_row_stride,
                                void *w_out, int64_t w_out_row_stride, float c_h,
                                const LayoutArgs *layout, hipStream_t stream) {
-    const dim3 grid((unsigned)(tokens + (layout ? 1 : 0))), block(256);
+    const dim3 grid((unsigned)(tokens + (layout ? 1 : 0)));
     auto *pp = static_cast<const uint16_t *>(projected);
-    auto *qq = static_cast<const uint16_t *>(q);
-    auto *cc = static_cast<uint8_t *>(cache);
-    auto *qo = static_cast<uint8_t *>(q_out);
-    auto *wo = static_cast<uint16_t *>(w_out);
-    const LayoutArgs la = layout ? *layout : LayoutArgs{};
-    if (fmt == kFmtMxfp4)
-        hipLaunchKernelGGL(index_inputs_kernel<kFmtMxfp4>, grid, block, 0, stream, pp,
-                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
-                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
-    else if (fmt == kFmtFp8)
-        hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8>, grid, block, 0, stream, pp,
-                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
-                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
-    else
-        hipLaunchKernelGGL(index_inputs_kernel<kFmtFp8Mx>, grid, block, 0, stream, pp,
-                           proj_row_stride, key_col, weight_col, qq, heads, q_row_stride,
-                           q_head_stride, gamma, beta, eps, slots, cc, num_pages, page_stride, qo,
-                           q_out_row_stride, wo, w_out_row_stride, c_h, tokens, la);
+    const IndexInputs a{tokens, static_cast<const uint16_t *>(q), q_row_stride, q_head_stride,
+                        pp + weight_col, proj_row_stride, pp + key_col,
+                        static_cast<uint8_t *>(q_out), q_out_row_stride,
+                        static_cast<uint16_t *>(w_out), w_out_row_stride, c_h, gamma, beta, eps,
+                        slots, static_cast<uint8_t *>(cache), num_pages, page_stride,
+                        layout ? *layout : LayoutArgs{}};
+    if (fmt == kFmtMxfp4) launch_index_inputs_fmt<kFmtMxfp4>(heads, a, grid, stream);
+    else if (fmt == kFmtFp8) launch_index_inputs_fmt<kFmtFp8>(heads, a, grid, stream);
+    else launch_index_inputs_fmt<kFmtFp8Mx>(heads, a, grid, stream);
     return hipGetLastError();
 }
 

@@ -201,13 +201,33 @@ struct RowGroup {
         }
     }
 
-    // Logits of one page for the group's rows (rows past `count` are skipped). Each tile's
-    // RG x HT contractions are issued back to back into separate results before any is read,
-    // so the matrix unit pipelines them instead of waiting on each result in turn.
+    // Logits of one page for the group's rows. Rows past `count` are not computed: row 0, then
+    // row 1 if present, then rows 2..RG-1 if any is present (one uniform branch each).
     __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
                                           float *logits, int64_t first_row,
                                           int64_t logits_row_stride, int lane, int grp,
                                           uint32_t *hist) const {
+        score_rows<0, 1>(pg, kbase, count, logits, first_row, logits_row_stride, lane, grp, hist);
+        if constexpr (RG > 1) {
+            if (count > 1)
+                score_rows<1, 2>(pg, kbase, count, logits, first_row, logits_row_stride, lane,
+                                 grp, hist);
+        }
+        if constexpr (RG > 2) {
+            if (count > 2)
+                score_rows<2, RG>(pg, kbase, count, logits, first_row, logits_row_stride, lane,
+                                  grp, hist);
+        }
+    }
+
+    // Rows [J0, J1) of the group. Each tile's (J1 - J0) x HT contractions are issued back to
+    // back into separate results before any is read, so the matrix unit pipelines them instead
+    // of waiting on each result in turn.
+    template <int J0, int J1>
+    __device__ __forceinline__ void score_rows(const PageRegs<FMT> &pg, int kbase, int count,
+                                               float *logits, int64_t first_row,
+                                               int64_t logits_row_stride, int lane, int grp,
+                                               uint32_t *hist) const {
         float part[RG][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -215,7 +235,7 @@ struct RowGroup {
             if constexpr (is_fp8(FMT)) e4m3x32_to_bf16(pg.kp[t][0], pg.kp[t][1], kb);
             v4f c[RG][HT];
 #pragma unroll
-            for (int j = 0; j < RG; ++j) {
+            for (int j = J0; j < J1; ++j) {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
                     if constexpr (FMT == kFmtMxfp4)
@@ -225,7 +245,7 @@ struct RowGroup {
                 }
             }
 #pragma unroll
-            for (int j = 0; j < RG; ++j) {
+            for (int j = J0; j < J1; ++j) {
                 float acc = 0.f;
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) acc = relu_dot4(c[j][ht], wt[j][ht], acc);
@@ -236,7 +256,7 @@ struct RowGroup {
             }
         }
 #pragma unroll
-        for (int j = 0; j < RG; ++j) {
+        for (int j = J0; j < J1; ++j) {
             if (j >= count || kbase >= rend[j]) continue;
             const float out = head_sum_to_token(part[j][0], part[j][1], part[j][2], part[j][3]);
             float *row = logits + (first_row + j) * logits_row_stride + kbase;
@@ -251,22 +271,23 @@ struct RowGroup {
     }
 };
 
-// Grid: requests x chunks; a workgroup's 4 wavefronts take consecutive runs of PW pages of
-// the request. Each wavefront streams its run through a ring of NB page buffers: the next
-// NB - 1 pages' loads are in flight while one page is scored. Every prefetch is issued
-// unconditionally (a page that is not scored reads page 0 instead), so the loop carries the
-// same loads across its back edge on every path and the hardware wait counts stay exact;
-// conditional prefetches made the compiler wait for all loads there. The first NB - 1 loads
-// go out as soon as the block table slice arrives, while the row bounds are still in flight.
-// The arguments the first loads need come first: the library is built to preload the leading
+// Grid: requests x chunks; a workgroup's chunk is 4 PW consecutive pages of the request, which
+// its 4 wavefronts take in turn (PW pages each). Each wavefront streams its pages through a
+// ring of NB page buffers: the next NB - 1 pages' loads are in flight while one page is
+// scored. Every prefetch is issued unconditionally (a page that is not scored reads page 0
+// instead), so the loop carries the same loads across its back edge on every path and the
+// hardware wait counts stay exact; conditional prefetches made the compiler wait for all loads
+// there. The first NB - 1 page loads go out right after the query and row-bound loads. The
+// arguments the first loads need come first: the library is built to preload the leading
 // kernel arguments into scalar registers at wave launch.
 template <int FMT, int H, int RG, int NB, bool HIST>
 __global__ __launch_bounds__(256) void score_paged_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
-    int64_t max_blocks, int64_t chunks, int pages_per_wave, const uint8_t *__restrict__ cache,
-    int64_t page_stride, int64_t num_pages, const uint8_t *__restrict__ q, int64_t q_row_stride,
-    const uint16_t *__restrict__ w, int64_t w_row_stride, const int32_t *__restrict__ row_ends,
-    int64_t num_rows, int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
+    int64_t max_blocks, int64_t num_requests, int pages_per_wave,
+    const uint8_t *__restrict__ cache, int64_t page_stride, int64_t num_pages, int64_t chunks,
+    const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
+    int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
+    int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
     uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse) {
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
@@ -276,23 +297,30 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
-    // the grid has requests x chunks < 2^31 workgroups: 32-bit division
-    const uint32_t req32 = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)chunks);
-    const int64_t req = req32;
-    const int64_t chunk = blockIdx.x - req32 * (uint32_t)chunks;
+    // Workgroup b takes chunk b / R of request b % R (R requests; fewer than 2^31 workgroups,
+    // so 32-bit division). Workgroups go to the XCDs in turn by index, so with the request
+    // varying fastest every XCD gets every chunk position of its share of the requests: the
+    // early chunks, which every request fills, no longer all land on the same XCDs.
+    const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)num_requests);
+    const int64_t chunk = chunk32;
+    const int64_t req = blockIdx.x - chunk32 * (uint32_t)num_requests;
     const int64_t width = max_blocks * kPageTokens;
     const int PW = pages_per_wave;
-    const int64_t blk_begin = (chunk * kWaves + wave) * (int64_t)PW;
-    if (!HIST && blk_begin >= max_blocks) return;
+    // The workgroup's chunk is blocks [chunk_begin, chunk_begin + 4 PW); its wavefronts take
+    // them in turn (wavefront w: blocks chunk_begin + w + 4 p), so a chunk that the request's
+    // keys only partly fill still gives its four wavefronts equal work.
+    const int64_t chunk_begin = chunk * kWaves * (int64_t)PW;
+    const int64_t blk_first = chunk_begin + wave;
+    auto block_of = [&](int p) -> int64_t { return blk_first + (int64_t)kWaves * p; };
     // At wave launch (every operand is a preloaded argument): the request's rows (scalar loads;
     // nothing before them in the kernel writes memory) and this wavefront's slice of the block
     // table (one entry per lane; every entry below max_blocks is in bounds). Then every other
     // argument at once, in the same round trip.
     int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
     const int32_t *bt = block_table + req * max_blocks;
-    const int bt_lane = lane < PW && blk_begin + lane < max_blocks ? bt[blk_begin + lane] : -1;
-    hoist_args(num_pages, q, q_row_stride, w, w_row_stride, row_ends, num_rows, max_query_len,
-               logits, logits_row_stride, seghist, coarse);
+    const int bt_lane = lane < PW && block_of(lane) < max_blocks ? bt[block_of(lane)] : -1;
+    hoist_args(num_pages, chunks, q, q_row_stride, w, w_row_stride, row_ends, num_rows,
+               max_query_len, logits, logits_row_stride, seghist, coarse);
 
     // Table entry of run page p (uniform), or -1 if it names no page of the cache.
     const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
@@ -333,9 +361,13 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     kmax = __builtin_amdgcn_readfirstlane(kmax);
     const int64_t kext = kmax < width ? kmax : width;
     const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
-    const int64_t blk_end = blk_begin + PW < nblk ? blk_begin + PW : nblk;
-    if (!HIST && blk_begin >= blk_end) return;
-    const int run = blk_begin < blk_end ? (int)(blk_end - blk_begin) : 0;
+    // a chunk past the request's keys has nothing to score and no histogram to write (the
+    // selection reads only segments that hold keys of the row): the whole workgroup leaves
+    if (chunk_begin >= nblk) return;
+    const int64_t chunk_end = chunk_begin + kWaves * (int64_t)PW < nblk
+                                  ? chunk_begin + kWaves * (int64_t)PW : nblk;
+    // pages of this wavefront below chunk_end
+    const int run = blk_first < chunk_end ? (int)((chunk_end - blk_first + kWaves - 1) / kWaves) : 0;
 
     // Requests with more rows than one register group stream their pages once per group
     // (the second and later passes mostly hit the L2).
@@ -362,7 +394,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 const int p = base + slot;
                 load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
                 if (p < run && table_page(p) >= 0)
-                    rows.score(buf[slot], (int)((blk_begin + p) * kPageTokens), count, logits,
+                    rows.score(buf[slot], (int)(block_of(p) * kPageTokens), count, logits,
                                first, logits_row_stride, lane, grp, HIST ? hist : nullptr);
             }
         }
@@ -370,7 +402,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
             // (row, segment = chunk) histograms of the rows whose keys reach this chunk; the
             // packed 16-bit counts are already the workspace's layout
             __syncthreads();
-            const int64_t seg_begin = chunk * kWaves * (int64_t)PW * kPageTokens;
+            const int64_t seg_begin = chunk_begin * kPageTokens;
 #pragma unroll
             for (int j = 0; j < RG; ++j) {  // unrolled: a runtime index would put `rows` in scratch
                 if (j >= count || seg_begin >= rows.rend[j]) continue;
@@ -439,9 +471,9 @@ static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, h
     // registers a deeper ring would need)
     constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 3 : 2;
     hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST>), grid, block, 0, stream,
-                       a.block_table, a.query_starts, a.max_blocks, geo.chunks,
+                       a.block_table, a.query_starts, a.max_blocks, a.num_requests,
                        geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,
-                       a.num_pages, static_cast<const uint8_t *>(a.q), a.q_row_stride,
+                       a.num_pages, geo.chunks, static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
                        ws.coarse);

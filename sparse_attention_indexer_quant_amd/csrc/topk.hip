@@ -10,7 +10,7 @@
 // needs a device-scope fence per workgroup, an L2 write-back on every XCD, and atomics on a
 // row's shared counters serialize; both measured slower than the selection itself):
 //
-//   1. topk_hist (rows x segments): each workgroup histograms the top 12 key bits of its
+//   1. topk_hist (segments x rows): each workgroup histograms the top 12 key bits of its
 //      segment in LDS and stores the counts (16-bit) in the workspace. (The scorer can write
 //      these histograms itself, segment = one scoring workgroup's keys; then the selection
 //      starts at step 2.)
@@ -19,7 +19,7 @@
 //      k-th largest key, then counts each segment's keys above b and inside b and stores
 //      their exclusive prefix sums over the segments: every segment's first output slot and
 //      first candidate slot.
-//   3. topk_collect (rows x segments): writes the positions of keys above bin b to the
+//   3. topk_collect (segments x rows): writes the positions of keys above bin b to the
 //      output and the (key, position) pairs of keys inside bin b to the row's candidate
 //      list, at the offsets from step 2 plus an in-workgroup prefix sum -- no atomics, and
 //      the positions above b come out in ascending order.
@@ -65,6 +65,18 @@ __device__ __forceinline__ int64_t row_bound(const int32_t *row_ends, int64_t ro
     return n < 0 ? 0 : (n > width ? width : n);
 }
 
+// Row and segment of this workgroup in a rows x nseg grid: workgroup b takes segment b / rows
+// of row b % rows (fewer than 2^31 workgroups: 32-bit division, made explicitly uniform so
+// the row arithmetic stays scalar). Workgroups go to the XCDs in turn by index; with the row
+// varying fastest the leading segments, which every row fills, spread over all of them.
+struct RowSeg {
+    int64_t row, seg;
+};
+__device__ __forceinline__ RowSeg row_segment(int64_t rows) {
+    const uint32_t sg = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)rows);
+    return {(int64_t)(blockIdx.x - sg * (uint32_t)rows), (int64_t)sg};
+}
+
 template <int VEC, typename F>
 __device__ __forceinline__ void for_segment(const float *x, int64_t lo, int64_t hi, F &&fn) {
     if constexpr (VEC == 4) {
@@ -82,14 +94,18 @@ __device__ __forceinline__ void for_segment(const float *x, int64_t lo, int64_t 
     }
 }
 
+// Kernel arguments: the ones the first loads need lead (the library preloads the leading
+// arguments into scalar registers at wave launch); the rest are loaded in one batch.
 template <int VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
-    const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
-    const int32_t *__restrict__ row_ends, int k, TopkWorkspace ws, int64_t nseg,
-    int64_t seg_len) {
+    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int64_t seg_len,
+    int64_t rows, const int32_t *__restrict__ row_ends, int k, int64_t nseg,
+    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse) {
     __shared__ __align__(16) uint32_t hist[kBins];
-    const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const RowSeg rs = row_segment(rows);
+    const int64_t row = rs.row, seg = rs.seg;
     const int64_t n = row_bound(row_ends, row, width);
+    hoist_args(nseg, seghist, coarse);
     if (n <= k) return;   // written by the threshold kernel
     const int64_t lo = seg * seg_len;
     if (lo >= n) return;  // only the segments that hold keys take part below
@@ -114,14 +130,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
         c[2 * v + 1] = q.z | (q.w << 16);
         sum16 += q.x + q.y + q.z + q.w;
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(ws.seghist + (row * nseg + seg) * kBins +
+    uint4 *dst = reinterpret_cast<uint4 *>(seghist + (row * nseg + seg) * kBins +
                                            16 * threadIdx.x);
     dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
     dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
     sum16 += __shfl_xor(sum16, 1);
     sum16 += __shfl_xor(sum16, 2);
     if ((threadIdx.x & 3) == 0)
-        ws.coarse[(row * nseg + seg) * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)sum16;
+        coarse[(row * nseg + seg) * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)sum16;
 }
 
 // One workgroup per row: a row with at most k keys is written whole (all positions, then
@@ -182,8 +198,10 @@ __device__ __forceinline__ void find_in_64(uint32_t c, int k, uint32_t *bin, int
 }
 
 __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
-    const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
-    int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
+    const uint16_t *__restrict__ coarse_hist, const uint16_t *__restrict__ fine_hist,
+    int64_t nseg, const int32_t *__restrict__ row_ends, int64_t width, int k,
+    int32_t *__restrict__ indices, int64_t indices_row_stride, int64_t seg_len,
+    RowState *__restrict__ state, uint2 *__restrict__ segoff) {
     __shared__ uint32_t part[kRowThreads / 64][64];
     __shared__ uint32_t seg_above[kMaxRowSegments], seg_in[kMaxRowSegments];
     __shared__ int partials[kRowThreads / 64];
@@ -194,11 +212,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const int p8 = t & 7, s0 = t >> 3;
     // the coarse word of this lane's first segment, issued before the row bound is known
     // (every segment < nseg lies in the workspace; those past the row's keys are masked below)
-    const uint4 *coarse = reinterpret_cast<const uint4 *>(ws.coarse + row * nseg * kCoarseBins);
-    const uint4 *fine = reinterpret_cast<const uint4 *>(ws.seghist + row * nseg * kBins);
+    const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
+    const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
     uint4 cw0 = s0 < nseg ? coarse[s0 * (kCoarseBins / 8) + p8] : zero4;
     const int64_t n = row_bound(row_ends, row, width);
+    hoist_args(indices_row_stride, seg_len, state, segoff);
     if (n <= k) {
         int32_t *out = indices + row * indices_row_stride;
         for (int i = t; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
@@ -303,10 +322,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const int ia = scan_block<kRowThreads>((int)my_above, partials);
     const int ic = scan_block<kRowThreads>((int)my_in, partials);
     if (t < row_segments)
-        ws.segoff[row * nseg + t] = make_uint2((uint32_t)ia - my_above, (uint32_t)ic - my_in);
+        segoff[row * nseg + t] = make_uint2((uint32_t)ia - my_above, (uint32_t)ic - my_in);
     if (t == 0) {
         const int above = above_c + above_f;
-        RowState &st = ws.state[row];
+        RowState &st = state[row];
         st.bin = bin;
         st.above = above;
         st.remaining = k - above;
@@ -316,43 +335,59 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
 
 template <int VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
-    const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
-    const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
-    int64_t indices_row_stride, TopkWorkspace ws, int64_t nseg, int64_t seg_len) {
+    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int64_t seg_len,
+    int64_t rows, const int32_t *__restrict__ row_ends, const RowState *__restrict__ state,
+    int64_t nseg, const uint2 *__restrict__ segoff, uint2 *__restrict__ cand_all, int k,
+    int32_t *__restrict__ indices, int64_t indices_row_stride) {
     __shared__ int partials[kTopkThreads / 64];
-    const int64_t row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t n = row_bound(row_ends, row, width);
-    if (n <= k) return;
-    const int64_t lo = seg * seg_len;
-    if (lo >= n) return;
-    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
+    const RowSeg rs = row_segment(rows);
+    const int64_t row = rs.row, seg = rs.seg;
     const float *x = logits + row * logits_row_stride;
-    int32_t *out = indices + row * indices_row_stride;
-    const RowState &st = ws.state[row];
-    const uint32_t bin = st.bin, above = (uint32_t)st.above;
-    const uint2 off = ws.segoff[row * nseg + seg];
-    uint2 *cand = ws.cand + row * kCandCap;
+    const int64_t lo = seg * seg_len;
 
     // Chunks of 4096 keys (16 per lane, in registers): lane counts and a workgroup prefix
     // sum place every key after the segment's offsets and the earlier chunks' keys.
     constexpr int kPer = 16, kChunk = kPer * kTopkThreads;
-    uint32_t base_above = off.x, base_in = off.y;
-    for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
-        uint32_t u[kPer];
-        const int64_t first = cbase + (int64_t)threadIdx.x * kPer;
-        if (VEC == 4 && first + kPer <= hi) {
+    float raw[kPer];
+    auto load_chunk = [&](int64_t first, int64_t bound) {
+        if (VEC == 4 && first + kPer <= bound) {
 #pragma unroll
             for (int j = 0; j < kPer; j += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(x + first + j);
-                u[j] = order_key(v.x);
-                u[j + 1] = order_key(v.y);
-                u[j + 2] = order_key(v.z);
-                u[j + 3] = order_key(v.w);
+                raw[j] = v.x;
+                raw[j + 1] = v.y;
+                raw[j + 2] = v.z;
+                raw[j + 3] = v.w;
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) u[j] = first + j < hi ? order_key(x[first + j]) : 0u;
+            for (int j = 0; j < kPer; ++j) raw[j] = first + j < bound ? x[first + j] : 0.f;
         }
+    };
+    // Issued at once, in this order: the row bound and threshold state (scalar loads), the
+    // first chunk of keys -- before either arrives: every key below the row's width is in
+    // bounds and keys past the row bound are masked below -- and the other arguments. The
+    // compiler-only fence keeps the loads above the early returns (it emits nothing).
+    const int64_t n = row_bound(row_ends, row, width);
+    const RowState st = state[row];
+    load_chunk(lo + (int64_t)threadIdx.x * kPer, lo + seg_len < width ? lo + seg_len : width);
+    asm volatile("" ::: "memory");
+    hoist_args(nseg, segoff, cand_all, k, indices, indices_row_stride);
+    if (n <= k) return;
+    if (lo >= n) return;
+    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
+    int32_t *out = indices + row * indices_row_stride;
+    const uint32_t bin = st.bin, above = (uint32_t)st.above;
+    const uint2 off = segoff[row * nseg + seg];
+    uint2 *cand = cand_all + row * kCandCap;
+
+    uint32_t base_above = off.x, base_in = off.y;
+    for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
+        const int64_t first = cbase + (int64_t)threadIdx.x * kPer;
+        if (cbase != lo) load_chunk(first, hi);
+        uint32_t u[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) u[j] = order_key(raw[j]);
         int n_above = 0, n_in = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -408,23 +443,40 @@ struct RowBin {  // every key of the row inside the threshold bin, read from the
 };
 
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
-    const float *__restrict__ logits, int64_t width, int64_t logits_row_stride,
-    const int32_t *__restrict__ row_ends, int k, int32_t *__restrict__ indices,
-    int64_t indices_row_stride, TopkWorkspace ws) {
+    const uint2 *__restrict__ cand_all, const RowState *__restrict__ state,
+    const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
+    int64_t indices_row_stride, const float *__restrict__ logits, int64_t logits_row_stride) {
     __shared__ uint64_t cands[kCandCap];
     __shared__ SelectShared sh;
     const int64_t row = blockIdx.x;
     // the first kSpec candidates, loaded before their count is known (the list always has
     // kCandCap slots; slots past the count are ignored)
+    // Issued at once (the scheduling barrier keeps the bound's arithmetic after every load):
+    // the speculative candidates, the row bound and state (scalar loads) and the other
+    // arguments.
     constexpr int kSpec = 4;
-    const uint2 *cand = ws.cand + row * kCandCap;
+    const uint2 *cand = cand_all + row * kCandCap;
     uint2 pre[kSpec];
 #pragma unroll
     for (int i = 0; i < kSpec; ++i) pre[i] = cand[threadIdx.x + i * kSelectThreads];
-    const int64_t n = row_bound(row_ends, row, width);
-    if (n <= k) return;
+    const RowState st = state[row];
+    const int32_t end = row_ends[row];
+    hoist_args(logits, logits_row_stride);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t n = end < 0 ? 0 : (end > width ? width : end);
+    if (n <= k) {
+#pragma unroll
+        for (int i = 0; i < kSpec; ++i) {
+            keep_loaded(pre[i].x);
+            keep_loaded(pre[i].y);
+        }
+        keep_loaded(st.bin);
+        keep_loaded((uint32_t)st.above);
+        keep_loaded((uint32_t)st.remaining);
+        keep_loaded(st.n_cand);
+        return;
+    }
     const float *x = logits + row * logits_row_stride;
-    const RowState &st = ws.state[row];
     const uint32_t bin = st.bin, ncand = st.n_cand;
     const int remaining = st.remaining;
     if (remaining <= 0 || remaining > k) return;
@@ -463,18 +515,19 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
-                       row_ends, width, k, indices, indices_row_stride, ws, nseg, seg_len);
+                       ws.coarse, ws.seghist, nseg, row_ends, width, k, indices,
+                       indices_row_stride, seg_len, ws.state, ws.segoff);
     if (vec)
-        hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
-                           seg_len);
+        hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits,
+                           logits_row_stride, width, seg_len, rows, row_ends, ws.state, nseg,
+                           ws.segoff, ws.cand, k, indices, indices_row_stride);
     else
-        hipLaunchKernelGGL(topk_collect_kernel<1>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, indices, indices_row_stride, ws, nseg,
-                           seg_len);
+        hipLaunchKernelGGL(topk_collect_kernel<1>, grid, block, 0, stream, logits,
+                           logits_row_stride, width, seg_len, rows, row_ends, ws.state, nseg,
+                           ws.segoff, ws.cand, k, indices, indices_row_stride);
     hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads), 0, stream,
-                       logits, width, logits_row_stride, row_ends, k, indices, indices_row_stride,
-                       ws);
+                       ws.cand, ws.state, row_ends, width, k, indices, indices_row_stride, logits,
+                       logits_row_stride);
     return hipGetLastError();
 }
 
@@ -487,11 +540,13 @@ hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
     if (vec)
-        hipLaunchKernelGGL(topk_hist_kernel<4>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, ws, nseg, seg_len);
+        hipLaunchKernelGGL(topk_hist_kernel<4>, grid, block, 0, stream, logits,
+                           logits_row_stride, width, seg_len, rows, row_ends, k, nseg,
+                           ws.seghist, ws.coarse);
     else
-        hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, logits, width,
-                           logits_row_stride, row_ends, k, ws, nseg, seg_len);
+        hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, logits,
+                           logits_row_stride, width, seg_len, rows, row_ends, k, nseg,
+                           ws.seghist, ws.coarse);
     return launch_topk_after_histograms(logits, rows, width, logits_row_stride, row_ends, k,
                                         indices, indices_row_stride, workspace, nseg, seg_len,
                                         stream);
