@@ -333,64 +333,46 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     }
 }
 
+// Keys [lo, hi) of a row held by one workgroup of kTopkThreads lanes, in chunks of 4096 (16 per
+// lane, in registers). The caller has loaded the first chunk (`raw`, bounded by the row's
+// width: keys past `hi` are masked here). Positions of keys above bin `bin` go to the output
+// and (key, position) pairs inside it to the candidate list, after the segment's offsets `off`
+// and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
+constexpr int kCollectPer = 16;
 template <int VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
-    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int64_t seg_len,
-    int64_t rows, const int32_t *__restrict__ row_ends, const RowState *__restrict__ state,
-    int64_t nseg, const uint2 *__restrict__ segoff, uint2 *__restrict__ cand_all, int k,
-    int32_t *__restrict__ indices, int64_t indices_row_stride) {
-    __shared__ int partials[kTopkThreads / 64];
-    const RowSeg rs = row_segment(rows);
-    const int64_t row = rs.row, seg = rs.seg;
-    const float *x = logits + row * logits_row_stride;
-    const int64_t lo = seg * seg_len;
-
-    // Chunks of 4096 keys (16 per lane, in registers): lane counts and a workgroup prefix
-    // sum place every key after the segment's offsets and the earlier chunks' keys.
-    constexpr int kPer = 16, kChunk = kPer * kTopkThreads;
-    float raw[kPer];
-    auto load_chunk = [&](int64_t first, int64_t bound) {
-        if (VEC == 4 && first + kPer <= bound) {
+__device__ __forceinline__ void load_keys16(float (&raw)[kCollectPer], const float *x,
+                                            int64_t first, int64_t bound) {
+    if (VEC == 4 && first + kCollectPer <= bound) {
 #pragma unroll
-            for (int j = 0; j < kPer; j += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(x + first + j);
-                raw[j] = v.x;
-                raw[j + 1] = v.y;
-                raw[j + 2] = v.z;
-                raw[j + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) raw[j] = first + j < bound ? x[first + j] : 0.f;
+        for (int j = 0; j < kCollectPer; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + first + j);
+            raw[j] = v.x;
+            raw[j + 1] = v.y;
+            raw[j + 2] = v.z;
+            raw[j + 3] = v.w;
         }
-    };
-    // Issued at once, in this order: the row bound and threshold state (scalar loads), the
-    // first chunk of keys -- before either arrives: every key below the row's width is in
-    // bounds and keys past the row bound are masked below -- and the other arguments. The
-    // compiler-only fence keeps the loads above the early returns (it emits nothing).
-    const int64_t n = row_bound(row_ends, row, width);
-    const RowState st = state[row];
-    load_chunk(lo + (int64_t)threadIdx.x * kPer, lo + seg_len < width ? lo + seg_len : width);
-    asm volatile("" ::: "memory");
-    hoist_args(nseg, segoff, cand_all, k, indices, indices_row_stride);
-    if (n <= k) return;
-    if (lo >= n) return;
-    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
-    int32_t *out = indices + row * indices_row_stride;
-    const uint32_t bin = st.bin, above = (uint32_t)st.above;
-    const uint2 off = segoff[row * nseg + seg];
-    uint2 *cand = cand_all + row * kCandCap;
+    } else {
+#pragma unroll
+        for (int j = 0; j < kCollectPer; ++j) raw[j] = first + j < bound ? x[first + j] : 0.f;
+    }
+}
 
+template <int VEC>
+__device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const float *x,
+                                                int64_t lo, int64_t hi, uint32_t bin,
+                                                uint32_t above, uint2 off, int32_t *out,
+                                                uint2 *cand, int *partials) {
+    constexpr int kChunk = kCollectPer * kTopkThreads;
     uint32_t base_above = off.x, base_in = off.y;
     for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
-        const int64_t first = cbase + (int64_t)threadIdx.x * kPer;
-        if (cbase != lo) load_chunk(first, hi);
-        uint32_t u[kPer];
+        const int64_t first = cbase + (int64_t)threadIdx.x * kCollectPer;
+        if (cbase != lo) load_keys16<VEC>(raw, x, first, hi);
+        uint32_t u[kCollectPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) u[j] = order_key(raw[j]);
+        for (int j = 0; j < kCollectPer; ++j) u[j] = order_key(raw[j]);
         int n_above = 0, n_in = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
+        for (int j = 0; j < kCollectPer; ++j) {
             const uint32_t d = u[j] >> kBinShift;
             n_above += first + j < hi && d > bin;
             n_in += first + j < hi && d == bin;
@@ -400,7 +382,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
         uint32_t pa = base_above + ((incl - mine) & 0xFFFF);
         uint32_t pc = base_in + ((incl - mine) >> 16);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
+        for (int j = 0; j < kCollectPer; ++j) {
             const int64_t i = first + j;
             const uint32_t d = u[j] >> kBinShift;
             const bool live = i < hi;
@@ -420,6 +402,183 @@ __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
         base_in += (uint32_t)(tot >> 16);
         __syncthreads();
     }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
+    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int64_t seg_len,
+    int64_t rows, const int32_t *__restrict__ row_ends, const RowState *__restrict__ state,
+    int64_t nseg, const uint2 *__restrict__ segoff, uint2 *__restrict__ cand_all, int k,
+    int32_t *__restrict__ indices, int64_t indices_row_stride) {
+    __shared__ int partials[kTopkThreads / 64];
+    const RowSeg rs = row_segment(rows);
+    const int64_t row = rs.row, seg = rs.seg;
+    const float *x = logits + row * logits_row_stride;
+    const int64_t lo = seg * seg_len;
+    // Issued at once, in this order: the row bound and threshold state (scalar loads), the
+    // first chunk of keys -- before either arrives: every key below the row's width is in
+    // bounds and keys past the row bound are masked -- and the other arguments. The
+    // compiler-only fence keeps the loads above the early returns (it emits nothing).
+    const int64_t n = row_bound(row_ends, row, width);
+    const RowState st = state[row];
+    float raw[kCollectPer];
+    load_keys16<VEC>(raw, x, lo + (int64_t)threadIdx.x * kCollectPer,
+                     lo + seg_len < width ? lo + seg_len : width);
+    asm volatile("" ::: "memory");
+    hoist_args(nseg, segoff, cand_all, k, indices, indices_row_stride);
+    if (n <= k) return;
+    if (lo >= n) return;
+    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
+    collect_segment<VEC>(raw, x, lo, hi, st.bin, (uint32_t)st.above, segoff[row * nseg + seg],
+                         indices + row * indices_row_stride, cand_all + row * kCandCap,
+                         partials);
+}
+
+// Steps 2 and 3 in one kernel, for rows of at most kFusedSegments segments (segments x rows
+// workgroups): every workgroup of a row finds the row's threshold bin and its own segment's
+// offsets from the row's histograms as topk_threshold does (its two levels, the same sums),
+// reading 2 x 128 B per segment of the row, then collects its segment. The row's first
+// segment also stores the threshold state for step 4, or, for a row of at most k keys, the
+// whole output.
+constexpr int kFusedSegments = 64;
+static_assert(kFusedSegments == 64 && kTopkThreads == 256, "lane t covers word t % 8 of two segments");
+
+template <int VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
+    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width,
+    const int32_t *__restrict__ row_ends, const uint16_t *__restrict__ coarse_hist, int rows,
+    int nseg, int seg_len, int k, const uint16_t *__restrict__ fine_hist,
+    int32_t *__restrict__ indices, int64_t indices_row_stride, RowState *__restrict__ state,
+    uint2 *__restrict__ cand_all) {
+    __shared__ int partials[kTopkThreads / 64];
+    __shared__ uint32_t part[kTopkThreads / 64][64];
+    __shared__ uint32_t seg_above[kFusedSegments], seg_in[kFusedSegments];
+    __shared__ uint32_t found_c, found_f, count_c, count_f;
+    __shared__ int above_c, above_f;
+    __shared__ uint2 my_off;
+    const RowSeg rs = row_segment(rows);
+    const int64_t row = rs.row, seg = rs.seg;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int p8 = t & 7, s0 = t >> 3;  // word p8 of segments s0 and s0 + 32
+    const float *x = logits + row * logits_row_stride;
+    const int64_t lo = seg * (int64_t)seg_len;
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+    // Issued at once: the row bound, the coarse words of the row's segments (every segment
+    // below nseg lies in the workspace; those past the row's keys are masked below), the first
+    // chunk of keys (as in topk_collect) and the other arguments.
+    const int64_t n = row_bound(row_ends, row, width);
+    const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
+    uint4 cw0 = s0 < nseg ? coarse[s0 * (kCoarseBins / 8) + p8] : zero4;
+    uint4 cw1 = s0 + 32 < nseg ? coarse[(s0 + 32) * (kCoarseBins / 8) + p8] : zero4;
+    float raw[kCollectPer];
+    load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer,
+                     lo + seg_len < width ? lo + seg_len : width);
+    asm volatile("" ::: "memory");
+    hoist_args(fine_hist, indices, indices_row_stride, state, cand_all);
+    if (n <= k) {
+        if (seg == 0) {
+            int32_t *out = indices + row * indices_row_stride;
+            for (int i = t; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        }
+        return;
+    }
+    if (lo >= n) return;
+    const int row_segments = (int)((n + seg_len - 1) / seg_len);
+    if (s0 >= row_segments) cw0 = zero4;
+    if (s0 + 32 >= row_segments) cw1 = zero4;
+    if (t == 0) {
+        found_c = 0;  // kept only if the counts do not reach k (they always do)
+        above_c = 0;
+        count_c = 0;
+        found_f = 0;
+        above_f = 0;
+        count_f = 0;
+    }
+
+    // (a) coarse totals: bins [8 p8, 8 p8 + 8) over this lane's segments, then over the lanes
+    // sharing p8 (in the wavefront by lane swaps, across wavefronts in LDS)
+    uint32_t csum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) csum[e] = sum_over_segments_in_wave(count8(cw0, e) + count8(cw1, e));
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = csum[e];
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane l holds coarse bin 63 - l (descending)
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k, &found_c, &above_c, &count_c);
+    }
+    __syncthreads();
+    const uint32_t B = 63u - found_c;  // coarse bin, in ascending order
+
+    // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
+    const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
+    const uint4 fw0 = s0 < row_segments ? fine[(int64_t)s0 * (kBins / 8) + B * 8 + p8] : zero4;
+    const uint4 fw1 =
+        s0 + 32 < row_segments ? fine[(int64_t)(s0 + 32) * (kBins / 8) + B * 8 + p8] : zero4;
+    uint32_t fsum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw0, e) + count8(fw1, e));
+    __syncthreads();  // part[] is rewritten below
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = fsum[e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k - above_c, &found_f, &above_f, &count_f);
+    }
+    __syncthreads();
+    const uint32_t f = 63u - found_f;  // fine bin inside B, ascending
+    const uint32_t bin = B * 64 + f;   // threshold bin of the 4096
+    const int above = above_c + above_f;
+
+    // (c) per segment: coarse bins above B, fine bins in B above f, and fine bin f; wavefront 0
+    // then takes the exclusive prefix sums over the segments for this workgroup's segment
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4 &cw = h ? cw1 : cw0;
+        const uint4 &fw = h ? fw1 : fw0;
+        uint32_t up = 0, in = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b8 = 8u * p8 + e;
+            up += b8 > B ? count8(cw, e) : 0u;
+            up += b8 > f ? count8(fw, e) : 0u;
+            in += b8 == f ? count8(fw, e) : 0u;
+        }
+        up = sum_over_parts(up);
+        in = sum_over_parts(in);
+        if (p8 == 0) {
+            seg_above[s0 + 32 * h] = up;  // zero for segments past the row's keys
+            seg_in[s0 + 32 * h] = in;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int a = (int)seg_above[lane], c = (int)seg_in[lane];
+        const int ia = wave_incl_scan(a), ic = wave_incl_scan(c);
+        if (lane == (int)seg) my_off = make_uint2((uint32_t)(ia - a), (uint32_t)(ic - c));
+        if (seg == 0 && lane == 0) {
+            RowState &st = state[row];
+            st.bin = bin;
+            st.above = above;
+            st.remaining = k - above;
+            st.n_cand = count_f;
+        }
+    }
+    __syncthreads();
+    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
+    collect_segment<VEC>(raw, x, lo, hi, bin, (uint32_t)above, my_off,
+                         indices + row * indices_row_stride, cand_all + row * kCandCap,
+                         partials);
 }
 
 // Composite of a key inside the threshold bin: smaller for a larger value, and for equal
@@ -514,6 +673,22 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
     const TopkWorkspace ws = carve(workspace, rows, nseg);
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
+    if (nseg <= kFusedSegments) {
+        if (vec)
+            hipLaunchKernelGGL(topk_threshold_collect_kernel<4>, grid, block, 0, stream, logits,
+                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride, ws.state, ws.cand);
+        else
+            hipLaunchKernelGGL(topk_threshold_collect_kernel<1>, grid, block, 0, stream, logits,
+                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride, ws.state, ws.cand);
+        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads), 0,
+                           stream, ws.cand, ws.state, row_ends, width, k, indices,
+                           indices_row_stride, logits, logits_row_stride);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
                        ws.coarse, ws.seghist, nseg, row_ends, width, k, indices,
                        indices_row_stride, seg_len, ws.state, ws.segoff);
