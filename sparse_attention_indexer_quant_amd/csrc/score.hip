@@ -297,13 +297,19 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
-    // Workgroup b takes chunk b / R of request b % R (R requests; fewer than 2^31 workgroups,
-    // so 32-bit division). Workgroups go to the XCDs in turn by index, so with the request
-    // varying fastest every XCD gets every chunk position of its share of the requests: the
-    // early chunks, which every request fills, no longer all land on the same XCDs.
-    const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)num_requests);
+    // Workgroup b takes chunk c = b / R of request (b + c) mod R (R requests; fewer than 2^31
+    // workgroups, so 32-bit arithmetic). Workgroups go to the 8 XCDs in turn by index, b mod 8:
+    // rotating the requests by one per chunk makes the chunks of one request visit the XCDs in
+    // turn, so every XCD gets an equal share of every request's work however the requests'
+    // lengths differ, and a grid of one workgroup per compute unit still gives each XCD as many
+    // workgroups as it has compute units.
+    const uint32_t R = (uint32_t)num_requests;
+    const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(blockIdx.x / R);
+    const uint32_t rot = chunk32 % R;
+    uint32_t req32 = blockIdx.x - chunk32 * R + rot;
+    if (req32 >= R) req32 -= R;
     const int64_t chunk = chunk32;
-    const int64_t req = blockIdx.x - chunk32 * (uint32_t)num_requests;
+    const int64_t req = req32;
     const int64_t width = max_blocks * kPageTokens;
     const int PW = pages_per_wave;
     // The workgroup's chunk is blocks [chunk_begin, chunk_begin + 4 PW); its wavefronts take
@@ -466,10 +472,10 @@ template <int FMT, int H, int RG, bool HIST>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
-    // page buffers per wavefront: 3 for MXFP4 with up to 2 rows per group (measured best of
-    // 2-6 on the long-context workload), else 2 (FP8 pages and 4-row query groups take the
-    // registers a deeper ring would need)
-    constexpr int NB = (FMT == kFmtMxfp4 && RG <= 2) ? 3 : 2;
+    // page buffers per wavefront: 3 for MXFP4 (measured best of 2-6 on the long-context
+    // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
+    // take the registers a deeper ring would need)
+    constexpr int NB = FMT == kFmtMxfp4 ? 3 : 2;
     hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST>), grid, block, 0, stream,
                        a.block_table, a.query_starts, a.max_blocks, a.num_requests,
                        geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,

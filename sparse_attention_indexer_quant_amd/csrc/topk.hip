@@ -65,16 +65,20 @@ __device__ __forceinline__ int64_t row_bound(const int32_t *row_ends, int64_t ro
     return n < 0 ? 0 : (n > width ? width : n);
 }
 
-// Row and segment of this workgroup in a rows x nseg grid: workgroup b takes segment b / rows
-// of row b % rows (fewer than 2^31 workgroups: 32-bit division, made explicitly uniform so
-// the row arithmetic stays scalar). Workgroups go to the XCDs in turn by index; with the row
-// varying fastest the leading segments, which every row fills, spread over all of them.
+// Row and segment of this workgroup in a grid of nseg x rows workgroups: workgroup b takes
+// segment s = b / rows of row (b + s) mod rows (fewer than 2^31 workgroups: 32-bit arithmetic,
+// made explicitly uniform so the row arithmetic stays scalar). Workgroups go to the 8 XCDs in
+// turn by index, b mod 8; rotating the rows by one per segment makes the segments of one row
+// visit the XCDs in turn, so rows of different lengths still give every XCD an equal share.
 struct RowSeg {
     int64_t row, seg;
 };
 __device__ __forceinline__ RowSeg row_segment(int64_t rows) {
-    const uint32_t sg = __builtin_amdgcn_readfirstlane(blockIdx.x / (uint32_t)rows);
-    return {(int64_t)(blockIdx.x - sg * (uint32_t)rows), (int64_t)sg};
+    const uint32_t R = (uint32_t)rows;
+    const uint32_t sg = __builtin_amdgcn_readfirstlane(blockIdx.x / R);
+    uint32_t r = blockIdx.x - sg * R + sg % R;
+    if (r >= R) r -= R;
+    return {(int64_t)r, (int64_t)sg};
 }
 
 template <int VEC, typename F>
