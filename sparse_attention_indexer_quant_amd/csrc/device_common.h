@@ -95,9 +95,75 @@ __device__ __forceinline__ float sqrt_rn(float x) {
     return y;
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int lanes) {
-    for (int m = 1; m < lanes; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+// Cross-lane exchanges in registers: DPP for partners inside a row of 16 lanes, the gfx950
+// lane swaps across rows (an LDS permute costs a round trip through the LDS unit instead).
+// lane_xor<H>(v), H = 1, 2, 4, 8: the value of lane l ^ H.
+template <int H>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    static_assert(H == 1 || H == 2 || H == 4 || H == 8, "partner inside a row of 16 lanes");
+    if constexpr (H == 1) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (H == 2) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (H == 4) {
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x104, 0xF, 0xF, false);  // row_shl:4: i + 4
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4: i - 4
+        return (threadIdx.x & 4) ? dn : up;
+    } else {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);  // row_ror:8: i ^ 8
+    }
+}
+
+// op(v, v of lane l ^ H) in every lane, H = 1 .. 32; `op` commutative, so the result is
+// exactly op(own, partner) whichever operand order the lane swaps deliver.
+template <int H, typename T, typename Op>
+__device__ __forceinline__ T xor_combine(T v, Op op) {
+    static_assert(sizeof(T) == 4, "32-bit values");
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if constexpr (H <= 8) {
+        return op(v, __builtin_bit_cast(T, lane_xor<H>(u)));
+    } else if constexpr (H == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
+        return op(__builtin_bit_cast(T, (uint32_t)r[0]), __builtin_bit_cast(T, (uint32_t)r[1]));
+    } else {
+        static_assert(H == 32, "H = 1 .. 32");
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // halves
+        return op(__builtin_bit_cast(T, (uint32_t)r[0]), __builtin_bit_cast(T, (uint32_t)r[1]));
+    }
+}
+
+__device__ __forceinline__ float max_of(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ int max_of(int a, int b) { return max(a, b); }
+
+// max over each aligned group of LANES lanes (a power of two up to 64), in all of them (fmaxf
+// for floats: a NaN operand gives the other one)
+template <int LANES, typename T>
+__device__ __forceinline__ T group_max(T v) {
+    auto mx = [](T a, T b) { return max_of(a, b); };
+    if constexpr (LANES > 1) v = xor_combine<1>(v, mx);
+    if constexpr (LANES > 2) v = xor_combine<2>(v, mx);
+    if constexpr (LANES > 4) v = xor_combine<4>(v, mx);
+    if constexpr (LANES > 8) v = xor_combine<8>(v, mx);
+    if constexpr (LANES > 16) v = xor_combine<16>(v, mx);
+    if constexpr (LANES > 32) v = xor_combine<32>(v, mx);
     return v;
+}
+
+// value of lane l + D (D = 1, 2, 3) inside each quad of lanes, for lane l % 4 == 0 (other
+// lanes get a value of no use)
+template <int D>
+__device__ __forceinline__ uint32_t quad_down(uint32_t v) {
+    static_assert(D >= 1 && D <= 3, "inside a quad");
+    // quad_perm selectors: lane 0 <- D, lanes 1..3 <- min(lane + D, 3)
+    constexpr int c = D == 1 ? 0xF9 : D == 2 ? 0xFE : 0xFF;
+    return __builtin_amdgcn_update_dpp(0u, v, c, 0xF, 0xF, false);
+}
+
+// value of lane l + D (D = 4, 8, 12) inside each row of 16 lanes, for lane l % 16 == 0
+template <int D>
+__device__ __forceinline__ uint32_t row_down(uint32_t v) {
+    static_assert(D == 4 || D == 8 || D == 12, "inside a row of 16");
+    return __builtin_amdgcn_update_dpp(0u, v, 0x100 + D, 0xF, 0xF, false);  // row_shl:D
 }
 
 // Kernel arguments are read from memory, and the compiler loads each one next to its first use;

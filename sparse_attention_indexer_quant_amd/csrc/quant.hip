@@ -68,7 +68,7 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-            amax = wave_max_xor(amax, 4);  // the 4 lanes of one 32-value block
+            amax = group_max<4>(amax);  // the 4 lanes of one 32-value block
             const int e = ue8m0_exponent(amax);
             const float inv = pow2_neg(e);
             uint32_t word = 0;
@@ -77,8 +77,8 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             *reinterpret_cast<uint32_t *>(out_row + head * 64 + part * 4) = word;
             // UE8M0 bytes of blocks 0..3 live in lanes part = 0, 4, 8, 12 of the head.
             const uint32_t byte = (uint32_t)(e + 127);
-            const uint32_t b1 = __shfl_down(byte, 4, 16), b2 = __shfl_down(byte, 8, 16),
-                           b3 = __shfl_down(byte, 12, 16);
+            const uint32_t b1 = row_down<4>(byte), b2 = row_down<8>(byte),
+                           b3 = row_down<12>(byte);
             if (part == 0) {
                 *reinterpret_cast<uint32_t *>(out_row + heads * 64 + head * 4) =
                     byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
@@ -91,7 +91,7 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             float amax = 1e-10f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-            amax = wave_max_xor(amax, 16);  // the 16 lanes of the head
+            amax = group_max<16>(amax);  // the 16 lanes of the head
             const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
             const float inv = __fdiv_rn(1.0f, s);
             uint32_t lo = 0, hi = 0;
@@ -141,13 +141,22 @@ __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
     const float x0 = bf16_lo(in.pair), x1 = bf16_hi(in.pair);
 
     float sum = __fadd_rn(x0, x1);
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) sum = __fadd_rn(sum, __shfl_xor(sum, h));
+    auto add_rn = [](float a, float b) { return __fadd_rn(a, b); };
+    sum = xor_combine<32>(sum, add_rn);
+    sum = xor_combine<16>(sum, add_rn);
+    sum = xor_combine<8>(sum, add_rn);
+    sum = xor_combine<4>(sum, add_rn);
+    sum = xor_combine<2>(sum, add_rn);
+    sum = xor_combine<1>(sum, add_rn);
     const float mean = __fmul_rn(sum, 0.0078125f);
     const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
     float sq = __fadd_rn(__fmul_rn(d0, d0), __fmul_rn(d1, d1));
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) sq = __fadd_rn(sq, __shfl_xor(sq, h));
+    sq = xor_combine<32>(sq, add_rn);
+    sq = xor_combine<16>(sq, add_rn);
+    sq = xor_combine<8>(sq, add_rn);
+    sq = xor_combine<4>(sq, add_rn);
+    sq = xor_combine<2>(sq, add_rn);
+    sq = xor_combine<1>(sq, add_rn);
     const float var = __fmul_rn(sq, 0.0078125f);
     const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
     const float2 g = in.g, b = in.b;
@@ -157,22 +166,24 @@ __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
     uint8_t *sec = cache + (slot >> 6) * page_stride;
     const int off = (int)(slot & 63);
     if constexpr (FMT == kFmtMxfp4) {
-        const float amax = wave_max_xor(fmaxf(fabsf(n0), fabsf(n1)), 16);  // 16 lanes = 32 columns
+        const float amax = group_max<16>(fmaxf(fabsf(n0), fabsf(n1)));  // 16 lanes = 32 columns
         const int e = ue8m0_exponent(amax);
         const float inv = pow2_neg(e);
         const uint32_t byte = e2m1_code(__fmul_rn(n0, inv)) | (e2m1_code(__fmul_rn(n1, inv)) << 4);
-        const uint32_t word = byte | (__shfl_down(byte, 1) << 8) | (__shfl_down(byte, 2) << 16) |
-                              (__shfl_down(byte, 3) << 24);
+        const uint32_t word = byte | (quad_down<1>(byte) << 8) | (quad_down<2>(byte) << 16) |
+                              (quad_down<3>(byte) << 24);
         if ((lane & 3) == 0) *reinterpret_cast<uint32_t *>(sec + off * 64 + lane) = word;
         const uint32_t sb = (uint32_t)(e + 127);
-        const uint32_t scales = sb | (__shfl(sb, 16) << 8) | (__shfl(sb, 32) << 16) | (__shfl(sb, 48) << 24);
+        const uint32_t scales = sb | (__builtin_amdgcn_readlane(sb, 16) << 8) |
+                                (__builtin_amdgcn_readlane(sb, 32) << 16) |
+                                (__builtin_amdgcn_readlane(sb, 48) << 24);
         if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
     } else {
-        const float amax = wave_max_xor(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))), 64);
+        const float amax = group_max<64>(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))));
         const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
         const float inv = __fdiv_rn(1.0f, s);
         const uint32_t two = e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8);
-        const uint32_t word = two | (__shfl_down(two, 1) << 16);
+        const uint32_t word = two | (quad_down<1>(two) << 16);
         if ((lane & 1) == 0) *reinterpret_cast<uint32_t *>(sec + off * 128 + 2 * lane) = word;
         if (lane == 0) {
             if constexpr (FMT == kFmtFp8Mx) {

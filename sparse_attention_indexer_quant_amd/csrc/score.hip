@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 #pragma unroll
     for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
     asm volatile("" ::: "memory");
-    for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, __shfl_xor(kmax, m));
+    kmax = group_max<64>(kmax);
     kmax = __builtin_amdgcn_readfirstlane(kmax);
     const int64_t kext = kmax < width ? kmax : width;
     const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
@@ -425,8 +425,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s16 += (w8[e] & 0xFFFFu) + (w8[e] >> 16);
-                s16 += __shfl_xor(s16, 1);
-                s16 += __shfl_xor(s16, 2);
+                s16 += lane_xor<1>(s16);
+                s16 += lane_xor<2>(s16);
                 if ((threadIdx.x & 3) == 0)
                     coarse[at * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)s16;
             }

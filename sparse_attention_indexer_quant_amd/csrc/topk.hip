@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
                                            16 * threadIdx.x);
     dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
     dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-    sum16 += __shfl_xor(sum16, 1);
-    sum16 += __shfl_xor(sum16, 2);
+    sum16 += lane_xor<1>(sum16);
+    sum16 += lane_xor<2>(sum16);
     if ((threadIdx.x & 3) == 0)
         coarse[(row * nseg + seg) * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)sum16;
 }
