@@ -338,8 +338,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
 }
 
 // Keys [lo, hi) of a row held by one workgroup of kTopkThreads lanes, in chunks of 4096 (16 per
-// lane, in registers). The caller has loaded the first chunk (`raw`, bounded by the row's
-// width: keys past `hi` are masked here). Positions of keys above bin `bin` go to the output
+// lane, in registers). The caller has loaded the first chunk (`raw`, bounded by `hi` or by the
+// row's width: keys past `hi` are masked here). Positions of keys above bin `bin` go to the output
 // and (key, position) pairs inside it to the candidate list, after the segment's offsets `off`
 // and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
 constexpr int kCollectPer = 16;
@@ -469,15 +469,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
     // Issued at once: the row bound, the coarse words of the row's segments (every segment
-    // below nseg lies in the workspace; those past the row's keys are masked below), the first
-    // chunk of keys (as in topk_collect) and the other arguments.
+    // below nseg lies in the workspace; those past the row's keys are masked below) and the
+    // other arguments. The segment's keys go out once the bound shows the segment holds keys
+    // of the row, and arrive while the fine histogram words are fetched: loading them before
+    // that, for every segment of every row, read tens of MB of logits past the rows' ends on
+    // ragged workloads.
     const int64_t n = row_bound(row_ends, row, width);
     const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
     uint4 cw0 = s0 < nseg ? coarse[s0 * (kCoarseBins / 8) + p8] : zero4;
     uint4 cw1 = s0 + 32 < nseg ? coarse[(s0 + 32) * (kCoarseBins / 8) + p8] : zero4;
-    float raw[kCollectPer];
-    load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer,
-                     lo + seg_len < width ? lo + seg_len : width);
     asm volatile("" ::: "memory");
     hoist_args(fine_hist, indices, indices_row_stride, state, cand_all);
     if (n <= k) {
@@ -485,9 +485,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
             int32_t *out = indices + row * indices_row_stride;
             for (int i = t; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         }
+        keep_loaded(cw0.x);
+        keep_loaded(cw1.x);
         return;
     }
     if (lo >= n) return;
+    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
+    float raw[kCollectPer];
+    load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer, hi);
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
     if (s0 >= row_segments) cw0 = zero4;
     if (s0 + 32 >= row_segments) cw1 = zero4;
@@ -579,7 +584,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         }
     }
     __syncthreads();
-    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
     collect_segment<VEC>(raw, x, lo, hi, bin, (uint32_t)above, my_off,
                          indices + row * indices_row_stride, cand_all + row * kCandCap,
                          partials);
