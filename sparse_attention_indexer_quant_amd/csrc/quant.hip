@@ -231,12 +231,16 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
 // The indexer inputs of one step in one launch (page
 // "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex): one workgroup
 // per token quantizes the token's query with the head weights read from the packed projection
-// row, and its last wavefront then normalizes, quantizes and inserts the key held in the same
-// row (at H = 16, 32, 64 every wavefront quantizes the same number of heads). With a layout,
+// row, and normalizes, quantizes and inserts the key held in the same row. With a layout,
 // one more workgroup computes the row bounds (decode_layout) in the same launch. `w_in` and
 // `key_in` point at the weight and key columns of projection row 0.
+// Five wavefronts: four quantize the query, the fifth normalizes, quantizes and inserts the
+// key at the same time (with the key on one of the four, its work followed that wavefront's
+// share of the query).
+constexpr int kInputsThreads = 320;
+
 template <int FMT, int H>
-__global__ __launch_bounds__(256) void index_inputs_kernel(
+__global__ __launch_bounds__(kInputsThreads) void index_inputs_kernel(
     int64_t tokens, const uint16_t *__restrict__ q, int64_t q_row_stride, int64_t q_head_stride,
     const uint16_t *__restrict__ w_in, int64_t proj_row_stride,
     const uint16_t *__restrict__ key_in, uint8_t *__restrict__ q_out, int64_t q_out_row_stride,
@@ -246,23 +250,26 @@ __global__ __launch_bounds__(256) void index_inputs_kernel(
     int64_t page_stride, LayoutArgs layout) {
     const int64_t token = blockIdx.x;
     if (token == tokens) {  // the extra workgroup of the combined call: the row bounds
-        decode_layout_body<256>(layout);
+        decode_layout_body<kInputsThreads>(layout);
         return;
     }
-    // Issue order: the query row and its weights (every operand a preloaded argument), every
-    // other argument in one batch, then the key (its last wavefront).
+    // uniform across the wavefront, said explicitly so the split below is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave == 4) {
+        const int lane = threadIdx.x & 63;
+        hoist_args(gamma, beta, eps, slots, cache, num_pages, page_stride);
+        store_key<FMT>(load_key(key_in + token * proj_row_stride, gamma, beta, slots + token, lane),
+                       eps, cache, num_pages, page_stride, lane);
+        return;
+    }
+    // the query row and its weights (every operand a preloaded argument), then the other
+    // arguments in one batch
     QueryLoads<H> in;
     in.load(q + token * q_row_stride, q_head_stride, threadIdx.x);
     in.load_weights(w_in + token * proj_row_stride, threadIdx.x);
-    hoist_args(q_out, q_out_row_stride, w_out, w_out_row_stride, c_h, gamma, beta, eps, slots,
-               cache, num_pages, page_stride);
-    const int lane = threadIdx.x & 63;
-    const bool key_wave = (threadIdx.x >> 6) == 3;
-    KeyLane key{};
-    if (key_wave) key = load_key(key_in + token * proj_row_stride, gamma, beta, slots + token, lane);
+    hoist_args(q_out, q_out_row_stride, w_out, w_out_row_stride, c_h);
     quantize_query_row<FMT, H>(in, true, q_out + token * q_out_row_stride,
                                w_out + token * w_out_row_stride, c_h, threadIdx.x);
-    if (key_wave) store_key<FMT>(key, eps, cache, num_pages, page_stride, lane);
 }
 
 template <int FMT, int H>
@@ -356,7 +363,7 @@ struct IndexInputs {
 
 template <int FMT, int H>
 static void launch_index_inputs_h(const IndexInputs &a, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((index_inputs_kernel<FMT, H>), grid, dim3(256), 0, stream, a.tokens, a.q,
+    hipLaunchKernelGGL((index_inputs_kernel<FMT, H>), grid, dim3(kInputsThreads), 0, stream, a.tokens, a.q,
                        a.q_row_stride, a.q_head_stride, a.w_in, a.proj_row_stride, a.key_in,
                        a.q_out, a.q_out_row_stride, a.w_out, a.w_out_row_stride, a.c_h, a.gamma,
                        a.beta, a.eps, a.slots, a.cache, a.num_pages, a.page_stride, a.layout);
