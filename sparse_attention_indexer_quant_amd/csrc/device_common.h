@@ -32,15 +32,17 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 
 __device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(bf16_bits_rne(f) << 16); }
 
-// E2M1 code of an FP32 value (grid 0, .5, 1, 1.5, 2, 3, 4, 6): each comparison crosses one
-// midpoint between neighbouring grid values; at a midpoint the even code wins, so the
-// comparison is strict where the lower neighbour is even and inclusive where the upper one
-// is. Magnitudes above 5 all give 6 (saturation). Bit 3 is the input's sign bit.
-__device__ __forceinline__ uint32_t e2m1_code(float s) {
-    const float m = fabsf(s);
-    uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
-                 (m >= 3.5f) + (m > 5.0f);
-    return c | ((__float_as_uint(s) >> 28) & 8u);
+// Two E2M1 codes, of a (low nibble) and b (high nibble), into byte `Byte` of `word` (the
+// other bytes kept), by the gfx950 scaled conversion with scale 1. The code of a value is its
+// nearest point of the grid 0, .5, 1, 1.5, 2, 3, 4, 6 (ties to the even code: 0.25 -> 0,
+// 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), magnitudes above 5 saturate
+// to 6, and bit 3 is the input's sign bit (so -0 gives 8). A probe on the device compared
+// the instruction with these comparisons written out over the grid, every midpoint, their
+// FP32 neighbours, both signs, subnormals, huge values and 200,000 random values in [-7, 7]:
+// no difference.
+template <int Byte>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, Byte);
 }
 
 // E4M3FN code of an FP32 value, round to nearest even, saturating to 448 (finite inputs).

@@ -71,9 +71,14 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             amax = group_max<4>(amax);  // the 4 lanes of one 32-value block
             const int e = ue8m0_exponent(amax);
             const float inv = pow2_neg(e);
-            uint32_t word = 0;
+            float sv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) word |= e2m1_code(__fmul_rn(v[i], inv)) << (4 * i);
+            for (int i = 0; i < 8; ++i) sv[i] = __fmul_rn(v[i], inv);  // exact: inv = 2^-e
+            uint32_t word = 0;
+            word = e2m1_pair<0>(word, sv[0], sv[1]);
+            word = e2m1_pair<1>(word, sv[2], sv[3]);
+            word = e2m1_pair<2>(word, sv[4], sv[5]);
+            word = e2m1_pair<3>(word, sv[6], sv[7]);
             *reinterpret_cast<uint32_t *>(out_row + head * 64 + part * 4) = word;
             // UE8M0 bytes of blocks 0..3 live in lanes part = 0, 4, 8, 12 of the head.
             const uint32_t byte = (uint32_t)(e + 127);
@@ -169,7 +174,7 @@ __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
         const float amax = group_max<16>(fmaxf(fabsf(n0), fabsf(n1)));  // 16 lanes = 32 columns
         const int e = ue8m0_exponent(amax);
         const float inv = pow2_neg(e);
-        const uint32_t byte = e2m1_code(__fmul_rn(n0, inv)) | (e2m1_code(__fmul_rn(n1, inv)) << 4);
+        const uint32_t byte = e2m1_pair<0>(0u, __fmul_rn(n0, inv), __fmul_rn(n1, inv)) & 0xFFu;
         const uint32_t word = byte | (quad_down<1>(byte) << 8) | (quad_down<2>(byte) << 16) |
                               (quad_down<3>(byte) << 24);
         if ((lane & 3) == 0) *reinterpret_cast<uint32_t *>(sec + off * 64 + lane) = word;
