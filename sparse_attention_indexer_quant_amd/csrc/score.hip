@@ -447,16 +447,21 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Pages per wavefront: enough work to stream through the ring, with about one wavefront per
-// SIMD (four per compute unit) over the whole (request x block) space (multiple of 4). Fewer,
-// longer wavefronts measured faster than two or more per SIMD: each wavefront's start (row
-// bounds, query operands, first pages) and histogram flush is paid fewer times, and one
-// wavefront's loads in flight already cover the memory latency.
+// Pages per wavefront: about one wavefront per SIMD (four per compute unit) over the whole
+// (request x block) space, 1 to 16 pages (a multiple of 4 above 4). Fewer, longer wavefronts
+// measured faster than two or more per SIMD: each wavefront's start (row bounds, query
+// operands, first pages) and histogram flush is paid fewer times, and one wavefront's loads in
+// flight already cover the memory latency. A small workload spreads over more wavefronts with
+// fewer pages each: the launch is then as long as one wavefront's start and few pages.
 int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
     const int64_t target_waves = (int64_t)device_cus() * 4;
     int64_t ppw = (num_requests * max_blocks + target_waves - 1) / target_waves;
-    ppw = (ppw + 3) / 4 * 4;
-    return (int)(ppw < 4 ? 4 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
+    if (ppw > 4) ppw = (ppw + 3) / 4 * 4;
+    int p = (int)(ppw < 1 ? 1 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
+    // a row spans at most kMaxRowSegments scoring workgroups
+    while (p < kMaxPagesPerWave && (max_blocks + 4 * p - 1) / (4 * p) > kMaxRowSegments)
+        p = p < 4 ? p + 1 : p + 4;
+    return p;
 }
 
 ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {

@@ -235,14 +235,17 @@ def test_score_paged_hist_checks(lib):
     assert lib.dsaidx_score_topk_workspace_bytes(1, 70000, 1) == 0
     assert score_hist(lib, r=1, mb=70000, ls=70000 * 64) == EUNSUP
     # segment = one scoring workgroup: 4 wavefronts x pages per wavefront x 64 keys, pages per
-    # wavefront a multiple of 4 in [4, 16] sized for one wavefront per SIMD (256 compute units
-    # assumed where no GPU is visible)
+    # wavefront 1..16 (a multiple of 4 above 4) sized for one wavefront per SIMD (256 compute
+    # units assumed where no GPU is visible)
     lib.dsaidx_score_segment_keys.restype = ctypes.c_int64
     assert lib.dsaidx_score_segment_keys(0, 4) == 0
-    assert lib.dsaidx_score_segment_keys(2, 4) == 4 * 4 * 64
+    assert lib.dsaidx_score_segment_keys(2, 4) == 4 * 1 * 64
     if not torch.cuda.is_available():
         assert lib.dsaidx_score_segment_keys(8, 2048) == 4 * 16 * 64
-        assert lib.dsaidx_score_segment_keys(16, 128) == 4 * 4 * 64
+        assert lib.dsaidx_score_segment_keys(16, 128) == 4 * 2 * 64
+        assert lib.dsaidx_score_segment_keys(24, 128) == 4 * 3 * 64
+        assert lib.dsaidx_score_segment_keys(40, 128) == 4 * 8 * 64
+        assert lib.dsaidx_score_segment_keys(64, 128) == 4 * 8 * 64
 
 
 def topk_scored(lib, **kw):
