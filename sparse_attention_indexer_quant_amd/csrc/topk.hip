@@ -668,6 +668,151 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     }
 }
 
+// Steps 2 to 4 in one workgroup per row, for rows of at most kRowTopkWidth keys and 64
+// segments: the threshold bin from the row's histograms (the same two levels and sums as
+// topk_threshold), then the row's keys once -- positions above the bin to the output, in
+// ascending order, (key, position) pairs inside it to LDS -- then the radix select of step 4 on
+// those candidates, all without leaving the workgroup: one launch instead of two. Measured, it
+// wins only while a row is one chunk of 8192 keys: classifying 32K-key rows on one compute
+// unit took longer than the two segmented launches (decode workload step 49 -> 57 us).
+constexpr int kRowTopkWidth = 8192;
+static_assert(kSelectThreads == 512 && kFusedSegments == 64, "lane t covers word t % 8 of segment t / 8");
+
+template <int VEC>
+__global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
+    const int32_t *__restrict__ row_ends, const uint16_t *__restrict__ coarse_hist,
+    const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int nseg,
+    int seg_len, int k, const uint16_t *__restrict__ fine_hist, int32_t *__restrict__ indices,
+    int64_t indices_row_stride) {
+    __shared__ uint64_t cands[kCandCap];
+    __shared__ SelectShared sh;
+    __shared__ uint32_t part[kSelectThreads / 64][64];
+    __shared__ uint32_t found_c, found_f, count_c, count_f;
+    __shared__ int above_c, above_f;
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int p8 = t & 7, sg = t >> 3;  // word p8 of segment sg
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+    // issued at once: the row bound, the coarse words of the row's segments (every segment
+    // below nseg lies in the workspace; those past the row's keys are masked below) and the
+    // other arguments
+    const int64_t n = row_bound(row_ends, row, width);
+    const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
+    uint4 cw = sg < nseg ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
+    asm volatile("" ::: "memory");
+    hoist_args(fine_hist, indices, indices_row_stride);
+    int32_t *out = indices + row * indices_row_stride;
+    if (n <= k) {
+        for (int i = t; i < k; i += kSelectThreads) out[i] = i < n ? i : -1;
+        keep_loaded(cw.x);
+        return;
+    }
+    const float *x = logits + row * logits_row_stride;
+    // the first chunk of keys, in flight while the threshold is found
+    constexpr int kChunk = kCollectPer * kSelectThreads;
+    float raw[kCollectPer];
+    load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, n);
+    const int row_segments = (int)((n + seg_len - 1) / seg_len);
+    if (sg >= row_segments) cw = zero4;
+    if (t == 0) {
+        found_c = 0;  // kept only if the counts do not reach k (they always do)
+        above_c = 0;
+        count_c = 0;
+        found_f = 0;
+        above_f = 0;
+        count_f = 0;
+    }
+    // (a) coarse totals and the coarse bin B holding the k-th largest key
+    uint32_t csum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) csum[e] = sum_over_segments_in_wave(count8(cw, e));
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = csum[e];
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane l holds coarse bin 63 - l (descending)
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kSelectThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k, &found_c, &above_c, &count_c);
+    }
+    __syncthreads();
+    const uint32_t B = 63u - found_c;
+    // (b) the fine bins inside B and the fine bin f
+    const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
+    const uint4 fw = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+    uint32_t fsum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw, e));
+    __syncthreads();  // part[] is rewritten below
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = fsum[e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kSelectThreads / 64; ++w) c += part[w][63 - lane];
+        find_in_64(c, k - above_c, &found_f, &above_f, &count_f);
+    }
+    __syncthreads();
+    const uint32_t bin = B * 64 + (63u - found_f);
+    const int above = above_c + above_f;
+    const uint32_t ncand = count_f;
+    const bool keep = ncand <= (uint32_t)kCandCap;  // else step 4 reads the row again
+    int pos_bits = 1;
+    while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
+
+    // (c) the row's keys once: lane counts and a workgroup prefix sum place every key
+    uint32_t base_above = 0, base_in = 0;
+    for (int64_t cbase = 0; cbase < n; cbase += kChunk) {
+        const int64_t first = cbase + (int64_t)t * kCollectPer;
+        if (cbase != 0) load_keys16<VEC>(raw, x, first, n);
+        uint32_t u[kCollectPer];
+        int n_above = 0, n_in = 0;
+#pragma unroll
+        for (int j = 0; j < kCollectPer; ++j) {
+            u[j] = order_key(raw[j]);
+            const uint32_t d = u[j] >> kBinShift;
+            n_above += first + j < n && d > bin;
+            n_in += first + j < n && d == bin;
+        }
+        const int mine = n_above | (n_in << 16);
+        const int incl = scan_block<kSelectThreads>(mine, sh.partials);
+        uint32_t pa = base_above + ((incl - mine) & 0xFFFF);
+        uint32_t pc = base_in + ((incl - mine) >> 16);
+#pragma unroll
+        for (int j = 0; j < kCollectPer; ++j) {
+            const int64_t i = first + j;
+            const uint32_t d = u[j] >> kBinShift;
+            const bool live = i < n;
+            if (live && d > bin) {
+                if (pa < (uint32_t)above) out[pa] = (int32_t)i;
+                ++pa;
+            } else if (live && d == bin) {
+                if (keep && pc < (uint32_t)kCandCap) cands[pc] = composite(u[j], (uint32_t)i, pos_bits);
+                ++pc;
+            }
+        }
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kSelectThreads / 64; ++w) tot += sh.partials[w];
+        base_above += (uint32_t)(tot & 0xFFFF);
+        base_in += (uint32_t)(tot >> 16);
+        __syncthreads();
+    }
+    // (d) the k - above smallest composites inside the bin
+    const int remaining = k - above;
+    const int bits = 20 + pos_bits;
+    if (keep)
+        select_smallest(LdsCandidates{cands, (int)ncand}, remaining, bits, pos_bits, out + above, sh);
+    else
+        select_smallest(RowBin{x, n, bin, pos_bits}, remaining, bits, pos_bits, out + above, sh);
+}
+
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int) {
     return topk_layout_bytes(rows, topk_nseg(width, topk_segment(rows, width)));
 }
@@ -681,6 +826,19 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
     const TopkWorkspace ws = carve(workspace, rows, nseg);
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
+    if (nseg <= kFusedSegments && width <= kRowTopkWidth) {
+        if (vec)
+            hipLaunchKernelGGL(topk_row_kernel<4>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
+                               stream, row_ends, ws.coarse, logits, logits_row_stride, width,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride);
+        else
+            hipLaunchKernelGGL(topk_row_kernel<1>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
+                               stream, row_ends, ws.coarse, logits, logits_row_stride, width,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride);
+        return hipGetLastError();
+    }
     if (nseg <= kFusedSegments) {
         if (vec)
             hipLaunchKernelGGL(topk_threshold_collect_kernel<4>, grid, block, 0, stream, logits,

@@ -379,12 +379,17 @@ def _topk_inputs(seed):
     return lg, ends
 
 
+@pytest.mark.parametrize("pad", [0, 4200])
 @pytest.mark.parametrize("k", [1, 64, 2048, 4999, 6000])
-def test_topk_sets_match_oracle(k):
+def test_topk_sets_match_oracle(k, pad):
+    # pad 0: rows of 5000 keys take the one-workgroup-per-row kernel; pad 4200: the same bounds
+    # in rows 9200 wide take the segmented kernels (keys past the bounds are 1e38 decoys)
     lg, ends = _topk_inputs(14)
+    wide = np.full((lg.shape[0], lg.shape[1] + pad), 1e38, np.float32)
+    wide[:, :lg.shape[1]] = lg
     want = oracle.topk(lg, ends, k)
-    got = dsa.topk(dev(lg), dev(ends), k).cpu().numpy()
-    assert_topk_sets(got, want, range(lg.shape[0]), f"k={k}")
+    got = dsa.topk(dev(wide), dev(ends), k).cpu().numpy()
+    assert_topk_sets(got, want, range(lg.shape[0]), f"k={k} pad={pad}")
 
 
 def test_topk_strided_rows():
