@@ -1,14 +1,16 @@
 """Benchmark of the DSA lightning-indexer hot path on one MI355X.
 
-One step = one pass of the whole path over one decode batch, inputs resident in HBM:
-index_inputs_layout (one launch: every row's query quantized with its head weights, the step's
-new keys normalized, quantized and inserted, and the decode_layout row bounds),
-score_paged_hist (scoring that also writes the top-k segment histograms) and topk_scored. The same step with the separate
-score_paged + topk is timed too (per_config ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of the whole
-step, plus the score kernel's key-cache GB/s and its roofline fraction (HIP events on the
-launch stream around every score launch in the timed region, created without the
-system-scope cache fence a default event's record adds), and the CPU oracle timed on
-a bounded sample of the same workload.
+One step = one pass of the whole path over one decode batch, inputs resident in HBM: every
+row's query quantized with its head weights, the step's new keys normalized, quantized and
+inserted, the decode_layout row bounds, scoring that also writes the top-k segment
+histograms, and topk_scored. On MXFP4 workloads with at most 4 rows per request the first
+four are one launch (index_score_hist); otherwise index_inputs_layout + score_paged_hist. The
+separate-input form and the form with score_paged + topk are timed too (per_config
+..._separate_inputs, ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of
+the whole step, plus the scoring kernel's key-cache GB/s and its roofline fraction (HIP events
+on the launch stream around the scoring launch of sampled timed steps, created without the
+system-scope cache fence a default event's record adds), and the CPU oracle timed on a
+bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config long_mxfp4] [--configs all|none|a,b]
 
@@ -33,8 +35,11 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer scored (row,key) pairs/s + key-cache HBM GB/s (fraction of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 MAIN_CONFIG = "long_mxfp4"
-PROFILE_PMC = os.path.join(ROOT, "profiles", "score_paged_long_mxfp4_pmc.txt")
-SCORE_SOURCE = os.path.join(ROOT, "sparse_attention_indexer_quant_amd", "csrc", "score.hip")
+# rocprofv3 byte counters per scoring kernel, and the sources that kernel is built from (the
+# counters count only while those are unchanged)
+PROFILE_PMC = os.path.join(ROOT, "profiles", "{kernel}_{workload}_pmc.txt")
+SCORE_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_quant_amd", "csrc", f)
+                 for f in ("score.hip", "device_common.h", "key_norm.h")]
 
 
 def parse():
@@ -207,7 +212,9 @@ class Setup:
                                     self.idx.data_ptr(), self.idx.stride(0), wl.num_requests,
                                     wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
         self.store, self.score, self.inputs, self.score_hist = [], [], [], []
-        self.inputs_layout = []
+        self.inputs_layout, self.index_score = [], []
+        # the step's inputs made inside the scorer: MXFP4 with at most 4 rows per request
+        self.inline_ok = wl.fmt == "mxfp4" and wl.max_query_len <= 4
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(
@@ -237,6 +244,16 @@ class Setup:
                 wl.page_stride, self.block_table.data_ptr(), wl.num_requests, wl.max_blocks,
                 self.starts.data_ptr(), self.ends.data_ptr(), wl.num_rows, wl.max_query_len,
                 self.logits.data_ptr(), self.logits.stride(0), sp))
+            if self.inline_ok:
+                self.index_score.append(Prepared(
+                    lib.dsaidx_index_score_hist, fmt, self.projected.data_ptr(),
+                    self.projected.stride(0), 0, 128, self.q.data_ptr(), wl.heads,
+                    self.q.stride(0), self.q.stride(1), self.gamma.data_ptr(),
+                    self.beta.data_ptr(), ctypes.c_float(wl.eps), self.seq_lens.data_ptr(),
+                    self.query_lens.data_ptr(), wl.num_requests, wl.num_rows, wl.max_query_len,
+                    base, wl.num_pages, wl.page_stride, self.block_table.data_ptr(),
+                    wl.max_blocks, self.starts.data_ptr(), self.ends.data_ptr(),
+                    self.logits.data_ptr(), self.logits.stride(0), self.hws.data_ptr(), hwsb, sp))
             self.score_hist.append(Prepared(
                 lib.dsaidx_score_paged_hist, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
                 wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
@@ -259,6 +276,13 @@ class Setup:
         seg = hist_segment_keys(wl)
         self.hist_bytes = int(sum((8192 + 128) * ((int(e) + seg - 1) // seg) for e in ends))
         self.score_hist_bytes = self.score_bytes + self.hist_bytes
+        # index_score_hist reads the BF16 query rows, raw head weights and pre-norm keys instead
+        # of the quantized rows and weights, and also writes the step's keys and row layout
+        live = int(wl.query_lens.sum())
+        self.inline_bytes = (self.score_hist_bytes - wl.num_rows * per_row_q
+                             + wl.num_rows * (wl.heads * 256 + 2 * wl.heads + 256)
+                             + live * (wl.section_bytes // 64)
+                             + 4 * wl.num_rows + 4 * (wl.num_requests + 1) + 8 * wl.num_requests)
 
     def prologue(self, i):
         """index_inputs and decode_layout in one launch (index_inputs_layout). (Running
@@ -272,6 +296,16 @@ class Setup:
         if ev is not None:
             ev[0].record(self.stream)
         self.score_hist[i % len(self.caches)]()
+        if ev is not None:
+            ev[1].record(self.stream)
+        self.topk_scored()
+
+    def step_inline(self, i, ev=None):
+        """index_score_hist (the step's inputs and layout made inside the scorer; timed),
+        topk_scored."""
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.index_score[i % len(self.caches)]()
         if ev is not None:
             ev[1].record(self.stream)
         self.topk_scored()
@@ -293,11 +327,11 @@ class Setup:
 EVENT_EVERY = 4
 
 
-def time_steps(s: Setup, steps: int, warmup: int, fused: bool = True):
+def time_steps(s: Setup, steps: int, warmup: int, mode: str = "fused"):
     """Wall time of `steps` steps (after `warmup` untimed ones) and the score launch times
     (ms) of the sampled steps inside that timed loop."""
     import torch
-    step = s.step if fused else s.step_unfused
+    step = {"inline": s.step_inline, "fused": s.step, "unfused": s.step_unfused}[mode]
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -325,6 +359,8 @@ def kernel_times(s: Setup, reps: int = 30):
               ("topk", lambda i: s.topk()),
               ("score_paged_hist", lambda i: s.score_hist[i % len(s.caches)]()),
               ("topk_scored", lambda i: s.topk_scored())]
+    if s.inline_ok:
+        stages.append(("index_score_hist", lambda i: s.index_score[i % len(s.caches)]()))
     for name, fn in stages:
         ts = []
         for i in range(reps):
@@ -391,11 +427,18 @@ def cpu_model():
     return "unknown"
 
 
-def measured_traffic(score_bytes):
-    """HBM bytes per score launch from the committed rocprofv3 counter summary, if it was
-    taken on the current score kernel source; else None."""
+def scorer_source_hash():
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter
+    summary, if it was taken on the current scorer sources; else None."""
     try:
-        text = open(PROFILE_PMC).read()
+        text = open(PROFILE_PMC.format(kernel=kernel, workload=workload)).read()
     except OSError:
         return None
     vals = {}
@@ -403,8 +446,7 @@ def measured_traffic(score_bytes):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()[:16]
-    if vals.get("score_source_sha256_16") != src_hash:
+    if vals.get("scorer_sources_sha256_16") != scorer_source_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -415,10 +457,19 @@ def measured_traffic(score_bytes):
 def run_config(name, args, steps, warmup, cpu_budget):
     import torch
     s = Setup(name, args.min_rotation_mb)
-    wall_u, score_ms_u = time_steps(s, steps, warmup, fused=False)
-    wall, score_ms = time_steps(s, steps, warmup, fused=True)
+    wall_u, score_ms_u = time_steps(s, steps, warmup, mode="unfused")
+    wall_f, score_ms_f = time_steps(s, steps, warmup, mode="fused")
+    # the step the library offers for this workload: the inputs made inside the scorer where
+    # that path applies (MXFP4, at most 4 rows per request), else the separate input launch
+    if s.inline_ok:
+        wall, score_ms = time_steps(s, steps, warmup, mode="inline")
+        kernel, kbytes = "index_score_hist", s.inline_bytes
+    else:
+        wall, score_ms = wall_f, score_ms_f
+        kernel, kbytes = "score_paged_hist", s.score_hist_bytes
     ms_step = wall / steps * 1e3
     score_us = float(score_ms.mean() * 1e3)
+    score_us_f = float(score_ms_f.mean() * 1e3)
     score_us_u = float(score_ms_u.mean() * 1e3)
     res = {
         "workload": name,
@@ -432,10 +483,15 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "score_us_p10_p50_p90": [float(np.percentile(score_ms, p) * 1e3) for p in (10, 50, 90)],
         "score_pairs_per_s": s.pairs / (score_us / 1e6),
         "score_key_GBps": s.wl.key_bytes() / (score_us / 1e6) / 1e9,
-        "score_algorithmic_GBps": s.score_hist_bytes / (score_us / 1e6) / 1e9,
-        "score_algorithmic_bytes": s.score_hist_bytes,
+        "score_algorithmic_GBps": kbytes / (score_us / 1e6) / 1e9,
+        "score_algorithmic_bytes": kbytes,
         "score_histogram_bytes": s.hist_bytes,
-        "score_kernel": "score_paged_hist",
+        "score_kernel": kernel,
+        "step": "index_score_hist + topk_scored" if s.inline_ok else
+                "index_inputs_layout + score_paged_hist + topk_scored",
+        "ms_per_step_separate_inputs": wall_f / steps * 1e3,
+        "score_paged_hist_us_mean": score_us_f,
+        "score_paged_hist_algorithmic_GBps": s.score_hist_bytes / (score_us_f / 1e6) / 1e9,
         "ms_per_step_unfused": wall_u / steps * 1e3,
         "step_pairs_per_s_unfused": s.pairs / (wall_u / steps),
         "score_paged_us_mean_unfused": score_us_u,
@@ -490,7 +546,7 @@ def main():
               f"{per_config[name]['score_us_mean']:.2f} us", file=sys.stderr, flush=True)
 
     m = main_res
-    traffic = measured_traffic(m["score_algorithmic_bytes"])
+    traffic = measured_traffic(m["score_kernel"], args.config)
     achieved = m["score_algorithmic_GBps"]
     line = {
         "metric": METRIC,
@@ -512,7 +568,7 @@ def main():
         "key_cache_frac_of_peak": m["score_key_frac_of_peak"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "score_paged_hist",
+                     "kernel": m["score_kernel"],
                      "bytes_per_launch": m["score_algorithmic_bytes"],
                      "launch_us_mean": m["score_us_mean"],
                      "launches_timed": m["score_launches_timed"]},

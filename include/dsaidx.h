@@ -266,6 +266,43 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * index_score_hist -- one decode or verify step's indexer inputs and its scoring in one
+ * launch, MXFP4 ([idx] DsaIndex: the quantized query, the head weights and the inserted key
+ * feed the logits; [fp4ops] decode_layout for the rows). Each scoring workgroup quantizes its
+ * request's query rows itself, and the wavefront that scores the page of a new key
+ * normalizes, quantizes and inserts that key. The results equal those of
+ * dsaidx_index_inputs_layout (dcp_world_size 1) followed by dsaidx_score_paged_hist, bit for
+ * bit, when each row's key slot is the position the block table gives it: row
+ * query_starts[q] + i of request q holds the key at position
+ * pos = seq_lens[q] - query_lens[q] + i, token pos % 64 of page block_table[q, pos / 64].
+ * dsaidx_topk_scored then selects.
+ *  fmt      DSAIDX_MXFP4 (another valid format gives DSAIDX_EUNSUPPORTED).
+ *  projected, proj_row_stride, key_col, weight_col, q, heads, q_row_stride, q_head_stride,
+ *  gamma, beta, eps  as in dsaidx_index_inputs, one packed row and one query row per row.
+ *  seq_lens, query_lens, num_requests, num_rows, query_starts, row_ends  as in
+ *           dsaidx_decode_layout with dcp_world_size 1 (the two outputs are written).
+ *  cache, num_pages, page_stride, block_table, max_blocks  as in dsaidx_score_paged; the
+ *           cache is written too (the new keys). No quantized query rows or head weights
+ *           are written: they stay on chip.
+ *  max_query_len  1..4: the most rows any request has.
+ *  logits, logits_row_stride, workspace, workspace_bytes  as in dsaidx_score_paged_hist.
+ *  Caller contract: every request has at most max_query_len rows (further rows get neither
+ *  logits nor keys); a page that receives a new key is in no other request's block table;
+ *  a key whose position is negative, at or past max_blocks * 64, or on a block-table entry
+ *  outside [0, num_pages) is not inserted.
+ *  Errors: as the calls it replaces; max_query_len above 4 gives DSAIDX_EUNSUPPORTED. With
+ *  num_rows, num_requests, max_blocks or num_pages == 0 only the row layout is written.
+ */
+dsaidx_status dsaidx_index_score_hist(
+    int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+    const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
+    const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
+    int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
+    int32_t *row_ends, float *logits, int64_t logits_row_stride, void *workspace,
+    size_t workspace_bytes, void *stream);
+
+/*
  * topk_scored -- the per-row top-k of logits that dsaidx_score_paged_hist has just written,
  * using its histograms. Rows, bounds and output as dsaidx_topk with width = max_blocks * 64.
  *  num_requests, max_blocks, workspace  exactly as passed to the dsaidx_score_paged_hist call

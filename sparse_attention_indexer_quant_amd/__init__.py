@@ -71,6 +71,9 @@ def library():
             "dsaidx_score_segment_keys": (I64, [I64, I64]),
             "dsaidx_score_paged_hist": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
                                               P, P, I64, I32, P, I64, P, SZ, P]),
+            "dsaidx_index_score_hist": (I32, [I32, P, I64, I64, I64, P, I32, I64, I64, P, P, F32,
+                                              P, P, I64, I64, I32, P, I64, I64, P, I64, P, P, P,
+                                              I64, P, SZ, P]),
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
             "dsaidx_dcp_candidates": (I32, [P, I64, I64, I64, P, I32, I64, I32, I32, I32, P, P, P]),
@@ -340,6 +343,56 @@ def score_topk(q_rows, heads, weights, cache, num_pages, page_stride, block_tabl
                                 workspace.data_ptr(), workspace.numel(), _stream(q_rows))
     _check("topk_scored", st)
     return out, indices
+
+
+def index_score_topk(projected, key_col, weight_col, q, gamma, beta, eps, seq_lens, query_lens,
+                     num_rows, cache, num_pages, page_stride, block_table, max_query_len, k,
+                     fmt="mxfp4", section_offset=0, out=None, indices=None, workspace=None):
+    """One step in two launches: the step's inputs made inside the scorer (index_score_hist:
+    query quantization, key insert at the block table's positions, row layout, logits and
+    histograms), then topk_scored. Returns (query_starts, row_ends, logits, indices)."""
+    import torch
+    _dev(projected, "projected", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(query_lens, "query_lens", torch.int32)
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    if projected.dim() != 2 or projected.stride(1) != 1 or q.dim() != 3 or q.stride(2) != 1 \
+            or q.shape[0] < int(num_rows) or projected.shape[0] < int(num_rows):
+        raise ValueError("index_score_topk: projected [rows, cols], q [rows, heads, 128]")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("index_score_topk: block_table must be [requests, max_blocks], row-major")
+    dev = q.device
+    R, mb = block_table.shape
+    num_rows = int(num_rows)
+    starts = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    ends = torch.empty(max(num_rows, 0), dtype=torch.int32, device=dev)
+    logits = out
+    if logits is None:
+        logits = torch.empty((num_rows, mb * PAGE_TOKENS), dtype=torch.float32, device=dev)
+    if indices is None:
+        indices = torch.empty((num_rows, int(k)), dtype=torch.int32, device=dev)
+    _dev(logits, "out", torch.float32)
+    _dev(indices, "indices", torch.int32)
+    if workspace is None:
+        need = score_topk_workspace_bytes(R, mb, num_rows)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    lib = library()
+    st = lib.dsaidx_index_score_hist(
+        _fmt(fmt), projected.data_ptr(), projected.stride(0), int(key_col), int(weight_col),
+        q.data_ptr(), q.shape[1], q.stride(0), q.stride(1), gamma.data_ptr(), beta.data_ptr(),
+        float(eps), seq_lens.contiguous().data_ptr(), query_lens.contiguous().data_ptr(), R,
+        num_rows, int(max_query_len), cache.data_ptr() + int(section_offset), int(num_pages),
+        int(page_stride), block_table.data_ptr(), mb, starts.data_ptr(), ends.data_ptr(),
+        logits.data_ptr(), logits.stride(0), workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check("index_score_hist", st)
+    if num_rows > 0 and R > 0 and mb > 0 and int(num_pages) > 0:
+        st = lib.dsaidx_topk_scored(logits.data_ptr(), num_rows, logits.stride(0), ends.data_ptr(),
+                                    int(k), indices.data_ptr(), indices.stride(0), R, mb,
+                                    workspace.data_ptr(), workspace.numel(), _stream(q))
+        _check("topk_scored", st)
+    return starts, ends, logits, indices
 
 
 def topk_workspace_bytes(rows, width, k) -> int:

@@ -312,6 +312,61 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
     return hip_status(dsaidx::launch_score_paged_hist(a, workspace, as_stream(stream)));
 }
 
+dsaidx_status dsaidx_index_score_hist(
+    int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+    const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
+    const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
+    int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
+    int32_t *row_ends, float *logits, int64_t logits_row_stride, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0 ||
+        key_col < 0 || weight_col < 0 || !std::isfinite(eps) || eps < 0.0f)
+        return DSAIDX_EINVAL;
+    if (fmt != DSAIDX_MXFP4 || !valid_heads(heads) || max_query_len < 1 || max_query_len > 4)
+        return DSAIDX_EUNSUPPORTED;
+    dsaidx_status st = check_layout(seq_lens, query_lens, num_requests, num_rows, 0, 1, 1,
+                                    query_starts, row_ends);
+    if (st != DSAIDX_OK) return st;
+    // nothing to score and no key with a place in the cache: the row layout alone
+    if (num_rows == 0 || num_requests == 0 || max_blocks == 0 || num_pages == 0)
+        return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests,
+                                                       num_rows, 0, 1, 1, query_starts,
+                                                       row_ends, as_stream(stream)));
+    if (!projected || !q || !gamma || !beta || !cache || !block_table || !logits)
+        return DSAIDX_EINVAL;
+    // the index-input rules (packed rows, BF16 query rows, LayerNorm parameters)
+    if (proj_row_stride < key_col + DSAIDX_DIM || proj_row_stride < weight_col + heads ||
+        !aligned(projected, 4) || proj_row_stride % 2 || key_col % 2)
+        return DSAIDX_ELAYOUT;
+    if (q_head_stride < DSAIDX_DIM || q_row_stride < (int64_t)(heads - 1) * q_head_stride + DSAIDX_DIM)
+        return DSAIDX_ELAYOUT;
+    if (!aligned(q, 16) || q_head_stride % 8 || q_row_stride % 8) return DSAIDX_ELAYOUT;
+    if (!aligned(gamma, 8) || !aligned(beta, 8)) return DSAIDX_ELAYOUT;
+    // the scoring rules
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS ||
+        logits_row_stride < max_blocks * DSAIDX_PAGE_TOKENS || !aligned(logits, 4))
+        return DSAIDX_ELAYOUT;
+    const dsaidx::ScoreGeometry geo = dsaidx::score_geometry(num_requests, max_blocks);
+    if (geo.chunks * num_requests > kMaxGrid || geo.chunks > dsaidx::kMaxRowSegments)
+        return DSAIDX_EUNSUPPORTED;
+    const size_t need = dsaidx::score_topk_workspace_bytes(num_requests, max_blocks, num_rows);
+    if (!workspace || workspace_bytes < need) return DSAIDX_EINVAL;
+    if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
+    // `q` carries the BF16 query and `query_starts` the query lengths in this mode
+    const dsaidx::ScoreArgs a{fmt,          q,          q_row_stride, heads,      nullptr,
+                              0,            cache,      num_pages,    page_stride, block_table,
+                              num_requests, max_blocks, query_lens,   nullptr,    num_rows,
+                              max_query_len, logits,    logits_row_stride};
+    auto *pp = static_cast<const uint16_t *>(projected);
+    const dsaidx::FusedInputs fin{seq_lens, pp + key_col, pp + weight_col, proj_row_stride,
+                                  q_head_stride, gamma, beta, eps, head_weight_scale(heads),
+                                  query_starts, row_ends};
+    return hip_status(dsaidx::launch_index_score_hist(a, fin, workspace, as_stream(stream)));
+}
+
 dsaidx_status dsaidx_topk_scored(const float *logits, int64_t num_rows, int64_t logits_row_stride,
                                  const int32_t *row_ends, int32_t k, int32_t *indices,
                                  int64_t indices_row_stride, int64_t num_requests,

@@ -45,6 +45,19 @@ __device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, Byte);
 }
 
+// The E2M1 codes of the two BF16 values packed in `pair` (low half -> low nibble) times 2^-e,
+// e in [-126, 126], into byte Byte of `word`: the gfx950 BF16 scaled conversion with scale
+// 2^e, which divides by its scale. A probe on the device compared it with e2m1_pair of the
+// exact FP32 products for every finite BF16 pattern (and its negation) at every such e: no
+// difference.
+template <int Byte>
+__device__ __forceinline__ uint32_t e2m1_bf16_pair(uint32_t word, uint32_t pair, int e) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const float scale = __uint_as_float((uint32_t)(127 + e) << 23);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, pair), scale,
+                                                     Byte);
+}
+
 // E4M3FN code of an FP32 value, round to nearest even, saturating to 448 (finite inputs).
 // Normal range: round the FP32 mantissa to 3 bits in the integer domain (a carry moves into
 // the exponent) and rebias 127 -> 7. Below 2^-6: the value in units of 2^-9, rounded to

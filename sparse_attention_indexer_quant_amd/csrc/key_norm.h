@@ -1,0 +1,90 @@
+// The key path shared by the key-insert kernels and the scorer that inserts a step's keys
+// itself: LayerNorm of one 128-value BF16 key on one wavefront (FP32, then rounded to BF16)
+// and its MXFP4 encoding.
+//
+// Page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", insert_key and
+// insert_fp4_key: the key is LayerNorm(wk projection) in FP32, then BF16, then quantized; the
+// MXFP4 section holds the 64 B payload at token * 64 and the four UE8M0 bytes at
+// 64 * 64 + token * 4.
+#pragma once
+
+#include "device_common.h"
+
+namespace dsaidx {
+
+// One key's inputs as one lane of its wavefront holds them: columns 2l and 2l+1 (one 4-byte
+// load), their LayerNorm weights and biases, and the key's slot.
+struct KeyLane {
+    uint32_t pair;
+    float2 g, b;
+    int64_t slot;
+};
+
+__device__ __forceinline__ KeyLane load_key(const uint16_t *__restrict__ key,
+                                            const float *__restrict__ gamma,
+                                            const float *__restrict__ beta,
+                                            const int64_t *__restrict__ slot, int lane) {
+    KeyLane k;
+    k.pair = *reinterpret_cast<const uint32_t *>(key + 2 * lane);
+    k.g = *reinterpret_cast<const float2 *>(gamma + 2 * lane);
+    k.b = *reinterpret_cast<const float2 *>(beta + 2 * lane);
+    k.slot = slot ? *slot : 0;
+    return k;
+}
+
+// The lane's two LayerNorm outputs (columns 2l, 2l+1), rounded to BF16. The sums run as the
+// pairwise tree "adjacent pair, then fold 32, 16, 8, 4, 2, 1 apart", which the exchanges below
+// compute in every lane with exact partners.
+__device__ __forceinline__ void layer_norm_pair(const KeyLane &in, float eps, float &n0,
+                                                float &n1) {
+    const float x0 = bf16_lo(in.pair), x1 = bf16_hi(in.pair);
+    auto add_rn = [](float a, float b) { return __fadd_rn(a, b); };
+    float sum = __fadd_rn(x0, x1);
+    sum = xor_combine<32>(sum, add_rn);
+    sum = xor_combine<16>(sum, add_rn);
+    sum = xor_combine<8>(sum, add_rn);
+    sum = xor_combine<4>(sum, add_rn);
+    sum = xor_combine<2>(sum, add_rn);
+    sum = xor_combine<1>(sum, add_rn);
+    const float mean = __fmul_rn(sum, 0.0078125f);
+    const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
+    float sq = __fadd_rn(__fmul_rn(d0, d0), __fmul_rn(d1, d1));
+    sq = xor_combine<32>(sq, add_rn);
+    sq = xor_combine<16>(sq, add_rn);
+    sq = xor_combine<8>(sq, add_rn);
+    sq = xor_combine<4>(sq, add_rn);
+    sq = xor_combine<2>(sq, add_rn);
+    sq = xor_combine<1>(sq, add_rn);
+    const float var = __fmul_rn(sq, 0.0078125f);
+    const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
+    n0 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d0, rstd), in.g.x), in.b.x));
+    n1 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d1, rstd), in.g.y), in.b.y));
+}
+
+// The lane's MXFP4 payload byte (columns 2l, 2l+1: byte l of the token's 64) and the UE8M0
+// byte of its 32-column block (block l / 16; the 16 lanes of a block hold the same value).
+struct Mxfp4KeyLane {
+    uint32_t byte;
+    uint32_t scale;
+};
+
+__device__ __forceinline__ Mxfp4KeyLane mxfp4_key_lane(float n0, float n1) {
+    const float amax = group_max<16>(fmaxf(fabsf(n0), fabsf(n1)));  // 16 lanes = 32 columns
+    const int e = ue8m0_exponent(amax);
+    const float inv = pow2_neg(e);
+    return {e2m1_pair<0>(0u, __fmul_rn(n0, inv), __fmul_rn(n1, inv)) & 0xFFu, (uint32_t)(e + 127)};
+}
+
+// Writes the key to token `off` of the MXFP4 section `sec`.
+__device__ __forceinline__ void store_mxfp4_key(const Mxfp4KeyLane &k, uint8_t *sec, int off,
+                                                int lane) {
+    const uint32_t word = k.byte | (quad_down<1>(k.byte) << 8) | (quad_down<2>(k.byte) << 16) |
+                          (quad_down<3>(k.byte) << 24);
+    if ((lane & 3) == 0) *reinterpret_cast<uint32_t *>(sec + off * 64 + lane) = word;
+    const uint32_t scales = k.scale | (__builtin_amdgcn_readlane(k.scale, 16) << 8) |
+                            (__builtin_amdgcn_readlane(k.scale, 32) << 16) |
+                            (__builtin_amdgcn_readlane(k.scale, 48) << 24);
+    if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
+}
+
+}  // namespace dsaidx

@@ -59,6 +59,24 @@ struct ScoreArgs {
 
 hipError_t launch_score_paged(const ScoreArgs &args, hipStream_t stream);
 
+// The step's inputs, made inside the scorer (index_score_hist, MXFP4): in ScoreArgs, `q` is
+// then the BF16 query [rows, H, 128] (q_row_stride in elements), `query_starts` the query
+// lengths, and `w` / `row_ends` are unused.
+struct FusedInputs {
+    const int32_t *seq_lens;
+    const uint16_t *key_in;  // key column of projection row 0 (BF16)
+    const uint16_t *w_in;    // head-weight column of projection row 0 (BF16)
+    int64_t proj_row_stride;
+    int64_t q_head_stride;
+    const float *gamma, *beta;
+    float eps, c_h;
+    int32_t *query_starts;   // written: [0, cumsum(query_lens)]
+    int32_t *row_ends;       // written: decode_layout's row bounds
+};
+
+hipError_t launch_index_score_hist(const ScoreArgs &args, const FusedInputs &fin,
+                                   void *workspace, hipStream_t stream);
+
 // How score_paged splits a request's pages: pages per wavefront, workgroups ("chunks") per
 // request, and the keys one workgroup covers (the top-k segment when the scorer writes the
 // selection's histograms). Depends on the current device's compute-unit count.

@@ -16,6 +16,7 @@
 // with the __f*_rn intrinsics, so the bytes do not depend on contraction choices.
 #include "device_common.h"
 #include "launch.h"
+#include "key_norm.h"
 #include "layout.h"
 
 namespace dsaidx {
@@ -70,15 +71,11 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
             amax = group_max<4>(amax);  // the 4 lanes of one 32-value block
             const int e = ue8m0_exponent(amax);
-            const float inv = pow2_neg(e);
-            float sv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sv[i] = __fmul_rn(v[i], inv);  // exact: inv = 2^-e
-            uint32_t word = 0;
-            word = e2m1_pair<0>(word, sv[0], sv[1]);
-            word = e2m1_pair<1>(word, sv[2], sv[3]);
-            word = e2m1_pair<2>(word, sv[4], sv[5]);
-            word = e2m1_pair<3>(word, sv[6], sv[7]);
+            uint32_t word = 0;  // E2M1 of v * 2^-e, straight from the BF16 pairs
+            word = e2m1_bf16_pair<0>(word, raw.x, e);
+            word = e2m1_bf16_pair<1>(word, raw.y, e);
+            word = e2m1_bf16_pair<2>(word, raw.z, e);
+            word = e2m1_bf16_pair<3>(word, raw.w, e);
             *reinterpret_cast<uint32_t *>(out_row + head * 64 + part * 4) = word;
             // UE8M0 bytes of blocks 0..3 live in lanes part = 0, 4, 8, 12 of the head.
             const uint32_t byte = (uint32_t)(e + 127);
@@ -114,75 +111,22 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
     }
 }
 
-// One key's inputs as one lane of its wavefront holds them: columns 2l and 2l+1 (one 4-byte
-// load), their LayerNorm weights and biases, and the key's slot.
-struct KeyLane {
-    uint32_t pair;
-    float2 g, b;
-    int64_t slot;
-};
-
-__device__ __forceinline__ KeyLane load_key(const uint16_t *__restrict__ key,
-                                            const float *__restrict__ gamma,
-                                            const float *__restrict__ beta,
-                                            const int64_t *__restrict__ slot, int lane) {
-    KeyLane k;
-    k.pair = *reinterpret_cast<const uint32_t *>(key + 2 * lane);
-    k.g = *reinterpret_cast<const float2 *>(gamma + 2 * lane);
-    k.b = *reinterpret_cast<const float2 *>(beta + 2 * lane);
-    k.slot = *slot;
-    return k;
-}
-
-// One key on one wavefront. The LayerNorm sums run as the pairwise tree "adjacent pair, then
-// fold 32, 16, 8, 4, 2, 1 apart", which the xor butterfly below computes in every lane. Slots
-// outside [0, num_pages * 64) (negative slots are padding) write nothing.
+// One key on one wavefront (the LayerNorm and MXFP4 steps live in key_norm.h, shared with the
+// scorer that inserts a step's keys itself). Slots outside [0, num_pages * 64) (negative slots
+// are padding) write nothing.
 template <int FMT>
 __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
                                           uint8_t *__restrict__ cache, int64_t num_pages,
                                           int64_t page_stride, int lane) {
     const int64_t slot = in.slot;
     if (slot < 0 || slot >= num_pages * kPageTokens) return;
-    const float x0 = bf16_lo(in.pair), x1 = bf16_hi(in.pair);
-
-    float sum = __fadd_rn(x0, x1);
-    auto add_rn = [](float a, float b) { return __fadd_rn(a, b); };
-    sum = xor_combine<32>(sum, add_rn);
-    sum = xor_combine<16>(sum, add_rn);
-    sum = xor_combine<8>(sum, add_rn);
-    sum = xor_combine<4>(sum, add_rn);
-    sum = xor_combine<2>(sum, add_rn);
-    sum = xor_combine<1>(sum, add_rn);
-    const float mean = __fmul_rn(sum, 0.0078125f);
-    const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
-    float sq = __fadd_rn(__fmul_rn(d0, d0), __fmul_rn(d1, d1));
-    sq = xor_combine<32>(sq, add_rn);
-    sq = xor_combine<16>(sq, add_rn);
-    sq = xor_combine<8>(sq, add_rn);
-    sq = xor_combine<4>(sq, add_rn);
-    sq = xor_combine<2>(sq, add_rn);
-    sq = xor_combine<1>(sq, add_rn);
-    const float var = __fmul_rn(sq, 0.0078125f);
-    const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
-    const float2 g = in.g, b = in.b;
-    const float n0 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d0, rstd), g.x), b.x));
-    const float n1 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d1, rstd), g.y), b.y));
+    float n0, n1;
+    layer_norm_pair(in, eps, n0, n1);
 
     uint8_t *sec = cache + (slot >> 6) * page_stride;
     const int off = (int)(slot & 63);
     if constexpr (FMT == kFmtMxfp4) {
-        const float amax = group_max<16>(fmaxf(fabsf(n0), fabsf(n1)));  // 16 lanes = 32 columns
-        const int e = ue8m0_exponent(amax);
-        const float inv = pow2_neg(e);
-        const uint32_t byte = e2m1_pair<0>(0u, __fmul_rn(n0, inv), __fmul_rn(n1, inv)) & 0xFFu;
-        const uint32_t word = byte | (quad_down<1>(byte) << 8) | (quad_down<2>(byte) << 16) |
-                              (quad_down<3>(byte) << 24);
-        if ((lane & 3) == 0) *reinterpret_cast<uint32_t *>(sec + off * 64 + lane) = word;
-        const uint32_t sb = (uint32_t)(e + 127);
-        const uint32_t scales = sb | (__builtin_amdgcn_readlane(sb, 16) << 8) |
-                                (__builtin_amdgcn_readlane(sb, 32) << 16) |
-                                (__builtin_amdgcn_readlane(sb, 48) << 24);
-        if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
+        store_mxfp4_key(mxfp4_key_lane(n0, n1), sec, off, lane);
     } else {
         const float amax = group_max<64>(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))));
         const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));

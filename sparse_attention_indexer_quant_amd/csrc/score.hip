@@ -32,9 +32,16 @@
 // row into an LDS histogram of the top 12 order-key bits (two 16-bit counts per word) and
 // writes it as the (row, segment) histogram of a top-k workspace, segment = the workgroup's
 // run of keys. The selection then skips its own pass over the logits.
-#include "device_common.h"
-#include "launch.h"
+//
+// With FUSED (index_score_hist), the kernel also makes the step's inputs (page
+// "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex; page
+// "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_layout): the MXFP4 query operands, the
+// head weights, the new keys' LayerNorm, quantization and insert, and the row layout.
 #include <type_traits>
+
+#include "device_common.h"
+#include "key_norm.h"
+#include "launch.h"
 #include "topk_layout.h"
 
 namespace dsaidx {
@@ -201,6 +208,28 @@ struct RowGroup {
         }
     }
 
+    // The operands made in the workgroup (StepQuery below), and bounds from the request's
+    // sequence length: row r0 + i ends at max(0, seq - qlen + i + 1).
+    template <typename Lds>
+    __device__ __forceinline__ void from_lds(const Lds &s, int64_t r0, int seq, int qlen,
+                                             int64_t first, int64_t last, int64_t width,
+                                             int lane) {
+        static_assert(FMT == kFmtMxfp4, "the step inputs are made in the scorer for MXFP4");
+#pragma unroll
+        for (int j = 0; j < RG; ++j) {
+            const int64_t row = first + j;
+            int64_t e = (int64_t)seq - qlen + (row - r0) + 1;
+            e = e < 0 ? 0 : (e < width ? e : width);
+            rend[j] = row < last ? (int)e : 0;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                qa[j][ht][0] = s.qa[j * HT + ht][lane];
+                qs[j][ht] = s.qs[j * HT + ht][lane];
+                wt[j][ht] = s.wt[j * HT + ht][lane];
+            }
+        }
+    }
+
     // Logits of one page for the group's rows. Rows past `count` are not computed: row 0, then
     // row 1 if present, then rows 2..RG-1 if any is present (one uniform branch each).
     __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
@@ -271,6 +300,131 @@ struct RowGroup {
     }
 };
 
+// The scorer's own MXFP4 query operands (fused step inputs), made with the step-input kernel's
+// arithmetic so that they are bit-identical to the bytes it writes. A row group's RG x H/16
+// operand tiles (row j, heads 16 ht .. 16 ht + 15) are dealt out over the workgroup's four
+// wavefronts; lane (l16, grp) of a tile encodes the 32-value block grp of head 16 ht + l16
+// -- the UE8M0 exponent of the block's largest magnitude, then the E2M1 codes of the values
+// times 2^-e -- and rounds its four head weights times c_h to BF16. The tiles meet in the LDS
+// in the lane layout of RowGroup's registers.
+template <int H, int RG>
+struct StepQueryLds {
+    static constexpr int kTiles = RG * (H / 16);
+    uint4 qa[kTiles][64];
+    uint2 wt[kTiles][64];
+    int qs[kTiles][64];
+};
+
+template <int H, int RG>
+struct StepQuery {
+    static constexpr int HT = H / 16, kTiles = RG * HT, kPer = (kTiles + kWaves - 1) / kWaves;
+    uint4 raw[kPer][4];
+    uint32_t wraw[kPer][4];  // 32-bit: 16-bit lanes would be packed in pairs, which waits for the loads
+
+    // Every load is issued, with no branch around it (a tile past the group reads tile 0's
+    // rows), so that the wait for them leaves the page loads issued after them in flight.
+    __device__ __forceinline__ void load(const uint16_t *q, int64_t q_row_stride,
+                                         int64_t q_head_stride, const uint16_t *w_in,
+                                         int64_t proj_row_stride, int64_t first, int64_t last,
+                                         int wave, int l16, int grp) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            int it = wave + kWaves * m;
+            if (it >= kTiles) it = 0;
+            const int j = it / HT, ht = it % HT;
+            const int64_t rr = first + j < last ? first + j : first;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                q + rr * q_row_stride + (int64_t)(ht * 16 + l16) * q_head_stride + grp * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw[m][i] = src[i];
+            const uint16_t *wrow = w_in + rr * proj_row_stride + ht * 16 + grp * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wraw[m][i] = wrow[i];
+        }
+    }
+
+    __device__ __forceinline__ void encode(StepQueryLds<H, RG> &s, float c_h, int wave,
+                                           int lane) const {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int it = wave + kWaves * m;
+            if (it >= kTiles) continue;
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wd[4] = {raw[m][i].x, raw[m][i].y, raw[m][i].z, raw[m][i].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wd[c])), fabsf(bf16_hi(wd[c]))));
+            }
+            const int ex = ue8m0_exponent(amax);
+            uint32_t out[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t word = 0;
+                word = e2m1_bf16_pair<0>(word, raw[m][i].x, ex);
+                word = e2m1_bf16_pair<1>(word, raw[m][i].y, ex);
+                word = e2m1_bf16_pair<2>(word, raw[m][i].z, ex);
+                word = e2m1_bf16_pair<3>(word, raw[m][i].w, ex);
+                out[i] = word;
+            }
+            uint32_t wb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wb[i] = bf16_bits_rne(__fmul_rn(bf16_val((uint16_t)wraw[m][i]), c_h));
+            s.qa[it][lane] = make_uint4(out[0], out[1], out[2], out[3]);
+            s.qs[it][lane] = ex + 127;
+            s.wt[it][lane] = make_uint2(wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16));
+        }
+    }
+};
+
+// A new key in the page registers of the wavefront that scores its page: lane (l16, grp) of
+// tile o / 16 with l16 = o % 16 takes the key's 16 payload bytes of block grp and its UE8M0
+// byte from the staged key (64 payload bytes, then the 4 scale bytes).
+__device__ __forceinline__ void patch_key(PageRegs<kFmtMxfp4> &pg, const uint8_t *staged, int o,
+                                          int l16, int grp) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(staged + grp * 16);
+    const uint8_t sc = staged[64 + grp];
+    const bool mine = l16 == (o & 15);
+    // bit masks in every tile: a branch or a select over the registers' values gets folded
+    // into one access at a computed tile index or address, which puts them in scratch memory
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t m = mine && t == (o >> 4) ? 0xFFFFFFFFu : 0u;
+        uint4 &k = pg.kp[t][0];
+        k = make_uint4((v.x & m) | (k.x & ~m), (v.y & m) | (k.y & ~m), (v.z & m) | (k.z & ~m),
+                       (v.w & m) | (k.w & ~m));
+        pg.ks[t] = (uint8_t)((sc & m) | (pg.ks[t] & ~m));
+    }
+}
+
+// Rows of request `req` from the query lengths: the first is the sum of the lengths before it
+// (a wavefront sum, uniform), the count its own length.
+__device__ __forceinline__ int64_t request_first_row(const int32_t *lens, int64_t req, int lane) {
+    // 256 lengths per round trip: each pass issues its four loads before adding any
+    int acc = 0;
+    for (int64_t base = 0; base < req; base += 256) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + 64 * u + lane;
+            v[u] = i < req ? lens[i] : 0;
+        }
+        acc += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    auto add = [](int a, int b) { return a + b; };
+    acc = xor_combine<1>(acc, add);
+    acc = xor_combine<2>(acc, add);
+    acc = xor_combine<4>(acc, add);
+    acc = xor_combine<8>(acc, add);
+    acc = xor_combine<16>(acc, add);
+    acc = xor_combine<32>(acc, add);
+    return __builtin_amdgcn_readfirstlane(acc);
+}
+
+constexpr int kStagedKeyBytes = 80;  // 64 payload + 4 scale bytes, padded to 16
+
 // Grid: requests x chunks; a workgroup's chunk is 4 PW consecutive pages of the request, which
 // its 4 wavefronts take in turn (PW pages each). Each wavefront streams its pages through a
 // ring of NB page buffers: the next NB - 1 pages' loads are in flight while one page is
@@ -280,7 +434,16 @@ struct RowGroup {
 // there. The first NB - 1 page loads go out right after the query and row-bound loads. The
 // arguments the first loads need come first: the library is built to preload the leading
 // kernel arguments into scalar registers at wave launch.
-template <int FMT, int H, int RG, int NB, bool HIST>
+//
+// FUSED (MXFP4 with histograms, one row group per request): the step's inputs are made here
+// instead of read -- `query_starts` holds the query lengths and `q` the BF16 query -- and the
+// result equals the step-input kernel with decode_layout followed by the plain launch, with
+// each row's new key at position seq - qlen + i of its request (the slot its block table
+// gives): the rows come from the lengths' prefix sum, the bounds from the sequence length, the
+// query operands are quantized by each wavefront, the wavefront that scores a page holding a
+// new key normalizes, quantizes and inserts that key and scores its own copy of it, and the
+// workgroups of chunk 0 write query_starts and row_ends.
+template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false>
 __global__ __launch_bounds__(256) void score_paged_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
     int64_t max_blocks, int64_t num_requests, int pages_per_wave,
@@ -288,10 +451,15 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
     int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
     int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
-    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse) {
+    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin) {
+    static_assert(!FUSED || (FMT == kFmtMxfp4 && HIST), "fused inputs: MXFP4 with histograms");
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
     __shared__ __align__(16) uint32_t hist[HIST ? RG * (kBins / 2) : 1];
+    // FUSED: the workgroup's query operands, and each wavefront's staged new keys
+    __shared__ __align__(16) uint8_t step_lds_bytes[FUSED ? sizeof(StepQueryLds<H, RG>) : 16];
+    __shared__ __align__(16) uint8_t staged_keys[FUSED ? kWaves * RG * kStagedKeyBytes : 16];
+    auto &step_lds = *reinterpret_cast<StepQueryLds<H, RG> *>(step_lds_bytes);
     const int lane = threadIdx.x & 63;
     // uniform across the wavefront; said explicitly so that all page and bound arithmetic
     // below stays in scalar registers
@@ -322,11 +490,41 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // nothing before them in the kernel writes memory) and this wavefront's slice of the block
     // table (one entry per lane; every entry below max_blocks is in bounds). Then every other
     // argument at once, in the same round trip.
-    int64_t r0 = query_starts[req], r1 = query_starts[req + 1];
+    int64_t r0, r1;
+    int qlen = 0, seq = 0;
+    if constexpr (!FUSED) {
+        r0 = query_starts[req];
+        r1 = query_starts[req + 1];
+    } else {
+        // `query_starts` holds the query lengths; the request's own length and sequence length
+        // are scalar loads, its first row a sum over the lengths before it
+        qlen = query_starts[req];
+        seq = fin.seq_lens[req];
+        r0 = request_first_row(query_starts, req, lane);
+        r1 = r0 + qlen;
+    }
     const int32_t *bt = block_table + req * max_blocks;
     const int bt_lane = lane < PW && block_of(lane) < max_blocks ? bt[block_of(lane)] : -1;
     hoist_args(num_pages, chunks, q, q_row_stride, w, w_row_stride, row_ends, num_rows,
                max_query_len, logits, logits_row_stride, seghist, coarse);
+    if constexpr (FUSED) {
+        hoist_args(fin.key_in, fin.w_in, fin.proj_row_stride, fin.q_head_stride, fin.gamma,
+                   fin.beta, fin.eps, fin.c_h, fin.query_starts, fin.row_ends);
+        // decode_layout's outputs, from the workgroups of chunk 0 (before any early exit)
+        if (chunk == 0 && wave == 0) {
+            if (req == 0 && lane == 0) fin.query_starts[0] = 0;
+            if (lane == 0) fin.query_starts[req + 1] = (int32_t)(r0 + qlen);
+            for (int64_t i = lane; r0 >= 0 && i < qlen && r0 + i < num_rows; i += 64) {
+                const int64_t e = (int64_t)seq - qlen + i + 1;
+                fin.row_ends[r0 + i] = (int32_t)(e < 0 ? 0 : e);
+            }
+            if (req == (int64_t)R - 1) {  // rows from query_starts[R] on are graph padding
+                const int64_t total = r0 + qlen;
+                for (int64_t row = (total > 0 ? total : 0) + lane; row < num_rows; row += 64)
+                    fin.row_ends[row] = 0;
+            }
+        }
+    }
 
     // Table entry of run page p (uniform), or -1 if it names no page of the cache.
     const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
@@ -350,10 +548,31 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // Query operands of the first row group, in flight together with the row bounds.
     const int ngroups = (nrows + RG - 1) / RG;
     RowGroup<FMT, H, RG> rows;
-    rows.load(q, q_row_stride, w, w_row_stride, row_ends, r0, r1, width, l16, grp);
-
-    // Keys this request needs: the largest bound over its rows.
-    int kmax = lane < nrows ? row_ends[r0 + lane] : 0;
+    int kmax;
+    // FUSED: the raw query tiles and head weights of this wavefront's share, and the step's
+    // keys (one row each; a key past the rows reads the first row's)
+    StepQuery<H, RG> sq;
+    KeyLane key;  // columns 2 lane, 2 lane + 1 of the LayerNorm weights and biases
+    uint32_t key_pair[FUSED ? RG : 1];
+    if constexpr (!FUSED) {
+        rows.load(q, q_row_stride, w, w_row_stride, row_ends, r0, r1, width, l16, grp);
+        // Keys this request needs: the largest bound over its rows.
+        kmax = lane < nrows ? row_ends[r0 + lane] : 0;
+    } else {
+        const int64_t e = (int64_t)seq - qlen + nrows;  // the last row's bound is the largest
+        kmax = (int)(e < 0 ? 0 : (e > width ? width : e));
+        // the bounds need no loads here: a chunk past the request's keys leaves before any
+        // query work (no new key lies in it: every key's position is below the last bound)
+        if (chunk_begin * kPageTokens >= kmax) return;
+        sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride, fin.w_in,
+                fin.proj_row_stride, r0, r1, wave, l16, grp);
+        key = load_key(fin.key_in + r0 * fin.proj_row_stride, fin.gamma, fin.beta, nullptr, lane);
+        key_pair[0] = key.pair;
+#pragma unroll
+        for (int i = 1; i < RG; ++i)
+            key_pair[i] = *reinterpret_cast<const uint32_t *>(
+                fin.key_in + (r0 + (i < nrows ? i : 0)) * fin.proj_row_stride + 2 * lane);
+    }
 
     // The first NB - 1 pages go out after the query and bound loads: loads complete in issue
     // order, so the first page's math then waits for that page and not for the whole ring.
@@ -363,6 +582,55 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 #pragma unroll
     for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
     asm volatile("" ::: "memory");
+
+    // FUSED: the new key at position seq - qlen + i belongs to the wavefront whose run holds
+    // its block. The step's keys are consecutive positions (at most 4), so they span at most
+    // two consecutive blocks, which belong to different wavefronts: a wavefront owns at most
+    // one page of new keys (own_pp, its run page, or -1; own_mask, the keys on it). It
+    // normalizes, quantizes and inserts those keys, keeps a copy in the LDS, and loads the page
+    // once more for itself: that copy takes the new keys and is scored on its own, and the
+    // ring skips the page, so that the ring's registers are never rewritten (rewriting them
+    // in place made the compiler wait for each page's loads as soon as they were issued).
+    int own_pp = -1;
+    uint32_t own_mask = 0;
+    int own_o[FUSED ? RG : 1];
+    PageRegs<FMT> own_pg;
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+            own_o[i] = 0;
+            const int64_t pos = (int64_t)seq - qlen + i;
+            if (i >= nrows || pos < 0 || pos >= width) continue;
+            const int64_t rel = (pos >> 6) - chunk_begin;
+            if (rel < 0 || rel >= kWaves * (int64_t)PW || (rel & (kWaves - 1)) != wave) continue;
+            if (table_page((int)(rel >> 2)) < 0) continue;
+            own_pp = (int)(rel >> 2);
+            own_mask |= 1u << i;
+            own_o[i] = (int)(pos & 63);
+        }
+        // issued by every wavefront (a non-owner reads its first ring page again, which the
+        // ring is loading anyway), so that no branch joins around loads in flight
+        load_page(own_pg, section(own_pp >= 0 ? own_pp : 0, PW), off);
+        sq.encode(step_lds, fin.c_h, wave, lane);
+        if (own_pp >= 0) {
+            uint8_t *sec = const_cast<uint8_t *>(section(own_pp, PW));  // the caller's writable cache
+#pragma unroll
+            for (int i = 0; i < RG; ++i) {
+                if (!((own_mask >> i) & 1u)) continue;
+                KeyLane k = key;
+                k.pair = key_pair[i];
+                float n0, n1;
+                layer_norm_pair(k, fin.eps, n0, n1);
+                const Mxfp4KeyLane mk = mxfp4_key_lane(n0, n1);
+                store_mxfp4_key(mk, sec, own_o[i], lane);
+                uint8_t *staged = staged_keys + (wave * RG + i) * kStagedKeyBytes;
+                staged[lane] = (uint8_t)mk.byte;
+                if ((lane & 15) == 0) staged[64 + (lane >> 4)] = (uint8_t)mk.scale;
+            }
+        }
+        __syncthreads();
+        rows.from_lds(step_lds, r0, seq, qlen, r0, r1, width, lane);
+    }
     kmax = group_max<64>(kmax);
     kmax = __builtin_amdgcn_readfirstlane(kmax);
     const int64_t kext = kmax < width ? kmax : width;
@@ -380,7 +648,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     for (int g = 0; g < ngroups; ++g) {
         const int64_t first = r0 + (int64_t)g * RG;
         if (g > 0) {
-            rows.load(q, q_row_stride, w, w_row_stride, row_ends, first, r1, width, l16, grp);
+            if constexpr (!FUSED)  // a fused launch has a single row group
+                rows.load(q, q_row_stride, w, w_row_stride, row_ends, first, r1, width, l16, grp);
 #pragma unroll
             for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, run), off);
         }
@@ -389,6 +658,17 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
             __syncthreads();  // the previous group's histograms are written out
             for (int i = threadIdx.x; i < RG * (kBins / 2); i += 256) hist[i] = 0;
             __syncthreads();
+        }
+        if constexpr (FUSED) {  // the page of new keys (a fused launch has one row group)
+            if (own_pp >= 0) {
+#pragma unroll
+                for (int i = 0; i < RG; ++i)
+                    if ((own_mask >> i) & 1u)
+                        patch_key(own_pg, staged_keys + (wave * RG + i) * kStagedKeyBytes,
+                                  own_o[i], l16, grp);
+                rows.score(own_pg, (int)(block_of(own_pp) * kPageTokens), count, logits, first,
+                           logits_row_stride, lane, grp, HIST ? hist : nullptr);
+            }
         }
         for (int base = 0; base < run; base += NB) {
 #pragma unroll
@@ -399,7 +679,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 asm volatile("" ::: "memory");
                 const int p = base + slot;
                 load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
-                if (p < run && table_page(p) >= 0)
+                if (p < run && table_page(p) >= 0 && (!FUSED || p != own_pp))
                     rows.score(buf[slot], (int)(block_of(p) * kPageTokens), count, logits,
                                first, logits_row_stride, lane, grp, HIST ? hist : nullptr);
             }
@@ -473,21 +753,22 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
     return g;
 }
 
-template <int FMT, int H, int RG, bool HIST>
-static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream) {
+template <int FMT, int H, int RG, bool HIST, bool FUSED = false>
+static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream,
+                                  const FusedInputs &fin = FusedInputs{}) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
     // page buffers per wavefront: 3 for MXFP4 (measured best of 2-6 on the long-context
     // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
     // take the registers a deeper ring would need)
     constexpr int NB = FMT == kFmtMxfp4 ? 3 : 2;
-    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST>), grid, block, 0, stream,
+    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST, FUSED>), grid, block, 0, stream,
                        a.block_table, a.query_starts, a.max_blocks, a.num_requests,
                        geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,
                        a.num_pages, geo.chunks, static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
-                       ws.coarse);
+                       ws.coarse, fin);
     return hipGetLastError();
 }
 
@@ -531,6 +812,29 @@ hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStrea
         case kFmtMxfp4: return launch_score_fmt<kFmtMxfp4, true>(a, ws, stream);
         case kFmtFp8: return launch_score_fmt<kFmtFp8, true>(a, ws, stream);
         default: return launch_score_fmt<kFmtFp8Mx, true>(a, ws, stream);
+    }
+}
+
+// The step's inputs and its scoring in one launch (MXFP4, histograms, one row group: at most
+// 4 rows per request).
+template <int H>
+static hipError_t launch_index_score_h(const ScoreArgs &a, const FusedInputs &fin,
+                                       const TopkWorkspace &ws, hipStream_t stream) {
+    if (a.max_query_len <= 1) return launch_score_rg<kFmtMxfp4, H, 1, true, true>(a, ws, stream, fin);
+    if (a.max_query_len <= 2) return launch_score_rg<kFmtMxfp4, H, 2, true, true>(a, ws, stream, fin);
+    return launch_score_rg<kFmtMxfp4, H, 4, true, true>(a, ws, stream, fin);
+}
+
+hipError_t launch_index_score_hist(const ScoreArgs &a, const FusedInputs &fin, void *workspace,
+                                   hipStream_t stream) {
+    if (a.fmt != kFmtMxfp4 || a.max_query_len < 1 || a.max_query_len > 4)
+        return hipErrorInvalidValue;
+    const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
+    const TopkWorkspace ws = carve(workspace, a.num_rows, geo.chunks);
+    switch (a.heads) {
+        case 16: return launch_index_score_h<16>(a, fin, ws, stream);
+        case 32: return launch_index_score_h<32>(a, fin, ws, stream);
+        default: return launch_index_score_h<64>(a, fin, ws, stream);
     }
 }
 

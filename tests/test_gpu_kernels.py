@@ -329,6 +329,114 @@ def test_score_topk_matches_separate_calls(name, k):
     assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), f"{name} k={k}")
 
 
+# ---- index_score_hist (step inputs made inside the scorer) ----------------------------------
+
+FUSED_CASES = {
+    "fp4_h32_ragged": SCORE_CASES["fp4_h32_ragged"],
+    "fp4_h16_verify": SCORE_CASES["fp4_h16_verify"],
+    "fp4_h64_merged": SCORE_CASES["fp4_h64_merged"],
+    "fp4_h32_scaled_heads": SCORE_CASES["fp4_h32_scaled_heads"],
+    # keys at the first positions, a request with no rows, keys that straddle a page boundary
+    # and end a page, padding rows, and a row whose keys start past its request's first chunk
+    "fp4_h64_edges": dict(fmt="mxfp4", heads=64, seq_lens=[2, 130, 4098, 64, 9000],
+                          query_lens=[2, 0, 4, 1, 3], num_rows=13),
+}
+
+
+def _step_projection(wl, key_col, weight_col, cols, rng):
+    """Packed projection rows of the step, one per query row: the row's new key and raw head
+    weights at the given columns, other columns (and padding rows) NaN / Inf / junk bits."""
+    proj = rng.choice(np.array([0x7FC0, 0xFF80, 0x7F80, 0x3F80], np.uint16), size=(wl.num_rows, cols))
+    sk = wl.step_key_index()
+    proj[:sk.size, key_col:key_col + 128] = wl.key_bits[sk]
+    proj[:, weight_col:weight_col + wl.heads] = wl.wv_bits
+    slots = np.full(wl.num_rows, -1, np.int64)
+    slots[:sk.size] = wl.key_slots[sk]
+    return proj, slots
+
+
+def _cache_without_step_keys(wl):
+    """A device cache holding every key but the step's (their slots keep the filler)."""
+    keep = np.ones(wl.total_keys, bool)
+    keep[wl.step_key_index()] = False
+    dw = DeviceWorkload(wl)
+    if keep.any():
+        dsa.store_keys(bf16_dev(wl.key_bits[keep]), dw.gamma, dw.beta, wl.eps,
+                       dev(wl.key_slots[keep]), dw.cache, wl.num_pages, wl.page_stride, wl.fmt,
+                       wl.section_offset)
+    return dw
+
+
+@pytest.mark.parametrize("name", list(FUSED_CASES))
+@pytest.mark.parametrize("k", [1, 700])
+def test_index_score_matches_oracle_and_separate_calls(name, k):
+    # the fused step against the oracle (cache bytes with the new keys, row layout, logits,
+    # top-k sets), and bit for bit against index_inputs_layout + score_paged_hist + topk_scored
+    wl = make_workload(name, topk=64, seed=17, extra_pages=3, **FUSED_CASES[name])
+    rng = np.random.default_rng(5)
+    key_col, weight_col, cols = 6, 140, 210
+    proj, slots = _step_projection(wl, key_col, weight_col, cols, rng)
+    ocache = oracle_cache(wl)
+    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+    os_, oe = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+    ref = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride,
+                             wl.block_table, os_, oe, wl.fmt, wl.section_offset)
+
+    a = _cache_without_step_keys(wl)
+    b = _cache_without_step_keys(wl)
+    pd = bf16_dev(proj)
+    la = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    wsa = torch.full((dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows),),
+                     0x5C, dtype=torch.uint8, device="cuda")
+    starts, ends, _, idx = dsa.index_score_topk(
+        pd, key_col, weight_col, a.q, a.gamma, a.beta, wl.eps, a.seq_lens, a.query_lens,
+        wl.num_rows, a.cache, wl.num_pages, wl.page_stride, a.block_table, wl.max_query_len, k,
+        wl.fmt, wl.section_offset, out=la, workspace=wsa)
+    assert np.array_equal(a.cache.cpu().numpy(), ocache), f"{name}: cache bytes"
+    assert np.array_equal(starts.cpu().numpy(), os_) and np.array_equal(ends.cpu().numpy(), oe)
+    got = la.cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{name}: written entries"
+    assert_logits_close(got, ref, oe, range(wl.num_rows), name)
+    want = oracle.topk(np.nan_to_num(got, nan=0.0), oe, k)
+    assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), f"{name} k={k}")
+
+    qb, wb, sb, eb = dsa.index_inputs_layout(pd, key_col, weight_col, b.q, b.gamma, b.beta, wl.eps,
+                                             dev(slots), b.cache, wl.num_pages, wl.page_stride,
+                                             b.seq_lens, b.query_lens, wl.num_rows, wl.fmt,
+                                             wl.section_offset)
+    lb = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, idx_b = dsa.score_topk(qb, wl.heads, wb, b.cache, wl.num_pages, wl.page_stride,
+                              b.block_table, sb, eb, wl.max_query_len, k, wl.fmt,
+                              wl.section_offset, out=lb)
+    assert torch.equal(a.cache, b.cache)
+    assert np.array_equal(got.view(np.uint32), lb.cpu().numpy().view(np.uint32)), f"{name}: logits bits"
+    assert_topk_sets(idx.cpu().numpy(), idx_b.cpu().numpy(), range(wl.num_rows), f"{name} k={k}")
+
+
+def test_index_score_degenerate_sizes():
+    # no pages or no blocks: only the row layout is written; more than 4 rows per request and
+    # other formats are refused
+    rng = np.random.default_rng(9)
+    seq = np.array([5, 70], np.int32)
+    ql = np.array([1, 2], np.int32)
+    q = bf16_dev(bf16_bits(rng.standard_normal((4, 16, 128)).astype(np.float32)))
+    pd = bf16_dev(bf16_bits(rng.standard_normal((4, 200)).astype(np.float32)))
+    g, b = dev(np.ones(128, np.float32)), dev(np.zeros(128, np.float32))
+    cache = torch.full((4352,), 0x33, dtype=torch.uint8, device="cuda")
+    bt = dev(np.zeros((2, 2), np.int32))
+    os_, oe = oracle.decode_layout(seq, ql, 4)
+    s, e, _, _ = dsa.index_score_topk(pd, 0, 130, q, g, b, 1e-6, dev(seq), dev(ql), 4, cache, 0,
+                                      4352, bt, 2, 8)
+    assert np.array_equal(s.cpu().numpy(), os_) and np.array_equal(e.cpu().numpy(), oe)
+    assert torch.all(cache == 0x33)
+    with pytest.raises(RuntimeError):
+        dsa.index_score_topk(pd, 0, 130, q, g, b, 1e-6, dev(seq), dev(ql), 4, cache, 1, 4352, bt,
+                             5, 8)
+    with pytest.raises(RuntimeError):
+        dsa.index_score_topk(pd, 0, 130, q, g, b, 1e-6, dev(seq), dev(ql), 4, cache, 1, 8448, bt,
+                             2, 8, "fp8")
+
+
 def test_score_paged_placement_invariance_and_determinism():
     outs = []
     for permute, stride, offset in [(True, 4352, 0), (False, 4352, 0), (True, 8192, 3840)]:
