@@ -1,7 +1,10 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration bench.py times:
 the whole cache, every quantized query byte and every row bound bit-exact; logits of
 sampled rows within 1e-5 * max |logit| of the oracle; top-k sets equal on identical
-(oracle) logits; and end-to-end top-k differing only by boundary swaps within tolerance."""
+(oracle) logits; end-to-end top-k differing only by boundary swaps within tolerance; and
+the step bench.py times (the inputs made inside the scorer where that path applies), run
+from a cache without the step's keys, giving the same cache bytes, row layout and logits
+bit for bit, and the oracle's top-k sets of those logits."""
 import gc
 import sys
 
@@ -11,7 +14,8 @@ import torch
 
 import oracle
 import sparse_attention_indexer_quant_amd as dsa
-from gpu_util import DeviceWorkload, assert_logits_close, assert_topk_sets, bf16_host, dev, oracle_cache
+from gpu_util import (DeviceWorkload, assert_logits_close, assert_topk_sets, bf16_dev, bf16_host, dev,
+                      oracle_cache)
 from sparse_attention_indexer_quant_amd.workloads import CONFIG_NAMES, config
 
 pytestmark = pytest.mark.gpu
@@ -112,3 +116,53 @@ def test_topk_end_to_end_boundary_swaps_only(run):
             kth = np.sort(ref[i, :n])[::-1][min(wl.topk, n) - 1]
             assert np.all(diff >= 0) and np.all(np.abs(ref[i, diff] - kth) <= 2 * tol), run["name"]
     print(f"[config {run['name']}] end-to-end top-k boundary swaps: {swaps}", file=sys.stderr)
+
+
+def test_bench_step_path(run):
+    # MXFP4 with at most 4 rows per request: index_score_hist + topk_scored; otherwise
+    # index_inputs_layout + score_paged_hist + topk_scored. Packed projection rows
+    # [key 128 | head weights H] per query row, as bench.py builds them.
+    wl = run["wl"]
+    sk = wl.step_key_index()
+    proj = np.zeros((wl.num_rows, 128 + wl.heads), np.uint16)
+    proj[:sk.size, :128] = wl.key_bits[sk]
+    proj[:, 128:] = wl.wv_bits
+    slots = np.full(wl.num_rows, -1, np.int64)
+    slots[:sk.size] = wl.key_slots[sk]
+    keep = np.ones(wl.total_keys, bool)
+    keep[sk] = False
+    b = DeviceWorkload(wl)
+    chunk = 1 << 21
+    rest = np.flatnonzero(keep)
+    for s in range(0, rest.size, chunk):
+        part = rest[s:s + chunk]
+        dsa.store_keys(bf16_dev(wl.key_bits[part]), b.gamma, b.beta, wl.eps, dev(wl.key_slots[part]),
+                       b.cache, wl.num_pages, wl.page_stride, wl.fmt, wl.section_offset)
+    pd = bf16_dev(proj)
+    inline = wl.fmt == "mxfp4" and wl.max_query_len <= 4
+    if inline:
+        starts, ends, logits, idx = dsa.index_score_topk(
+            pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens, wl.num_rows,
+            b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, wl.topk,
+            wl.fmt, wl.section_offset)
+    else:
+        q_rows, w, starts, ends = dsa.index_inputs_layout(
+            pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, dev(slots), b.cache, wl.num_pages,
+            wl.page_stride, b.seq_lens, b.query_lens, wl.num_rows, wl.fmt, wl.section_offset)
+        logits, idx = dsa.score_topk(q_rows, wl.heads, w, b.cache, wl.num_pages, wl.page_stride,
+                                     b.block_table, starts, ends, wl.max_query_len, wl.topk,
+                                     wl.fmt, wl.section_offset)
+    torch.cuda.synchronize()
+    print(f"[config {run['name']}] bench step path ({'inline inputs' if inline else 'separate inputs'})",
+          flush=True)
+    assert torch.equal(b.cache, run["dw"].cache), f"{run['name']}: cache bytes"
+    assert np.array_equal(starts.cpu().numpy(), run["os"]) and np.array_equal(ends.cpu().numpy(), run["oe"])
+    cols = torch.arange(wl.width, device=logits.device)
+    valid = cols[None, :] < ends.to(torch.int64)[:, None]
+    assert torch.equal(logits.view(torch.int32)[valid], run["logits"].view(torch.int32)[valid]), \
+        f"{run['name']}: logits bits"
+    rows = run["rows"]
+    lg = np.nan_to_num(logits[rows].cpu().numpy(), nan=0.0)
+    want = oracle.topk(lg, run["oe"][rows].astype(np.int32), wl.topk)
+    assert_topk_sets(idx[rows].cpu().numpy(), want, range(len(rows)), run["name"])
+    del b, logits, idx, valid
