@@ -373,6 +373,58 @@ def kernel_times(s: Setup, reps: int = 30):
     return out
 
 
+def read_reference(s: Setup, reps: int = 24, warmup: int = 4):
+    """HIP-event times of read_sections (a plain read of the same key sections in the scorer's
+    grid, no arithmetic) over the rotating replicas: with the workload's page table and
+    stride, and with the same pages laid out contiguously (page stride = section)."""
+    import torch
+    import sparse_attention_indexer_quant_amd as dsa
+    wl = s.wl
+    lib = dsa.library()
+    fmt = dsa._FORMATS[wl.fmt]
+    dev = s.block_table.device
+    words = int(lib.dsaidx_read_sections_words(wl.num_requests, wl.max_blocks))
+    out = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
+    # the same pages, consecutive: request q's blocks get the next ceil(seq_q / 64) page ids
+    nblk = np.minimum((np.maximum(wl.seq_lens.astype(np.int64), 0) + 63) // 64, wl.max_blocks)
+    bt_c = np.full((wl.num_requests, wl.max_blocks), -1, np.int32)
+    nxt = 0
+    for q in range(wl.num_requests):
+        bt_c[q, :nblk[q]] = np.arange(nxt, nxt + nblk[q], dtype=np.int32)
+        nxt += int(nblk[q])
+    bt_contig = torch.from_numpy(bt_c).to(dev)
+    sp = s.stream.cuda_stream
+    key_bytes = int(nblk.sum()) * wl.section_bytes
+
+    def timed(paged):
+        calls = []
+        for c in s.caches:
+            if paged:
+                args = (fmt, c.data_ptr() + wl.section_offset, wl.num_pages, wl.page_stride,
+                        s.block_table.data_ptr())
+            else:
+                args = (fmt, c.data_ptr(), nxt, wl.section_bytes, bt_contig.data_ptr())
+            calls.append(Prepared(lib.dsaidx_read_sections, *args, wl.num_requests,
+                                  wl.max_blocks, s.seq_lens.data_ptr(), out.data_ptr(),
+                                  out.numel(), sp))
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        ts = []
+        for i in range(reps):
+            a, b = TimingEvent(), TimingEvent()
+            a.record(s.stream)
+            calls[i % len(calls)]()
+            b.record(s.stream)
+            ts.append(a.elapsed_time(b) * 1e3)
+        torch.cuda.synchronize()
+        return float(np.mean(ts))
+
+    paged_us, contig_us = timed(True), timed(False)
+    return {"kernel": "read_sections", "key_bytes": key_bytes,
+            "paged_us_mean": paged_us, "paged_GBps": key_bytes / paged_us / 1e3,
+            "contiguous_us_mean": contig_us, "contiguous_GBps": key_bytes / contig_us / 1e3}
+
+
 def cpu_baseline(s: Setup, budget_s: float):
     """The oracle, untuned, on the host cores: score + top-k of a bounded sample of rows
     (plus the step's query quantization and key inserts), scaled to pairs/s."""
@@ -500,6 +552,10 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "cache_replicas": len(s.caches),
         "kernel_us_alone": {k: v * 1e3 for k, v in kernel_times(s).items()},
     }
+    ref = read_reference(s)
+    # the scoring launch's time over a plain read of its key sections in the same grid
+    ref["score_time_over_paged_read"] = score_us / ref["paged_us_mean"]
+    res["read_reference"] = ref
     res["score_key_frac_of_peak"] = res["score_key_GBps"] / HBM_PEAK_GBPS
     if cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(s, cpu_budget)
@@ -571,7 +627,9 @@ def main():
                      "kernel": m["score_kernel"],
                      "bytes_per_launch": m["score_algorithmic_bytes"],
                      "launch_us_mean": m["score_us_mean"],
-                     "launches_timed": m["score_launches_timed"]},
+                     "launches_timed": m["score_launches_timed"],
+                     "read_reference_GBps": m["read_reference"]["paged_GBps"],
+                     "read_reference_contiguous_GBps": m["read_reference"]["contiguous_GBps"]},
         "cpu_baseline": m.get("cpu_baseline"),
         "per_config": per_config,
     }

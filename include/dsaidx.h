@@ -248,6 +248,29 @@ size_t dsaidx_score_topk_workspace_bytes(int64_t num_requests, int64_t max_block
 int64_t dsaidx_score_segment_keys(int64_t num_requests, int64_t max_blocks);
 
 /*
+ * read_sections -- a bandwidth reference for dsaidx_score_paged, not a step of the indexer
+ * path: a plain read of exactly the cache bytes score_paged reads -- for every request q and
+ * block b < ceil(seq_lens[q] / 64) (at most max_blocks), the section (4352 B MXFP4, 8448 B FP8)
+ * of page block_table[q, b] at cache + page * page_stride; entries outside [0, num_pages) are
+ * skipped -- in score_paged's grid and with its per-lane loads, but no arithmetic. Each
+ * wavefront writes the XOR of the 32-bit words it read; the XOR of all of out[0..words) is
+ * the XOR of every word of every section read (each once).
+ *
+ *  cache, num_pages, page_stride, block_table, num_requests, max_blocks  as dsaidx_score_paged.
+ *  seq_lens   device, int32 [num_requests]: keys per request (negative counts as 0).
+ *  out        device, uint32 [out_words], out_words >= dsaidx_read_sections_words(
+ *             num_requests, max_blocks) (that many words are written, on the current device).
+ *  Errors: as dsaidx_score_paged for the shared arguments; a short `out` gives DSAIDX_EINVAL.
+ *  num_requests, max_blocks or num_pages == 0 enqueues nothing.
+ */
+int64_t dsaidx_read_sections_words(int64_t num_requests, int64_t max_blocks);
+dsaidx_status dsaidx_read_sections(int fmt, const void *cache, int64_t num_pages,
+                                   int64_t page_stride, const int32_t *block_table,
+                                   int64_t num_requests, int64_t max_blocks,
+                                   const int32_t *seq_lens, uint32_t *out, int64_t out_words,
+                                   void *stream);
+
+/*
  * score_paged_hist -- dsaidx_score_paged plus the top-k segment histograms.
  *  All arguments as dsaidx_score_paged, and
  *  workspace  device, >= dsaidx_score_topk_workspace_bytes(num_requests, max_blocks,

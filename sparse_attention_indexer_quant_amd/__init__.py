@@ -69,6 +69,8 @@ def library():
             "dsaidx_topk_workspace_bytes": (SZ, [I64, I64, I32]),
             "dsaidx_score_topk_workspace_bytes": (SZ, [I64, I64, I64]),
             "dsaidx_score_segment_keys": (I64, [I64, I64]),
+            "dsaidx_read_sections_words": (I64, [I64, I64]),
+            "dsaidx_read_sections": (I32, [I32, P, I64, I64, P, I64, I64, P, P, I64, P]),
             "dsaidx_score_paged_hist": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
                                               P, P, I64, I32, P, I64, P, SZ, P]),
             "dsaidx_index_score_hist": (I32, [I32, P, I64, I64, I64, P, I32, I64, I64, P, P, F32,
@@ -303,6 +305,31 @@ def score_topk_workspace_bytes(num_requests, max_blocks, num_rows) -> int:
 def score_segment_keys(num_requests, max_blocks) -> int:
     """Keys per top-k histogram segment (one scoring workgroup's keys) for these sizes."""
     return int(library().dsaidx_score_segment_keys(int(num_requests), int(max_blocks)))
+
+
+def read_sections(cache, num_pages, page_stride, block_table, seq_lens, fmt="mxfp4",
+                  section_offset=0, out=None):
+    """A plain read of the cache sections score_paged reads (a bandwidth reference, not a step
+    of the path). Returns uint32 [words]: one XOR word per wavefront; their XOR is the XOR of
+    every 32-bit word of every section read."""
+    import torch
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [num_requests, max_blocks] tensor")
+    nreq, max_blocks = block_table.shape
+    if seq_lens.shape != (nreq,):
+        raise ValueError("seq_lens must be [num_requests]")
+    lib = library()
+    words = int(lib.dsaidx_read_sections_words(int(nreq), int(max_blocks)))
+    if out is None:
+        out = torch.zeros(max(words, 1), dtype=torch.int32, device=cache.device)
+    _check("read_sections", lib.dsaidx_read_sections(
+        _fmt(fmt), cache.data_ptr() + section_offset, num_pages, page_stride,
+        block_table.data_ptr(), nreq, max_blocks, seq_lens.data_ptr(), out.data_ptr(),
+        out.numel(), _stream(cache)))
+    return out
 
 
 def score_topk(q_rows, heads, weights, cache, num_pages, page_stride, block_table, query_starts,

@@ -274,6 +274,31 @@ int64_t dsaidx_score_segment_keys(int64_t num_requests, int64_t max_blocks) {
     return dsaidx::score_geometry(num_requests, max_blocks).segment_keys;
 }
 
+int64_t dsaidx_read_sections_words(int64_t num_requests, int64_t max_blocks) {
+    if (num_requests < 1 || max_blocks < 1 || max_blocks > (int64_t)INT32_MAX / 64) return 0;
+    return dsaidx::read_sections_words(num_requests, max_blocks);
+}
+
+dsaidx_status dsaidx_read_sections(int fmt, const void *cache, int64_t num_pages,
+                                   int64_t page_stride, const int32_t *block_table,
+                                   int64_t num_requests, int64_t max_blocks,
+                                   const int32_t *seq_lens, uint32_t *out, int64_t out_words,
+                                   void *stream) {
+    if (!valid_fmt(fmt) || num_requests < 0 || max_blocks < 0 || num_pages < 0 || out_words < 0)
+        return DSAIDX_EINVAL;
+    if (num_requests == 0 || max_blocks == 0 || num_pages == 0) return DSAIDX_OK;
+    if (!cache || !block_table || !seq_lens || !out) return DSAIDX_EINVAL;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16) ||
+        !aligned(out, 4) || max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS)
+        return DSAIDX_ELAYOUT;
+    const int64_t words = dsaidx::read_sections_words(num_requests, max_blocks);
+    if (words / dsaidx::kScoreWaves > kMaxGrid) return DSAIDX_EUNSUPPORTED;
+    if (out_words < words) return DSAIDX_EINVAL;
+    return hip_status(dsaidx::launch_read_sections(fmt, cache, num_pages, page_stride, block_table,
+                                                   num_requests, max_blocks, seq_lens, out,
+                                                   as_stream(stream)));
+}
+
 dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stride,
                                       int32_t heads, const void *w, int64_t w_row_stride,
                                       const void *cache, int64_t num_pages, int64_t page_stride,

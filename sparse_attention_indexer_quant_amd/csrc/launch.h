@@ -80,6 +80,7 @@ hipError_t launch_index_score_hist(const ScoreArgs &args, const FusedInputs &fin
 // How score_paged splits a request's pages: pages per wavefront, workgroups ("chunks") per
 // request, and the keys one workgroup covers (the top-k segment when the scorer writes the
 // selection's histograms). Depends on the current device's compute-unit count.
+constexpr int kScoreWaves = 4;  // wavefronts per scoring workgroup
 struct ScoreGeometry {
     int pages_per_wave;
     int64_t chunks;
@@ -102,6 +103,14 @@ hipError_t launch_dcp_merge(const float *values, const int32_t *positions, int w
                             int64_t rows, int kc, int k, int32_t *merged,
                             int64_t merged_row_stride, int rank, int interleave,
                             int32_t *local_slots, int64_t local_row_stride, hipStream_t stream);
+
+// A plain read of the sections score_paged reads, in its grid (a bandwidth reference): one
+// XOR word per wavefront into `out` (read_sections_words words).
+int64_t read_sections_words(int64_t num_requests, int64_t max_blocks);
+hipError_t launch_read_sections(int fmt, const void *cache, int64_t num_pages, int64_t page_stride,
+                                const int32_t *block_table, int64_t num_requests,
+                                int64_t max_blocks, const int32_t *seq_lens, uint32_t *out,
+                                hipStream_t stream);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int k);
 hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64_t width,

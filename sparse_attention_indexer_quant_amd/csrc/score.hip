@@ -37,8 +37,6 @@
 // "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex; page
 // "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_layout): the MXFP4 query operands, the
 // head weights, the new keys' LayerNorm, quantization and insert, and the row layout.
-#include <type_traits>
-
 #include "device_common.h"
 #include "key_norm.h"
 #include "launch.h"
@@ -49,15 +47,39 @@ namespace dsaidx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kScoreWaves;
 constexpr int kMaxPagesPerWave = 16;
 
+// A's scale is byte 0 of `sa`; B's is byte T of `sb` (T = the key tile: the page's scale
+// dword holds one byte per tile, see tile_scales)
+template <int T>
 __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, int sa, int sb) {
     const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
     const v8i vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    // format selectors 4 = E2M1 for both operands; byte 0 of each scale register
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, zero, 4, 4, 0, sa, 0, sb);
+    // format selectors 4 = E2M1 for both operands
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, zero, 4, 4, 0, sa, T, sb);
+}
+
+__device__ __forceinline__ v4f mfma_fp4_tile(const uint4 &a, const uint4 &b, int sa, int sb, int t) {
+    switch (t) {  // t is a constant after unrolling
+        case 0: return mfma_fp4<0>(a, b, sa, sb);
+        case 1: return mfma_fp4<1>(a, b, sa, sb);
+        case 2: return mfma_fp4<2>(a, b, sa, sb);
+        default: return mfma_fp4<3>(a, b, sa, sb);
+    }
+}
+
+// A page's 256 UE8M0 bytes are loaded as one dword per lane: lane L holds the four block
+// scales of token L. The MFMA wants, in lane (l16, grp) for tile t, the scale of token
+// 16 t + l16, block grp: byte grp of lane (t, l16). That is a 4 x 4 byte transpose over the
+// four lane rows, done as two exchanges: rows r and r ^ 2 swap 16-bit halves, then rows r
+// and r ^ 1 swap bytes. `sel32` / `sel16` are the lane's byte selectors of the two steps.
+__device__ __forceinline__ uint32_t tile_scales(uint32_t raw, uint32_t sel32, uint32_t sel16) {
+    const auto a = __builtin_amdgcn_permlane32_swap(raw, raw, false, false);
+    const uint32_t y = __builtin_amdgcn_perm(a[1], a[0], sel32);
+    const auto b = __builtin_amdgcn_permlane16_swap(y, y, false, false);
+    return __builtin_amdgcn_perm(b[1], b[0], sel16);
 }
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -132,9 +154,9 @@ __device__ __forceinline__ float head_sum_to_token(float p0, float p1, float p2,
 template <int FMT>
 struct PageRegs {
     uint4 kp[4][FMT == kFmtMxfp4 ? 1 : 2];
-    // MXFP4: the byte as loaded (a 32-bit copy would be masked where it is made, which waits
-    // for the load there); FP8: the token's 32-bit scale
-    typename std::conditional<FMT == kFmtMxfp4, uint8_t, uint32_t>::type ks[4];
+    // MXFP4: the four block scales of token `lane` (as loaded; tile_scales rearranges them);
+    // FP8: per tile, the token's 32-bit scale
+    uint32_t ks[FMT == kFmtMxfp4 ? 1 : 4];
 };
 
 // Loads one page section into registers. The caller always issues the loads (a page that
@@ -148,7 +170,7 @@ struct LaneOffsets {
     uint32_t scale;  // the lane's scale byte (MXFP4) or its token's FP32 scale (FP8)
     __device__ __forceinline__ LaneOffsets(uint32_t l16, uint32_t grp)
         : key(FMT == kFmtMxfp4 ? l16 * 64u + grp * 16u : l16 * 128u + grp * 32u),
-          scale(FMT == kFmtMxfp4 ? 4096u + l16 * 4u + grp : 8192u + l16 * 4u) {}
+          scale(FMT == kFmtMxfp4 ? 4096u + (grp * 16u + l16) * 4u : 8192u + l16 * 4u) {}
 };
 
 template <int FMT>
@@ -159,8 +181,8 @@ __device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec,
         if constexpr (FMT == kFmtMxfp4) {
             const uint8_t *tile = sec + t * 1024u;         // 16 tokens x 64 B
             pg.kp[t][0] = *reinterpret_cast<const uint4 *>(tile + off.key);
-            // the lane's own UE8M0 byte (its token, its 32-value block), used as loaded
-            pg.ks[t] = (sec + t * 64u)[off.scale];
+            // token `lane`'s four UE8M0 bytes (one load for the page's 256 scale bytes)
+            if (t == 0) pg.ks[0] = *reinterpret_cast<const uint32_t *>(sec + off.scale);
         } else {
             const uint8_t *tile = sec + t * 2048u;         // 16 tokens x 128 B
             pg.kp[t][0] = *reinterpret_cast<const uint4 *>(tile + off.key);
@@ -231,21 +253,28 @@ struct RowGroup {
     }
 
     // Logits of one page for the group's rows. Rows past `count` are not computed: row 0, then
-    // row 1 if present, then rows 2..RG-1 if any is present (one uniform branch each).
+    // rows 1, 2 and 3 each only if present (one uniform branch each).
     __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
                                           float *logits, int64_t first_row,
                                           int64_t logits_row_stride, int lane, int grp,
-                                          uint32_t *hist) const {
-        score_rows<0, 1>(pg, kbase, count, logits, first_row, logits_row_stride, lane, grp, hist);
+                                          uint32_t *hist, uint32_t sel32, uint32_t sel16) const {
+        const uint32_t ksw = FMT == kFmtMxfp4 ? tile_scales(pg.ks[0], sel32, sel16) : 0u;
+        score_rows<0, 1>(pg, ksw, kbase, count, logits, first_row, logits_row_stride, lane, grp,
+                         hist);
         if constexpr (RG > 1) {
             if (count > 1)
-                score_rows<1, 2>(pg, kbase, count, logits, first_row, logits_row_stride, lane,
-                                 grp, hist);
+                score_rows<1, 2>(pg, ksw, kbase, count, logits, first_row, logits_row_stride,
+                                 lane, grp, hist);
         }
         if constexpr (RG > 2) {
             if (count > 2)
-                score_rows<2, RG>(pg, kbase, count, logits, first_row, logits_row_stride, lane,
-                                  grp, hist);
+                score_rows<2, 3>(pg, ksw, kbase, count, logits, first_row, logits_row_stride,
+                                 lane, grp, hist);
+        }
+        if constexpr (RG > 3) {
+            if (count > 3)
+                score_rows<3, RG>(pg, ksw, kbase, count, logits, first_row, logits_row_stride,
+                                  lane, grp, hist);
         }
     }
 
@@ -253,7 +282,8 @@ struct RowGroup {
     // back into separate results before any is read, so the matrix unit pipelines them instead
     // of waiting on each result in turn.
     template <int J0, int J1>
-    __device__ __forceinline__ void score_rows(const PageRegs<FMT> &pg, int kbase, int count,
+    __device__ __forceinline__ void score_rows(const PageRegs<FMT> &pg, uint32_t ksw, int kbase,
+                                               int count,
                                                float *logits, int64_t first_row,
                                                int64_t logits_row_stride, int lane, int grp,
                                                uint32_t *hist) const {
@@ -268,7 +298,7 @@ struct RowGroup {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
                     if constexpr (FMT == kFmtMxfp4)
-                        c[j][ht] = mfma_fp4(qa[j][ht][0], pg.kp[t][0], qs[j][ht], (int)pg.ks[t]);
+                        c[j][ht] = mfma_fp4_tile(qa[j][ht][0], pg.kp[t][0], qs[j][ht], (int)ksw, t);
                     else
                         c[j][ht] = mfma_bf16_head(qa[j][ht], kb);
                 }
@@ -385,8 +415,10 @@ struct StepQuery {
 __device__ __forceinline__ void patch_key(PageRegs<kFmtMxfp4> &pg, const uint8_t *staged, int o,
                                           int l16, int grp) {
     const uint4 v = *reinterpret_cast<const uint4 *>(staged + grp * 16);
-    const uint8_t sc = staged[64 + grp];
+    const uint32_t sc = *reinterpret_cast<const uint32_t *>(staged + 64);
     const bool mine = l16 == (o & 15);
+    const uint32_t ms = grp * 16 + l16 == o ? 0xFFFFFFFFu : 0u;  // lane o holds token o's scales
+    pg.ks[0] = (sc & ms) | (pg.ks[0] & ~ms);
     // bit masks in every tile: a branch or a select over the registers' values gets folded
     // into one access at a computed tile index or address, which puts them in scratch memory
 #pragma unroll
@@ -395,7 +427,6 @@ __device__ __forceinline__ void patch_key(PageRegs<kFmtMxfp4> &pg, const uint8_t
         uint4 &k = pg.kp[t][0];
         k = make_uint4((v.x & m) | (k.x & ~m), (v.y & m) | (k.y & ~m), (v.z & m) | (k.z & ~m),
                        (v.w & m) | (k.w & ~m));
-        pg.ks[t] = (uint8_t)((sc & m) | (pg.ks[t] & ~m));
     }
 }
 
@@ -465,6 +496,9 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
+    // byte selectors of tile_scales: rows 0-1 / 2-3, then even / odd rows
+    const uint32_t sel32 = lane < 32 ? 0x05040100u : 0x07060302u;
+    const uint32_t sel16 = (grp & 1) == 0 ? 0x06020400u : 0x07030501u;
     // Workgroup b takes chunk c = b / R of request (b + c) mod R (R requests; fewer than 2^31
     // workgroups, so 32-bit arithmetic). Workgroups go to the 8 XCDs in turn by index, b mod 8:
     // rotating the requests by one per chunk makes the chunks of one request visit the XCDs in
@@ -667,7 +701,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                         patch_key(own_pg, staged_keys + (wave * RG + i) * kStagedKeyBytes,
                                   own_o[i], l16, grp);
                 rows.score(own_pg, (int)(block_of(own_pp) * kPageTokens), count, logits, first,
-                           logits_row_stride, lane, grp, HIST ? hist : nullptr);
+                           logits_row_stride, lane, grp, HIST ? hist : nullptr, sel32, sel16);
             }
         }
         for (int base = 0; base < run; base += NB) {
@@ -681,7 +715,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
                 if (p < run && table_page(p) >= 0 && (!FUSED || p != own_pp))
                     rows.score(buf[slot], (int)(block_of(p) * kPageTokens), count, logits,
-                               first, logits_row_stride, lane, grp, HIST ? hist : nullptr);
+                               first, logits_row_stride, lane, grp, HIST ? hist : nullptr,
+                               sel32, sel16);
             }
         }
         if constexpr (HIST) {

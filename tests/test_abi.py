@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
               "dsaidx_decode_layout", "dsaidx_topk_workspace_bytes", "dsaidx_status_string",
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
-              "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys"):
+              "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys",
+              "dsaidx_read_sections", "dsaidx_read_sections_words"):
         assert n in names
 
 
@@ -246,6 +247,32 @@ def test_score_paged_hist_checks(lib):
         assert lib.dsaidx_score_segment_keys(24, 128) == 4 * 3 * 64
         assert lib.dsaidx_score_segment_keys(40, 128) == 4 * 8 * 64
         assert lib.dsaidx_score_segment_keys(64, 128) == 4 * 8 * 64
+
+
+def read_sections(lib, **kw):
+    a = dict(fmt=MX, cache=P, np_=8, ps=4352, bt=P, r=2, mb=4, seq=P, out=P, ow=1 << 20)
+    a.update(kw)
+    return lib.dsaidx_read_sections(a["fmt"], a["cache"], a["np_"], a["ps"], a["bt"], a["r"],
+                                    a["mb"], a["seq"], a["out"], a["ow"], None)
+
+
+def test_read_sections_checks(lib):
+    assert read_sections(lib, fmt=5) == EINVAL
+    assert read_sections(lib, r=-1) == EINVAL
+    assert read_sections(lib, ow=-1) == EINVAL
+    assert read_sections(lib, r=0, cache=None) == OK
+    assert read_sections(lib, np_=0, cache=None) == OK
+    assert read_sections(lib, seq=None) == EINVAL
+    assert read_sections(lib, ps=4350) == ELAYOUT
+    assert read_sections(lib, fmt=FP8, ps=4352) == ELAYOUT
+    assert read_sections(lib, cache=P + 8) == ELAYOUT
+    assert read_sections(lib, out=P + 2) == ELAYOUT
+    assert read_sections(lib, ow=1) == EINVAL  # shorter than one word per wavefront
+    # one word per wavefront of the scorer's grid: 4 per workgroup, chunks x requests workgroups
+    assert lib.dsaidx_read_sections_words(0, 4) == 0
+    assert lib.dsaidx_read_sections_words(2, 4) == 4 * 2 * 1
+    if not torch.cuda.is_available():
+        assert lib.dsaidx_read_sections_words(8, 2048) == 4 * 8 * 32
 
 
 def topk_scored(lib, **kw):
