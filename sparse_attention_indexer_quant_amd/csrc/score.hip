@@ -192,14 +192,41 @@ __device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec,
     }
 }
 
-// Query operands, head weights and key bounds of one group of RG rows.
-template <int FMT, int H, int RG>
+template <int H, int RG>
+struct StepQueryLds {
+    static constexpr int kTiles = RG * (H / 16);
+    uint4 qa[kTiles][64];
+    uint2 wt[kTiles][64];
+    int qs[kTiles][64];
+};
+
+// Query operands, head weights and key bounds of one group of RG rows. With OPS_IN_LDS (the
+// fused step inputs of four-row groups) the operands stay in the workgroup's LDS tiles and each
+// page reads them there: holding a four-row group in registers took the kernel to about 200
+// VGPRs, two wavefronts per SIMD, too few to hide the math's dependency chains.
+template <int FMT, int H, int RG, bool OPS_IN_LDS = false>
 struct RowGroup {
     static constexpr int HT = H / 16;
-    uint4 qa[RG][HT][FMT == kFmtMxfp4 ? 1 : 4];
-    int qs[RG][HT];
-    uint2 wt[RG][HT];  // 4 BF16 head weights, widened at use
+    static constexpr int RR = OPS_IN_LDS ? 1 : RG;  // rows held in registers
+    uint4 qa[RR][HT][FMT == kFmtMxfp4 ? 1 : 4];
+    int qs[RR][HT];
+    uint2 wt[RR][HT];  // 4 BF16 head weights, widened at use
+    const StepQueryLds<H, RG> *ops = nullptr;
+    int ops_lane = 0;
     int rend[RG];
+
+    __device__ __forceinline__ uint4 qa_at(int j, int ht) const {
+        if constexpr (OPS_IN_LDS) return ops->qa[j * HT + ht][ops_lane];
+        else return qa[j][ht][0];
+    }
+    __device__ __forceinline__ int qs_at(int j, int ht) const {
+        if constexpr (OPS_IN_LDS) return ops->qs[j * HT + ht][ops_lane];
+        else return qs[j][ht];
+    }
+    __device__ __forceinline__ uint2 wt_at(int j, int ht) const {
+        if constexpr (OPS_IN_LDS) return ops->wt[j * HT + ht][ops_lane];
+        else return wt[j][ht];
+    }
 
     __device__ __forceinline__ void load(const uint8_t *q, int64_t q_row_stride, const uint16_t *w,
                                          int64_t w_row_stride, const int32_t *row_ends,
@@ -237,17 +264,21 @@ struct RowGroup {
                                              int64_t first, int64_t last, int64_t width,
                                              int lane) {
         static_assert(FMT == kFmtMxfp4, "the step inputs are made in the scorer for MXFP4");
+        ops = &s;
+        ops_lane = lane;
 #pragma unroll
         for (int j = 0; j < RG; ++j) {
             const int64_t row = first + j;
             int64_t e = (int64_t)seq - qlen + (row - r0) + 1;
             e = e < 0 ? 0 : (e < width ? e : width);
             rend[j] = row < last ? (int)e : 0;
+            if constexpr (!OPS_IN_LDS) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                qa[j][ht][0] = s.qa[j * HT + ht][lane];
-                qs[j][ht] = s.qs[j * HT + ht][lane];
-                wt[j][ht] = s.wt[j * HT + ht][lane];
+                for (int ht = 0; ht < HT; ++ht) {
+                    qa[j][ht][0] = s.qa[j * HT + ht][lane];
+                    qs[j][ht] = s.qs[j * HT + ht][lane];
+                    wt[j][ht] = s.wt[j * HT + ht][lane];
+                }
             }
         }
     }
@@ -298,7 +329,7 @@ struct RowGroup {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
                     if constexpr (FMT == kFmtMxfp4)
-                        c[j][ht] = mfma_fp4_tile(qa[j][ht][0], pg.kp[t][0], qs[j][ht], (int)ksw, t);
+                        c[j][ht] = mfma_fp4_tile(qa_at(j, ht), pg.kp[t][0], qs_at(j, ht), (int)ksw, t);
                     else
                         c[j][ht] = mfma_bf16_head(qa[j][ht], kb);
                 }
@@ -307,7 +338,7 @@ struct RowGroup {
             for (int j = J0; j < J1; ++j) {
                 float acc = 0.f;
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) acc = relu_dot4(c[j][ht], wt[j][ht], acc);
+                for (int ht = 0; ht < HT; ++ht) acc = relu_dot4(c[j][ht], wt_at(j, ht), acc);
                 // the token's scale s_k > 0 (a power of two): FP32, or its UE8M0 exponent byte
                 if constexpr (FMT == kFmtFp8) acc *= __uint_as_float(pg.ks[t]);
                 if constexpr (FMT == kFmtFp8Mx) acc *= __uint_as_float((pg.ks[t] & 0xFFu) << 23);
@@ -337,14 +368,6 @@ struct RowGroup {
 // -- the UE8M0 exponent of the block's largest magnitude, then the E2M1 codes of the values
 // times 2^-e -- and rounds its four head weights times c_h to BF16. The tiles meet in the LDS
 // in the lane layout of RowGroup's registers.
-template <int H, int RG>
-struct StepQueryLds {
-    static constexpr int kTiles = RG * (H / 16);
-    uint4 qa[kTiles][64];
-    uint2 wt[kTiles][64];
-    int qs[kTiles][64];
-};
-
 template <int H, int RG>
 struct StepQuery {
     static constexpr int HT = H / 16, kTiles = RG * HT, kPer = (kTiles + kWaves - 1) / kWaves;
@@ -581,7 +604,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 
     // Query operands of the first row group, in flight together with the row bounds.
     const int ngroups = (nrows + RG - 1) / RG;
-    RowGroup<FMT, H, RG> rows;
+    RowGroup<FMT, H, RG, FUSED && RG == 4> rows;
     int kmax;
     // FUSED: the raw query tiles and head weights of this wavefront's share, and the step's
     // keys (one row each; a key past the rows reads the first row's)
