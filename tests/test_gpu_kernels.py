@@ -527,6 +527,25 @@ def test_topk_candidate_overflow_and_workspace_reuse():
         assert_topk_sets(got, want, range(3), f"k={k}")
 
 
+def test_topk_threshold_bin_sizes_in_the_last_workgroup():
+    # Segmented rows (40000 keys) whose threshold bin holds a few candidates, 3000 equal keys
+    # (ties go to the lower position) and 5000 distinct keys -- more than the row's last
+    # workgroup keeps in LDS, fewer than the candidate list holds -- twice on one workspace.
+    rng = np.random.default_rng(17)
+    n = 40000
+    lg = (0.1 * rng.random((3, n))).astype(np.float32)
+    lg[0] = rng.standard_normal(n).astype(np.float32)
+    lg[1, rng.choice(n, 3000, replace=False)] = 1.0
+    hot = rng.choice(n, 5000, replace=False)
+    lg[2, hot] = (1.0 + 0.12 * rng.random(5000)).astype(np.float32)  # one 12-bit bin: [1, 1.125)
+    ends = np.array([n, n - 17, n], np.int32)
+    ws = torch.full((dsa.topk_workspace_bytes(3, n, 2048),), 0x5A, dtype=torch.uint8, device="cuda")
+    for k in (2048, 1000, 2048):
+        want = oracle.topk(lg, ends, k)
+        got = dsa.topk(dev(lg), dev(ends), k, workspace=ws).cpu().numpy()
+        assert_topk_sets(got, want, range(3), f"k={k}")
+
+
 @pytest.mark.parametrize("rows,width,k", [(1, 3_000_000, 2048), (40, 300_000, 2048), (3, 70_000, 1)])
 def test_topk_wide_rows(rows, width, k):
     # hundreds of segments per row (733 for the 3M-key row); 40 rows double the segment
