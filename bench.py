@@ -364,7 +364,8 @@ def time_steps(s: Setup, steps: int, warmup: int, mode: str = "fused"):
 
 
 def kernel_times(s: Setup, reps: int = 30):
-    """Per-kernel HIP-event times (ms, median) of each stage launched alone."""
+    """Per-kernel HIP-event times (ms, median) of each stage launched on its own (repeated
+    back to back, not inside the step)."""
     import torch
     out = {}
     stages = [("index_inputs_layout", lambda i: s.inputs_layout[i % len(s.caches)]()),
@@ -379,14 +380,14 @@ def kernel_times(s: Setup, reps: int = 30):
     if s.inline_ok:
         stages.append(("index_score_hist", lambda i: s.index_score[i % len(s.caches)]()))
     for name, fn in stages:
-        ts = []
-        for i in range(reps):
-            a, b = TimingEvent(), TimingEvent()
+        # launched back to back, each between its own pair of events, read after the last
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
             a.record(s.stream)
             fn(i)
             b.record(s.stream)
-            ts.append(a.elapsed_time(b))
-        out[name] = float(np.median(ts))
+        torch.cuda.synchronize()
+        out[name] = float(np.median([a.elapsed_time(b) for a, b in evs]))
     return out
 
 
@@ -424,17 +425,18 @@ def read_reference(s: Setup, reps: int = 24, warmup: int = 4):
             calls.append(Prepared(lib.dsaidx_read_sections, *args, wl.num_requests,
                                   wl.max_blocks, s.seq_lens.data_ptr(), out.data_ptr(),
                                   out.numel(), sp))
+        # back to back with the events between them, read after the last launch (as the
+        # scorer's launches are timed inside the step loop): waiting on each pair would leave
+        # the GPU idle between launches
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         for i in range(warmup):
             calls[i % len(calls)]()
-        ts = []
-        for i in range(reps):
-            a, b = TimingEvent(), TimingEvent()
+        for i, (a, b) in enumerate(evs):
             a.record(s.stream)
             calls[i % len(calls)]()
             b.record(s.stream)
-            ts.append(a.elapsed_time(b) * 1e3)
         torch.cuda.synchronize()
-        return float(np.mean(ts))
+        return float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
 
     paged_us, contig_us = timed(True), timed(False)
     return {"kernel": "read_sections", "key_bytes": key_bytes,

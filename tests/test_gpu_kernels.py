@@ -127,6 +127,30 @@ def test_store_keys_bulk_layernorm_bit_exact(fmt):
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:4]}"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "fp8_mx"])
+@pytest.mark.parametrize("lead,width", [(2, 130), (8, 136), (0, 132)])
+def test_store_keys_strided_rows_bit_exact(fmt, lead, width):
+    # Key rows that are not 16-byte rows (a 4-byte-aligned start, a row stride that is not a
+    # multiple of 8 elements) take the one-wavefront-per-key kernel; 16-byte rows with a
+    # stride of 136 take the sixteen-lanes-per-key one. Both write the oracle's bytes.
+    rng = np.random.default_rng(23)
+    T = 3000
+    wide = bf16_bits((rng.standard_normal((T, width)) * 3 + 0.5).astype(np.float32))
+    keys = wide[:, lead:lead + 128]
+    pages = (T + 63) // 64 + 1
+    section = 4352 if fmt == "mxfp4" else 8448
+    slots = rng.permutation(pages * 64)[:T].astype(np.int64)
+    slots[::7] = -1
+    gamma = bf16_to_f32(bf16_bits(1 + 0.1 * rng.standard_normal(128).astype(np.float32)))
+    beta = bf16_to_f32(bf16_bits(0.1 * rng.standard_normal(128).astype(np.float32)))
+    want = np.full(pages * section, 0x3C, np.uint8)
+    oracle.store_keys(np.ascontiguousarray(keys), gamma, beta, 1e-6, slots, want, pages, section, 0, fmt)
+    got = torch.full((pages * section,), 0x3C, dtype=torch.uint8, device="cuda")
+    kdev = bf16_dev(wide)[:, lead:lead + 128]
+    dsa.store_keys(kdev, dev(gamma), dev(beta), 1e-6, dev(slots), got, pages, section, fmt)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 def test_store_keys_empty_and_all_padding():
     cache = torch.full((4352,), 0x5A, dtype=torch.uint8, device="cuda")
     g = torch.ones(128, device="cuda")
