@@ -177,15 +177,18 @@ class Setup:
         self.caches = [cache0] + [cache0.clone() for _ in range(reps - 1)]
         # bulk fill (store_keys of every key of the workload, timed): the same keys into the
         # same slots of replica 1 leave its bytes as they are
-        a, b = TimingEvent(), TimingEvent()
-        a.record(self.stream)
-        for keys, slots in fill:
-            dsa.store_keys(keys, self.gamma, self.beta, wl.eps, slots, self.caches[1],
-                           wl.num_pages, wl.page_stride, wl.fmt, wl.section_offset)
-        b.record(self.stream)
-        fill_us = a.elapsed_time(b) * 1e3
+        fills = [(TimingEvent(), TimingEvent()) for _ in range(4)]
+        for a, b in fills:  # back to back, read after the last
+            a.record(self.stream)
+            for keys, slots in fill:
+                dsa.store_keys(keys, self.gamma, self.beta, wl.eps, slots, self.caches[1],
+                               wl.num_pages, wl.page_stride, wl.fmt, wl.section_offset)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        fill_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in fills[1:]]))
         fill_bytes = wl.total_keys * (256 + 8 + wl.section_bytes // 64)
-        self.bulk_fill = {"keys": int(wl.total_keys), "launches": len(fill), "us": fill_us,
+        self.bulk_fill = {"keys": int(wl.total_keys), "launches": len(fill), "fills_timed": 3,
+                          "us": fill_us,
                           "algorithmic_bytes": int(fill_bytes),
                           "GBps": fill_bytes / fill_us / 1e3}
         del fill

@@ -177,91 +177,141 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
                    num_pages, page_stride, lane);
 }
 
-// Many keys (a cache fill): 16 lanes per key, four keys per wavefront, eight columns per lane
-// from one 16-byte load. One key per wavefront spends most of its instructions on work done
-// once per key (the sums' exchanges, the square root and division, the scale), with 64 lanes
-// for 128 values; here that work serves four keys at once. The LayerNorm sums follow the same
-// pairwise tree as layer_norm_pair -- adjacent pairs, then folds 32, 16, 8, 4, 2, 1 apart over
-// the 64 pair sums -- with pair sum 4 l + m in slot m of lane l: the folds 32 .. 4 apart pair
-// lanes l ^ 8, 4, 2, 1 (same slot) and the folds 2 and 1 pair slots inside the lane. Every
-// operation has the same two operands as there, so the bytes are the same.
-template <int FMT>
+// Many keys (a cache fill): LPK = 8 lanes per key, eight keys per wavefront, 16 columns per
+// lane from two 16-byte loads. One key per wavefront spends most of its instructions on work
+// done once per key (the sums' exchanges, the square root and division, the scale), with 64
+// lanes for 128 values; here that work serves eight keys at once. The LayerNorm sums follow the
+// same pairwise tree as layer_norm_pair -- adjacent pairs, then folds 32, 16, 8, 4, 2, 1 apart
+// over the 64 pair sums -- with pair sum S l + m in slot m of lane l (S = 64 / LPK slots): the
+// folds of 32 .. S apart pair lanes l ^ (LPK / 2) .. l ^ 1 (same slot), the smaller folds pair
+// slots inside the lane. Every operation has the same two operands as there, so the bytes are
+// the same.
+template <int LPK>
+__device__ __forceinline__ float bulk_tree_sum(float (&p)[64 / LPK]) {
+    constexpr int S = 64 / LPK;  // pair sums per lane
+    auto add_rn = [](float a, float c) { return __fadd_rn(a, c); };
+#pragma unroll
+    for (int m = 0; m < S; ++m) {
+        if constexpr (LPK >= 16) p[m] = xor_combine<8>(p[m], add_rn);
+        if constexpr (LPK >= 8) p[m] = xor_combine<4>(p[m], add_rn);
+        p[m] = xor_combine<2>(p[m], add_rn);
+        p[m] = xor_combine<1>(p[m], add_rn);
+    }
+#pragma unroll
+    for (int h = S / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int m = 0; m < h; ++m) p[m] = __fadd_rn(p[m], p[m + h]);
+    return p[0];
+}
+
+// value of lane l + D inside its row of 16 lanes (D < 16 - l % 16)
+template <int D>
+__device__ __forceinline__ uint32_t row_shl(uint32_t v) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x100 + D, 0xF, 0xF, false);
+}
+
+template <int FMT, int LPK>
 __global__ __launch_bounds__(256) void store_keys_bulk_kernel(
     const uint16_t *__restrict__ keys, int64_t k_row_stride, int64_t tokens,
     const float *__restrict__ gamma, const float *__restrict__ beta,
     const int64_t *__restrict__ slots, uint8_t *__restrict__ cache, float eps, int64_t num_pages,
     int64_t page_stride) {
-    const int sub = threadIdx.x & 15;  // the lane's place in its key's row of 16
-    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int64_t tk = t < tokens ? t : tokens - 1;  // a row past the end redoes the last key
-    const uint4 raw = *reinterpret_cast<const uint4 *>(keys + tk * k_row_stride + 8 * sub);
-    const float4 *g4 = reinterpret_cast<const float4 *>(gamma + 8 * sub);
-    const float4 *b4 = reinterpret_cast<const float4 *>(beta + 8 * sub);
-    const float4 ga = g4[0], gb = g4[1], ba = b4[0], bb = b4[1];
+    static_assert(LPK == 8 || LPK == 16, "8 or 16 lanes per key");
+    constexpr int C = 128 / LPK;  // columns per lane
+    constexpr int S = C / 2;      // pair sums per lane
+    const int sub = threadIdx.x & (LPK - 1);  // the lane's place among its key's lanes
+    const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPK;
+    const int64_t tk = t < tokens ? t : tokens - 1;  // lanes past the end redo the last key
+    const uint4 *kr = reinterpret_cast<const uint4 *>(keys + tk * k_row_stride + C * sub);
+    const float4 *g4 = reinterpret_cast<const float4 *>(gamma + C * sub);
+    const float4 *b4 = reinterpret_cast<const float4 *>(beta + C * sub);
+    uint4 raw[C / 8];
+    float4 gv[C / 4], bv[C / 4];
+#pragma unroll
+    for (int i = 0; i < C / 8; ++i) raw[i] = kr[i];
+#pragma unroll
+    for (int i = 0; i < C / 4; ++i) {
+        gv[i] = g4[i];
+        bv[i] = b4[i];
+    }
     const int64_t slot = slots[tk];
     hoist_args(cache, eps, num_pages, page_stride);
-    const float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                        bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-    const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-    const float b[8] = {ba.x, ba.y, ba.z, ba.w, bb.x, bb.y, bb.z, bb.w};
-    auto add_rn = [](float a, float c) { return __fadd_rn(a, c); };
-    auto tree = [&](float (&p)[4]) {
+    float x[C], g[C], b[C];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            p[m] = xor_combine<8>(p[m], add_rn);  // 32 apart
-            p[m] = xor_combine<4>(p[m], add_rn);  // 16 apart
-            p[m] = xor_combine<2>(p[m], add_rn);  // 8 apart
-            p[m] = xor_combine<1>(p[m], add_rn);  // 4 apart
+    for (int i = 0; i < C / 8; ++i) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[8 * i + 2 * k] = bf16_lo(w[k]);
+            x[8 * i + 2 * k + 1] = bf16_hi(w[k]);
         }
-        return __fadd_rn(__fadd_rn(p[0], p[2]), __fadd_rn(p[1], p[3]));  // 2 apart, then 1
-    };
-    float p[4];
+    }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) p[m] = __fadd_rn(x[2 * m], x[2 * m + 1]);
-    const float mean = __fmul_rn(tree(p), 0.0078125f);
-    float d[8];
+    for (int i = 0; i < C / 4; ++i) {
+        g[4 * i] = gv[i].x, g[4 * i + 1] = gv[i].y, g[4 * i + 2] = gv[i].z, g[4 * i + 3] = gv[i].w;
+        b[4 * i] = bv[i].x, b[4 * i + 1] = bv[i].y, b[4 * i + 2] = bv[i].z, b[4 * i + 3] = bv[i].w;
+    }
+    float p[S];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = __fsub_rn(x[j], mean);
+    for (int m = 0; m < S; ++m) p[m] = __fadd_rn(x[2 * m], x[2 * m + 1]);
+    const float mean = __fmul_rn(bulk_tree_sum<LPK>(p), 0.0078125f);
+    float d[C];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int j = 0; j < C; ++j) d[j] = __fsub_rn(x[j], mean);
+#pragma unroll
+    for (int m = 0; m < S; ++m)
         p[m] = __fadd_rn(__fmul_rn(d[2 * m], d[2 * m]), __fmul_rn(d[2 * m + 1], d[2 * m + 1]));
-    const float var = __fmul_rn(tree(p), 0.0078125f);
+    const float var = __fmul_rn(bulk_tree_sum<LPK>(p), 0.0078125f);
     const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
-    float n[8];
+    float n[C];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) n[j] = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d[j], rstd), g[j]), b[j]));
+    for (int j = 0; j < C; ++j) n[j] = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d[j], rstd), g[j]), b[j]));
 
-    // the whole row of 16 lanes leaves together (padding slot, or a row past the end), so the
-    // exchanges below only meet lanes of their own key
+    // all lanes of a key leave together (padding slot, or lanes past the end), so the exchanges
+    // below only meet lanes of their own key
     if (t >= tokens || slot < 0 || slot >= num_pages * kPageTokens) return;
     uint8_t *sec = cache + (slot >> 6) * page_stride;
     const int off = (int)(slot & 63);
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[j]));
+    for (int j = 0; j < C; ++j) amax = fmaxf(amax, fabsf(n[j]));
     if constexpr (FMT == kFmtMxfp4) {
-        amax = group_max<4>(amax);  // 4 lanes = the 32-column block
+        amax = group_max<32 / C>(amax);  // the lanes of one 32-column block
         const int e = ue8m0_exponent(amax);
         const float inv = pow2_neg(e);
-        uint32_t word = e2m1_pair<0>(0u, __fmul_rn(n[0], inv), __fmul_rn(n[1], inv));
-        word = e2m1_pair<1>(word, __fmul_rn(n[2], inv), __fmul_rn(n[3], inv));
-        word = e2m1_pair<2>(word, __fmul_rn(n[4], inv), __fmul_rn(n[5], inv));
-        word = e2m1_pair<3>(word, __fmul_rn(n[6], inv), __fmul_rn(n[7], inv));
-        *reinterpret_cast<uint32_t *>(sec + off * 64 + 4 * sub) = word;
-        const uint32_t sc = (uint32_t)(e + 127);  // block sub / 4; lanes 0, 4, 8, 12 hold blocks 0..3
-        const uint32_t scales = sc | (row_down<4>(sc) << 8) | (row_down<8>(sc) << 16) |
-                                (row_down<12>(sc) << 24);
+        uint32_t word[C / 8];
+#pragma unroll
+        for (int i = 0; i < C / 8; ++i) {
+            uint32_t w = e2m1_pair<0>(0u, __fmul_rn(n[8 * i], inv), __fmul_rn(n[8 * i + 1], inv));
+            w = e2m1_pair<1>(w, __fmul_rn(n[8 * i + 2], inv), __fmul_rn(n[8 * i + 3], inv));
+            w = e2m1_pair<2>(w, __fmul_rn(n[8 * i + 4], inv), __fmul_rn(n[8 * i + 5], inv));
+            w = e2m1_pair<3>(w, __fmul_rn(n[8 * i + 6], inv), __fmul_rn(n[8 * i + 7], inv));
+            word[i] = w;
+        }
+        if constexpr (C == 16)
+            *reinterpret_cast<uint2 *>(sec + off * 64 + 8 * sub) = make_uint2(word[0], word[1]);
+        else
+            *reinterpret_cast<uint32_t *>(sec + off * 64 + 4 * sub) = word[0];
+        // block k's exponent sits in the key's lane k * 32 / C; one lane writes the four bytes
+        const uint32_t sc = (uint32_t)(e + 127);
+        constexpr int B = 32 / C;  // lanes per block
+        const uint32_t scales = sc | (row_shl<B>(sc) << 8) | (row_shl<2 * B>(sc) << 16) |
+                                (row_shl<3 * B>(sc) << 24);
         if (sub == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
     } else {
-        amax = group_max<16>(fmaxf(1e-10f, amax));
+        amax = group_max<LPK>(fmaxf(1e-10f, amax));
         const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
         const float inv = __fdiv_rn(1.0f, s);
-        uint32_t c[8];
+        uint32_t w[C / 4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = e4m3_code(__fmul_rn(n[j], inv));
-        *reinterpret_cast<uint2 *>(sec + off * 128 + 8 * sub) =
-            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+        for (int i = 0; i < C / 4; ++i)
+            w[i] = e4m3_code(__fmul_rn(n[4 * i], inv)) | (e4m3_code(__fmul_rn(n[4 * i + 1], inv)) << 8) |
+                   (e4m3_code(__fmul_rn(n[4 * i + 2], inv)) << 16) |
+                   (e4m3_code(__fmul_rn(n[4 * i + 3], inv)) << 24);
+        if constexpr (C == 16)
+            *reinterpret_cast<uint4 *>(sec + off * 128 + 16 * sub) = make_uint4(w[0], w[1], w[2], w[3]);
+        else
+            *reinterpret_cast<uint2 *>(sec + off * 128 + 8 * sub) = make_uint2(w[0], w[1]);
         if (sub == 0) {
             if constexpr (FMT == kFmtFp8Mx)
                 *reinterpret_cast<uint32_t *>(sec + 64 * 128 + off * 4) =
@@ -374,17 +424,21 @@ hipError_t launch_store_keys(int fmt, const void *keys, int64_t tokens, int64_t 
     auto *cc = static_cast<uint8_t *>(cache);
     auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     if (a16(keys) && k_row_stride % 8 == 0 && a16(gamma) && a16(beta)) {
-        // 16-byte rows and LayerNorm parameters: sixteen lanes per key
-        const dim3 grid16((unsigned)((tokens + 15) / 16)), block16(256);
+        // 16-byte rows and LayerNorm parameters: eight lanes per key
+        constexpr int kLanes = 8;
+        const dim3 gridb((unsigned)((tokens * kLanes + 255) / 256)), blockb(256);
         if (fmt == kFmtMxfp4)
-            hipLaunchKernelGGL(store_keys_bulk_kernel<kFmtMxfp4>, grid16, block16, 0, stream, kk,
-                               k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
+            hipLaunchKernelGGL((store_keys_bulk_kernel<kFmtMxfp4, kLanes>), gridb, blockb, 0, stream,
+                               kk, k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages,
+                               page_stride);
         else if (fmt == kFmtFp8)
-            hipLaunchKernelGGL(store_keys_bulk_kernel<kFmtFp8>, grid16, block16, 0, stream, kk,
-                               k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
+            hipLaunchKernelGGL((store_keys_bulk_kernel<kFmtFp8, kLanes>), gridb, blockb, 0, stream,
+                               kk, k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages,
+                               page_stride);
         else
-            hipLaunchKernelGGL(store_keys_bulk_kernel<kFmtFp8Mx>, grid16, block16, 0, stream, kk,
-                               k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages, page_stride);
+            hipLaunchKernelGGL((store_keys_bulk_kernel<kFmtFp8Mx, kLanes>), gridb, blockb, 0, stream,
+                               kk, k_row_stride, tokens, gamma, beta, slots, cc, eps, num_pages,
+                               page_stride);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((tokens + 3) / 4)), block(256);
