@@ -233,7 +233,9 @@ class Setup:
                                     wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
         self.store, self.score, self.inputs, self.score_hist = [], [], [], []
         self.inputs_layout, self.index_score = [], []
-        # the step's inputs made inside the scorer: MXFP4 with at most 4 rows per request
+        # the step's inputs made inside the scorer: MXFP4 with at most 4 rows per request (FP8
+        # has the fused call too, but on the FP8 decode workload each workgroup's query encode
+        # costs about what the separate input launch does: 19.2 against 19.0 us per step)
         self.inline_ok = wl.fmt == "mxfp4" and wl.max_query_len <= 4
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset

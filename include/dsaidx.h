@@ -290,7 +290,7 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
 
 /*
  * index_score_hist -- one decode or verify step's indexer inputs and its scoring in one
- * launch, MXFP4 ([idx] DsaIndex: the quantized query, the head weights and the inserted key
+ * launch ([idx] DsaIndex: the quantized query, the head weights and the inserted key
  * feed the logits; [fp4ops] decode_layout for the rows). Each scoring workgroup quantizes its
  * request's query rows itself, and the wavefront that scores the page of a new key
  * normalizes, quantizes and inserts that key. The results equal those of
@@ -299,7 +299,8 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
  * query_starts[q] + i of request q holds the key at position
  * pos = seq_lens[q] - query_lens[q] + i, token pos % 64 of page block_table[q, pos / 64].
  * dsaidx_topk_scored then selects.
- *  fmt      DSAIDX_MXFP4 (another valid format gives DSAIDX_EUNSUPPORTED).
+ *  fmt      DSAIDX_MXFP4, DSAIDX_FP8 or DSAIDX_FP8_MX (the query quantized as
+ *           dsaidx_quantize_queries does, its FP8 scale folded into the head weights).
  *  projected, proj_row_stride, key_col, weight_col, q, heads, q_row_stride, q_head_stride,
  *  gamma, beta, eps  as in dsaidx_index_inputs, one packed row and one query row per row.
  *  seq_lens, query_lens, num_requests, num_rows, query_starts, row_ends  as in
@@ -307,13 +308,14 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
  *  cache, num_pages, page_stride, block_table, max_blocks  as in dsaidx_score_paged; the
  *           cache is written too (the new keys). No quantized query rows or head weights
  *           are written: they stay on chip.
- *  max_query_len  1..4: the most rows any request has.
+ *  max_query_len  1..4 for MXFP4, 1..2 for FP8: the most rows any request has.
  *  logits, logits_row_stride, workspace, workspace_bytes  as in dsaidx_score_paged_hist.
  *  Caller contract: every request has at most max_query_len rows (further rows get neither
  *  logits nor keys); a page that receives a new key is in no other request's block table;
  *  a key whose position is negative, at or past max_blocks * 64, or on a block-table entry
  *  outside [0, num_pages) is not inserted.
- *  Errors: as the calls it replaces; max_query_len above 4 gives DSAIDX_EUNSUPPORTED. With
+ *  Errors: as the calls it replaces; max_query_len above 4 (MXFP4) or 2 (FP8) gives
+ *  DSAIDX_EUNSUPPORTED. With
  *  num_rows, num_requests, max_blocks or num_pages == 0 only the row layout is written.
  */
 dsaidx_status dsaidx_index_score_hist(

@@ -348,7 +348,8 @@ dsaidx_status dsaidx_index_score_hist(
     if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0 ||
         key_col < 0 || weight_col < 0 || !std::isfinite(eps) || eps < 0.0f)
         return DSAIDX_EINVAL;
-    if (fmt != DSAIDX_MXFP4 || !valid_heads(heads) || max_query_len < 1 || max_query_len > 4)
+    if (!valid_heads(heads) || max_query_len < 1 ||
+        max_query_len > dsaidx::index_score_max_query_len(fmt))
         return DSAIDX_EUNSUPPORTED;
     dsaidx_status st = check_layout(seq_lens, query_lens, num_requests, num_rows, 0, 1, 1,
                                     query_starts, row_ends);

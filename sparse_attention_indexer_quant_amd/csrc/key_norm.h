@@ -87,4 +87,34 @@ __device__ __forceinline__ void store_mxfp4_key(const Mxfp4KeyLane &k, uint8_t *
     if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 64 + off * 4) = scales;
 }
 
+// The lane's two E4M3 codes (columns 2l, 2l+1, low byte first) and the key's power-of-two
+// scale s = pow2_ceil(max(1e-10, amax) / 448) (insert_key's FP8 writer).
+struct Fp8KeyLane {
+    uint32_t two;
+    float s;
+};
+
+__device__ __forceinline__ Fp8KeyLane fp8_key_lane(float n0, float n1) {
+    const float amax = group_max<64>(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))));
+    const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
+    const float inv = __fdiv_rn(1.0f, s);
+    return {e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8), s};
+}
+
+// The 4-byte scale word of an FP8 section row: the FP32 scale, or with mx its exponent field
+// (s = 2^e is a normal FP32, 2^-42 <= s <= 2^120: the field is e + 127) as four equal bytes.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_scale_word(float s) {
+    if constexpr (FMT == kFmtFp8Mx) return (__float_as_uint(s) >> 23) * 0x01010101u;
+    else return __float_as_uint(s);
+}
+
+// Writes the key to token `off` of the FP8 section `sec`: 128 code bytes, then the scale word.
+template <int FMT>
+__device__ __forceinline__ void store_fp8_key(const Fp8KeyLane &k, uint8_t *sec, int off, int lane) {
+    const uint32_t word = k.two | (quad_down<1>(k.two) << 16);
+    if ((lane & 1) == 0) *reinterpret_cast<uint32_t *>(sec + off * 128 + 2 * lane) = word;
+    if (lane == 0) *reinterpret_cast<uint32_t *>(sec + 64 * 128 + off * 4) = fp8_scale_word<FMT>(k.s);
+}
+
 }  // namespace dsaidx

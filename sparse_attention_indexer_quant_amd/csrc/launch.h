@@ -76,6 +76,8 @@ struct FusedInputs {
 
 hipError_t launch_index_score_hist(const ScoreArgs &args, const FusedInputs &fin,
                                    void *workspace, hipStream_t stream);
+// The most rows per request index_score_hist takes for a format (4 MXFP4, 2 FP8).
+int index_score_max_query_len(int fmt);
 
 // How score_paged splits a request's pages: pages per wavefront, workgroups ("chunks") per
 // request, and the keys one workgroup covers (the top-k segment when the scorer writes the

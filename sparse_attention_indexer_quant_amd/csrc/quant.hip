@@ -128,21 +128,7 @@ __device__ __forceinline__ void store_key(const KeyLane &in, float eps,
     if constexpr (FMT == kFmtMxfp4) {
         store_mxfp4_key(mxfp4_key_lane(n0, n1), sec, off, lane);
     } else {
-        const float amax = group_max<64>(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))));
-        const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
-        const float inv = __fdiv_rn(1.0f, s);
-        const uint32_t two = e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8);
-        const uint32_t word = two | (quad_down<1>(two) << 16);
-        if ((lane & 1) == 0) *reinterpret_cast<uint32_t *>(sec + off * 128 + 2 * lane) = word;
-        if (lane == 0) {
-            if constexpr (FMT == kFmtFp8Mx) {
-                // s = 2^e is a normal FP32 (2^-42 <= s <= 2^120): its exponent field is e + 127
-                const uint32_t b = __float_as_uint(s) >> 23;
-                *reinterpret_cast<uint32_t *>(sec + 64 * 128 + off * 4) = b * 0x01010101u;
-            } else {
-                *reinterpret_cast<float *>(sec + 64 * 128 + off * 4) = s;
-            }
-        }
+        store_fp8_key<FMT>(fp8_key_lane(n0, n1), sec, off, lane);
     }
 }
 

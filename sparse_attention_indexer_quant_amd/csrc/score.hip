@@ -192,12 +192,13 @@ __device__ __forceinline__ void load_page(PageRegs<FMT> &pg, const uint8_t *sec,
     }
 }
 
-template <int H, int RG>
+template <int FMT, int H, int RG>
 struct StepQueryLds {
     static constexpr int kTiles = RG * (H / 16);
-    uint4 qa[kTiles][64];
+    static constexpr int kParts = FMT == kFmtMxfp4 ? 1 : 4;  // FP8: 32 values widened to BF16
+    uint4 qa[kTiles][kParts][64];
     uint2 wt[kTiles][64];
-    int qs[kTiles][64];
+    int qs[kTiles][FMT == kFmtMxfp4 ? 64 : 1];
 };
 
 // Query operands, head weights and key bounds of one group of RG rows. With OPS_IN_LDS (the
@@ -211,12 +212,12 @@ struct RowGroup {
     uint4 qa[RR][HT][FMT == kFmtMxfp4 ? 1 : 4];
     int qs[RR][HT];
     uint2 wt[RR][HT];  // 4 BF16 head weights, widened at use
-    const StepQueryLds<H, RG> *ops = nullptr;
+    const StepQueryLds<FMT, H, RG> *ops = nullptr;
     int ops_lane = 0;
     int rend[RG];
 
     __device__ __forceinline__ uint4 qa_at(int j, int ht) const {
-        if constexpr (OPS_IN_LDS) return ops->qa[j * HT + ht][ops_lane];
+        if constexpr (OPS_IN_LDS) return ops->qa[j * HT + ht][0][ops_lane];
         else return qa[j][ht][0];
     }
     __device__ __forceinline__ int qs_at(int j, int ht) const {
@@ -263,7 +264,6 @@ struct RowGroup {
     __device__ __forceinline__ void from_lds(const Lds &s, int64_t r0, int seq, int qlen,
                                              int64_t first, int64_t last, int64_t width,
                                              int lane) {
-        static_assert(FMT == kFmtMxfp4, "the step inputs are made in the scorer for MXFP4");
         ops = &s;
         ops_lane = lane;
 #pragma unroll
@@ -275,8 +275,10 @@ struct RowGroup {
             if constexpr (!OPS_IN_LDS) {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) {
-                    qa[j][ht][0] = s.qa[j * HT + ht][lane];
-                    qs[j][ht] = s.qs[j * HT + ht][lane];
+#pragma unroll
+                    for (int k = 0; k < (FMT == kFmtMxfp4 ? 1 : 4); ++k)
+                        qa[j][ht][k] = s.qa[j * HT + ht][k][lane];
+                    qs[j][ht] = FMT == kFmtMxfp4 ? s.qs[j * HT + ht][lane] : 0;
                     wt[j][ht] = s.wt[j * HT + ht][lane];
                 }
             }
@@ -368,7 +370,7 @@ struct RowGroup {
 // -- the UE8M0 exponent of the block's largest magnitude, then the E2M1 codes of the values
 // times 2^-e -- and rounds its four head weights times c_h to BF16. The tiles meet in the LDS
 // in the lane layout of RowGroup's registers.
-template <int H, int RG>
+template <int FMT, int H, int RG>
 struct StepQuery {
     static constexpr int HT = H / 16, kTiles = RG * HT, kPer = (kTiles + kWaves - 1) / kWaves;
     uint4 raw[kPer][4];
@@ -396,8 +398,12 @@ struct StepQuery {
         }
     }
 
-    __device__ __forceinline__ void encode(StepQueryLds<H, RG> &s, float c_h, int wave,
+    __device__ __forceinline__ void encode(StepQueryLds<FMT, H, RG> &s, float c_h, int wave,
                                            int lane) const {
+        if constexpr (FMT != kFmtMxfp4) {
+            encode_fp8(s, c_h, wave, lane);
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
             const int it = wave + kWaves * m;
@@ -425,8 +431,63 @@ struct StepQuery {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 wb[i] = bf16_bits_rne(__fmul_rn(bf16_val((uint16_t)wraw[m][i]), c_h));
-            s.qa[it][lane] = make_uint4(out[0], out[1], out[2], out[3]);
+            s.qa[it][0][lane] = make_uint4(out[0], out[1], out[2], out[3]);
             s.qs[it][lane] = ex + 127;
+            s.wt[it][lane] = make_uint2(wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16));
+        }
+    }
+
+    // FP8 (the separate quantizer's arithmetic): per head, s = pow2_ceil(max(1e-10, amax) / 448)
+    // over its 128 values -- the four lanes (l16, 0..3) of a head hold its four 32-value blocks
+    // -- the E4M3 codes of v / s, widened exactly to BF16 for the MFMA, and the head weights
+    // BF16(w * s * c_h); lane (l16, grp) weighs heads 4 grp + i, whose scales it takes from
+    // lanes 4 grp + i.
+    __device__ __forceinline__ void encode_fp8(StepQueryLds<FMT, H, RG> &s, float c_h, int wave,
+                                               int lane) const {
+        auto mx = [](float a, float b) { return fmaxf(a, b); };
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int it = wave + kWaves * m;
+            if (it >= kTiles) continue;
+            float amax = 1e-10f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wd[4] = {raw[m][i].x, raw[m][i].y, raw[m][i].z, raw[m][i].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wd[c])), fabsf(bf16_hi(wd[c]))));
+            }
+            amax = xor_combine<16>(amax, mx);
+            amax = xor_combine<32>(amax, mx);
+            const float sc = pow2_ceil(__fdiv_rn(amax, 448.0f));
+            const float inv = __fdiv_rn(1.0f, sc);
+            uint32_t codes[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wd[4] = {raw[m][i].x, raw[m][i].y, raw[m][i].z, raw[m][i].w};
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    lo |= e4m3_code(__fmul_rn(bf16_lo(wd[c]), inv)) << (16 * c);
+                    lo |= e4m3_code(__fmul_rn(bf16_hi(wd[c]), inv)) << (16 * c + 8);
+                    hi |= e4m3_code(__fmul_rn(bf16_lo(wd[c + 2]), inv)) << (16 * c);
+                    hi |= e4m3_code(__fmul_rn(bf16_hi(wd[c + 2]), inv)) << (16 * c + 8);
+                }
+                codes[2 * i] = lo;
+                codes[2 * i + 1] = hi;
+            }
+            uint4 widened[4];
+            e4m3x32_to_bf16(make_uint4(codes[0], codes[1], codes[2], codes[3]),
+                            make_uint4(codes[4], codes[5], codes[6], codes[7]), widened);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s.qa[it][k][lane] = widened[k];
+            const int grp = lane >> 4;
+            uint32_t wb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float si = __shfl(sc, 4 * grp + i);  // head 4 grp + i of the tile
+                wb[i] = bf16_bits_rne(__fmul_rn(__fmul_rn(bf16_val((uint16_t)wraw[m][i]), si), c_h));
+            }
             s.wt[it][lane] = make_uint2(wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16));
         }
     }
@@ -453,6 +514,32 @@ __device__ __forceinline__ void patch_key(PageRegs<kFmtMxfp4> &pg, const uint8_t
     }
 }
 
+// The FP8 form: lane (l16, grp) of tile o / 16 with l16 = o % 16 takes the key's 32 code bytes
+// of block grp, and every lane of that token its scale word (staged: 128 code bytes, then the
+// 4-byte scale word).
+__device__ __forceinline__ void patch_key(PageRegs<kFmtFp8> &pg, const uint8_t *staged, int o,
+                                          int l16, int grp) {
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(staged + grp * 32);
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(staged + grp * 32 + 16);
+    const uint32_t sc = *reinterpret_cast<const uint32_t *>(staged + 128);
+    const bool mine = l16 == (o & 15);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t m = mine && t == (o >> 4) ? 0xFFFFFFFFu : 0u;
+        uint4 &a = pg.kp[t][0];
+        uint4 &b = pg.kp[t][1];
+        a = make_uint4((v0.x & m) | (a.x & ~m), (v0.y & m) | (a.y & ~m), (v0.z & m) | (a.z & ~m),
+                       (v0.w & m) | (a.w & ~m));
+        b = make_uint4((v1.x & m) | (b.x & ~m), (v1.y & m) | (b.y & ~m), (v1.z & m) | (b.z & ~m),
+                       (v1.w & m) | (b.w & ~m));
+        pg.ks[t] = (sc & m) | (pg.ks[t] & ~m);
+    }
+}
+__device__ __forceinline__ void patch_key(PageRegs<kFmtFp8Mx> &pg, const uint8_t *staged, int o,
+                                          int l16, int grp) {
+    patch_key(reinterpret_cast<PageRegs<kFmtFp8> &>(pg), staged, o, l16, grp);
+}
+
 // Rows of request `req` from the query lengths: the first is the sum of the lengths before it
 // (a wavefront sum, uniform), the count its own length.
 __device__ __forceinline__ int64_t request_first_row(const int32_t *lens, int64_t req, int lane) {
@@ -477,7 +564,10 @@ __device__ __forceinline__ int64_t request_first_row(const int32_t *lens, int64_
     return __builtin_amdgcn_readfirstlane(acc);
 }
 
-constexpr int kStagedKeyBytes = 80;  // 64 payload + 4 scale bytes, padded to 16
+// a staged new key: MXFP4 64 payload + 4 scale bytes, FP8 128 code bytes + the scale word,
+// padded to 16
+template <int FMT>
+constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 
 // Grid: requests x chunks; a workgroup's chunk is 4 PW consecutive pages of the request, which
 // its 4 wavefronts take in turn (PW pages each). Each wavefront streams its pages through a
@@ -506,14 +596,15 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
     int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
     uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin) {
-    static_assert(!FUSED || (FMT == kFmtMxfp4 && HIST), "fused inputs: MXFP4 with histograms");
+    static_assert(!FUSED || HIST, "fused inputs: with histograms");
+    constexpr int kStagedKeyBytes = staged_key_bytes<FMT>();
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
     __shared__ __align__(16) uint32_t hist[HIST ? RG * (kBins / 2) : 1];
     // FUSED: the workgroup's query operands, and each wavefront's staged new keys
-    __shared__ __align__(16) uint8_t step_lds_bytes[FUSED ? sizeof(StepQueryLds<H, RG>) : 16];
+    __shared__ __align__(16) uint8_t step_lds_bytes[FUSED ? sizeof(StepQueryLds<FMT, H, RG>) : 16];
     __shared__ __align__(16) uint8_t staged_keys[FUSED ? kWaves * RG * kStagedKeyBytes : 16];
-    auto &step_lds = *reinterpret_cast<StepQueryLds<H, RG> *>(step_lds_bytes);
+    auto &step_lds = *reinterpret_cast<StepQueryLds<FMT, H, RG> *>(step_lds_bytes);
     const int lane = threadIdx.x & 63;
     // uniform across the wavefront; said explicitly so that all page and bound arithmetic
     // below stays in scalar registers
@@ -608,7 +699,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
     int kmax;
     // FUSED: the raw query tiles and head weights of this wavefront's share, and the step's
     // keys (one row each; a key past the rows reads the first row's)
-    StepQuery<H, RG> sq;
+    StepQuery<FMT, H, RG> sq;
     KeyLane key;  // columns 2 lane, 2 lane + 1 of the LayerNorm weights and biases
     uint32_t key_pair[FUSED ? RG : 1];
     if constexpr (!FUSED) {
@@ -678,11 +769,18 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 k.pair = key_pair[i];
                 float n0, n1;
                 layer_norm_pair(k, fin.eps, n0, n1);
-                const Mxfp4KeyLane mk = mxfp4_key_lane(n0, n1);
-                store_mxfp4_key(mk, sec, own_o[i], lane);
                 uint8_t *staged = staged_keys + (wave * RG + i) * kStagedKeyBytes;
-                staged[lane] = (uint8_t)mk.byte;
-                if ((lane & 15) == 0) staged[64 + (lane >> 4)] = (uint8_t)mk.scale;
+                if constexpr (FMT == kFmtMxfp4) {
+                    const Mxfp4KeyLane mk = mxfp4_key_lane(n0, n1);
+                    store_mxfp4_key(mk, sec, own_o[i], lane);
+                    staged[lane] = (uint8_t)mk.byte;
+                    if ((lane & 15) == 0) staged[64 + (lane >> 4)] = (uint8_t)mk.scale;
+                } else {
+                    const Fp8KeyLane fk = fp8_key_lane(n0, n1);
+                    store_fp8_key<FMT>(fk, sec, own_o[i], lane);
+                    *reinterpret_cast<uint16_t *>(staged + 2 * lane) = (uint16_t)fk.two;
+                    if (lane == 0) *reinterpret_cast<uint32_t *>(staged + 128) = fp8_scale_word<FMT>(fk.s);
+                }
             }
         }
         __syncthreads();
@@ -873,26 +971,42 @@ hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStrea
     }
 }
 
-// The step's inputs and its scoring in one launch (MXFP4, histograms, one row group: at most
-// 4 rows per request).
-template <int H>
+// The step's inputs and its scoring in one launch (histograms, one row group: at most 4 rows
+// per request for MXFP4, 2 for FP8, whose widened operands take twice the registers).
+template <int FMT, int H>
 static hipError_t launch_index_score_h(const ScoreArgs &a, const FusedInputs &fin,
                                        const TopkWorkspace &ws, hipStream_t stream) {
-    if (a.max_query_len <= 1) return launch_score_rg<kFmtMxfp4, H, 1, true, true>(a, ws, stream, fin);
-    if (a.max_query_len <= 2) return launch_score_rg<kFmtMxfp4, H, 2, true, true>(a, ws, stream, fin);
-    return launch_score_rg<kFmtMxfp4, H, 4, true, true>(a, ws, stream, fin);
+    if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, true, true>(a, ws, stream, fin);
+    if constexpr (FMT == kFmtMxfp4) {
+        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, true, true>(a, ws, stream, fin);
+        return launch_score_rg<FMT, H, 4, true, true>(a, ws, stream, fin);
+    } else {
+        return launch_score_rg<FMT, H, 2, true, true>(a, ws, stream, fin);
+    }
 }
+
+template <int FMT>
+static hipError_t launch_index_score_fmt(const ScoreArgs &a, const FusedInputs &fin,
+                                         const TopkWorkspace &ws, hipStream_t stream) {
+    switch (a.heads) {
+        case 16: return launch_index_score_h<FMT, 16>(a, fin, ws, stream);
+        case 32: return launch_index_score_h<FMT, 32>(a, fin, ws, stream);
+        default: return launch_index_score_h<FMT, 64>(a, fin, ws, stream);
+    }
+}
+
+int index_score_max_query_len(int fmt) { return fmt == kFmtMxfp4 ? 4 : 2; }
 
 hipError_t launch_index_score_hist(const ScoreArgs &a, const FusedInputs &fin, void *workspace,
                                    hipStream_t stream) {
-    if (a.fmt != kFmtMxfp4 || a.max_query_len < 1 || a.max_query_len > 4)
+    if (a.max_query_len < 1 || a.max_query_len > index_score_max_query_len(a.fmt))
         return hipErrorInvalidValue;
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
     const TopkWorkspace ws = carve(workspace, a.num_rows, geo.chunks);
-    switch (a.heads) {
-        case 16: return launch_index_score_h<16>(a, fin, ws, stream);
-        case 32: return launch_index_score_h<32>(a, fin, ws, stream);
-        default: return launch_index_score_h<64>(a, fin, ws, stream);
+    switch (a.fmt) {
+        case kFmtMxfp4: return launch_index_score_fmt<kFmtMxfp4>(a, fin, ws, stream);
+        case kFmtFp8: return launch_index_score_fmt<kFmtFp8>(a, fin, ws, stream);
+        default: return launch_index_score_fmt<kFmtFp8Mx>(a, fin, ws, stream);
     }
 }
 

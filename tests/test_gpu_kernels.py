@@ -364,6 +364,14 @@ FUSED_CASES = {
     # and end a page, padding rows, and a row whose keys start past its request's first chunk
     "fp4_h64_edges": dict(fmt="mxfp4", heads=64, seq_lens=[2, 130, 4098, 64, 9000],
                           query_lens=[2, 0, 4, 1, 3], num_rows=13),
+    # FP8 (at most 2 rows per request): outliers, the mx scale bytes, merged pages, keys at
+    # position 0, straddling and ending pages, a request with no rows, padding rows
+    "fp8_h32": SCORE_CASES["fp8_h32"],
+    "fp8mx_h32_verify": SCORE_CASES["fp8mx_h32_verify"],
+    "fp8_h64_merged": dict(fmt="fp8", heads=64, seq_lens=[500, 129, 64], query_lens=[2, 1, 2],
+                           num_rows=7, page_stride=9216, section_offset=512),
+    "fp8mx_h16_edges": dict(fmt="fp8_mx", heads=16, seq_lens=[2, 130, 65, 700], query_lens=[2, 0, 2, 1],
+                            num_rows=8, outlier_frac=0.01, outlier_gain=20.0),
 }
 
 
@@ -438,8 +446,8 @@ def test_index_score_matches_oracle_and_separate_calls(name, k):
 
 
 def test_index_score_degenerate_sizes():
-    # no pages or no blocks: only the row layout is written; more than 4 rows per request and
-    # other formats are refused
+    # no pages or no blocks: only the row layout is written; more than 4 rows per request
+    # (MXFP4) or 2 (FP8) are refused
     rng = np.random.default_rng(9)
     seq = np.array([5, 70], np.int32)
     ql = np.array([1, 2], np.int32)
@@ -456,9 +464,9 @@ def test_index_score_degenerate_sizes():
     with pytest.raises(RuntimeError):
         dsa.index_score_topk(pd, 0, 130, q, g, b, 1e-6, dev(seq), dev(ql), 4, cache, 1, 4352, bt,
                              5, 8)
-    with pytest.raises(RuntimeError):
+    with pytest.raises(RuntimeError):  # FP8 takes at most 2 rows per request
         dsa.index_score_topk(pd, 0, 130, q, g, b, 1e-6, dev(seq), dev(ql), 4, cache, 1, 8448, bt,
-                             2, 8, "fp8")
+                             3, 8, "fp8")
 
 
 def test_score_paged_placement_invariance_and_determinism():
