@@ -3,7 +3,7 @@
 One step = one pass of the whole path over one decode batch, inputs resident in HBM: every
 row's query quantized with its head weights, the step's new keys normalized, quantized and
 inserted, the decode_layout row bounds, scoring that also writes the top-k segment
-histograms, and topk_scored. On MXFP4 workloads with at most 4 rows per request the first
+histograms, and topk_scored. With at most 4 rows per request (MXFP4) or 2 (FP8) the first
 four are one launch (index_score_hist); otherwise index_inputs_layout + score_paged_hist. The
 separate-input form and the form with score_paged + topk are timed too (per_config
 ..._separate_inputs, ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of
@@ -233,10 +233,8 @@ class Setup:
                                     wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
         self.store, self.score, self.inputs, self.score_hist = [], [], [], []
         self.inputs_layout, self.index_score = [], []
-        # the step's inputs made inside the scorer: MXFP4 with at most 4 rows per request (FP8
-        # has the fused call too, but on the FP8 decode workload each workgroup's query encode
-        # costs about what the separate input launch does: 19.2 against 19.0 us per step)
-        self.inline_ok = wl.fmt == "mxfp4" and wl.max_query_len <= 4
+        # the step's inputs made inside the scorer: at most 4 rows per request (MXFP4), 2 (FP8)
+        self.inline_ok = wl.max_query_len <= (4 if wl.fmt == "mxfp4" else 2)
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(

@@ -98,7 +98,7 @@ __device__ __forceinline__ Fp8KeyLane fp8_key_lane(float n0, float n1) {
     const float amax = group_max<64>(fmaxf(1e-10f, fmaxf(fabsf(n0), fabsf(n1))));
     const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
     const float inv = __fdiv_rn(1.0f, s);
-    return {e4m3_code(__fmul_rn(n0, inv)) | (e4m3_code(__fmul_rn(n1, inv)) << 8), s};
+    return {e4m3x2(__fmul_rn(n0, inv), __fmul_rn(n1, inv)), s};
 }
 
 // The 4-byte scale word of an FP8 section row: the FP32 scale, or with mx its exponent field

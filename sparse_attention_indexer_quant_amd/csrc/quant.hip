@@ -96,12 +96,10 @@ __device__ __forceinline__ void quantize_query_row(const QueryLoads<H> &in, bool
             amax = group_max<16>(amax);  // the 16 lanes of the head
             const float s = pow2_ceil(__fdiv_rn(amax, 448.0f));
             const float inv = __fdiv_rn(1.0f, s);
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lo |= e4m3_code(__fmul_rn(v[i], inv)) << (8 * i);
-                hi |= e4m3_code(__fmul_rn(v[4 + i], inv)) << (8 * i);
-            }
+            const uint32_t lo = e4m3x4(__fmul_rn(v[0], inv), __fmul_rn(v[1], inv),
+                                       __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
+            const uint32_t hi = e4m3x4(__fmul_rn(v[4], inv), __fmul_rn(v[5], inv),
+                                       __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
             *reinterpret_cast<uint2 *>(out_row + head * 128 + part * 8) = make_uint2(lo, hi);
             if (part == 0 && has_w) {
                 const float w = bf16_val((uint16_t)wraw[pass]);
@@ -291,9 +289,8 @@ __global__ __launch_bounds__(256) void store_keys_bulk_kernel(
         uint32_t w[C / 4];
 #pragma unroll
         for (int i = 0; i < C / 4; ++i)
-            w[i] = e4m3_code(__fmul_rn(n[4 * i], inv)) | (e4m3_code(__fmul_rn(n[4 * i + 1], inv)) << 8) |
-                   (e4m3_code(__fmul_rn(n[4 * i + 2], inv)) << 16) |
-                   (e4m3_code(__fmul_rn(n[4 * i + 3], inv)) << 24);
+            w[i] = e4m3x4(__fmul_rn(n[4 * i], inv), __fmul_rn(n[4 * i + 1], inv),
+                          __fmul_rn(n[4 * i + 2], inv), __fmul_rn(n[4 * i + 3], inv));
         if constexpr (C == 16)
             *reinterpret_cast<uint4 *>(sec + off * 128 + 16 * sub) = make_uint4(w[0], w[1], w[2], w[3]);
         else

@@ -465,14 +465,10 @@ struct StepQuery {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t wd[4] = {raw[m][i].x, raw[m][i].y, raw[m][i].z, raw[m][i].w};
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    lo |= e4m3_code(__fmul_rn(bf16_lo(wd[c]), inv)) << (16 * c);
-                    lo |= e4m3_code(__fmul_rn(bf16_hi(wd[c]), inv)) << (16 * c + 8);
-                    hi |= e4m3_code(__fmul_rn(bf16_lo(wd[c + 2]), inv)) << (16 * c);
-                    hi |= e4m3_code(__fmul_rn(bf16_hi(wd[c + 2]), inv)) << (16 * c + 8);
-                }
+                const uint32_t lo = e4m3x4(__fmul_rn(bf16_lo(wd[0]), inv), __fmul_rn(bf16_hi(wd[0]), inv),
+                                           __fmul_rn(bf16_lo(wd[1]), inv), __fmul_rn(bf16_hi(wd[1]), inv));
+                const uint32_t hi = e4m3x4(__fmul_rn(bf16_lo(wd[2]), inv), __fmul_rn(bf16_hi(wd[2]), inv),
+                                           __fmul_rn(bf16_lo(wd[3]), inv), __fmul_rn(bf16_hi(wd[3]), inv));
                 codes[2 * i] = lo;
                 codes[2 * i + 1] = hi;
             }

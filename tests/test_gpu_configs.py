@@ -119,7 +119,7 @@ def test_topk_end_to_end_boundary_swaps_only(run):
 
 
 def test_bench_step_path(run):
-    # MXFP4 with at most 4 rows per request: index_score_hist + topk_scored; otherwise
+    # At most 4 rows per request (MXFP4) or 2 (FP8): index_score_hist + topk_scored; otherwise
     # index_inputs_layout + score_paged_hist + topk_scored. Packed projection rows
     # [key 128 | head weights H] per query row, as bench.py builds them.
     wl = run["wl"]
@@ -139,7 +139,7 @@ def test_bench_step_path(run):
         dsa.store_keys(bf16_dev(wl.key_bits[part]), b.gamma, b.beta, wl.eps, dev(wl.key_slots[part]),
                        b.cache, wl.num_pages, wl.page_stride, wl.fmt, wl.section_offset)
     pd = bf16_dev(proj)
-    inline = wl.fmt == "mxfp4" and wl.max_query_len <= 4
+    inline = wl.max_query_len <= (4 if wl.fmt == "mxfp4" else 2)
     if inline:
         starts, ends, logits, idx = dsa.index_score_topk(
             pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens, wl.num_rows,
