@@ -655,6 +655,11 @@ def main():
                      "bytes_per_launch": m["score_algorithmic_bytes"],
                      "launch_us_mean": m["score_us_mean"],
                      "launches_timed": m["score_launches_timed"],
+                     # the same launch repeated back to back outside the step (no other kernel
+                     # between the launches): the kernel's own rate without the step around it
+                     "launch_us_alone": m["kernel_us_alone"][m["score_kernel"]],
+                     "frac_alone": m["score_algorithmic_bytes"] / m["kernel_us_alone"][m["score_kernel"]]
+                                   / 1e3 / HBM_PEAK_GBPS,
                      "read_reference_GBps": m["read_reference"]["paged_GBps"],
                      "read_reference_contiguous_GBps": m["read_reference"]["contiguous_GBps"]},
         "cpu_baseline": m.get("cpu_baseline"),

@@ -1,0 +1,47 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the step's packed projection rows,
+and the HBM byte counters read from a committed rocprofv3 summary only while the scorer
+sources they were taken on are unchanged."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from sparse_attention_indexer_quant_amd.workloads import config  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+
+
+def test_packed_rows_hold_the_step_keys_and_weights():
+    wl = config("tiny_mxfp4")
+    proj, slots = bench.packed_rows(wl)
+    sk = wl.step_key_index()
+    assert proj.shape == (wl.num_rows, 128 + wl.heads)
+    assert np.array_equal(proj[:sk.size, :128], wl.key_bits[sk])
+    assert np.array_equal(proj[:, 128:], wl.wv_bits)
+    assert np.array_equal(slots[:sk.size], wl.key_slots[sk])
+    assert np.all(slots[sk.size:] == -1)
+
+
+def test_traffic_only_for_the_profiled_sources(tmp_path, monkeypatch):
+    text = open(bench.PROFILE_PMC.format(kernel="index_score_hist", workload="long_mxfp4")).read()
+    got = bench.measured_traffic("index_score_hist", "long_mxfp4")
+    vals = dict(l.split(" = ", 1) for l in text.splitlines() if " = " in l and not l.startswith("#"))
+    if vals["scorer_sources_sha256_16"] == bench.scorer_source_hash():
+        assert got == float(vals["hbm_bytes_per_launch"])
+    else:
+        assert got is None
+    # a summary taken on other sources gives no traffic
+    stale = text.replace(vals["scorer_sources_sha256_16"], "0" * 16)
+    (tmp_path / "index_score_hist_long_mxfp4_pmc.txt").write_text(stale)
+    monkeypatch.setattr(bench, "PROFILE_PMC", str(tmp_path / "{kernel}_{workload}_pmc.txt"))
+    assert bench.measured_traffic("index_score_hist", "long_mxfp4") is None
