@@ -141,6 +141,24 @@ def hist_segment_keys(wl):
     return dsa.score_segment_keys(wl.num_requests, wl.max_blocks)
 
 
+def histogram_bytes(logits, ends, seg, width):
+    """Bytes the scorer writes for the selection's histograms: per (row, segment of `seg`
+    keys) holding keys of the row, 64 coarse 16-bit counts and one 128-B block of fine counts
+    for every coarse bin (top 6 bits of the order-preserving key, -0 as +0) its logits reach."""
+    total = 0
+    for r, e in enumerate(ends):
+        e = int(min(max(int(e), 0), width))
+        if e == 0:
+            continue
+        u = np.ascontiguousarray(logits[r, :e]).view(np.uint32)
+        u = np.where(u == 0x80000000, np.uint32(0), u)
+        key = np.where(u >> 31 == 1, ~u, u | np.uint32(0x80000000))
+        coarse = key >> 26
+        for s0 in range(0, e, seg):
+            total += 128 + 128 * np.unique(coarse[s0:s0 + seg]).size
+    return int(total)
+
+
 class Setup:
     """Device buffers of one workload, the cache replicas, and the prepared step calls."""
 
@@ -291,10 +309,16 @@ class Setup:
         per_row_q = rb + 2 * wl.heads
         self.score_bytes = wl.key_bytes() + 4 * self.pairs + wl.num_rows * per_row_q
         self.score_flops = 2 * wl.heads * 128 * self.pairs
-        # score_paged_hist also writes, per (row, scoring workgroup) holding keys of the row, an
-        # 8 KB histogram and its 128 B of coarse sums
+        # score_paged_hist also writes, per (row, scoring workgroup) holding keys of the row, the
+        # 64 coarse counts (128 B) and the 128-B fine block of each coarse bin its logits reach
+        # (counted from the logits of one step)
         seg = hist_segment_keys(wl)
-        self.hist_bytes = int(sum((8192 + 128) * ((int(e) + seg - 1) // seg) for e in ends))
+        if self.inline_ok:
+            self.step_inline(0)
+        else:
+            self.step(0)
+        torch.cuda.synchronize()
+        self.hist_bytes = histogram_bytes(self.logits.cpu().numpy(), ends, seg, wl.width)
         self.score_hist_bytes = self.score_bytes + self.hist_bytes
         # index_score_hist reads the BF16 query rows, raw head weights and pre-norm keys instead
         # of the quantized rows and weights, and also writes the step's keys and row layout

@@ -851,14 +851,18 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
                 const uint4 *src = reinterpret_cast<const uint4 *>(hist + j * (kBins / 2)) +
                                    2 * threadIdx.x;
                 const uint4 a = src[0], b = src[1];
-                dst[0] = a;
-                dst[1] = b;
                 uint32_t s16 = 0;
                 const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s16 += (w8[e] & 0xFFFFu) + (w8[e] >> 16);
                 s16 += lane_xor<1>(s16);
                 s16 += lane_xor<2>(s16);
+                // a fine block goes out only where its coarse count is nonzero (most of the
+                // 64 are empty); the selection reads a block only where the count says so
+                if (s16 != 0) {
+                    dst[0] = a;
+                    dst[1] = b;
+                }
                 if ((threadIdx.x & 3) == 0)
                     coarse[at * kCoarseBins + (threadIdx.x >> 2)] = (uint16_t)s16;
             }

@@ -167,6 +167,19 @@ __device__ __forceinline__ uint32_t count8(const uint4 &w, int i) {
     return (i & 1) ? d >> 16 : d & 0xFFFFu;
 }
 
+// Word p8 of fine block B (fine bins 64 B .. 64 B + 63) of segment sg, read by the eight
+// consecutive lanes of the segment, or zero where the segment has no key in coarse bin B: the
+// scorer writes a segment's fine blocks only where its coarse count is nonzero (the rest of a
+// reused workspace keeps earlier bytes). `cw` is the lane's word p8 of the segment's coarse
+// counts; the count of bin B is in word B / 8, held by the segment's lane p8 = B / 8. Every lane
+// of the wavefront calls it (a lane exchange).
+__device__ __forceinline__ uint4 fine_word(const uint4 *fine, int64_t sg, uint32_t B, int p8,
+                                           const uint4 &cw, bool live) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t cb = (uint32_t)__shfl((int)count8(cw, (int)(B & 7)), (lane & ~7) | (int)(B >> 3));
+    return live && cb != 0 ? fine[sg * (kBins / 8) + B * 8 + p8] : make_uint4(0, 0, 0, 0);
+}
+
 // Sum over the lanes of a wavefront that share t % 8 (lanes t % 8 + 8 j), in every one of
 // them, in registers: a DPP rotate by 8 within each row of 16, then the cross-row swaps
 // (with the value as both operands, each swap pairs rows 0-1 / 2-3, then halves).
@@ -264,13 +277,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const uint32_t B = 63u - found_c;  // coarse bin, in ascending order
 
     // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
-    const uint4 fw0 = s0 < row_segments ? fine[(int64_t)s0 * (kBins / 8) + B * 8 + p8] : zero4;
+    const uint4 fw0 = fine_word(fine, s0, B, p8, cw0, s0 < row_segments);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = count8(fw0, e);
     for (int i = 1; i < blocks; ++i) {
         const int sg = s0 + i * kSegBlock;
-        const uint4 w = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+        const uint4 cw = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
+        const uint4 w = fine_word(fine, sg, B, p8, cw, sg < row_segments);
 #pragma unroll
         for (int e = 0; e < 8; ++e) fsum[e] += count8(w, e);
     }
@@ -303,7 +317,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
         uint4 cw = cw0, fw = fw0;
         if (i > 0) {
             cw = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
-            fw = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+            fw = fine_word(fine, sg, B, p8, cw, sg < row_segments);
         }
         uint32_t up = 0, in = 0;
 #pragma unroll
@@ -526,9 +540,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
 
     // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
     const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
-    const uint4 fw0 = s0 < row_segments ? fine[(int64_t)s0 * (kBins / 8) + B * 8 + p8] : zero4;
-    const uint4 fw1 =
-        s0 + 32 < row_segments ? fine[(int64_t)(s0 + 32) * (kBins / 8) + B * 8 + p8] : zero4;
+    const uint4 fw0 = fine_word(fine, s0, B, p8, cw0, s0 < row_segments);
+    const uint4 fw1 = fine_word(fine, s0 + 32, B, p8, cw1, s0 + 32 < row_segments);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw0, e) + count8(fw1, e));
@@ -742,7 +755,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     const uint32_t B = 63u - found_c;
     // (b) the fine bins inside B and the fine bin f
     const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
-    const uint4 fw = sg < row_segments ? fine[(int64_t)sg * (kBins / 8) + B * 8 + p8] : zero4;
+    const uint4 fw = fine_word(fine, sg, B, p8, cw, sg < row_segments);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw, e));

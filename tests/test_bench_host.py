@@ -45,3 +45,13 @@ def test_traffic_only_for_the_profiled_sources(tmp_path, monkeypatch):
     (tmp_path / "index_score_hist_long_mxfp4_pmc.txt").write_text(stale)
     monkeypatch.setattr(bench, "PROFILE_PMC", str(tmp_path / "{kernel}_{workload}_pmc.txt"))
     assert bench.measured_traffic("index_score_hist", "long_mxfp4") is None
+
+
+def test_histogram_bytes_count_the_coarse_bins_reached():
+    # order keys: 1.0 -> coarse 47, 2.0 -> 48, -1.0 -> 16, -0.0 and 0.0 -> 32
+    lg = np.array([[1.0, 2.0, -1.0, -0.0, 0.0, 7.0, 7.0, 7.0]], np.float32)
+    assert bench.histogram_bytes(lg, np.array([5]), 8, 8) == 128 + 4 * 128
+    assert bench.histogram_bytes(lg, np.array([5]), 2, 8) == (128 + 256) * 2 + (128 + 128)
+    assert bench.histogram_bytes(lg, np.array([0]), 2, 8) == 0
+    # bound clamped to the width; 7.0 shares coarse bin 48 with 2.0
+    assert bench.histogram_bytes(lg, np.array([99]), 8, 8) == 128 + 4 * 128
