@@ -13,7 +13,9 @@
 //   1. topk_hist (segments x rows): each workgroup histograms the top 12 key bits of its
 //      segment in LDS and stores the counts (16-bit) in the workspace. (The scorer can write
 //      these histograms itself, segment = one scoring workgroup's keys; then the selection
-//      starts at step 2.)
+//      starts at step 2. It writes a segment's block of 64 fine counts only where the block's
+//      coarse sum is nonzero, so the steps below read fine blocks through the coarse sums,
+//      fine_word.)
 //   2. topk_threshold (one workgroup per row): rows with row_end <= k are written here
 //      directly. Otherwise it sums the row's segment histograms, finds the bin b holding the
 //      k-th largest key, then counts each segment's keys above b and inside b and stores

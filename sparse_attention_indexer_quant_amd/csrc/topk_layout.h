@@ -27,7 +27,8 @@ struct RowState {
 
 struct TopkWorkspace {
     RowState *state;
-    uint16_t *seghist;  // [rows][nseg][kBins]
+    uint16_t *seghist;  // [rows][nseg][kBins]; a block of 64 is valid only where its coarse sum
+                        // is nonzero (the scorer skips empty blocks)
     uint16_t *coarse;   // [rows][nseg][kCoarseBins]: sums of 64 consecutive fine bins
     uint2 *segoff;      // [rows][nseg]: first output slot, first candidate slot
     uint2 *cand;        // [rows][kCandCap]: order key, position
