@@ -202,9 +202,10 @@ struct StepQueryLds {
 };
 
 // Query operands, head weights and key bounds of one group of RG rows. With OPS_IN_LDS (the
-// fused step inputs of four-row groups) the operands stay in the workgroup's LDS tiles and each
-// page reads them there: holding a four-row group in registers took the kernel to about 200
-// VGPRs, two wavefronts per SIMD, too few to hide the math's dependency chains.
+// fused step inputs of four-row MXFP4 and two-row FP8 groups) the operands stay in the
+// workgroup's LDS tiles and each page reads them there: holding them in registers took a
+// four-row MXFP4 group to about 200 VGPRs (two wavefronts per SIMD) and a two-row FP8 group,
+// whose operands are widened to BF16, past the 256 VGPRs into AGPRs.
 template <int FMT, int H, int RG, bool OPS_IN_LDS = false>
 struct RowGroup {
     static constexpr int HT = H / 16;
@@ -216,9 +217,9 @@ struct RowGroup {
     int ops_lane = 0;
     int rend[RG];
 
-    __device__ __forceinline__ uint4 qa_at(int j, int ht) const {
-        if constexpr (OPS_IN_LDS) return ops->qa[j * HT + ht][0][ops_lane];
-        else return qa[j][ht][0];
+    __device__ __forceinline__ uint4 qa_at(int j, int ht, int part = 0) const {
+        if constexpr (OPS_IN_LDS) return ops->qa[j * HT + ht][part][ops_lane];
+        else return qa[j][ht][part];
     }
     __device__ __forceinline__ int qs_at(int j, int ht) const {
         if constexpr (OPS_IN_LDS) return ops->qs[j * HT + ht][ops_lane];
@@ -332,8 +333,11 @@ struct RowGroup {
                 for (int ht = 0; ht < HT; ++ht) {
                     if constexpr (FMT == kFmtMxfp4)
                         c[j][ht] = mfma_fp4_tile(qa_at(j, ht), pg.kp[t][0], qs_at(j, ht), (int)ksw, t);
-                    else
-                        c[j][ht] = mfma_bf16_head(qa[j][ht], kb);
+                    else {
+                        const uint4 q4[4] = {qa_at(j, ht, 0), qa_at(j, ht, 1), qa_at(j, ht, 2),
+                                             qa_at(j, ht, 3)};
+                        c[j][ht] = mfma_bf16_head(q4, kb);
+                    }
                 }
             }
 #pragma unroll
@@ -691,7 +695,9 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
 
     // Query operands of the first row group, in flight together with the row bounds.
     const int ngroups = (nrows + RG - 1) / RG;
-    RowGroup<FMT, H, RG, FUSED && RG == 4> rows;
+    // the fused operands of four-row MXFP4 groups and two-row FP8 groups (FP8 operands are
+    // widened to BF16, twice the registers) stay in the LDS
+    RowGroup<FMT, H, RG, FUSED && (RG == 4 || (is_fp8(FMT) && RG == 2))> rows;
     int kmax;
     // FUSED: the raw query tiles and head weights of this wavefront's share, and the step's
     // keys (one row each; a key past the rows reads the first row's)
