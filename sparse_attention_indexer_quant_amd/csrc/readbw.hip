@@ -40,7 +40,7 @@ __device__ __forceinline__ uint32_t xor_section(const SectionRegs<TILES> &r) {
 // entry that names no page, reads page 0 and is not counted), so the hardware wait before each
 // page's XOR counts exactly and the loads of the next pages stay in flight.
 template <int TILES>
-__global__ __launch_bounds__(256) void read_sections_kernel(
+__global__ __launch_bounds__(64 * kScoreWaves) void read_sections_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     int64_t max_blocks, int64_t num_requests, int pages_per_wave,
     const uint8_t *__restrict__ cache, int64_t page_stride, int64_t num_pages,
@@ -104,7 +104,7 @@ hipError_t launch_read_sections(int fmt, const void *cache, int64_t num_pages, i
                                 int64_t max_blocks, const int32_t *seq_lens, uint32_t *out,
                                 hipStream_t stream) {
     const ScoreGeometry geo = score_geometry(num_requests, max_blocks);
-    const dim3 grid((unsigned)(geo.chunks * num_requests)), block(256);
+    const dim3 grid((unsigned)(geo.chunks * num_requests)), block(64 * kScoreWaves);
     if (fmt == kFmtMxfp4)
         hipLaunchKernelGGL(read_sections_kernel<4>, grid, block, 0, stream, block_table, seq_lens,
                            max_blocks, num_requests, geo.pages_per_wave,

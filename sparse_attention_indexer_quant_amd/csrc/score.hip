@@ -48,6 +48,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kScoreWaves;
+// the histogram flush gives each lane of the workgroup 16 consecutive fine bins
+static_assert(64 * kWaves * 16 == kBins, "one flush lane per 16 fine bins");
 constexpr int kMaxPagesPerWave = 16;
 
 // A's scale is byte 0 of `sa`; B's is byte T of `sb` (T = the key tile: the page's scale
@@ -588,7 +590,7 @@ constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 // new key normalizes, quantizes and inserts that key and scores its own copy of it, and the
 // workgroups of chunk 0 write query_starts and row_ends.
 template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false>
-__global__ __launch_bounds__(256) void score_paged_kernel(
+__global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
     int64_t max_blocks, int64_t num_requests, int pages_per_wave,
     const uint8_t *__restrict__ cache, int64_t page_stride, int64_t num_pages, int64_t chunks,
@@ -753,8 +755,8 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
             if (i >= nrows || pos < 0 || pos >= width) continue;
             const int64_t rel = (pos >> 6) - chunk_begin;
             if (rel < 0 || rel >= kWaves * (int64_t)PW || (rel & (kWaves - 1)) != wave) continue;
-            if (table_page((int)(rel >> 2)) < 0) continue;
-            own_pp = (int)(rel >> 2);
+            if (table_page((int)(rel / kWaves)) < 0) continue;
+            own_pp = (int)(rel / kWaves);
             own_mask |= 1u << i;
             own_o[i] = (int)(pos & 63);
         }
@@ -813,7 +815,7 @@ __global__ __launch_bounds__(256) void score_paged_kernel(
         const int count = (int)(r1 - first);
         if constexpr (HIST) {
             __syncthreads();  // the previous group's histograms are written out
-            for (int i = threadIdx.x; i < RG * (kBins / 2); i += 256) hist[i] = 0;
+            for (int i = threadIdx.x; i < RG * (kBins / 2); i += 64 * kWaves) hist[i] = 0;
             __syncthreads();
         }
         if constexpr (FUSED) {  // the page of new keys (a fused launch has one row group)
@@ -896,12 +898,12 @@ static int device_cus() {
 // flight already cover the memory latency. A small workload spreads over more wavefronts with
 // fewer pages each: the launch is then as long as one wavefront's start and few pages.
 int score_pages_per_wave(int64_t num_requests, int64_t max_blocks) {
-    const int64_t target_waves = (int64_t)device_cus() * 4;
+    const int64_t target_waves = (int64_t)device_cus() * kWaves;
     int64_t ppw = (num_requests * max_blocks + target_waves - 1) / target_waves;
     if (ppw > 4) ppw = (ppw + 3) / 4 * 4;
     int p = (int)(ppw < 1 ? 1 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw));
     // a row spans at most kMaxRowSegments scoring workgroups
-    while (p < kMaxPagesPerWave && (max_blocks + 4 * p - 1) / (4 * p) > kMaxRowSegments)
+    while (p < kMaxPagesPerWave && (max_blocks + kWaves * p - 1) / (kWaves * p) > kMaxRowSegments)
         p = p < 4 ? p + 1 : p + 4;
     return p;
 }
@@ -919,7 +921,7 @@ template <int FMT, int H, int RG, bool HIST, bool FUSED = false>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream,
                                   const FusedInputs &fin = FusedInputs{}) {
     const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
-    const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(256);
+    const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(64 * kWaves);
     // page buffers per wavefront: 3 for MXFP4 (measured best of 2-6 on the long-context
     // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
     // take the registers a deeper ring would need)
