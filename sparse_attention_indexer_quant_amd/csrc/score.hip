@@ -636,10 +636,24 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const int64_t chunk_begin = chunk * kWaves * (int64_t)PW;
     const int64_t blk_first = chunk_begin + wave;
     auto block_of = [&](int p) -> int64_t { return blk_first + (int64_t)kWaves * p; };
-    // At wave launch (every operand is a preloaded argument): the request's rows (scalar loads;
-    // nothing before them in the kernel writes memory) and this wavefront's slice of the block
-    // table (one entry per lane; every entry below max_blocks is in bounds). Then every other
-    // argument at once, in the same round trip.
+    // At wave launch (every operand is a preloaded argument): this wavefront's slice of the
+    // block table (one entry per lane; every entry below max_blocks is in bounds), then the
+    // request's rows (nothing before these loads in the kernel writes memory). The table slice
+    // goes first because the fused form's first-row sum waits for its own loads, and a wait
+    // covers every load issued before it. Then every other argument at once.
+    const int32_t *bt = block_table + req * max_blocks;
+    const int bt_lane = lane < PW && block_of(lane) < max_blocks ? bt[block_of(lane)] : -1;
+    // FUSED one-row groups: the query and head weights of row `req` go out in the same round
+    // trip, before the request's first row is known. Where every request has one row (decode)
+    // that is its row, and the query's quantization then overlaps the first pages' loads
+    // instead of waiting for a second round trip; otherwise they are loaded again below.
+    // A launch has at least one row, so `spec_row` is a row of the inputs.
+    constexpr bool kSpecQuery = FUSED && RG == 1;
+    const int64_t spec_row = req < num_rows ? req : num_rows - 1;
+    StepQuery<FMT, H, RG> sq;
+    if constexpr (kSpecQuery)
+        sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride, fin.w_in,
+                fin.proj_row_stride, spec_row, spec_row + 1, wave, l16, grp);
     int64_t r0, r1;
     int qlen = 0, seq = 0;
     if constexpr (!FUSED) {
@@ -653,8 +667,6 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
         r0 = request_first_row(query_starts, req, lane);
         r1 = r0 + qlen;
     }
-    const int32_t *bt = block_table + req * max_blocks;
-    const int bt_lane = lane < PW && block_of(lane) < max_blocks ? bt[block_of(lane)] : -1;
     hoist_args(num_pages, chunks, q, q_row_stride, w, w_row_stride, row_ends, num_rows,
                max_query_len, logits, logits_row_stride, seghist, coarse);
     if constexpr (FUSED) {
@@ -701,9 +713,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     // widened to BF16, twice the registers) stay in the LDS
     RowGroup<FMT, H, RG, FUSED && (RG == 4 || (is_fp8(FMT) && RG == 2))> rows;
     int kmax;
-    // FUSED: the raw query tiles and head weights of this wavefront's share, and the step's
-    // keys (one row each; a key past the rows reads the first row's)
-    StepQuery<FMT, H, RG> sq;
+    // FUSED: the step's keys (one row each; a key past the rows reads the first row's)
     KeyLane key;  // columns 2 lane, 2 lane + 1 of the LayerNorm weights and biases
     uint32_t key_pair[FUSED ? RG : 1];
     if constexpr (!FUSED) {
@@ -716,8 +726,9 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
         // the bounds need no loads here: a chunk past the request's keys leaves before any
         // query work (no new key lies in it: every key's position is below the last bound)
         if (chunk_begin * kPageTokens >= kmax) return;
-        sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride, fin.w_in,
-                fin.proj_row_stride, r0, r1, wave, l16, grp);
+        if (!kSpecQuery || r0 != spec_row)
+            sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride,
+                    fin.w_in, fin.proj_row_stride, r0, r1, wave, l16, grp);
         key = load_key(fin.key_in + r0 * fin.proj_row_stride, fin.gamma, fin.beta, nullptr, lane);
         key_pair[0] = key.pair;
 #pragma unroll
