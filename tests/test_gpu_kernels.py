@@ -372,6 +372,13 @@ FUSED_CASES = {
                            num_rows=7, page_stride=9216, section_offset=512),
     "fp8mx_h16_edges": dict(fmt="fp8_mx", heads=16, seq_lens=[2, 130, 65, 700], query_lens=[2, 0, 2, 1],
                             num_rows=8, outlier_frac=0.01, outlier_gain=20.0),
+    # one-row groups whose first row is not the request's index (requests with no rows before
+    # them), more requests than rows, and a padding row: the query each workgroup loads before
+    # its row is known is the wrong one here and must be replaced
+    "fp4_h32_one_row_gaps": dict(fmt="mxfp4", heads=32, seq_lens=[70, 5, 300, 64, 1, 130],
+                                 query_lens=[1, 0, 1, 1, 0, 1], num_rows=5),
+    "fp8_h16_one_row_gaps": dict(fmt="fp8", heads=16, seq_lens=[200, 9, 64, 65],
+                                 query_lens=[0, 1, 1, 1], num_rows=3),
 }
 
 
