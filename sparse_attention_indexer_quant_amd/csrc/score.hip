@@ -136,6 +136,22 @@ __device__ __forceinline__ float relu_dot4(const v4f &c, const uint2 &w, float a
     return acc;
 }
 
+// The same sum with the weights already in FP32, in the same order.
+__device__ __forceinline__ float relu_dot4(const v4f &c, const float4 &w, float acc) {
+    acc = fmaf(w.x, relu(c[0]), acc);
+    acc = fmaf(w.y, relu(c[1]), acc);
+    acc = fmaf(w.z, relu(c[2]), acc);
+    acc = fmaf(w.w, relu(c[3]), acc);
+    return acc;
+}
+
+// 4 BF16-valued floats back to the packed BF16 pair layout of the registers (exact: their
+// low 16 bits are zero).
+__device__ __forceinline__ uint2 bf16_pair_bits(const float4 &w) {
+    return make_uint2((__float_as_uint(w.x) >> 16) | (__float_as_uint(w.y) & 0xFFFF0000u),
+                      (__float_as_uint(w.z) >> 16) | (__float_as_uint(w.w) & 0xFFFF0000u));
+}
+
 // Head sum across the four lane groups (rows of 16 lanes) for the page's four token tiles,
 // leaving tile t's token n in lane 16 t + n; p_t holds each lane's partial for tile t.
 // A reduce-scatter on the cross-row swap instructions: swapping halves pairs tiles (0, 2)
@@ -199,7 +215,9 @@ struct StepQueryLds {
     static constexpr int kTiles = RG * (H / 16);
     static constexpr int kParts = FMT == kFmtMxfp4 ? 1 : 4;  // FP8: 32 values widened to BF16
     uint4 qa[kTiles][kParts][64];
-    uint2 wt[kTiles][64];
+    // the lane's 4 head weights, BF16 values held as FP32 (exact), so that a page's weighted
+    // head sum reads them ready to use instead of widening them on every page
+    float4 wt[kTiles][64];
     int qs[kTiles][FMT == kFmtMxfp4 ? 64 : 1];
 };
 
@@ -227,7 +245,8 @@ struct RowGroup {
         if constexpr (OPS_IN_LDS) return ops->qs[j * HT + ht][ops_lane];
         else return qs[j][ht];
     }
-    __device__ __forceinline__ uint2 wt_at(int j, int ht) const {
+    // OPS_IN_LDS: 4 FP32 weights from the LDS tile; else 4 BF16 weights from registers
+    __device__ __forceinline__ auto wt_at(int j, int ht) const {
         if constexpr (OPS_IN_LDS) return ops->wt[j * HT + ht][ops_lane];
         else return wt[j][ht];
     }
@@ -282,7 +301,7 @@ struct RowGroup {
                     for (int k = 0; k < (FMT == kFmtMxfp4 ? 1 : 4); ++k)
                         qa[j][ht][k] = s.qa[j * HT + ht][k][lane];
                     qs[j][ht] = FMT == kFmtMxfp4 ? s.qs[j * HT + ht][lane] : 0;
-                    wt[j][ht] = s.wt[j * HT + ht][lane];
+                    wt[j][ht] = bf16_pair_bits(s.wt[j * HT + ht][lane]);
                 }
             }
         }
@@ -439,7 +458,8 @@ struct StepQuery {
                 wb[i] = bf16_bits_rne(__fmul_rn(bf16_val((uint16_t)wraw[m][i]), c_h));
             s.qa[it][0][lane] = make_uint4(out[0], out[1], out[2], out[3]);
             s.qs[it][lane] = ex + 127;
-            s.wt[it][lane] = make_uint2(wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16));
+            s.wt[it][lane] = make_float4(__uint_as_float(wb[0] << 16), __uint_as_float(wb[1] << 16),
+                                         __uint_as_float(wb[2] << 16), __uint_as_float(wb[3] << 16));
         }
     }
 
@@ -490,7 +510,8 @@ struct StepQuery {
                 const float si = __shfl(sc, 4 * grp + i);  // head 4 grp + i of the tile
                 wb[i] = bf16_bits_rne(__fmul_rn(__fmul_rn(bf16_val((uint16_t)wraw[m][i]), si), c_h));
             }
-            s.wt[it][lane] = make_uint2(wb[0] | (wb[1] << 16), wb[2] | (wb[3] << 16));
+            s.wt[it][lane] = make_float4(__uint_as_float(wb[0] << 16), __uint_as_float(wb[1] << 16),
+                                         __uint_as_float(wb[2] << 16), __uint_as_float(wb[3] << 16));
         }
     }
 };
