@@ -602,12 +602,14 @@ constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 // arguments the first loads need come first: the library is built to preload the leading
 // kernel arguments into scalar registers at wave launch.
 //
-// FUSED (MXFP4 with histograms, one row group per request): the step's inputs are made here
+// FUSED (with histograms, one row group per request: up to 4 rows for MXFP4, 2 for FP8 and
+// FP8 "mx"): the step's inputs are made here
 // instead of read -- `query_starts` holds the query lengths and `q` the BF16 query -- and the
 // result equals the step-input kernel with decode_layout followed by the plain launch, with
 // each row's new key at position seq - qlen + i of its request (the slot its block table
 // gives): the rows come from the lengths' prefix sum, the bounds from the sequence length, the
-// query operands are quantized by each wavefront, the wavefront that scores a page holding a
+// query operand tiles are quantized by the workgroup's wavefronts in turn and meet in the LDS,
+// the wavefront that scores a page holding a
 // new key normalizes, quantizes and inserts that key and scores its own copy of it, and the
 // workgroups of chunk 0 write query_starts and row_ends.
 template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false>
