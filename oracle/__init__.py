@@ -9,9 +9,13 @@ Every function takes and returns numpy arrays holding raw bits: BF16 as
 ``dsaidx_oracle.c`` (plain C, built with gcc and no floating-point contraction).
 
 Parity is pinned for every function here by the tests under ``tests/`` marked
-``not gpu``; the one reading with no outside pin is the LayerNorm reduction
-order, whose exact bits are pinned only against the fixed tree order (the
-result is pinned to within one BF16 step of the exact LayerNorm).
+``not gpu``. The LayerNorm follows the summation order the page shows (running
+totals of 8 consecutive columns per lane, pinned by a hand-worked key whose
+other orders give other bytes); three points of it stay unpinned because the
+page hides them: the lane combine (read as a butterfly over offsets 8, 4, 2, 1),
+whether the squares and the affine step are contracted to fused multiply-adds
+(read as not), and the rounding of the page's rsqrt (read as IEEE square root
+then IEEE divide).
 """
 from __future__ import annotations
 
@@ -59,6 +63,7 @@ def _load():
             "orc_ue8m0_byte": (I32, [F32]),
             "orc_pow2_ceil": (F32, [F32]),
             "orc_head_weight_scale": (F32, [I32]),
+            "orc_ln_sum128": (F32, [P]),
             "orc_layernorm128": (None, [P, P, P, F32, P]),
             "orc_quantize_queries": (I32, [I32, P, I64, I32, I64, I64, P, I64, P, I64, P, I64]),
             "orc_store_keys": (I32, [I32, P, I64, I64, P, P, F32, P, P, I64, I64]),
@@ -124,6 +129,13 @@ def pow2_ceil(x: float) -> float:
 
 def head_weight_scale(heads: int) -> float:
     return _load().orc_head_weight_scale(int(heads))
+
+
+def ln_sum128(z: np.ndarray) -> float:
+    """The LayerNorm's sum of 128 FP32 values in the order page "...cutedsl.dsa.index",
+    insert_key, shows (per-lane running totals of 8 columns, then the half-warp combine)."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    return _load().orc_ln_sum128(_ptr(z))
 
 
 def layernorm128(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:

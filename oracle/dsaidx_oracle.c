@@ -189,30 +189,44 @@ float orc_head_weight_scale(int heads) {
 /* Key LayerNorm ([idx] insert_key)                                         */
 /* ------------------------------------------------------------------------ */
 
-/* Sum of 128 FP32 values in a fixed pairwise tree: adjacent pairs first, then
- * halves folded onto the lower half (32, 16, 8, 4, 2, 1 apart). The page hides
- * its reduction order inside a half-warp sum; this tree is the order read for
- * it and both implementations follow it. */
-static float tree_sum128(const float *z) {
-    float u[64];
-    for (int l = 0; l < 64; ++l) u[l] = z[2 * l] + z[2 * l + 1];
-    for (int h = 32; h >= 1; h /= 2)
-        for (int l = 0; l < h; ++l) u[l] = u[l] + u[l + h];
-    return u[0];
+/* Sum of 128 FP32 values in the order [idx] insert_key shows: lane j of a
+ * half-warp holds columns 8j .. 8j+7 and adds them one by one to a running
+ * total that starts at 0; the sixteen lane totals are then combined by
+ * half_warp_sum, whose body the page does not print. It is read here as a
+ * butterfly over lane offsets 8, 4, 2, 1 (the descending order of the page's
+ * group_max): at each offset o every total t_j becomes t_j + t_(j xor o), and
+ * after the four steps every lane holds the same sum. */
+float orc_ln_sum128(const float *z) {
+    float t[16];
+    for (int j = 0; j < 16; ++j) {
+        float total = 0.0f;
+        for (int i = 0; i < 8; ++i) total += z[8 * j + i];
+        t[j] = total;
+    }
+    for (int o = 8; o >= 1; o /= 2) {
+        float next[16];
+        for (int j = 0; j < 16; ++j) next[j] = t[j] + t[j ^ o];
+        memcpy(t, next, sizeof t);
+    }
+    return t[0];
 }
 
 /* LayerNorm in FP32 of one 128-value key, then rounded to BF16 and widened
- * back to FP32: mean and variance over 128 values, rstd = 1 / sqrt(var + eps)
- * (IEEE square root, then IEEE divide), y = ((x - mean) * rstd) * gamma + beta. */
+ * back to FP32 ([idx] insert_key): mean = sum(x) / 128 and
+ * variance = sum((x - mean) * (x - mean)) / 128, both sums in the order of
+ * orc_ln_sum128, each square rounded before it is added (no fused multiply-
+ * add); rstd = 1 / sqrt(var + eps) (IEEE square root, then IEEE divide: the
+ * page's non-fast rsqrt is read as this); y = ((x - mean) * rstd) * gamma + beta
+ * with every operation rounded on its own. */
 void orc_layernorm128(const float *x, const float *gamma, const float *beta, float eps,
                       float *out) {
     float d[DIM], sq[DIM];
-    float mean = tree_sum128(x) / 128.0f;
+    float mean = orc_ln_sum128(x) / 128.0f;
     for (int i = 0; i < DIM; ++i) {
         d[i] = x[i] - mean;
         sq[i] = d[i] * d[i];
     }
-    float var = tree_sum128(sq) / 128.0f;
+    float var = orc_ln_sum128(sq) / 128.0f;
     float denom = sqrtf(var + eps);
     float rstd = 1.0f / denom;
     for (int i = 0; i < DIM; ++i) {

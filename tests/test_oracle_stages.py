@@ -8,7 +8,7 @@ import torch.nn.functional as F
 
 import oracle
 import npdecode
-from goldens import int_list, rows
+from goldens import byte_list, f32, int_list, layernorm_order_key, rows
 from sparse_attention_indexer_quant_amd.workloads import bf16_bits, bf16_to_f32, make_workload
 
 E2M1_GRID = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
@@ -49,6 +49,52 @@ def test_layernorm_within_one_bf16_step_of_exact():
                              torch.from_numpy(beta.astype(np.float64)), eps=1e-6).numpy()
         step = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
         assert np.all(np.abs(out - exact) <= step * 1.0001 + 1e-30), t
+
+
+def test_layernorm_page_summation_order_golden():
+    # tests/golden/layernorm_order.txt: a key whose sums, BF16 outputs and MXFP4 bytes differ
+    # between the page's per-lane running totals and other summation orders, worked by hand.
+    x, gamma, beta = layernorm_order_key()
+    gold = {}
+    for line in rows("layernorm_order.txt"):
+        kind, *vals = line.split()
+        gold.setdefault(kind, []).append(vals)
+    assert oracle.ln_sum128(x) == float(gold["sum"][0][0])
+    # a different order of the same values is not what the oracle computes
+    assert float(gold["mean_alternative_order_sum"][0][0]) != oracle.ln_sum128(x)
+    out = oracle.layernorm128(x, gamma, beta, 1e-6)
+    for col, val in gold["normed"]:
+        assert out[int(col)] == f32(val), col
+    cache = np.zeros(4352, np.uint8)
+    oracle.store_keys(bf16_bits(x).reshape(1, 128), gamma, beta, 1e-6, np.array([5]), cache, 1, 4352)
+    assert list(cache[5 * 64:6 * 64]) == byte_list(gold["mxfp4_payload"][0][0])
+    assert list(cache[4096 + 20:4096 + 24]) == byte_list(gold["mxfp4_scales"][0][0])
+    # every other byte of the section untouched
+    rest = np.delete(cache, np.r_[5 * 64:6 * 64, 4096 + 20:4096 + 24])
+    assert not rest.any()
+
+
+def test_ln_sum_running_totals_then_butterfly():
+    # Structure of the page's order on values where each step is exact except where stated:
+    # a lane's total absorbs ones into a leading 2^24 (ties to even), but ones summed before
+    # they meet 2^24 survive. Columns 0..7 = [1, 1, 1, 1, 1, 1, 1, 2^24]: the running total
+    # reaches 7 before adding 2^24, and 2^24 + 7 rounds to 2^24 + 8 (spacing 2, tie 7 -> 8).
+    z = np.zeros(128, np.float32)
+    z[:7] = 1.0
+    z[7] = 2.0 ** 24
+    assert oracle.ln_sum128(z) == 2.0 ** 24 + 8
+    # the same values in the other order (2^24 first) lose every one: 2^24
+    z2 = np.zeros(128, np.float32)
+    z2[0] = 2.0 ** 24
+    z2[1:8] = 1.0
+    assert oracle.ln_sum128(z2) == 2.0 ** 24
+    # ones in lanes that meet 2^24 only in the combine: lane j = 8 holds 2^24 alone, lanes
+    # 0..7 hold 8 ones each (total 8); offset 8 pairs lane 0 with lane 8: 8 + 2^24 (exact),
+    # then offsets 4, 2, 1 add 8 + 8, 16 + 16, 32 + ... -> 2^24 + 64 exactly.
+    z3 = np.zeros(128, np.float32)
+    z3[:64] = 1.0
+    z3[64] = 2.0 ** 24
+    assert oracle.ln_sum128(z3) == 2.0 ** 24 + 64
 
 
 # ---- quantize_queries layouts (page "...cutedsl.dsa.index", quantize_fp4_query, fp8_query) --
