@@ -172,6 +172,13 @@ __device__ __forceinline__ uint32_t quad_down(uint32_t v) {
     return __builtin_amdgcn_update_dpp(0u, v, c, 0xF, 0xF, false);
 }
 
+// value of lane 4 * (l / 4) + I (lane I of l's quad), in every lane
+template <int I>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+    static_assert(I >= 0 && I <= 3, "inside a quad");
+    return __builtin_amdgcn_update_dpp(0u, v, I * 0x55, 0xF, 0xF, false);  // quad_perm [I,I,I,I]
+}
+
 // value of lane l + D (D = 4, 8, 12) inside each row of 16 lanes, for lane l % 16 == 0
 template <int D>
 __device__ __forceinline__ uint32_t row_down(uint32_t v) {

@@ -32,31 +32,45 @@ __device__ __forceinline__ KeyLane load_key(const uint16_t *__restrict__ key,
     return k;
 }
 
-// The lane's two LayerNorm outputs (columns 2l, 2l+1), rounded to BF16. The sums run as the
-// pairwise tree "adjacent pair, then fold 32, 16, 8, 4, 2, 1 apart", which the exchanges below
-// compute in every lane with exact partners.
+// Sum of the key's 128 values in the order insert_key uses: 16 running totals, total j adding
+// columns 8j .. 8j+7 one at a time to 0, then the totals combined by a butterfly over total
+// offsets 8, 4, 2, 1 (the page hides that combine; read as the order of its group_max). Here
+// total j is formed, the same in every lane, by the quad of lanes 4j .. 4j+3 (which hold its
+// columns two per lane), so the butterfly's total offsets are lane offsets 32, 16, 8, 4.
+// `v` holds the quad's eight values in column order.
+__device__ __forceinline__ float page_order_sum(const float (&v)[8]) {
+    auto add_rn = [](float a, float b) { return __fadd_rn(a, b); };
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t = __fadd_rn(t, v[i]);
+    t = xor_combine<32>(t, add_rn);
+    t = xor_combine<16>(t, add_rn);
+    t = xor_combine<8>(t, add_rn);
+    t = xor_combine<4>(t, add_rn);
+    return t;
+}
+
+// The lane's two LayerNorm outputs (columns 2l, 2l+1), rounded to BF16: mean = S(x) / 128,
+// variance = S((x - mean) * (x - mean)) / 128 with each square rounded before it is added,
+// rstd = 1 / sqrt(variance + eps) (IEEE square root, then IEEE divide), y = ((x - mean) *
+// rstd) * gamma + beta, every step one RN operation.
 __device__ __forceinline__ void layer_norm_pair(const KeyLane &in, float eps, float &n0,
                                                 float &n1) {
     const float x0 = bf16_lo(in.pair), x1 = bf16_hi(in.pair);
-    auto add_rn = [](float a, float b) { return __fadd_rn(a, b); };
-    float sum = __fadd_rn(x0, x1);
-    sum = xor_combine<32>(sum, add_rn);
-    sum = xor_combine<16>(sum, add_rn);
-    sum = xor_combine<8>(sum, add_rn);
-    sum = xor_combine<4>(sum, add_rn);
-    sum = xor_combine<2>(sum, add_rn);
-    sum = xor_combine<1>(sum, add_rn);
-    const float mean = __fmul_rn(sum, 0.0078125f);
-    const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
-    float sq = __fadd_rn(__fmul_rn(d0, d0), __fmul_rn(d1, d1));
-    sq = xor_combine<32>(sq, add_rn);
-    sq = xor_combine<16>(sq, add_rn);
-    sq = xor_combine<8>(sq, add_rn);
-    sq = xor_combine<4>(sq, add_rn);
-    sq = xor_combine<2>(sq, add_rn);
-    sq = xor_combine<1>(sq, add_rn);
-    const float var = __fmul_rn(sq, 0.0078125f);
+    float v[8];  // columns 8 (l / 4) .. 8 (l / 4) + 7: the pairs of the lane's quad
+    const uint32_t q0 = quad_bcast<0>(in.pair), q1 = quad_bcast<1>(in.pair),
+                   q2 = quad_bcast<2>(in.pair), q3 = quad_bcast<3>(in.pair);
+    v[0] = bf16_lo(q0), v[1] = bf16_hi(q0), v[2] = bf16_lo(q1), v[3] = bf16_hi(q1);
+    v[4] = bf16_lo(q2), v[5] = bf16_hi(q2), v[6] = bf16_lo(q3), v[7] = bf16_hi(q3);
+    const float mean = __fmul_rn(page_order_sum(v), 0.0078125f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float d = __fsub_rn(v[i], mean);
+        v[i] = __fmul_rn(d, d);
+    }
+    const float var = __fmul_rn(page_order_sum(v), 0.0078125f);
     const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
+    const float d0 = __fsub_rn(x0, mean), d1 = __fsub_rn(x1, mean);
     n0 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d0, rstd), in.g.x), in.b.x));
     n1 = bf16_round(__fadd_rn(__fmul_rn(__fmul_rn(d1, rstd), in.g.y), in.b.y));
 }

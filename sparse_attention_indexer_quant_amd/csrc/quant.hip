@@ -164,28 +164,32 @@ __global__ __launch_bounds__(256) void store_keys_kernel(
 // Many keys (a cache fill): LPK = 8 lanes per key, eight keys per wavefront, 16 columns per
 // lane from two 16-byte loads. One key per wavefront spends most of its instructions on work
 // done once per key (the sums' exchanges, the square root and division, the scale), with 64
-// lanes for 128 values; here that work serves eight keys at once. The LayerNorm sums follow the
-// same pairwise tree as layer_norm_pair -- adjacent pairs, then folds 32, 16, 8, 4, 2, 1 apart
-// over the 64 pair sums -- with pair sum S l + m in slot m of lane l (S = 64 / LPK slots): the
-// folds of 32 .. S apart pair lanes l ^ (LPK / 2) .. l ^ 1 (same slot), the smaller folds pair
-// slots inside the lane. Every operation has the same two operands as there, so the bytes are
-// the same.
+// lanes for 128 values; here that work serves eight keys at once. The LayerNorm sums follow
+// insert_key's order, as layer_norm_pair does: 16 running totals of 8 consecutive columns, each
+// starting at 0, combined by a butterfly over total offsets 8, 4, 2, 1. Lane `sub` of a key
+// holds totals P sub .. P sub + P - 1 (P = 16 / LPK), so an offset of P or more pairs lanes
+// sub ^ (offset / P) and a smaller one pairs totals inside the lane. Every operation has the
+// same two operands as on one wavefront, so the bytes are the same.
 template <int LPK>
-__device__ __forceinline__ float bulk_tree_sum(float (&p)[64 / LPK]) {
-    constexpr int S = 64 / LPK;  // pair sums per lane
+__device__ __forceinline__ float bulk_page_sum(const float (&z)[128 / LPK]) {
+    constexpr int P = 16 / LPK;  // running totals per lane
     auto add_rn = [](float a, float c) { return __fadd_rn(a, c); };
+    float t[P];
 #pragma unroll
-    for (int m = 0; m < S; ++m) {
-        if constexpr (LPK >= 16) p[m] = xor_combine<8>(p[m], add_rn);
-        if constexpr (LPK >= 8) p[m] = xor_combine<4>(p[m], add_rn);
-        p[m] = xor_combine<2>(p[m], add_rn);
-        p[m] = xor_combine<1>(p[m], add_rn);
+    for (int m = 0; m < P; ++m) {
+        t[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[m] = __fadd_rn(t[m], z[8 * m + i]);
     }
 #pragma unroll
-    for (int h = S / 2; h >= 1; h /= 2)
-#pragma unroll
-        for (int m = 0; m < h; ++m) p[m] = __fadd_rn(p[m], p[m + h]);
-    return p[0];
+    for (int m = 0; m < P; ++m) {  // offsets 8, 4, 2 (P = 2) or 8, 4, 2, 1 (P = 1) across lanes
+        t[m] = xor_combine<8 / P>(t[m], add_rn);
+        t[m] = xor_combine<4 / P>(t[m], add_rn);
+        t[m] = xor_combine<2 / P>(t[m], add_rn);
+        if constexpr (P == 1) t[m] = xor_combine<1>(t[m], add_rn);
+    }
+    if constexpr (P == 2) return __fadd_rn(t[0], t[1]);  // offset 1 inside the lane
+    else return t[0];
 }
 
 // value of lane l + D inside its row of 16 lanes (D < 16 - l % 16)
@@ -202,7 +206,6 @@ __global__ __launch_bounds__(256) void store_keys_bulk_kernel(
     int64_t page_stride) {
     static_assert(LPK == 8 || LPK == 16, "8 or 16 lanes per key");
     constexpr int C = 128 / LPK;  // columns per lane
-    constexpr int S = C / 2;      // pair sums per lane
     const int sub = threadIdx.x & (LPK - 1);  // the lane's place among its key's lanes
     const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPK;
     const int64_t tk = t < tokens ? t : tokens - 1;  // lanes past the end redo the last key
@@ -235,17 +238,14 @@ __global__ __launch_bounds__(256) void store_keys_bulk_kernel(
         g[4 * i] = gv[i].x, g[4 * i + 1] = gv[i].y, g[4 * i + 2] = gv[i].z, g[4 * i + 3] = gv[i].w;
         b[4 * i] = bv[i].x, b[4 * i + 1] = bv[i].y, b[4 * i + 2] = bv[i].z, b[4 * i + 3] = bv[i].w;
     }
-    float p[S];
+    const float mean = __fmul_rn(bulk_page_sum<LPK>(x), 0.0078125f);
+    float d[C], sq[C];
 #pragma unroll
-    for (int m = 0; m < S; ++m) p[m] = __fadd_rn(x[2 * m], x[2 * m + 1]);
-    const float mean = __fmul_rn(bulk_tree_sum<LPK>(p), 0.0078125f);
-    float d[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) d[j] = __fsub_rn(x[j], mean);
-#pragma unroll
-    for (int m = 0; m < S; ++m)
-        p[m] = __fadd_rn(__fmul_rn(d[2 * m], d[2 * m]), __fmul_rn(d[2 * m + 1], d[2 * m + 1]));
-    const float var = __fmul_rn(bulk_tree_sum<LPK>(p), 0.0078125f);
+    for (int j = 0; j < C; ++j) {
+        d[j] = __fsub_rn(x[j], mean);
+        sq[j] = __fmul_rn(d[j], d[j]);
+    }
+    const float var = __fmul_rn(bulk_page_sum<LPK>(sq), 0.0078125f);
     const float rstd = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(var, eps)));
     float n[C];
 #pragma unroll
