@@ -1,7 +1,8 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration bench.py times:
-the whole cache, every quantized query byte and every row bound bit-exact; logits of
-sampled rows within 1e-5 * max |logit| of the oracle; top-k sets equal on identical
-(oracle) logits; end-to-end top-k differing only by boundary swaps within tolerance; and
+the whole cache, every quantized query byte and every row bound bit-exact; the logits of
+every row within 1e-5 * max |logit| of the oracle; top-k sets equal on identical (oracle)
+logits; end-to-end top-k differing only by boundary swaps that the measured logit error
+explains; and
 the step bench.py times (the inputs made inside the scorer where that path applies), run
 from a cache without the step's keys, giving the same cache bytes, row layout and logits
 bit for bit, and the oracle's top-k sets of those logits."""
@@ -19,19 +20,6 @@ from gpu_util import (DeviceWorkload, assert_logits_close, assert_topk_sets, bf1
 from sparse_attention_indexer_quant_amd.workloads import CONFIG_NAMES, config
 
 pytestmark = pytest.mark.gpu
-
-
-def _sample_rows(wl, starts, ends, n=4):
-    live = [r for r in range(wl.num_rows) if ends[r] > 0]
-    rng = np.random.default_rng(wl.seed)
-    pick = {live[0], live[-1]}
-    # every row of one multi-row request, if there is one
-    for q in range(wl.num_requests):
-        if starts[q + 1] - starts[q] >= 3:
-            pick.update(range(starts[q], starts[q + 1]))
-            break
-    pick.update(rng.choice(live, size=min(n, len(live)), replace=False).tolist())
-    return sorted(int(r) for r in pick)
 
 
 @pytest.fixture(scope="module", params=CONFIG_NAMES)
@@ -53,9 +41,10 @@ def run(request):
     ocache = oracle_cache(wl)
     oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
     os_, oe = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
-    rows = _sample_rows(wl, os_, oe)
+    rows = list(range(wl.num_rows))  # every row, graph padding included
     ref = oracle.score_paged(oq, wl.heads, ow, ocache, wl.num_pages, wl.page_stride, wl.block_table,
-                             os_, oe, wl.fmt, wl.section_offset, rows_subset=rows)
+                             os_, oe, wl.fmt, wl.section_offset)
+    print(f"[config {name}] oracle scored {wl.scored_pairs(oe)} pairs", flush=True)
     ctx = dict(name=name, wl=wl, dw=dw, q_rows=q_rows, w=w, starts=starts, ends=ends,
                logits=logits, idx=idx, ocache=ocache, oq=oq, ow=ow, os=os_, oe=oe, rows=rows, ref=ref)
     yield ctx
@@ -78,7 +67,7 @@ def test_row_bounds_exact(run):
     assert np.array_equal(run["ends"].cpu().numpy(), run["oe"])
 
 
-def test_sampled_logits_within_tolerance(run):
+def test_logits_within_tolerance_every_row(run):
     got = run["logits"][run["rows"]].cpu().numpy()
     ref = run["ref"][run["rows"]]
     ends = run["oe"][run["rows"]]
@@ -86,7 +75,7 @@ def test_sampled_logits_within_tolerance(run):
 
 
 def test_topk_on_identical_logits(run):
-    # both sides select from the oracle's logits of the sampled rows
+    # both sides select from the oracle's logits of every row
     wl, rows = run["wl"], run["rows"]
     lg = np.nan_to_num(run["ref"][rows], nan=0.0).astype(np.float32)
     ends = run["oe"][rows].astype(np.int32)
@@ -96,13 +85,17 @@ def test_topk_on_identical_logits(run):
 
 
 def test_topk_end_to_end_boundary_swaps_only(run):
-    # GPU logits -> GPU top-k against oracle logits -> oracle top-k: any index in one set but
-    # not the other must have an oracle logit within the logit tolerance of the k-th value.
+    # GPU logits -> GPU top-k against oracle logits -> oracle top-k. If the GPU logits G differ
+    # from the oracle's L by at most e on a row (e measured: the row's largest |G - L|, itself
+    # within the 1e-5 tolerance), an index a picked only by the GPU and b only by the oracle
+    # satisfy L(a) <= kth <= L(b) and G(a) >= G(b), so L(b) - 2e <= L(a): both lie within 2e of
+    # the oracle's k-th value. Every index in one set but not the other must be such a key.
     wl, rows = run["wl"], run["rows"]
     ref = run["ref"][rows]
     ends = run["oe"][rows].astype(np.int32)
     want = oracle.topk(np.nan_to_num(ref, nan=0.0).astype(np.float32), ends, wl.topk)
     got = run["idx"][rows].cpu().numpy()
+    glog = run["logits"][rows].cpu().numpy()
     swaps = 0
     for i in range(len(rows)):
         n = int(ends[i])
@@ -112,9 +105,10 @@ def test_topk_end_to_end_boundary_swaps_only(run):
         diff = np.setxor1d(got[i], want[i])
         swaps += diff.size // 2
         if diff.size:
-            tol = 1e-5 * float(np.max(np.abs(ref[i, :n])))
-            kth = np.sort(ref[i, :n])[::-1][min(wl.topk, n) - 1]
-            assert np.all(diff >= 0) and np.all(np.abs(ref[i, diff] - kth) <= 2 * tol), run["name"]
+            e = float(np.max(np.abs(glog[i, :n].astype(np.float64) - ref[i, :n].astype(np.float64))))
+            kth = float(np.sort(ref[i, :n])[::-1][min(wl.topk, n) - 1])
+            assert np.all(diff >= 0) and np.all(np.abs(ref[i, diff].astype(np.float64) - kth) <= 2 * e), \
+                f"{run['name']} row {rows[i]}: swap beyond the measured logit error {e:.3e}"
     print(f"[config {run['name']}] end-to-end top-k boundary swaps: {swaps}", file=sys.stderr)
 
 

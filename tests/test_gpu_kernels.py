@@ -11,6 +11,7 @@ import oracle
 import sparse_attention_indexer_quant_amd as dsa
 from gpu_util import (DeviceWorkload, assert_logits_close, assert_topk_sets, bf16_dev, bf16_host,
                       dev, oracle_cache)
+from goldens import byte_list, layernorm_order_key, rows
 from sparse_attention_indexer_quant_amd.workloads import bf16_bits, bf16_to_f32, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -160,6 +161,58 @@ def test_store_keys_empty_and_all_padding():
     dsa.store_keys(torch.ones((5, 128), dtype=torch.bfloat16, device="cuda"), g, b, 1e-6,
                    torch.full((5,), -1, dtype=torch.int64, device="cuda"), cache, 1, 4352)
     assert torch.all(cache == 0x5A)
+
+
+def _golden_order_bytes():
+    gold = {}
+    for line in rows("layernorm_order.txt"):
+        kind, *vals = line.split()
+        gold.setdefault(kind, []).append(vals)
+    return (np.array(byte_list(gold["mxfp4_payload"][0][0]), np.uint8),
+            np.array(byte_list(gold["mxfp4_scales"][0][0]), np.uint8))
+
+
+def _assert_golden_entry(cache: np.ndarray, slot: int, stride: int, offset: int, what: str):
+    payload, scales = _golden_order_bytes()
+    sec = offset + (slot // 64) * stride
+    off = slot % 64
+    assert np.array_equal(cache[sec + off * 64:sec + off * 64 + 64], payload), f"{what}: payload"
+    assert np.array_equal(cache[sec + 4096 + off * 4:sec + 4096 + off * 4 + 4], scales), f"{what}: scales"
+
+
+@pytest.mark.parametrize("path", ["bulk", "one_wave", "index_inputs"])
+def test_key_layernorm_summation_order_golden(path):
+    # tests/golden/layernorm_order.txt: a key whose MXFP4 bytes depend on the LayerNorm's
+    # summation order (page "...cutedsl.dsa.index", insert_key), worked by hand; every key
+    # path writes those bytes, among random keys that go through the oracle as usual.
+    x, gamma, beta = layernorm_order_key()
+    rng = np.random.default_rng(61)
+    T, pages = 40, 2
+    keys = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
+    gold_at = [0, 13, 39]
+    keys[gold_at] = bf16_bits(x)
+    slots = rng.permutation(pages * 64)[:T].astype(np.int64)
+    want = np.full(pages * 4352, 0xA5, np.uint8)
+    oracle.store_keys(keys, gamma, beta, 1e-6, slots, want, pages, 4352, 0, "mxfp4")
+    got = torch.full((pages * 4352,), 0xA5, dtype=torch.uint8, device="cuda")
+    if path == "bulk":
+        dsa.store_keys(bf16_dev(keys), dev(gamma), dev(beta), 1e-6, dev(slots), got, pages, 4352)
+    elif path == "one_wave":  # rows that are not 16-byte rows take the one-wavefront kernel
+        wide = np.zeros((T, 130), np.uint16)
+        wide[:, 2:] = keys
+        dsa.store_keys(bf16_dev(wide)[:, 2:], dev(gamma), dev(beta), 1e-6, dev(slots), got, pages, 4352)
+    else:
+        heads = 16
+        proj = np.zeros((T, 128 + heads + 8), np.uint16)
+        proj[:, 8:136] = keys
+        q = bf16_bits(rng.standard_normal((T, heads, 128)).astype(np.float32))
+        dsa.index_inputs(bf16_dev(proj), 8, 136, bf16_dev(q), dev(gamma), dev(beta), 1e-6,
+                         dev(slots), got, pages, 4352)
+    got = got.cpu().numpy()
+    for t in gold_at:
+        _assert_golden_entry(want, int(slots[t]), 4352, 0, "oracle")
+        _assert_golden_entry(got, int(slots[t]), 4352, 0, path)
+    assert np.array_equal(got, want)
 
 
 # ---- index_inputs (fused per-token query quant + weights + key insert) ---------------------
@@ -450,6 +503,85 @@ def test_index_score_matches_oracle_and_separate_calls(name, k):
     assert torch.equal(a.cache, b.cache)
     assert np.array_equal(got.view(np.uint32), lb.cpu().numpy().view(np.uint32)), f"{name}: logits bits"
     assert_topk_sets(idx.cpu().numpy(), idx_b.cpu().numpy(), range(wl.num_rows), f"{name} k={k}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_index_score_layernorm_order_golden(fmt):
+    # the fused step inserts the hand-worked key of tests/golden/layernorm_order.txt (as the
+    # step key of two of its rows) with the bytes worked out there, and the rest as the oracle
+    x, gamma, beta = layernorm_order_key()
+    wl = make_workload("ln_gold", fmt=fmt, heads=32, seq_lens=[300, 129, 70], query_lens=[2, 1, 2],
+                       topk=64, seed=19, extra_pages=2)
+    wl.gamma, wl.beta = gamma, beta
+    sk = wl.step_key_index()
+    wl.key_bits[sk[[0, 3]]] = bf16_bits(x)
+    rng = np.random.default_rng(6)
+    key_col, weight_col, cols = 0, 130, 170
+    proj, slots = _step_projection(wl, key_col, weight_col, cols, rng)
+    ocache = oracle_cache(wl)
+    a = _cache_without_step_keys(wl)
+    la = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    dsa.index_score_topk(bf16_dev(proj), key_col, weight_col, a.q, a.gamma, a.beta, wl.eps,
+                         a.seq_lens, a.query_lens, wl.num_rows, a.cache, wl.num_pages,
+                         wl.page_stride, a.block_table, wl.max_query_len, 16, wl.fmt,
+                         wl.section_offset, out=la)
+    got = a.cache.cpu().numpy()
+    if fmt == "mxfp4":
+        for t in (0, 3):
+            _assert_golden_entry(ocache, int(wl.key_slots[sk[t]]), wl.page_stride, 0, "oracle")
+            _assert_golden_entry(got, int(wl.key_slots[sk[t]]), wl.page_stride, 0, "fused")
+    assert np.array_equal(got, ocache)
+
+
+LONG_ROW_CASES = {
+    # one or two requests of 64K-131K keys: the scorer's segments number in the hundreds per
+    # row, so the selection takes the separate threshold and collect kernels over sparse
+    # histogram blocks (rows of more than 64 segments), and above 128 segments their
+    # multi-block loops
+    "fp4_one_64k": dict(fmt="mxfp4", heads=32, seq_lens=[65536], query_lens=[1]),
+    "fp4_two_long_verify": dict(fmt="mxfp4", heads=32, seq_lens=[131072, 70001], query_lens=[3, 1]),
+    "fp8_one_80k": dict(fmt="fp8", heads=32, seq_lens=[80000], query_lens=[2]),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_ROW_CASES))
+@pytest.mark.parametrize("k", [2048, 7])
+def test_score_topk_rows_of_many_segments(name, k):
+    # score_topk and index_score_topk on rows spanning hundreds of scoring segments, with a
+    # workspace of arbitrary bytes: logits bit for bit equal to score_paged's (and, fused, to
+    # the separate calls), index sets equal to the oracle's top-k of the same logits
+    wl = make_workload(name, topk=k, seed=23, extra_pages=1, **LONG_ROW_CASES[name])
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, ends = dw.layout()
+    oe = ends.cpu().numpy()
+    plain = dw.score(q_rows, w, starts, ends)
+    ws = torch.full((dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows),),
+                    0xC3, dtype=torch.uint8, device="cuda")
+    la = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, idx = dsa.score_topk(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride,
+                            dw.block_table, starts, ends, wl.max_query_len, k, wl.fmt,
+                            wl.section_offset, out=la, workspace=ws)
+    cols = torch.arange(wl.width, device="cuda")
+    valid = cols[None, :] < ends.to(torch.int64)[:, None]
+    assert torch.equal(la.view(torch.int32)[valid], plain.view(torch.int32)[valid]), f"{name}: logits"
+    got = la.cpu().numpy()
+    want = oracle.topk(np.nan_to_num(got, nan=0.0), oe, k)
+    assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), f"{name} k={k}")
+    # the fused step from a cache without the step keys, on the same (reused) workspace
+    rng = np.random.default_rng(8)
+    proj, _ = _step_projection(wl, 0, 128, 128 + wl.heads, rng)
+    b = _cache_without_step_keys(wl)
+    lb = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, fe, _, fidx = dsa.index_score_topk(
+        bf16_dev(proj), 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens,
+        wl.num_rows, b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, k,
+        wl.fmt, wl.section_offset, out=lb, workspace=ws)
+    assert torch.equal(b.cache, dw.cache), f"{name}: fused cache bytes"
+    assert torch.equal(fe, ends)
+    assert torch.equal(lb.view(torch.int32)[valid], plain.view(torch.int32)[valid]), f"{name}: fused logits"
+    assert_topk_sets(fidx.cpu().numpy(), want, range(wl.num_rows), f"{name} fused k={k}")
 
 
 def test_index_score_degenerate_sizes():
