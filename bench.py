@@ -371,28 +371,40 @@ class Setup:
 EVENT_EVERY = 4
 
 
+# At least this many sampled score launches back every roofline figure: when the timed loop
+# has fewer sampled steps, the loop carries on (after the wall clock stops) with more steps,
+# sampled the same way, until it has them.
+MIN_SAMPLES = 25
+
+
 def time_steps(s: Setup, steps: int, warmup: int, mode: str = "fused"):
     """Wall time of `steps` steps (after `warmup` untimed ones) and the score launch times
-    (ms) of the sampled steps inside that timed loop."""
+    (ms) of the sampled steps inside that timed loop (and of the steps after it that bring the
+    samples to MIN_SAMPLES)."""
     import torch
     step = {"inline": s.step_inline, "fused": s.step, "unfused": s.step_unfused}[mode]
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = {i: (TimingEvent(), TimingEvent()) for i in range(0, steps, EVENT_EVERY)}
+    total = max(steps, EVENT_EVERY * MIN_SAMPLES)
+    evs = {i: (TimingEvent(), TimingEvent()) for i in range(0, total, EVENT_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(warmup + i, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for i in range(steps, total):
+        step(warmup + i, evs.get(i))
+    torch.cuda.synchronize()
     score_ms = np.array([a.elapsed_time(b) for a, b in evs.values()])
     return wall, score_ms
 
 
-def kernel_times(s: Setup, reps: int = 30):
+def kernel_times(s: Setup, reps: int = 30, score_reps: int = 100):
     """Per-kernel HIP-event times (ms, median) of each stage launched on its own (repeated
-    back to back, not inside the step)."""
+    back to back, not inside the step): `score_reps` launches for the scoring kernels,
+    `reps` for the others."""
     import torch
     out = {}
     stages = [("index_inputs_layout", lambda i: s.inputs_layout[i % len(s.caches)]()),
@@ -408,7 +420,8 @@ def kernel_times(s: Setup, reps: int = 30):
         stages.append(("index_score_hist", lambda i: s.index_score[i % len(s.caches)]()))
     for name, fn in stages:
         # launched back to back, each between its own pair of events, read after the last
-        evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+        n = score_reps if name.startswith(("score", "index_score")) else reps
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(n)]
         for i, (a, b) in enumerate(evs):
             a.record(s.stream)
             fn(i)
@@ -416,6 +429,47 @@ def kernel_times(s: Setup, reps: int = 30):
         torch.cuda.synchronize()
         out[name] = float(np.median([a.elapsed_time(b) for a, b in evs]))
     return out
+
+
+def stream_ceiling(key_bytes: int, grids=(256, 512, 1024, 2048, 4096, 8192), reps: int = 20):
+    """The device's contiguous read rate at the scorer's key bytes, 300 MB and 1 GB: read_stream
+    (16-byte loads, eight in flight per lane) at each grid size, each launch reading a
+    different region of a buffer of at least 768 MB (so reads come from HBM, not the 256 MB
+    Infinity Cache), launched back to back between HIP events read after the last launch.
+    Returns the best grid's mean GB/s per size."""
+    import torch
+    import sparse_attention_indexer_quant_amd as dsa
+    lib = dsa.library()
+    sizes = [int(key_bytes) // 16 * 16, 300_000_000, 1_000_000_000]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    res = []
+    for size in sizes:
+        regions = max(2, -(-768_000_000 // size) + 1)
+        buf = torch.ones(size * regions, dtype=torch.uint8, device="cuda")
+        out = torch.zeros(4 * max(grids), dtype=torch.int32, device="cuda")
+        best = None
+        per_grid = {}
+        for g in grids:
+            calls = [Prepared(lib.dsaidx_read_stream, buf.data_ptr() + r * size, size, g,
+                              out.data_ptr(), out.numel(), sp) for r in range(regions)]
+            for i in range(3):
+                calls[i % regions]()
+            evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                calls[i % regions]()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            per_grid[g] = size / us / 1e3
+            if best is None or per_grid[g] > best[1]:
+                best = (g, per_grid[g], us)
+        res.append({"bytes": size, "best_workgroups": best[0], "GBps": best[1], "us_mean": best[2],
+                    "GBps_by_workgroups": per_grid})
+        del buf, out
+        torch.cuda.empty_cache()
+    return res
 
 
 def read_reference(s: Setup, reps: int = 24, warmup: int = 4):
@@ -504,7 +558,11 @@ def cpu_baseline(s: Setup, budget_s: float):
     pairs = int(np.minimum(ends[rows], wl.width).sum())
     # the whole step on the CPU would take fixed + el * (all pairs / sampled pairs)
     step_s = fixed + el * (s.pairs / max(pairs, 1))
-    return {"value": s.pairs / step_s, "unit": "pairs/s", "cores": oracle.num_threads(),
+    affinity = len(os.sched_getaffinity(0))
+    return {"value": s.pairs / step_s, "unit": "pairs/s",
+            # OpenMP threads the oracle ran, each on its own core of the affinity mask
+            "cores": min(oracle.num_threads(), affinity), "omp_threads": oracle.num_threads(),
+            "affinity_cores": affinity,
             "kind": "oracle",
             "sample": f"{wl.name}: score_paged + topk of {len(rows)} of {len(live)} live rows "
                       f"({pairs} pairs, {el:.2f} s), plus index_inputs of all {wl.num_rows} rows "
@@ -581,6 +639,7 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "score_us_p10_p50_p90": [float(np.percentile(score_ms, p) * 1e3) for p in (10, 50, 90)],
         "score_pairs_per_s": s.pairs / (score_us / 1e6),
         "score_key_GBps": s.wl.key_bytes() / (score_us / 1e6) / 1e9,
+        "score_key_bytes": s.wl.key_bytes(),
         "score_algorithmic_GBps": kbytes / (score_us / 1e6) / 1e9,
         "score_algorithmic_bytes": kbytes,
         "score_histogram_bytes": s.hist_bytes,
@@ -653,6 +712,9 @@ def main():
               f"{per_config[name]['score_us_mean']:.2f} us", file=sys.stderr, flush=True)
 
     m = main_res
+    ceiling = stream_ceiling(m["score_key_bytes"])
+    print(f"[bench] read ceiling: " + ", ".join(f"{c['bytes'] / 1e6:.0f} MB {c['GBps']:.0f} GB/s"
+                                                 for c in ceiling), file=sys.stderr, flush=True)
     traffic = measured_traffic(m["score_kernel"], args.config)
     achieved = m["score_algorithmic_GBps"]
     line = {
@@ -685,7 +747,12 @@ def main():
                      "frac_alone": m["score_algorithmic_bytes"] / m["kernel_us_alone"][m["score_kernel"]]
                                    / 1e3 / HBM_PEAK_GBPS,
                      "read_reference_GBps": m["read_reference"]["paged_GBps"],
-                     "read_reference_contiguous_GBps": m["read_reference"]["contiguous_GBps"]},
+                     "read_reference_contiguous_GBps": m["read_reference"]["contiguous_GBps"],
+                     # a plain contiguous read of the scorer's key bytes at its best grid: the
+                     # device's measured read rate at this size, and the scorer against it
+                     "stream_read_ceiling_GBps": ceiling[0]["GBps"],
+                     "frac_of_stream_read_ceiling": achieved / ceiling[0]["GBps"]},
+        "stream_read_ceiling": ceiling,
         "cpu_baseline": m.get("cpu_baseline"),
         "per_config": per_config,
     }

@@ -271,6 +271,21 @@ dsaidx_status dsaidx_read_sections(int fmt, const void *cache, int64_t num_pages
                                    void *stream);
 
 /*
+ * read_stream -- a bandwidth reference, not a step of the indexer path: a plain contiguous
+ * read of `bytes` bytes at `buf` by `workgroups` workgroups of 256 lanes (workgroup b reads
+ * 32 KB at b * 32 KB and then every workgroups * 32 KB further, as 16-byte loads), each
+ * wavefront writing the XOR of the 32-bit words it read to out[4 * b + wavefront].
+ *
+ *  buf        device, 16-byte aligned, `bytes` readable bytes (a multiple of 16).
+ *  workgroups 1 .. 1,048,576.
+ *  out        device, uint32 [out_words], out_words >= 4 * workgroups.
+ *  Errors: DSAIDX_EINVAL for a null pointer, negative or unaligned sizes, workgroups out of
+ *  range or a short `out`; bytes == 0 enqueues nothing.
+ */
+dsaidx_status dsaidx_read_stream(const void *buf, int64_t bytes, int32_t workgroups,
+                                 uint32_t *out, int64_t out_words, void *stream);
+
+/*
  * score_paged_hist -- dsaidx_score_paged plus the top-k segment histograms.
  *  All arguments as dsaidx_score_paged, and
  *  workspace  device, >= dsaidx_score_topk_workspace_bytes(num_requests, max_blocks,

@@ -71,6 +71,7 @@ def library():
             "dsaidx_score_segment_keys": (I64, [I64, I64]),
             "dsaidx_read_sections_words": (I64, [I64, I64]),
             "dsaidx_read_sections": (I32, [I32, P, I64, I64, P, I64, I64, P, P, I64, P]),
+            "dsaidx_read_stream": (I32, [P, I64, I32, P, I64, P]),
             "dsaidx_score_paged_hist": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
                                               P, P, I64, I32, P, I64, P, SZ, P]),
             "dsaidx_index_score_hist": (I32, [I32, P, I64, I64, I64, P, I32, I64, I64, P, P, F32,
@@ -329,6 +330,22 @@ def read_sections(cache, num_pages, page_stride, block_table, seq_lens, fmt="mxf
         _fmt(fmt), cache.data_ptr() + section_offset, num_pages, page_stride,
         block_table.data_ptr(), nreq, max_blocks, seq_lens.data_ptr(), out.data_ptr(),
         out.numel(), _stream(cache)))
+    return out
+
+
+def read_stream(buf, workgroups, nbytes=None, out=None):
+    """A plain contiguous read of the first `nbytes` (default: all) bytes of the uint8 device
+    tensor `buf` by `workgroups` workgroups (a bandwidth reference, not a step of the path).
+    Returns uint32 [4 * workgroups] XOR words, one per wavefront."""
+    import torch
+    _dev(buf, "buf", torch.uint8)
+    nbytes = buf.numel() if nbytes is None else int(nbytes)
+    if nbytes > buf.numel() or not buf.is_contiguous():
+        raise ValueError("read_stream: nbytes beyond a contiguous buffer")
+    if out is None:
+        out = torch.zeros(4 * int(workgroups), dtype=torch.int32, device=buf.device)
+    _check("read_stream", library().dsaidx_read_stream(buf.data_ptr(), nbytes, int(workgroups),
+                                                       out.data_ptr(), out.numel(), _stream(buf)))
     return out
 
 

@@ -299,6 +299,16 @@ dsaidx_status dsaidx_read_sections(int fmt, const void *cache, int64_t num_pages
                                                    as_stream(stream)));
 }
 
+dsaidx_status dsaidx_read_stream(const void *buf, int64_t bytes, int32_t workgroups,
+                                 uint32_t *out, int64_t out_words, void *stream) {
+    if (bytes < 0 || bytes % 16 || workgroups < 1 || workgroups > (1 << 20) || out_words < 0)
+        return DSAIDX_EINVAL;
+    if (bytes == 0) return DSAIDX_OK;
+    if (!buf || !out || !aligned(buf, 16) || !aligned(out, 4) || out_words < 4 * (int64_t)workgroups)
+        return DSAIDX_EINVAL;
+    return hip_status(dsaidx::launch_read_stream(buf, bytes, workgroups, out, as_stream(stream)));
+}
+
 dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stride,
                                       int32_t heads, const void *w, int64_t w_row_stride,
                                       const void *cache, int64_t num_pages, int64_t page_stride,

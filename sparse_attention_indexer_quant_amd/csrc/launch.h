@@ -107,6 +107,10 @@ hipError_t launch_dcp_merge(const float *values, const int32_t *positions, int w
                             int32_t *local_slots, int64_t local_row_stride, hipStream_t stream);
 
 // A plain read of the sections score_paged reads, in its grid (a bandwidth reference): one
+// A contiguous read of `bytes` (a multiple of 16) by `workgroups` workgroups of 256 lanes,
+// one XOR word per wavefront into `out` (4 * workgroups words).
+hipError_t launch_read_stream(const void *buf, int64_t bytes, int workgroups, uint32_t *out,
+                              hipStream_t stream);
 // XOR word per wavefront into `out` (read_sections_words words).
 int64_t read_sections_words(int64_t num_requests, int64_t max_blocks);
 hipError_t launch_read_sections(int fmt, const void *cache, int64_t num_pages, int64_t page_stride,

@@ -1,5 +1,7 @@
-// A plain read of paged key-cache sections: the bandwidth a kernel that only streams the
-// scorer's pages reaches, against which the scorer is measured. Not a step of the indexer path.
+// Bandwidth references, not steps of the indexer path: a plain read of paged key-cache
+// sections (the bandwidth a kernel that only streams the scorer's pages reaches, against which
+// the scorer is measured), and a plain contiguous read of a buffer (the device's read ceiling
+// at a given size).
 //
 // It reads exactly the bytes score_paged reads from the cache -- the section of every block of
 // every request below the request's key count -- with score_paged's grid (the same workgroups,
@@ -93,6 +95,41 @@ __global__ __launch_bounds__(64 * kScoreWaves) void read_sections_kernel(
     acc = xor_combine<16>(acc, x);
     acc = xor_combine<32>(acc, x);
     if (lane == 0) out[(int64_t)blockIdx.x * kScoreWaves + wave] = acc;
+}
+
+// A contiguous read of n16 16-byte words: workgroup b takes words [b * 256 U, (b + 1) * 256 U)
+// and then every gridDim.x * 256 U further; each lane issues its U loads (consecutive lanes on
+// consecutive words) before it uses any, and every wavefront writes the XOR of what it read.
+template <int U>
+__global__ __launch_bounds__(256) void read_stream_kernel(const uint4 *__restrict__ buf, int64_t n16,
+                                                          uint32_t *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    uint32_t acc = 0;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            v[u] = i < n16 ? buf[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    auto x = [](uint32_t a, uint32_t b) { return a ^ b; };
+    acc = xor_combine<1>(acc, x);
+    acc = xor_combine<2>(acc, x);
+    acc = xor_combine<4>(acc, x);
+    acc = xor_combine<8>(acc, x);
+    acc = xor_combine<16>(acc, x);
+    acc = xor_combine<32>(acc, x);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
+hipError_t launch_read_stream(const void *buf, int64_t bytes, int workgroups, uint32_t *out,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(read_stream_kernel<8>, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                       static_cast<const uint4 *>(buf), bytes / 16, out);
+    return hipGetLastError();
 }
 
 int64_t read_sections_words(int64_t num_requests, int64_t max_blocks) {

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
               "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys",
-              "dsaidx_read_sections", "dsaidx_read_sections_words"):
+              "dsaidx_read_sections", "dsaidx_read_sections_words", "dsaidx_read_stream"):
         assert n in names
 
 
@@ -254,6 +254,19 @@ def read_sections(lib, **kw):
     a.update(kw)
     return lib.dsaidx_read_sections(a["fmt"], a["cache"], a["np_"], a["ps"], a["bt"], a["r"],
                                     a["mb"], a["seq"], a["out"], a["ow"], None)
+
+
+def test_read_stream_checks(lib):
+    buf, out = 1 << 12, 1 << 16  # host-side stand-ins: every call below fails its checks first
+    f = lib.dsaidx_read_stream
+    assert f(buf, 17, 4, out, 16, None) == EINVAL          # not a multiple of 16
+    assert f(buf, -16, 4, out, 16, None) == EINVAL
+    assert f(buf, 64, 0, out, 16, None) == EINVAL          # no workgroups
+    assert f(buf, 64, (1 << 20) + 1, out, 1 << 23, None) == EINVAL
+    assert f(buf, 64, 4, out, 15, None) == EINVAL          # out shorter than 4 per workgroup
+    assert f(None, 64, 4, out, 16, None) == EINVAL
+    assert f(buf + 8, 64, 4, out, 16, None) == EINVAL      # unaligned
+    assert f(buf, 0, 4, out, 16, None) == OK               # nothing to read: nothing enqueued
 
 
 def test_read_sections_checks(lib):
