@@ -43,7 +43,9 @@ typedef enum {
     DSAIDX_EINVAL = 1,      /* a count, size, pointer or scalar argument is invalid */
     DSAIDX_ELAYOUT = 2,     /* a stride, alignment or buffer layout breaks the required layout */
     DSAIDX_EUNSUPPORTED = 3,/* a valid shape this build does not implement (heads, max_query_len) */
-    DSAIDX_EHIP = 4         /* the HIP runtime reported an error when enqueuing */
+    DSAIDX_EHIP = 4,        /* the HIP runtime reported an error when enqueuing */
+    DSAIDX_ESCRATCH = 5     /* the sizes need more than the allocation-free call's static
+                               scratch (DSAIDX_STATIC_SCRATCH_BYTES) */
 } dsaidx_status;
 
 typedef enum {
@@ -382,6 +384,28 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
                           int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
                           int32_t *indices, int64_t indices_row_stride, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * topk_noalloc -- dsaidx_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same selection,
+ * the same index sets, with the workspace taken from a static device array of
+ * DSAIDX_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on each device it runs on until
+ * the process ends, instead of a caller-supplied one. It calls no hipMalloc, hipFree or other
+ * allocating routine; its first call on a device looks up that device's array address (with
+ * the device current) and keeps it.
+ *
+ *  Arguments as dsaidx_topk, without the workspace.
+ *  Errors: as dsaidx_topk; sizes for which dsaidx_topk_workspace_bytes exceeds
+ *  DSAIDX_STATIC_SCRATCH_BYTES give DSAIDX_ESCRATCH (nothing enqueued).
+ *  Every call on a device shares that device's array, which keeps the last call's contents
+ *  (the selection writes every workspace field it reads, so nothing needs clearing): calls
+ *  that may overlap on one device (different streams, or different threads) race; order them
+ *  on one stream.
+ */
+#define DSAIDX_STATIC_SCRATCH_BYTES (64ull << 20)
+dsaidx_status dsaidx_topk_noalloc(const float *logits, int64_t rows, int64_t width,
+                                  int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
+                                  int32_t *indices, int64_t indices_row_stride, void *stream);
 
 /*
  * Decode context parallelism (DCP): [fp4ops] decode_layout deals a request's keys to W ranks

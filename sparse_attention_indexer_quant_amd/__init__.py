@@ -79,6 +79,7 @@ def library():
                                               I64, P, SZ, P]),
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
+            "dsaidx_topk_noalloc": (I32, [P, I64, I64, I64, P, I32, P, I64, P]),
             "dsaidx_dcp_candidates": (I32, [P, I64, I64, I64, P, I32, I64, I32, I32, I32, P, P, P]),
             "dsaidx_dcp_merge": (I32, [P, P, I32, I64, I32, I32, P, I64, I32, I32, P, I64, P]),
         }

@@ -45,6 +45,7 @@ dsaidx_status hip_status(hipError_t e) { return e == hipSuccess ? DSAIDX_OK : DS
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 static_assert(dsaidx::kTopkMaxWidth == DSAIDX_TOPK_MAX_WIDTH, "one top-k width limit");
+static_assert(dsaidx::kStaticScratchBytes == DSAIDX_STATIC_SCRATCH_BYTES, "one scratch size");
 
 }  // namespace
 
@@ -57,6 +58,7 @@ const char *dsaidx_status_string(int status) {
         case DSAIDX_ELAYOUT: return "unsupported stride, alignment or buffer layout";
         case DSAIDX_EUNSUPPORTED: return "unsupported shape";
         case DSAIDX_EHIP: return "HIP launch error";
+        case DSAIDX_ESCRATCH: return "sizes need more than the static scratch of the allocation-free call";
         default: return "unknown status";
     }
 }
@@ -451,6 +453,26 @@ dsaidx_status dsaidx_topk(const float *logits, int64_t rows, int64_t width,
     return hip_status(dsaidx::launch_topk(logits, rows, width, logits_row_stride, row_ends, k,
                                           indices, indices_row_stride, workspace,
                                           workspace_bytes, as_stream(stream)));
+}
+
+dsaidx_status dsaidx_topk_noalloc(const float *logits, int64_t rows, int64_t width,
+                                  int64_t logits_row_stride, const int32_t *row_ends, int32_t k,
+                                  int32_t *indices, int64_t indices_row_stride, void *stream) {
+    if (rows < 0 || width < 0 || k < 1) return DSAIDX_EINVAL;
+    if (width > DSAIDX_TOPK_MAX_WIDTH || rows * ((width + 4095) / 4096 + 1) > kMaxGrid)
+        return DSAIDX_EUNSUPPORTED;
+    if (rows == 0) return DSAIDX_OK;
+    if (!row_ends || !indices || (width > 0 && !logits)) return DSAIDX_EINVAL;
+    if (logits_row_stride < width || indices_row_stride < k || !aligned(logits, 4) ||
+        !aligned(indices, 4))
+        return DSAIDX_ELAYOUT;
+    if (dsaidx::topk_workspace_bytes(rows, width, k) > dsaidx::kStaticScratchBytes)
+        return DSAIDX_ESCRATCH;
+    void *ws = nullptr;
+    if (dsaidx::static_scratch(&ws) != hipSuccess) return DSAIDX_EHIP;
+    return hip_status(dsaidx::launch_topk(logits, rows, width, logits_row_stride, row_ends, k,
+                                          indices, indices_row_stride, ws,
+                                          dsaidx::kStaticScratchBytes, as_stream(stream)));
 }
 
 dsaidx_status dsaidx_dcp_candidates(const float *logits, int64_t rows, int64_t width,

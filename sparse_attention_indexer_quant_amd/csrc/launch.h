@@ -107,6 +107,12 @@ hipError_t launch_dcp_merge(const float *values, const int32_t *positions, int w
                             int32_t *local_slots, int64_t local_row_stride, hipStream_t stream);
 
 // A plain read of the sections score_paged reads, in its grid (a bandwidth reference): one
+// The allocation-free top-k's device scratch: its size, the devices it serves, and its
+// address on the current device (taken on the first call there, kept after).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch(void **out);
+
 // A contiguous read of `bytes` (a multiple of 16) by `workgroups` workgroups of 256 lanes,
 // one XOR word per wavefront into `out` (4 * workgroups words).
 hipError_t launch_read_stream(const void *buf, int64_t bytes, int workgroups, uint32_t *out,

@@ -35,6 +35,8 @@
 // 2048 workgroups and a row has at most 1024 segments (rows hold at most 2^25 keys). Every
 // workspace field is written before it is read within a call, so the workspace needs no
 // initialisation; calls sharing one must be ordered.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 #include "select.h"
@@ -906,6 +908,32 @@ hipError_t launch_topk(const float *logits, int64_t rows, int64_t width, int64_t
     return launch_topk_after_histograms(logits, rows, width, logits_row_stride, row_ends, k,
                                         indices, indices_row_stride, workspace, nseg, seg_len,
                                         stream);
+}
+
+// The workspace of the allocation-free top-k (dsaidx_topk_noalloc): a file-scope device
+// array, one copy per device, held until the process ends. In host code its name stands for
+// no device address; the address comes from hipGetSymbolAddress, taken once per device with
+// that device current and kept in scratch_address_of.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+static std::mutex scratch_mutex;
+static void *scratch_address_of[kMaxScratchDevices];
+
+hipError_t static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_address_of[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_address_of[dev] = p;
+    }
+    *out = scratch_address_of[dev];
+    return hipSuccess;
 }
 
 }  // namespace dsaidx

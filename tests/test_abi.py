@@ -13,7 +13,7 @@ import sparse_attention_indexer_quant_amd as dsa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsaidx.h")
 
-OK, EINVAL, ELAYOUT, EUNSUP = 0, 1, 2, 3
+OK, EINVAL, ELAYOUT, EUNSUP, ESCRATCH = 0, 1, 2, 3, 5
 P = 0x10000  # a 64 KiB-aligned stand-in pointer: every check below fails before any use
 MX, FP8 = 0, 1
 
@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "dsaidx_query_row_bytes", "dsaidx_index_inputs", "dsaidx_score_paged_hist",
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
               "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys",
-              "dsaidx_read_sections", "dsaidx_read_sections_words", "dsaidx_read_stream"):
+              "dsaidx_read_sections", "dsaidx_read_sections_words", "dsaidx_read_stream",
+              "dsaidx_topk_noalloc"):
         assert n in names
 
 
@@ -208,6 +209,29 @@ def test_topk_checks(lib):
     assert topk(lib, width=(1 << 25) + 1, ls=(1 << 25) + 1) == EUNSUP
     assert lib.dsaidx_topk_workspace_bytes(1, (1 << 25) + 1, 8) == 0
     assert lib.dsaidx_topk_workspace_bytes(1, 1 << 25, 8) > 0
+
+
+def topk_noalloc(lib, **kw):
+    a = dict(lg=P, rows=2, width=256, ls=256, ends=P, k=16, out=P, os=16)
+    a.update(kw)
+    return lib.dsaidx_topk_noalloc(a["lg"], a["rows"], a["width"], a["ls"], a["ends"], a["k"],
+                                   a["out"], a["os"], None)
+
+
+def test_topk_noalloc_checks(lib):
+    # the same checks as topk, and sizes beyond the static scratch rejected before any HIP call
+    assert topk_noalloc(lib, k=0) == EINVAL
+    assert topk_noalloc(lib, rows=-1) == EINVAL
+    assert topk_noalloc(lib, rows=0, lg=None) == OK
+    assert topk_noalloc(lib, ends=None) == EINVAL
+    assert topk_noalloc(lib, ls=255) == ELAYOUT
+    assert topk_noalloc(lib, os=15) == ELAYOUT
+    assert topk_noalloc(lib, width=(1 << 25) + 1, ls=(1 << 25) + 1) == EUNSUP
+    limit = 64 << 20
+    assert lib.dsaidx_topk_workspace_bytes(512, 65536, 2048) <= limit     # the verify workload fits
+    assert lib.dsaidx_topk_workspace_bytes(2048, 65536, 2048) > limit
+    assert topk_noalloc(lib, rows=2048, width=65536, ls=65536, k=2048, os=2048) == ESCRATCH
+    assert lib.dsaidx_status_string(ESCRATCH) != lib.dsaidx_status_string(99)
 
 
 def score_hist(lib, **kw):
