@@ -249,6 +249,14 @@ class Setup:
                                     self.logits.stride(0), self.ends.data_ptr(), wl.topk,
                                     self.idx.data_ptr(), self.idx.stride(0), wl.num_requests,
                                     wl.max_blocks, self.hws.data_ptr(), hwsb, sp)
+        # bounded logits: rows in tiles of decode_tile_size rows (max_model_len = the width)
+        self.tile_rows = dsa.decode_tile_size(wl.width, wl.width, wl.topk, wl.heads)
+        self.tiles = -(-wl.num_rows // self.tile_rows)
+        twsb = int(lib.dsaidx_score_topk_tiled_workspace_bytes(wl.num_requests, wl.max_blocks,
+                                                               self.tile_rows, wl.max_query_len))
+        self.tws = torch.empty(max(twsb, 1), dtype=torch.uint8, device=dev)
+        self.logits_tile = torch.empty((self.tile_rows, wl.width), dtype=torch.float32, device=dev)
+        self.tiled = []
         self.store, self.score, self.inputs, self.score_hist = [], [], [], []
         self.inputs_layout, self.index_score = [], []
         # the step's inputs made inside the scorer: at most 4 rows per request (MXFP4), 2 (FP8)
@@ -292,6 +300,14 @@ class Setup:
                     base, wl.num_pages, wl.page_stride, self.block_table.data_ptr(),
                     wl.max_blocks, self.starts.data_ptr(), self.ends.data_ptr(),
                     self.logits.data_ptr(), self.logits.stride(0), self.hws.data_ptr(), hwsb, sp))
+            self.tiled.append(Prepared(
+                lib.dsaidx_score_topk_tiled, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
+                wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
+                wl.page_stride, self.block_table.data_ptr(), wl.num_requests, wl.max_blocks,
+                self.starts.data_ptr(), self.ends.data_ptr(), wl.num_rows, wl.max_query_len,
+                wl.topk, self.idx.data_ptr(), self.idx.stride(0), self.tile_rows,
+                self.logits_tile.data_ptr(), self.logits_tile.stride(0), self.tws.data_ptr(),
+                twsb, sp))
             self.score_hist.append(Prepared(
                 lib.dsaidx_score_paged_hist, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
                 wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
@@ -354,6 +370,16 @@ class Setup:
             ev[1].record(self.stream)
         self.topk_scored()
 
+    def step_tiled(self, i, ev=None):
+        """index_inputs, decode_layout, then score_topk_tiled (scoring + selection per tile of
+        decode_tile_size rows: logits and selection scratch bounded to one tile; timed)."""
+        self.prologue(i)
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.tiled[i % len(self.caches)]()
+        if ev is not None:
+            ev[1].record(self.stream)
+
     def step_unfused(self, i, ev=None):
         """index_inputs, decode_layout, score_paged (timed), topk."""
         self.prologue(i)
@@ -382,7 +408,8 @@ def time_steps(s: Setup, steps: int, warmup: int, mode: str = "fused"):
     (ms) of the sampled steps inside that timed loop (and of the steps after it that bring the
     samples to MIN_SAMPLES)."""
     import torch
-    step = {"inline": s.step_inline, "fused": s.step, "unfused": s.step_unfused}[mode]
+    step = {"inline": s.step_inline, "fused": s.step, "unfused": s.step_unfused,
+            "tiled": s.step_tiled}[mode]
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -615,6 +642,7 @@ def run_config(name, args, steps, warmup, cpu_budget):
     s = Setup(name, args.min_rotation_mb)
     wall_u, score_ms_u = time_steps(s, steps, warmup, mode="unfused")
     wall_f, score_ms_f = time_steps(s, steps, warmup, mode="fused")
+    wall_t, tiled_ms = time_steps(s, steps, warmup, mode="tiled")
     # the step the library offers for this workload: the inputs made inside the scorer where
     # that path applies (MXFP4, at most 4 rows per request), else the separate input launch
     if s.inline_ok:
@@ -649,6 +677,12 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "ms_per_step_separate_inputs": wall_f / steps * 1e3,
         "score_paged_hist_us_mean": score_us_f,
         "score_paged_hist_algorithmic_GBps": s.score_hist_bytes / (score_us_f / 1e6) / 1e9,
+        # bounded logits: the same step with scoring + selection in row tiles
+        "tile_rows": s.tile_rows, "tiles": s.tiles,
+        "ms_per_step_tiled": wall_t / steps * 1e3,
+        "score_topk_tiled_us_mean": float(tiled_ms.mean() * 1e3),
+        "logits_bytes_tiled": s.tile_rows * s.wl.width * 4,
+        "logits_bytes_untiled": s.wl.num_rows * s.wl.width * 4,
         "ms_per_step_unfused": wall_u / steps * 1e3,
         "step_pairs_per_s_unfused": s.pairs / (wall_u / steps),
         "score_paged_us_mean_unfused": score_us_u,

@@ -306,6 +306,50 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * Bounded logits for verify batches ([fp4ops] decode_tile_size: logits, selection scratch and
+ * queries are bounded by grouping verify rows into tiles; score_paged scores one bounded
+ * query tile).
+ *
+ * dsaidx_decode_tile_size: rows per tile, max(32, 32 * 4 * max_model_len / row_bytes) with
+ * row_bytes = 4 * width + 24 * min(topk, width) + 64 * heads + 256 (integer division): the
+ * rows whose logits, selection scratch and query fit in the bytes of 32 rows of FP32 logits
+ * at max_model_len keys, at least 32. Returns 0 for max_model_len < 0, width < 0, topk < 1,
+ * heads < 1, or sizes above 2^40.
+ *
+ * dsaidx_score_topk_tiled: the rows [0, num_rows) in tiles of tile_rows consecutive rows (the
+ * last may be shorter), each scored as dsaidx_score_paged_hist scores it -- the same logits,
+ * bit for bit -- into `logits_tile`, then selected as dsaidx_topk_scored selects (the same
+ * index sets as dsaidx_topk on those logits) into its rows of `indices`. Only one tile's
+ * logits and selection scratch exist at a time: after the call `logits_tile` holds the last
+ * tile's logits (row r of it is row (num_rows - 1) / tile_rows * tile_rows + r). A tile may
+ * split a request's rows.
+ *  Scoring arguments as dsaidx_score_paged (query rows, weights and row bounds for all rows).
+ *  k, indices, indices_row_stride  as dsaidx_topk: every row's selection, -1 padded.
+ *  tile_rows  >= 1, e.g. dsaidx_decode_tile_size(...).
+ *  logits_tile  device, FP32 [tile_rows, >= max_blocks * 64], row stride
+ *             logits_tile_row_stride; caller-owned scratch.
+ *  workspace  device, >= dsaidx_score_topk_tiled_workspace_bytes(num_requests, max_blocks,
+ *             tile_rows, max_query_len) bytes, 256-byte aligned, caller-owned, no
+ *             initialisation needed (0 from that call: invalid sizes).
+ *  Two launches per tile on `stream`. Errors: as dsaidx_score_paged and dsaidx_topk_scored;
+ *  tile_rows < 1 or a missing or short workspace gives DSAIDX_EINVAL.
+ */
+int64_t dsaidx_decode_tile_size(int64_t max_model_len, int64_t width, int32_t topk,
+                                int32_t heads);
+size_t dsaidx_score_topk_tiled_workspace_bytes(int64_t num_requests, int64_t max_blocks,
+                                               int64_t tile_rows, int32_t max_query_len);
+dsaidx_status dsaidx_score_topk_tiled(int fmt, const void *q, int64_t q_row_stride,
+                                      int32_t heads, const void *w, int64_t w_row_stride,
+                                      const void *cache, int64_t num_pages, int64_t page_stride,
+                                      const int32_t *block_table, int64_t num_requests,
+                                      int64_t max_blocks, const int32_t *query_starts,
+                                      const int32_t *row_ends, int64_t num_rows,
+                                      int32_t max_query_len, int32_t k, int32_t *indices,
+                                      int64_t indices_row_stride, int64_t tile_rows,
+                                      float *logits_tile, int64_t logits_tile_row_stride,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * index_score_hist -- one decode or verify step's indexer inputs and its scoring in one
  * launch ([idx] DsaIndex: the quantized query, the head weights and the inserted key
  * feed the logits; [fp4ops] decode_layout for the rows). Each scoring workgroup quantizes its

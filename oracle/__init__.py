@@ -72,6 +72,7 @@ def _load():
                                       I64, P, I64, P, I64]),
             "orc_topk": (I32, [P, I64, I64, I64, P, I32, P, I64]),
             "orc_num_threads": (I32, []),
+            "orc_decode_tile_size": (I64, [I64, I64, I32, I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -322,6 +323,11 @@ def dcp_local_slots(merged: np.ndarray, rank: int, world: int, interleave: int):
         mine = local[owner == rank]
         out[r, :mine.size] = mine
     return out
+
+
+def decode_tile_size(max_model_len: int, width: int, topk: int, heads: int) -> int:
+    """Rows per verify tile (page "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_tile_size)."""
+    return int(_load().orc_decode_tile_size(int(max_model_len), int(width), int(topk), int(heads)))
 
 
 def num_threads() -> int:

@@ -393,6 +393,20 @@ int orc_decode_layout(const int32_t *seq_lens, const int32_t *query_lens, int64_
     return ORC_OK;
 }
 
+/* Rows per verify tile ([fp4ops] decode_tile_size): one row of a tile costs
+ * 4 B per key of FP32 logits, 24 B per selected key of selection scratch,
+ * 64 B per head of quantized query and 256 B more; a tile gets as many rows
+ * as fit in 32 rows of FP32 logits at max_model_len keys, and never fewer
+ * than 32. Integer division rounds down. */
+int64_t orc_decode_tile_size(int64_t max_model_len, int64_t width, int topk, int heads) {
+    int64_t selected = topk < width ? (int64_t)topk : width;
+    int64_t row_bytes = 4 * width + 24 * selected + 64 * (int64_t)heads + 256;
+    if (row_bytes < 1) row_bytes = 1;
+    int64_t budget = 32 * 4 * max_model_len;
+    int64_t rows = budget / row_bytes;
+    return rows < 32 ? 32 : rows;
+}
+
 /* ------------------------------------------------------------------------ */
 /* score_paged ([fp4ops] score_paged; [idx] module text: MX scales stay     */
 /* inside the logits contraction, head weights carry only the weight scale) */

@@ -80,6 +80,10 @@ def library():
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
             "dsaidx_topk_noalloc": (I32, [P, I64, I64, I64, P, I32, P, I64, P]),
+            "dsaidx_decode_tile_size": (I64, [I64, I64, I32, I32]),
+            "dsaidx_score_topk_tiled_workspace_bytes": (SZ, [I64, I64, I64, I32]),
+            "dsaidx_score_topk_tiled": (I32, [I32, P, I64, I32, P, I64, P, I64, I64, P, I64, I64,
+                                              P, P, I64, I32, I32, P, I64, I64, P, I64, P, SZ, P]),
             "dsaidx_dcp_candidates": (I32, [P, I64, I64, I64, P, I32, I64, I32, I32, I32, P, P, P]),
             "dsaidx_dcp_merge": (I32, [P, P, I32, I64, I32, I32, P, I64, I32, I32, P, I64, P]),
         }
@@ -388,6 +392,51 @@ def score_topk(q_rows, heads, weights, cache, num_pages, page_stride, block_tabl
                                 workspace.data_ptr(), workspace.numel(), _stream(q_rows))
     _check("topk_scored", st)
     return out, indices
+
+
+def decode_tile_size(max_model_len, width, topk, heads) -> int:
+    """Rows per tile that bound logits, selection scratch and queries (page
+    "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_tile_size)."""
+    return int(library().dsaidx_decode_tile_size(int(max_model_len), int(width), int(topk),
+                                                 int(heads)))
+
+
+def score_topk_tiled(q_rows, heads, weights, cache, num_pages, page_stride, block_table,
+                     query_starts, row_ends, max_query_len, k, tile_rows, fmt="mxfp4",
+                     section_offset=0, indices=None, logits_tile=None, workspace=None):
+    """score_topk over row tiles of `tile_rows` rows: only one tile's logits and selection
+    scratch exist at a time. Returns (indices int32 [rows, k], logits_tile FP32
+    [tile_rows, max_blocks*64] holding the last tile's logits)."""
+    import torch
+    _dev(q_rows, "q_rows", torch.uint8)
+    _dev(weights, "weights", torch.bfloat16)
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(query_starts, "query_starts", torch.int32)
+    _dev(row_ends, "row_ends", torch.int32)
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [num_requests, max_blocks] tensor")
+    nreq, max_blocks = block_table.shape
+    rows = q_rows.shape[0]
+    width = max_blocks * 64
+    dev_ = q_rows.device
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=dev_)
+    if logits_tile is None:
+        logits_tile = torch.empty((int(tile_rows), width), dtype=torch.float32, device=dev_)
+    lib = library()
+    need = int(lib.dsaidx_score_topk_tiled_workspace_bytes(nreq, max_blocks, int(tile_rows),
+                                                           int(max_query_len)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev_)
+    _check("score_topk_tiled", lib.dsaidx_score_topk_tiled(
+        _fmt(fmt), q_rows.data_ptr(), q_rows.stride(0), heads, weights.data_ptr(),
+        weights.stride(0), cache.data_ptr() + section_offset, num_pages, page_stride,
+        block_table.data_ptr(), nreq, max_blocks, query_starts.data_ptr(), row_ends.data_ptr(),
+        rows, max_query_len, k, indices.data_ptr(), indices.stride(0), int(tile_rows),
+        logits_tile.data_ptr(), logits_tile.stride(0), workspace.data_ptr(), workspace.numel(),
+        _stream(q_rows)))
+    return indices, logits_tile
 
 
 def index_score_topk(projected, key_col, weight_col, q, gamma, beta, eps, seq_lens, query_lens,

@@ -349,6 +349,75 @@ dsaidx_status dsaidx_score_paged_hist(int fmt, const void *q, int64_t q_row_stri
     return hip_status(dsaidx::launch_score_paged_hist(a, workspace, as_stream(stream)));
 }
 
+int64_t dsaidx_decode_tile_size(int64_t max_model_len, int64_t width, int32_t topk,
+                                int32_t heads) {
+    if (max_model_len < 0 || width < 0 || topk < 1 || heads < 1 ||
+        max_model_len > ((int64_t)1 << 40) || width > ((int64_t)1 << 40))
+        return 0;
+    const int64_t row_bytes = 4 * width + 24 * (topk < width ? (int64_t)topk : width) +
+                              64 * (int64_t)heads + 256;
+    const int64_t rows = 32 * 4 * max_model_len / (row_bytes > 1 ? row_bytes : 1);
+    return rows > 32 ? rows : 32;
+}
+
+size_t dsaidx_score_topk_tiled_workspace_bytes(int64_t num_requests, int64_t max_blocks,
+                                               int64_t tile_rows, int32_t max_query_len) {
+    if (num_requests < 1 || max_blocks < 1 || tile_rows < 1 || max_query_len < 1 ||
+        max_query_len > DSAIDX_MAX_QUERY_LEN || max_blocks > (int64_t)INT32_MAX / 64)
+        return 0;
+    const int64_t gr = dsaidx::tiled_geometry_requests(num_requests, tile_rows, max_query_len);
+    if (dsaidx::score_geometry(gr, max_blocks).chunks > dsaidx::kMaxRowSegments) return 0;
+    return dsaidx::score_topk_tiled_workspace_bytes(num_requests, max_blocks, tile_rows,
+                                                    max_query_len);
+}
+
+dsaidx_status dsaidx_score_topk_tiled(int fmt, const void *q, int64_t q_row_stride,
+                                      int32_t heads, const void *w, int64_t w_row_stride,
+                                      const void *cache, int64_t num_pages, int64_t page_stride,
+                                      const int32_t *block_table, int64_t num_requests,
+                                      int64_t max_blocks, const int32_t *query_starts,
+                                      const int32_t *row_ends, int64_t num_rows,
+                                      int32_t max_query_len, int32_t k, int32_t *indices,
+                                      int64_t indices_row_stride, int64_t tile_rows,
+                                      float *logits_tile, int64_t logits_tile_row_stride,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0 ||
+        k < 1 || tile_rows < 1)
+        return DSAIDX_EINVAL;
+    if (!valid_heads(heads) || max_query_len < 1 || max_query_len > DSAIDX_MAX_QUERY_LEN)
+        return DSAIDX_EUNSUPPORTED;
+    if (num_rows == 0) return DSAIDX_OK;
+    if (num_requests == 0 || max_blocks == 0 || num_pages == 0)
+        return DSAIDX_EINVAL;  // rows to select for, and no scoring geometry
+    if (!q || !w || !cache || !block_table || !query_starts || !row_ends || !logits_tile ||
+        !indices || !workspace)
+        return DSAIDX_EINVAL;
+    if (!aligned(q, 16) || q_row_stride % 16 || q_row_stride < dsaidx_query_row_bytes(fmt, heads))
+        return DSAIDX_ELAYOUT;
+    if (!aligned(w, 8) || w_row_stride % 4 || w_row_stride < heads) return DSAIDX_ELAYOUT;
+    if (page_stride < section_bytes(fmt) || page_stride % 16 || !aligned(cache, 16))
+        return DSAIDX_ELAYOUT;
+    if (max_blocks > (int64_t)INT32_MAX / DSAIDX_PAGE_TOKENS ||
+        logits_tile_row_stride < max_blocks * DSAIDX_PAGE_TOKENS || !aligned(logits_tile, 4) ||
+        indices_row_stride < k || !aligned(indices, 4))
+        return DSAIDX_ELAYOUT;
+    const int64_t gr = dsaidx::tiled_geometry_requests(num_requests, tile_rows, max_query_len);
+    const dsaidx::ScoreGeometry geo = dsaidx::score_geometry(gr, max_blocks);
+    if (geo.chunks * num_requests > kMaxGrid || geo.chunks > dsaidx::kMaxRowSegments ||
+        tile_rows * (geo.chunks + 1) > kMaxGrid)
+        return DSAIDX_EUNSUPPORTED;
+    if (workspace_bytes < dsaidx::score_topk_tiled_workspace_bytes(num_requests, max_blocks,
+                                                                   tile_rows, max_query_len))
+        return DSAIDX_EINVAL;
+    if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
+    const dsaidx::ScoreArgs a{fmt,         q,          q_row_stride, heads,         w,
+                              w_row_stride, cache,     num_pages,    page_stride,   block_table,
+                              num_requests, max_blocks, query_starts, row_ends,     num_rows,
+                              max_query_len, logits_tile, logits_tile_row_stride};
+    return hip_status(dsaidx::launch_score_topk_tiled(a, k, indices, indices_row_stride, tile_rows,
+                                                      workspace, as_stream(stream)));
+}
+
 dsaidx_status dsaidx_index_score_hist(
     int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
     const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,

@@ -55,6 +55,10 @@ struct ScoreArgs {
     int max_query_len;
     float *logits;
     int64_t logits_row_stride;
+    // the row window [row_lo, num_rows): logits and histograms of row r at row r - row_lo
+    int64_t row_lo = 0;
+    // requests the launch geometry is sized for (0: num_requests)
+    int64_t geometry_requests = 0;
 };
 
 hipError_t launch_score_paged(const ScoreArgs &args, hipStream_t stream);
@@ -94,6 +98,15 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks);
 // (num_rows, chunks) segments; then launch_topk_after_histograms finishes the selection.
 size_t score_topk_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t num_rows);
 hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStream_t stream);
+
+// Row-tiled scoring + selection ([fp4ops] decode_tile_size): the logits buffer and the
+// workspace hold one tile of `tile_rows` rows; indices are written for every row.
+int64_t tiled_geometry_requests(int64_t num_requests, int64_t tile_rows, int max_query_len);
+size_t score_topk_tiled_workspace_bytes(int64_t num_requests, int64_t max_blocks, int64_t tile_rows,
+                                        int max_query_len);
+hipError_t launch_score_topk_tiled(const ScoreArgs &a, int k, int32_t *indices,
+                                   int64_t indices_row_stride, int64_t tile_rows,
+                                   void *workspace, hipStream_t stream);
 
 // Decode context parallelism: one rank's merge candidates, and the merge.
 constexpr int kDcpMergeCap = 16384;  // world * candidates per rank, per row

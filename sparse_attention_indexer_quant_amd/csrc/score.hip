@@ -620,7 +620,8 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const uint8_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ w,
     int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
     int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
-    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin) {
+    uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin,
+    int64_t row_lo) {
     static_assert(!FUSED || HIST, "fused inputs: with histograms");
     constexpr int kStagedKeyBytes = staged_key_bytes<FMT>();
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
@@ -726,7 +727,11 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
 
     if (r0 < 0) return;
     if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
+    // the row window [row_lo, num_rows): rows outside it are neither scored nor written, and
+    // the logits and histograms of row r go to row r - row_lo of their buffers (row_lo is 0
+    // except for the tiles of a row-tiled selection)
     if (r1 > num_rows) r1 = num_rows;
+    if (r0 < row_lo) r0 = row_lo;
     const int nrows = (int)(r1 - r0);
     if (nrows <= 0) return;
 
@@ -859,8 +864,9 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                     if ((own_mask >> i) & 1u)
                         patch_key(own_pg, staged_keys + (wave * RG + i) * kStagedKeyBytes,
                                   own_o[i], l16, grp);
-                rows.score(own_pg, (int)(block_of(own_pp) * kPageTokens), count, logits, first,
-                           logits_row_stride, lane, grp, HIST ? hist : nullptr, sel32, sel16);
+                rows.score(own_pg, (int)(block_of(own_pp) * kPageTokens), count, logits,
+                           first - row_lo, logits_row_stride, lane, grp, HIST ? hist : nullptr,
+                           sel32, sel16);
             }
         }
         for (int base = 0; base < run; base += NB) {
@@ -874,8 +880,8 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 load_page(buf[(slot + NB - 1) % NB], section(p + NB - 1, run), off);
                 if (p < run && table_page(p) >= 0 && (!FUSED || p != own_pp))
                     rows.score(buf[slot], (int)(block_of(p) * kPageTokens), count, logits,
-                               first, logits_row_stride, lane, grp, HIST ? hist : nullptr,
-                               sel32, sel16);
+                               first - row_lo, logits_row_stride, lane, grp,
+                               HIST ? hist : nullptr, sel32, sel16);
             }
         }
         if constexpr (HIST) {
@@ -888,7 +894,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 if (j >= count || seg_begin >= rows.rend[j]) continue;
                 // lane t copies fine bins [16 t, 16 t + 16) and, with lanes 4c..4c+3, forms
                 // coarse bin c (fine bins [64 c, 64 c + 64))
-                const int64_t at = (first + j) * chunks + chunk;
+                const int64_t at = (first + j - row_lo) * chunks + chunk;
                 uint4 *dst = reinterpret_cast<uint4 *>(seghist + at * kBins) + 2 * threadIdx.x;
                 const uint4 *src = reinterpret_cast<const uint4 *>(hist + j * (kBins / 2)) +
                                    2 * threadIdx.x;
@@ -954,7 +960,9 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
 template <int FMT, int H, int RG, bool HIST, bool FUSED = false>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream,
                                   const FusedInputs &fin = FusedInputs{}) {
-    const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
+    const ScoreGeometry geo = score_geometry(a.geometry_requests > 0 ? a.geometry_requests
+                                                                     : a.num_requests,
+                                             a.max_blocks);
     const dim3 grid((unsigned)(geo.chunks * a.num_requests)), block(64 * kWaves);
     // page buffers per wavefront: 3 for MXFP4 (measured best of 2-6 on the long-context
     // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
@@ -966,7 +974,7 @@ static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, h
                        a.num_pages, geo.chunks, static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
-                       ws.coarse, fin);
+                       ws.coarse, fin, a.row_lo);
     return hipGetLastError();
 }
 
@@ -1011,6 +1019,54 @@ hipError_t launch_score_paged_hist(const ScoreArgs &a, void *workspace, hipStrea
         case kFmtFp8: return launch_score_fmt<kFmtFp8, true>(a, ws, stream);
         default: return launch_score_fmt<kFmtFp8Mx, true>(a, ws, stream);
     }
+}
+
+// Row-tiled scoring and selection: for each tile of `tile_rows` consecutive rows, the scorer
+// with that row window (logits and histograms in tile-row order, so both buffers hold one
+// tile), then the rest of the selection on the tile's rows. A tile holds the rows of about
+// tile_rows / max_query_len requests (at least that many when requests have their most rows),
+// so the scorer's geometry is sized for that many: a tile's pages spread over about one
+// wavefront per SIMD, as a whole batch's do.
+int64_t tiled_geometry_requests(int64_t num_requests, int64_t tile_rows, int max_query_len) {
+    const int64_t per = (tile_rows + max_query_len - 1) / max_query_len;
+    return per < num_requests ? per : num_requests;
+}
+
+size_t score_topk_tiled_workspace_bytes(int64_t num_requests, int64_t max_blocks,
+                                        int64_t tile_rows, int max_query_len) {
+    const int64_t gr = tiled_geometry_requests(num_requests, tile_rows, max_query_len);
+    return topk_layout_bytes(tile_rows, score_geometry(gr, max_blocks).chunks);
+}
+
+hipError_t launch_score_topk_tiled(const ScoreArgs &base, int k, int32_t *indices,
+                                   int64_t indices_row_stride, int64_t tile_rows,
+                                   void *workspace, hipStream_t stream) {
+    const int64_t gr = tiled_geometry_requests(base.num_requests, tile_rows, base.max_query_len);
+    const ScoreGeometry geo = score_geometry(gr, base.max_blocks);
+    const int64_t width = base.max_blocks * kPageTokens;
+    for (int64_t lo = 0; lo < base.num_rows; lo += tile_rows) {
+        const int64_t hi = lo + tile_rows < base.num_rows ? lo + tile_rows : base.num_rows;
+        // laid out for the tile's own row count, as the selection below carves it (the last
+        // tile may be shorter; a shorter layout fits in the space of a full one)
+        const TopkWorkspace ws = carve(workspace, hi - lo, geo.chunks);
+        ScoreArgs a = base;
+        a.geometry_requests = gr;
+        a.row_lo = lo;
+        a.num_rows = hi;
+        hipError_t e;
+        switch (a.fmt) {
+            case kFmtMxfp4: e = launch_score_fmt<kFmtMxfp4, true>(a, ws, stream); break;
+            case kFmtFp8: e = launch_score_fmt<kFmtFp8, true>(a, ws, stream); break;
+            default: e = launch_score_fmt<kFmtFp8Mx, true>(a, ws, stream); break;
+        }
+        if (e != hipSuccess) return e;
+        e = launch_topk_after_histograms(base.logits, hi - lo, width, base.logits_row_stride,
+                                         base.row_ends + lo, k, indices + lo * indices_row_stride,
+                                         indices_row_stride, workspace, geo.chunks,
+                                         geo.segment_keys, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // The step's inputs and its scoring in one launch (histograms, one row group: at most 4 rows

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import sparse_attention_indexer_quant_amd as dsa
+from goldens import rows
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsaidx.h")
@@ -39,7 +40,8 @@ def test_header_declares_the_entry_points():
               "dsaidx_topk_scored", "dsaidx_score_topk_workspace_bytes", "dsaidx_dcp_candidates",
               "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys",
               "dsaidx_read_sections", "dsaidx_read_sections_words", "dsaidx_read_stream",
-              "dsaidx_topk_noalloc"):
+              "dsaidx_topk_noalloc", "dsaidx_decode_tile_size", "dsaidx_score_topk_tiled",
+              "dsaidx_score_topk_tiled_workspace_bytes"):
         assert n in names
 
 
@@ -278,6 +280,50 @@ def read_sections(lib, **kw):
     a.update(kw)
     return lib.dsaidx_read_sections(a["fmt"], a["cache"], a["np_"], a["ps"], a["bt"], a["r"],
                                     a["mb"], a["seq"], a["out"], a["ow"], None)
+
+
+def test_decode_tile_size_matches_golden(lib):
+    # a host function of the library: the hand-worked values of tests/golden/decode_tile_size.txt
+    for line in rows("decode_tile_size.txt"):
+        mml, width, topk, heads, want = (int(v) for v in line.split())
+        assert lib.dsaidx_decode_tile_size(mml, width, topk, heads) == want, line
+    assert lib.dsaidx_decode_tile_size(-1, 64, 8, 32) == 0
+    assert lib.dsaidx_decode_tile_size(64, 64, 0, 32) == 0
+    assert lib.dsaidx_decode_tile_size(64, 64, 8, 0) == 0
+
+
+def tiled(lib, **kw):
+    a = dict(fmt=0, q=P, qs=2176, h=32, w=P, ws_=32, cache=P, np_=10, ps=4352, bt=P, r=2, mb=4,
+             st=P, ends=P, rows=8, mql=4, k=16, out=P, os=16, tile=4, lt=P, lts=256, wsp=P,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.dsaidx_score_topk_tiled(a["fmt"], a["q"], a["qs"], a["h"], a["w"], a["ws_"],
+                                       a["cache"], a["np_"], a["ps"], a["bt"], a["r"], a["mb"],
+                                       a["st"], a["ends"], a["rows"], a["mql"], a["k"], a["out"],
+                                       a["os"], a["tile"], a["lt"], a["lts"], a["wsp"], a["wsb"],
+                                       None)
+
+
+def test_score_topk_tiled_checks(lib):
+    assert tiled(lib, tile=0) == EINVAL
+    assert tiled(lib, k=0) == EINVAL
+    assert tiled(lib, fmt=7) == EINVAL
+    assert tiled(lib, h=24) == EUNSUP
+    assert tiled(lib, mql=17) == EUNSUP
+    assert tiled(lib, rows=0, q=None) == OK
+    assert tiled(lib, r=0) == EINVAL            # rows to select for, nothing to score with
+    assert tiled(lib, lt=None) == EINVAL
+    assert tiled(lib, wsp=None) == EINVAL
+    assert tiled(lib, wsb=16) == EINVAL
+    assert tiled(lib, lts=255) == ELAYOUT       # a tile row narrower than max_blocks * 64
+    assert tiled(lib, os=15) == ELAYOUT
+    assert tiled(lib, ps=4096) == ELAYOUT
+    assert tiled(lib, wsp=P + 16) == ELAYOUT
+    # the workspace holds one tile: it grows with tile_rows, not with the rows
+    one = lib.dsaidx_score_topk_tiled_workspace_bytes(128, 1024, 32, 4)
+    assert 0 < one < lib.dsaidx_score_topk_tiled_workspace_bytes(128, 1024, 64, 4)
+    assert lib.dsaidx_score_topk_tiled_workspace_bytes(128, 1024, 0, 4) == 0
+    assert lib.dsaidx_score_topk_tiled_workspace_bytes(128, 1024, 32, 0) == 0
 
 
 def test_read_stream_checks(lib):

@@ -406,6 +406,59 @@ def test_score_topk_matches_separate_calls(name, k):
     assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), f"{name} k={k}")
 
 
+# ---- bounded logits: row tiles (page "...amd.ops.fp4_indexer", decode_tile_size) -------------
+
+TILED_CASES = {
+    # verify rows (1..4 per request, tiles splitting requests) with graph padding rows
+    "fp4_h32_verify": (dict(fmt="mxfp4", heads=32, seq_lens=[700, 129, 2000, 64, 1500, 5, 900],
+                            query_lens=[3, 1, 4, 2, 4, 1, 2], num_rows=21), [1, 3, 5, 8, 32]),
+    "fp4_h64_merged": (dict(fmt="mxfp4", heads=64, seq_lens=[600, 1300, 70], query_lens=[2, 1, 3],
+                            page_stride=8192, section_offset=3840), [2, 4]),
+    "fp8_h32_verify": (dict(fmt="fp8", heads=32, seq_lens=[500, 129, 1000], query_lens=[2, 1, 2],
+                            num_rows=7, outlier_frac=0.01, outlier_gain=20.0), [3]),
+}
+
+
+@pytest.mark.parametrize("name", list(TILED_CASES))
+@pytest.mark.parametrize("k", [64, 700])
+def test_score_topk_tiled_matches_untiled_and_oracle(name, k):
+    kw, tiles = TILED_CASES[name]
+    wl = make_workload(name, topk=k, seed=29, extra_pages=2, **kw)
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, ends = dw.layout()
+    oe = ends.cpu().numpy()
+    full = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, idx_full = dsa.score_topk(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride,
+                                 dw.block_table, starts, ends, wl.max_query_len, k, wl.fmt,
+                                 wl.section_offset, out=full)
+    full_np = full.cpu().numpy()
+    oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+    os_, _ = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+    ref = oracle.score_paged(oq, wl.heads, ow, oracle_cache(wl), wl.num_pages, wl.page_stride,
+                             wl.block_table, os_, oe, wl.fmt, wl.section_offset)
+    assert_logits_close(full_np, ref, oe, range(wl.num_rows), name)
+    want = oracle.topk(np.nan_to_num(full_np, nan=0.0), oe, k)
+    for tile in tiles + [wl.num_rows + 5]:
+        ws = torch.full((dsa.library().dsaidx_score_topk_tiled_workspace_bytes(
+            wl.num_requests, wl.max_blocks, tile, wl.max_query_len),), 0xA7, dtype=torch.uint8,
+            device="cuda")
+        lt = torch.full((tile, wl.width), float("nan"), device="cuda")
+        idx, lt = dsa.score_topk_tiled(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride,
+                                       dw.block_table, starts, ends, wl.max_query_len, k, tile,
+                                       wl.fmt, wl.section_offset, logits_tile=lt, workspace=ws)
+        what = f"{name} k={k} tile={tile}"
+        assert_topk_sets(idx.cpu().numpy(), idx_full.cpu().numpy(), range(wl.num_rows), what)
+        assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), what)
+        # the buffer holds the last tile's logits, bit for bit those of the untiled scorer
+        last = (wl.num_rows - 1) // tile * tile
+        got = lt.cpu().numpy()
+        for r in range(last, wl.num_rows):
+            n = min(int(oe[r]), wl.width)
+            assert np.array_equal(got[r - last, :n].view(np.uint32), full_np[r, :n].view(np.uint32)), what
+
+
 # ---- index_score_hist (step inputs made inside the scorer) ----------------------------------
 
 FUSED_CASES = {

@@ -344,6 +344,16 @@ def test_decode_layout_golden():
     assert n == 10
 
 
+def test_decode_tile_size_golden():
+    # tests/golden/decode_tile_size.txt, worked by hand from page "...amd.ops.fp4_indexer"
+    n = 0
+    for line in rows("decode_tile_size.txt"):
+        mml, width, topk, heads, want = (int(v) for v in line.split())
+        assert oracle.decode_tile_size(mml, width, topk, heads) == want, line
+        n += 1
+    assert n == 7
+
+
 def test_decode_layout_dcp_shares_sum_to_global():
     rng = np.random.default_rng(14)
     for _ in range(50):
