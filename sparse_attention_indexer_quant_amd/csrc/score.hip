@@ -564,11 +564,30 @@ __device__ __forceinline__ void patch_key(PageRegs<kFmtFp8Mx> &pg, const uint8_t
 }
 
 // Rows of request `req` from the query lengths: the first is the sum of the lengths before it
-// (a wavefront sum, uniform), the count its own length.
-__device__ __forceinline__ int64_t request_first_row(const int32_t *lens, int64_t req, int lane) {
-    // 256 lengths per round trip: each pass issues its four loads before adding any
+// (a wavefront sum, uniform), the count its own length. The first 256 lengths (four per lane)
+// are loaded without conditions, at indices clamped into [0, R) (all in bounds), so a kernel
+// can issue them early and later loads' waits count exactly; lengths beyond are summed in a
+// loop of their own (requests past the 256th only).
+struct FirstRowLoads {
+    int v[4];
+};
+
+__device__ __forceinline__ FirstRowLoads issue_first_row(const int32_t *lens, int64_t R, int lane) {
+    FirstRowLoads f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = 64 * u + lane;
+        f.v[u] = lens[i < R ? i : R - 1];
+    }
+    return f;
+}
+
+__device__ __forceinline__ int64_t finish_first_row(const FirstRowLoads &f, const int32_t *lens,
+                                                    int64_t req, int lane) {
     int acc = 0;
-    for (int64_t base = 0; base < req; base += 256) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += 64 * u + lane < req ? f.v[u] : 0;
+    for (int64_t base = 256; base < req; base += 256) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -678,17 +697,44 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     if constexpr (kSpecQuery)
         sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride, fin.w_in,
                 fin.proj_row_stride, spec_row, spec_row + 1, wave, l16, grp);
+    // FUSED: `query_starts` holds the query lengths; the first round of the first-row sum's
+    // loads goes out in the same round trip (after the query's, which arrive with them)
+    FirstRowLoads first_row_loads;
+    if constexpr (FUSED) first_row_loads = issue_first_row(query_starts, num_requests, lane);
+
+    // Table entry of run page p (uniform), or -1 if it names no page of the cache.
+    const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
+    auto table_page = [&](int p) -> int {
+        const int pg = __builtin_amdgcn_readlane(bt_lane, p);
+        return (uint32_t)pg < npages ? pg : -1;
+    };
+    // Section that run page p's loads read: the page itself, or page 0 as a stand-in for a
+    // page that is not scored (past `limit`, or not a page of the cache).
+    auto section = [&](int p, int limit) {
+        const int pg = p < limit ? table_page(p) : -1;
+        return cache + (int64_t)(pg >= 0 ? pg : 0) * page_stride;
+    };
+    const LaneOffsets<FMT> off(l16, grp);
+    PageRegs<FMT> buf[NB];
+
     int64_t r0, r1;
     int qlen = 0, seq = 0;
     if constexpr (!FUSED) {
         r0 = query_starts[req];
         r1 = query_starts[req + 1];
     } else {
-        // `query_starts` holds the query lengths; the request's own length and sequence length
-        // are scalar loads, its first row a sum over the lengths before it
+        // the request's own length and sequence length are scalar loads
         qlen = query_starts[req];
         seq = fin.seq_lens[req];
-        r0 = request_first_row(query_starts, req, lane);
+        // The first NB - 1 pages go out as soon as the table slice is in, before the first-row
+        // sum waits for its loads (issued before them, so that wait does not cover the pages):
+        // the pages stream while the rows are found and the query is encoded. A chunk past the
+        // request's keys (known below) reads pages it does not score.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
+        asm volatile("" ::: "memory");
+        r0 = finish_first_row(first_row_loads, query_starts, req, lane);
         r1 = r0 + qlen;
     }
     hoist_args(num_pages, chunks, q, q_row_stride, w, w_row_stride, row_ends, num_rows,
@@ -711,19 +757,6 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
             }
         }
     }
-
-    // Table entry of run page p (uniform), or -1 if it names no page of the cache.
-    const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
-    auto table_page = [&](int p) -> int {
-        const int pg = __builtin_amdgcn_readlane(bt_lane, p);
-        return (uint32_t)pg < npages ? pg : -1;
-    };
-    // Section that run page p's loads read: the page itself, or page 0 as a stand-in for a
-    // page that is not scored (past `limit`, or not a page of the cache).
-    auto section = [&](int p, int limit) {
-        const int pg = p < limit ? table_page(p) : -1;
-        return cache + (int64_t)(pg >= 0 ? pg : 0) * page_stride;
-    };
 
     if (r0 < 0) return;
     if (r1 > r0 + max_query_len) r1 = r0 + max_query_len;
@@ -765,14 +798,15 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 fin.key_in + (r0 + (i < nrows ? i : 0)) * fin.proj_row_stride + 2 * lane);
     }
 
-    // The first NB - 1 pages go out after the query and bound loads: loads complete in issue
-    // order, so the first page's math then waits for that page and not for the whole ring.
-    const LaneOffsets<FMT> off(l16, grp);
-    PageRegs<FMT> buf[NB];
-    asm volatile("" ::: "memory");
+    // The plain form's first NB - 1 pages go out after the query and bound loads: loads
+    // complete in issue order, so the first page's math then waits for that page and not for
+    // the whole ring.
+    if constexpr (!FUSED) {
+        asm volatile("" ::: "memory");
 #pragma unroll
-    for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
-    asm volatile("" ::: "memory");
+        for (int p = 0; p < NB - 1; ++p) load_page(buf[p], section(p, PW), off);
+        asm volatile("" ::: "memory");
+    }
 
     // FUSED: the new key at position seq - qlen + i belongs to the wavefront whose run holds
     // its block. The step's keys are consecutive positions (at most 4), so they span at most

@@ -379,50 +379,99 @@ __device__ __forceinline__ void load_keys16(float (&raw)[kCollectPer], const flo
     }
 }
 
+// The float of an order key (the inverse of order_key on keys of non-NaN floats; +0 for the
+// key of zero).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The threshold bin as two float bounds: a logit f is above the bin when f >= hi and inside it
+// when lo <= f < hi. Float comparison agrees with the order keys here, signed zeros included:
+// order_key gives -0 the key of +0, and IEEE comparison takes -0 equal to +0. A bin holding a
+// finite logit lies between the keys of -FLT_MAX and +inf, so both bounds are numbers (the
+// upper one +inf for the bin of the largest finite values, above which nothing lies).
+struct BinBounds {
+    float lo, hi;
+    __device__ __forceinline__ explicit BinBounds(uint32_t bin)
+        : lo(key_float(bin << kBinShift)), hi(key_float((bin + 1) << kBinShift)) {}
+};
+
+// Bit j of `above` / `in`: key j of the lane's 16 (position first + j) lies above the threshold
+// bin / inside it; keys at or past `bound` (live = bound - first of them are live) in neither.
+struct Masks16 {
+    uint32_t above, in;
+};
+__device__ __forceinline__ Masks16 classify16(const float (&raw)[kCollectPer], int64_t live,
+                                              const BinBounds &b) {
+    Masks16 m{0u, 0u};
+    if (live <= 0) return m;  // a wavefront with no live key skips the work
+#pragma unroll
+    for (int j = 0; j < kCollectPer; ++j) {
+        const float f = raw[j];
+        m.above |= f >= b.hi ? 1u << j : 0u;
+        m.in |= (f >= b.lo && f < b.hi) ? 1u << j : 0u;
+    }
+    const uint32_t lm = live >= kCollectPer ? 0xFFFFu : (1u << live) - 1u;
+    m.above &= lm;
+    m.in &= lm;
+    return m;
+}
+
+// Waits for every load in flight, so that no later instruction does: placed after the keys'
+// loads and before any store, it keeps the compiler from waiting on a register a load might
+// still write (a path that skips the keys' use) at a point where stores are in flight too --
+// the counter it waits on counts both, and a store's round trip is as long as a load's.
+__device__ __forceinline__ void loads_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Positions of the lane's keys above the bin to out[pa], out[pa + 1], .. (while below `cap`),
+// in ascending order: one step per set bit.
+__device__ __forceinline__ void write_above(uint32_t mask, int64_t first, uint32_t pa,
+                                            uint32_t cap, int32_t *out) {
+    for (; mask; mask &= mask - 1u, ++pa)
+        if (pa < cap) out[pa] = (int32_t)(first + __builtin_ctz(mask));
+}
+
+// Keys [lo, hi) of a row held by one workgroup of kTopkThreads lanes, in chunks of 4096 (16 per
+// lane, in registers). The caller has loaded the first chunk (`raw`, bounded by `hi` or by the
+// row's width: keys past `hi` are masked here). Positions of keys above bin `bin` go to the output
+// and (key, position) pairs inside it to the candidate list, after the segment's offsets `off`
+// and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
 template <int VEC>
 __device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const float *x,
                                                 int64_t lo, int64_t hi, uint32_t bin,
                                                 uint32_t above, uint2 off, int32_t *out,
                                                 uint2 *cand, int *partials) {
     constexpr int kChunk = kCollectPer * kTopkThreads;
+    const BinBounds bb(bin);
     uint32_t base_above = off.x, base_in = off.y;
     for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
         const int64_t first = cbase + (int64_t)threadIdx.x * kCollectPer;
         if (cbase != lo) load_keys16<VEC>(raw, x, first, hi);
-        uint32_t u[kCollectPer];
-#pragma unroll
-        for (int j = 0; j < kCollectPer; ++j) u[j] = order_key(raw[j]);
-        int n_above = 0, n_in = 0;
-#pragma unroll
-        for (int j = 0; j < kCollectPer; ++j) {
-            const uint32_t d = u[j] >> kBinShift;
-            n_above += first + j < hi && d > bin;
-            n_in += first + j < hi && d == bin;
-        }
-        const int mine = n_above | (n_in << 16);
+        const Masks16 m = classify16(raw, hi - first, bb);
+        loads_done();
+        const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
         const int incl = scan_block<kTopkThreads>(mine, partials);
-        uint32_t pa = base_above + ((incl - mine) & 0xFFFF);
-        uint32_t pc = base_in + ((incl - mine) >> 16);
+        // the keys' last use comes before any store: a use of a loaded register after a store
+        // makes the compiler wait for every store in flight as well (the counter it waits on
+        // counts both)
+        if (m.in) {
+            uint32_t pc = base_in + ((incl - mine) >> 16);
 #pragma unroll
-        for (int j = 0; j < kCollectPer; ++j) {
-            const int64_t i = first + j;
-            const uint32_t d = u[j] >> kBinShift;
-            const bool live = i < hi;
-            if (live && d > bin) {
-                if (pa < above) out[pa] = (int32_t)i;
-                ++pa;
-            } else if (live && d == bin) {
-                if (pc < (uint32_t)kCandCap) cand[pc] = make_uint2(u[j], (uint32_t)i);
+            for (int j = 0; j < kCollectPer; ++j) {
+                if (!((m.in >> j) & 1u)) continue;
+                if (pc < (uint32_t)kCandCap)
+                    cand[pc] = make_uint2(order_key(raw[j]), (uint32_t)(first + j));
                 ++pc;
             }
         }
+        write_above(m.above, first, base_above + ((incl - mine) & 0xFFFF), above, out);
         // the chunk's totals are the sum of the wave totals the scan left in `partials`
         int tot = 0;
 #pragma unroll
         for (int w = 0; w < kTopkThreads / 64; ++w) tot += partials[w];
         base_above += (uint32_t)(tot & 0xFFFF);
         base_in += (uint32_t)(tot >> 16);
-        __syncthreads();
+        if (cbase + kChunk < hi) __syncthreads();  // `partials` is written again by the next scan
     }
 }
 
@@ -784,42 +833,33 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
 
     // (c) the row's keys once: lane counts and a workgroup prefix sum place every key
+    const BinBounds bb(bin);
     uint32_t base_above = 0, base_in = 0;
     for (int64_t cbase = 0; cbase < n; cbase += kChunk) {
         const int64_t first = cbase + (int64_t)t * kCollectPer;
         if (cbase != 0) load_keys16<VEC>(raw, x, first, n);
-        uint32_t u[kCollectPer];
-        int n_above = 0, n_in = 0;
-#pragma unroll
-        for (int j = 0; j < kCollectPer; ++j) {
-            u[j] = order_key(raw[j]);
-            const uint32_t d = u[j] >> kBinShift;
-            n_above += first + j < n && d > bin;
-            n_in += first + j < n && d == bin;
-        }
-        const int mine = n_above | (n_in << 16);
+        const Masks16 m = classify16(raw, n - first, bb);
+        loads_done();
+        const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
         const int incl = scan_block<kSelectThreads>(mine, sh.partials);
-        uint32_t pa = base_above + ((incl - mine) & 0xFFFF);
-        uint32_t pc = base_in + ((incl - mine) >> 16);
+        // the keys' last use before any store (see collect_segment)
+        if (keep && m.in) {
+            uint32_t pc = base_in + ((incl - mine) >> 16);
 #pragma unroll
-        for (int j = 0; j < kCollectPer; ++j) {
-            const int64_t i = first + j;
-            const uint32_t d = u[j] >> kBinShift;
-            const bool live = i < n;
-            if (live && d > bin) {
-                if (pa < (uint32_t)above) out[pa] = (int32_t)i;
-                ++pa;
-            } else if (live && d == bin) {
-                if (keep && pc < (uint32_t)kCandCap) cands[pc] = composite(u[j], (uint32_t)i, pos_bits);
+            for (int j = 0; j < kCollectPer; ++j) {
+                if (!((m.in >> j) & 1u)) continue;
+                if (pc < (uint32_t)kCandCap)
+                    cands[pc] = composite(order_key(raw[j]), (uint32_t)(first + j), pos_bits);
                 ++pc;
             }
         }
+        write_above(m.above, first, base_above + ((incl - mine) & 0xFFFF), (uint32_t)above, out);
         int tot = 0;
 #pragma unroll
         for (int w = 0; w < kSelectThreads / 64; ++w) tot += sh.partials[w];
         base_above += (uint32_t)(tot & 0xFFFF);
         base_in += (uint32_t)(tot >> 16);
-        __syncthreads();
+        __syncthreads();  // `partials` is written again; the candidates are complete in LDS
     }
     // (d) the k - above smallest composites inside the bin
     const int remaining = k - above;
