@@ -175,13 +175,16 @@ __device__ __forceinline__ uint32_t count8(const uint4 &w, int i) {
 // consecutive lanes of the segment, or zero where the segment has no key in coarse bin B: the
 // scorer writes a segment's fine blocks only where its coarse count is nonzero (the rest of a
 // reused workspace keeps earlier bytes). `cw` is the lane's word p8 of the segment's coarse
-// counts; the count of bin B is in word B / 8, held by the segment's lane p8 = B / 8. Every lane
-// of the wavefront calls it (a lane exchange).
-__device__ __forceinline__ uint4 fine_word(const uint4 *fine, int64_t sg, uint32_t B, int p8,
-                                           const uint4 &cw, bool live) {
+// counts (zero for a segment past the row's keys); the count of bin B is in word B / 8, held
+// by the segment's lane p8 = B / 8. Every lane of the wavefront calls it (a lane exchange). The
+// load is issued in every lane, at a segment clamped below nseg (in the workspace), so that the
+// waits after it count exactly; the words it is not meant to read are masked.
+__device__ __forceinline__ uint4 fine_word(const uint4 *fine, int64_t sg, int64_t nseg, uint32_t B,
+                                           int p8, const uint4 &cw) {
     const int lane = threadIdx.x & 63;
     const uint32_t cb = (uint32_t)__shfl((int)count8(cw, (int)(B & 7)), (lane & ~7) | (int)(B >> 3));
-    return live && cb != 0 ? fine[sg * (kBins / 8) + B * 8 + p8] : make_uint4(0, 0, 0, 0);
+    const uint4 w = fine[(sg < nseg ? sg : nseg - 1) * (kBins / 8) + B * 8 + p8];
+    return cb != 0 ? w : make_uint4(0, 0, 0, 0);
 }
 
 // Sum over the lanes of a wavefront that share t % 8 (lanes t % 8 + 8 j), in every one of
@@ -281,14 +284,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
     const uint32_t B = 63u - found_c;  // coarse bin, in ascending order
 
     // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
-    const uint4 fw0 = fine_word(fine, s0, B, p8, cw0, s0 < row_segments);
+    const uint4 fw0 = fine_word(fine, s0, nseg, B, p8, cw0);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = count8(fw0, e);
     for (int i = 1; i < blocks; ++i) {
         const int sg = s0 + i * kSegBlock;
         const uint4 cw = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
-        const uint4 w = fine_word(fine, sg, B, p8, cw, sg < row_segments);
+        const uint4 w = fine_word(fine, sg, nseg, B, p8, cw);
 #pragma unroll
         for (int e = 0; e < 8; ++e) fsum[e] += count8(w, e);
     }
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
         uint4 cw = cw0, fw = fw0;
         if (i > 0) {
             cw = sg < row_segments ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
-            fw = fine_word(fine, sg, B, p8, cw, sg < row_segments);
+            fw = fine_word(fine, sg, nseg, B, p8, cw);
         }
         uint32_t up = 0, in = 0;
 #pragma unroll
@@ -361,10 +364,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_threshold_kernel(
 // and (key, position) pairs inside it to the candidate list, after the segment's offsets `off`
 // and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
 constexpr int kCollectPer = 16;
+// VEC = 16: rows of whole 16-key runs (width a multiple of 16, 16-byte aligned rows): every lane
+// loads one run -- a lane at or past the row's width the row's last run instead, whose keys the
+// caller masks (they lie past `bound`) -- so the loads carry no condition and the waits after
+// them count exactly. VEC = 4: 16-byte loads for runs below `bound`, single keys for a run it
+// cuts. VEC = 1: single keys.
 template <int VEC>
 __device__ __forceinline__ void load_keys16(float (&raw)[kCollectPer], const float *x,
-                                            int64_t first, int64_t bound) {
-    if (VEC == 4 && first + kCollectPer <= bound) {
+                                            int64_t first, int64_t bound, int64_t width) {
+    if constexpr (VEC == 16) {
+        const int64_t at = first < width ? first : width - kCollectPer;
+#pragma unroll
+        for (int j = 0; j < kCollectPer; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + at + j);
+            raw[j] = v.x;
+            raw[j + 1] = v.y;
+            raw[j + 2] = v.z;
+            raw[j + 3] = v.w;
+        }
+    } else if (VEC == 4 && first + kCollectPer <= bound) {
 #pragma unroll
         for (int j = 0; j < kCollectPer; j += 4) {
             const float4 v = *reinterpret_cast<const float4 *>(x + first + j);
@@ -438,7 +456,7 @@ __device__ __forceinline__ void write_above(uint32_t mask, int64_t first, uint32
 // and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
 template <int VEC>
 __device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const float *x,
-                                                int64_t lo, int64_t hi, uint32_t bin,
+                                                int64_t lo, int64_t hi, int64_t width, uint32_t bin,
                                                 uint32_t above, uint2 off, int32_t *out,
                                                 uint2 *cand, int *partials) {
     constexpr int kChunk = kCollectPer * kTopkThreads;
@@ -446,7 +464,7 @@ __device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const
     uint32_t base_above = off.x, base_in = off.y;
     for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
         const int64_t first = cbase + (int64_t)threadIdx.x * kCollectPer;
-        if (cbase != lo) load_keys16<VEC>(raw, x, first, hi);
+        if (cbase != lo) load_keys16<VEC>(raw, x, first, hi, width);
         const Masks16 m = classify16(raw, hi - first, bb);
         loads_done();
         const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
@@ -494,13 +512,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
     const RowState st = state[row];
     float raw[kCollectPer];
     load_keys16<VEC>(raw, x, lo + (int64_t)threadIdx.x * kCollectPer,
-                     lo + seg_len < width ? lo + seg_len : width);
+                     lo + seg_len < width ? lo + seg_len : width, width);
     asm volatile("" ::: "memory");
     hoist_args(nseg, segoff, cand_all, k, indices, indices_row_stride);
     if (n <= k) return;
     if (lo >= n) return;
     const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
-    collect_segment<VEC>(raw, x, lo, hi, st.bin, (uint32_t)st.above, segoff[row * nseg + seg],
+    collect_segment<VEC>(raw, x, lo, hi, width, st.bin, (uint32_t)st.above, segoff[row * nseg + seg],
                          indices + row * indices_row_stride, cand_all + row * kCandCap,
                          partials);
 }
@@ -541,10 +559,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     // of the row, and arrive while the fine histogram words are fetched: loading them before
     // that, for every segment of every row, read tens of MB of logits past the rows' ends on
     // ragged workloads.
+    // (Loads are issued in every lane, at segments clamped below nseg, and masked at their
+    // use: conditional loads, or registers of loads in flight written over, make the compiler
+    // wait for every load in flight, the segment's keys included.)
     const int64_t n = row_bound(row_ends, row, width);
     const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
-    uint4 cw0 = s0 < nseg ? coarse[s0 * (kCoarseBins / 8) + p8] : zero4;
-    uint4 cw1 = s0 + 32 < nseg ? coarse[(s0 + 32) * (kCoarseBins / 8) + p8] : zero4;
+    const int sa = s0 < nseg ? s0 : nseg - 1, sb = s0 + 32 < nseg ? s0 + 32 : nseg - 1;
+    const uint4 cl0 = coarse[sa * (kCoarseBins / 8) + p8];
+    const uint4 cl1 = coarse[sb * (kCoarseBins / 8) + p8];
     asm volatile("" ::: "memory");
     hoist_args(fine_hist, indices, indices_row_stride, state, cand_all);
     if (n <= k) {
@@ -552,17 +574,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
             int32_t *out = indices + row * indices_row_stride;
             for (int i = t; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         }
-        keep_loaded(cw0.x);
-        keep_loaded(cw1.x);
+        keep_loaded(cl0.x);
+        keep_loaded(cl1.x);
         return;
     }
     if (lo >= n) return;
     const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
     float raw[kCollectPer];
-    load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer, hi);
+    load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer, hi, width);
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
-    if (s0 >= row_segments) cw0 = zero4;
-    if (s0 + 32 >= row_segments) cw1 = zero4;
+    const uint4 cw0 = s0 < row_segments ? cl0 : zero4;
+    const uint4 cw1 = s0 + 32 < row_segments ? cl1 : zero4;
     if (t == 0) {
         found_c = 0;  // kept only if the counts do not reach k (they always do)
         above_c = 0;
@@ -593,8 +615,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
 
     // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
     const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
-    const uint4 fw0 = fine_word(fine, s0, B, p8, cw0, s0 < row_segments);
-    const uint4 fw1 = fine_word(fine, s0 + 32, B, p8, cw1, s0 + 32 < row_segments);
+    const uint4 fw0 = fine_word(fine, s0, nseg, B, p8, cw0);
+    const uint4 fw1 = fine_word(fine, s0 + 32, nseg, B, p8, cw1);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw0, e) + count8(fw1, e));
@@ -650,7 +672,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         }
     }
     __syncthreads();
-    collect_segment<VEC>(raw, x, lo, hi, bin, (uint32_t)above, my_off,
+    collect_segment<VEC>(raw, x, lo, hi, width, bin, (uint32_t)above, my_off,
                          indices + row * indices_row_stride, cand_all + row * kCandCap,
                          partials);
 }
@@ -760,27 +782,31 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     const int p8 = t & 7, sg = t >> 3;  // word p8 of segment sg
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-    // issued at once: the row bound, the coarse words of the row's segments (every segment
-    // below nseg lies in the workspace; those past the row's keys are masked below) and the
-    // other arguments
+    // issued at once: the row bound, the coarse words of the row's segments (every lane loads,
+    // at a segment clamped below nseg, in the workspace; those past the row's keys are masked
+    // at their use), with whole 16-key runs the row's keys up to its width (a row here is one
+    // chunk), and the other arguments. Unconditional loads masked at use keep the compiler's
+    // waits exact.
     const int64_t n = row_bound(row_ends, row, width);
     const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
-    uint4 cw = sg < nseg ? coarse[sg * (kCoarseBins / 8) + p8] : zero4;
+    const uint4 cl = coarse[(sg < nseg ? sg : nseg - 1) * (kCoarseBins / 8) + p8];
+    const float *x = logits + row * logits_row_stride;
+    constexpr int kChunk = kCollectPer * kSelectThreads;
+    float raw[kCollectPer];
+    if constexpr (VEC == 16) load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, width, width);
     asm volatile("" ::: "memory");
     hoist_args(fine_hist, indices, indices_row_stride);
     int32_t *out = indices + row * indices_row_stride;
     if (n <= k) {
         for (int i = t; i < k; i += kSelectThreads) out[i] = i < n ? i : -1;
-        keep_loaded(cw.x);
+        keep_loaded(cl.x);
+        if constexpr (VEC == 16) keep_loaded(__float_as_uint(raw[0]));
         return;
     }
-    const float *x = logits + row * logits_row_stride;
-    // the first chunk of keys, in flight while the threshold is found
-    constexpr int kChunk = kCollectPer * kSelectThreads;
-    float raw[kCollectPer];
-    load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, n);
+    // otherwise the first chunk of keys goes out here, in flight while the threshold is found
+    if constexpr (VEC != 16) load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, n, width);
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
-    if (sg >= row_segments) cw = zero4;
+    const uint4 cw = sg < row_segments ? cl : zero4;
     if (t == 0) {
         found_c = 0;  // kept only if the counts do not reach k (they always do)
         above_c = 0;
@@ -808,7 +834,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     const uint32_t B = 63u - found_c;
     // (b) the fine bins inside B and the fine bin f
     const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
-    const uint4 fw = fine_word(fine, sg, B, p8, cw, sg < row_segments);
+    const uint4 fw = fine_word(fine, sg, nseg, B, p8, cw);
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw, e));
@@ -837,7 +863,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     uint32_t base_above = 0, base_in = 0;
     for (int64_t cbase = 0; cbase < n; cbase += kChunk) {
         const int64_t first = cbase + (int64_t)t * kCollectPer;
-        if (cbase != 0) load_keys16<VEC>(raw, x, first, n);
+        if (cbase != 0) load_keys16<VEC>(raw, x, first, n, width);
         const Masks16 m = classify16(raw, n - first, bb);
         loads_done();
         const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
@@ -883,8 +909,15 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
     const TopkWorkspace ws = carve(workspace, rows, nseg);
     const dim3 grid((unsigned)(nseg * rows)), block(kTopkThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && logits_row_stride % 4 == 0;
+    // rows of whole 16-key runs (every scorer-made row: its width is a multiple of 64 keys)
+    const bool runs = vec && width >= kCollectPer && width % kCollectPer == 0;
     if (nseg <= kFusedSegments && width <= kRowTopkWidth) {
-        if (vec)
+        if (runs)
+            hipLaunchKernelGGL(topk_row_kernel<16>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
+                               stream, row_ends, ws.coarse, logits, logits_row_stride, width,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride);
+        else if (vec)
             hipLaunchKernelGGL(topk_row_kernel<4>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
                                stream, row_ends, ws.coarse, logits, logits_row_stride, width,
                                (int)nseg, (int)seg_len, k, ws.seghist, indices,
@@ -897,7 +930,12 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
         return hipGetLastError();
     }
     if (nseg <= kFusedSegments) {
-        if (vec)
+        if (runs)
+            hipLaunchKernelGGL(topk_threshold_collect_kernel<16>, grid, block, 0, stream, logits,
+                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
+                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
+                               indices_row_stride, ws.state, ws.cand);
+        else if (vec)
             hipLaunchKernelGGL(topk_threshold_collect_kernel<4>, grid, block, 0, stream, logits,
                                logits_row_stride, width, row_ends, ws.coarse, (int)rows,
                                (int)nseg, (int)seg_len, k, ws.seghist, indices,
@@ -915,7 +953,11 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
                        ws.coarse, ws.seghist, nseg, row_ends, width, k, indices,
                        indices_row_stride, seg_len, ws.state, ws.segoff);
-    if (vec)
+    if (runs)
+        hipLaunchKernelGGL(topk_collect_kernel<16>, grid, block, 0, stream, logits,
+                           logits_row_stride, width, seg_len, rows, row_ends, ws.state, nseg,
+                           ws.segoff, ws.cand, k, indices, indices_row_stride);
+    else if (vec)
         hipLaunchKernelGGL(topk_collect_kernel<4>, grid, block, 0, stream, logits,
                            logits_row_stride, width, seg_len, rows, row_ends, ws.state, nseg,
                            ws.segoff, ws.cand, k, indices, indices_row_stride);
