@@ -42,14 +42,37 @@ def common_flags() -> list[str]:
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
+def kernel_resources(remarks: str) -> dict[str, dict[str, str]]:
+    """Per-kernel resource lines of hipcc's kernel-resource-usage remarks."""
+    out: dict[str, dict[str, str]] = {}
+    name = None
+    for line in remarks.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        text = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+        key, _, val = text.partition(":")
+        if key == "Function Name":
+            name = val.strip()
+            out[name] = {}
+        elif name is not None:
+            out[name][key.strip()] = val.strip()
+    return out
+
+
 def _compile(src: str) -> str:
+    """Compile one source; a kernel that spills to scratch memory fails the build (scratch
+    setup slows every wave launch, and a spill in a hot loop costs a memory round trip)."""
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + common_flags() + ["-Rpass-analysis=kernel-resource-usage", "-c", src,
+                                        "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{proc.stderr}")
+    for kernel, res in kernel_resources(proc.stderr).items():
+        if res.get("ScratchSize [bytes/lane]", "0") != "0":
+            raise RuntimeError(f"{src}: kernel {kernel} uses scratch memory: {res}")
     return obj
 
 

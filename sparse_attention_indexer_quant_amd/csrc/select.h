@@ -109,6 +109,20 @@ __device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectS
     return threshold;
 }
 
+// Slots for the lanes of a wavefront whose `take` is set (among the active lanes), from the
+// counter `n`: one atomic per wavefront, then each lane's rank among the taken lanes.
+__device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t *n) {
+    const uint64_t mask = __ballot(take);
+    uint32_t base = 0;
+    if (mask) {
+        const int leader = __builtin_ctzll(mask);
+        if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(n, (uint32_t)__builtin_popcountll(mask));
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+    }
+    return base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Writes the low `pos_bits` bits (the position) of the r smallest composites to out[0..r),
 // in no particular order.
 template <typename Source>
@@ -119,10 +133,9 @@ __device__ void select_smallest(const Source &src, int r, int bits, int pos_bits
     __syncthreads();
     const uint64_t pos_mask = ((uint64_t)1 << pos_bits) - 1;
     src.for_each([&](uint64_t c) {
-        if (c <= threshold) {
-            const uint32_t slot = atomicAdd(&sh.n_out, 1u);
-            if (slot < (uint32_t)r) out[slot] = (int32_t)(c & pos_mask);
-        }
+        const bool take = c <= threshold;
+        const uint32_t slot = wave_slot(take, &sh.n_out);
+        if (take && slot < (uint32_t)r) out[slot] = (int32_t)(c & pos_mask);
     });
 }
 

@@ -397,6 +397,31 @@ __device__ __forceinline__ void load_keys16(float (&raw)[kCollectPer], const flo
     }
 }
 
+// (a & m) | (b & ~m) as one bitfield select. Written as the instruction itself: as plain
+// selects, the tree in pick16 is recognised as an indexed read of the register array, which
+// the compiler then places in scratch memory.
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+}
+
+// raw[j] for a per-lane j < 16: a tree of 15 bitfield selects on the bits of j.
+__device__ __forceinline__ float pick16(const float (&raw)[kCollectPer], uint32_t j) {
+    static_assert(kCollectPer == 16, "four levels");
+    uint32_t a[8], b[4], c[2];
+    const uint32_t m0 = 0u - (j & 1u), m1 = 0u - ((j >> 1) & 1u), m2 = 0u - ((j >> 2) & 1u),
+                   m3 = 0u - ((j >> 3) & 1u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        a[i] = bit_select(m0, __float_as_uint(raw[2 * i + 1]), __float_as_uint(raw[2 * i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = bit_select(m1, a[2 * i + 1], a[2 * i]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c[i] = bit_select(m2, b[2 * i + 1], b[2 * i]);
+    return __uint_as_float(bit_select(m3, c[1], c[0]));
+}
+
 // The float of an order key (the inverse of order_key on keys of non-NaN floats; +0 for the
 // key of zero).
 __device__ __forceinline__ float key_float(uint32_t k) {
@@ -472,15 +497,12 @@ __device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const
         // the keys' last use comes before any store: a use of a loaded register after a store
         // makes the compiler wait for every store in flight as well (the counter it waits on
         // counts both)
-        if (m.in) {
-            uint32_t pc = base_in + ((incl - mine) >> 16);
-#pragma unroll
-            for (int j = 0; j < kCollectPer; ++j) {
-                if (!((m.in >> j) & 1u)) continue;
-                if (pc < (uint32_t)kCandCap)
-                    cand[pc] = make_uint2(order_key(raw[j]), (uint32_t)(first + j));
-                ++pc;
-            }
+        // one step per key inside the bin (few per lane), not one per key of the lane
+        uint32_t pc = base_in + ((incl - mine) >> 16);
+        for (uint32_t in = m.in; in; in &= in - 1u, ++pc) {
+            const uint32_t j = __builtin_ctz(in);
+            if (pc < (uint32_t)kCandCap)
+                cand[pc] = make_uint2(order_key(pick16(raw, j)), (uint32_t)(first + j));
         }
         write_above(m.above, first, base_above + ((incl - mine) & 0xFFFF), above, out);
         // the chunk's totals are the sum of the wave totals the scan left in `partials`
@@ -562,13 +584,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     // (Loads are issued in every lane, at segments clamped below nseg, and masked at their
     // use: conditional loads, or registers of loads in flight written over, make the compiler
     // wait for every load in flight, the segment's keys included.)
-    const int64_t n = row_bound(row_ends, row, width);
     const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
     const int sa = s0 < nseg ? s0 : nseg - 1, sb = s0 + 32 < nseg ? s0 + 32 : nseg - 1;
     const uint4 cl0 = coarse[sa * (kCoarseBins / 8) + p8];
     const uint4 cl1 = coarse[sb * (kCoarseBins / 8) + p8];
-    asm volatile("" ::: "memory");
+    const int32_t end = row_ends[row];
     hoist_args(fine_hist, indices, indices_row_stride, state, cand_all);
+    // nothing that needs the row bound moves above the loads: the coarse words leave in the
+    // bound's round trip instead of one round trip after it
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t n = end < 0 ? 0 : (end > width ? width : (int64_t)end);
     if (n <= k) {
         if (seg == 0) {
             int32_t *out = indices + row * indices_row_stride;
@@ -756,144 +781,198 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     }
 }
 
+// The lane of a wavefront holding the k-th largest of 64 descending counts (one per lane), the
+// count before it and its own count, as wavefront-uniform values. The counts reach k.
+struct Found64 {
+    int lane, before;
+    uint32_t count;
+};
+__device__ __forceinline__ Found64 find_in_64_wave(uint32_t c, int k) {
+    const int incl = wave_incl_scan((int)c);
+    const int before = incl - (int)c;
+    const uint64_t hit = __ballot(before < k && incl >= k);
+    const int L = hit ? __builtin_ctzll(hit) : 63;
+    return {L, __builtin_amdgcn_readlane(before, L), (uint32_t)__builtin_amdgcn_readlane((int)c, L)};
+}
+
+// The r smallest of m <= 64 distinct composites (`bits` significant bits), one per lane of a
+// wavefront in lanes [0, m): bit by bit from the top, the undecided composites whose bit is 0
+// are all taken if they fit in what is left of r, else the search continues among them.
+// Returns the mask of the taken lanes.
+__device__ __forceinline__ uint64_t wave_select_smallest(uint64_t c, int m, int r, int bits) {
+    const int lane = threadIdx.x & 63;
+    uint64_t active = __ballot(lane < m), taken = 0;
+    for (int b = bits - 1; b >= 0 && r > 0; --b) {
+        const uint64_t zeros = active & __ballot(((c >> b) & 1ull) == 0);
+        const int nz = __builtin_popcountll(zeros);
+        if (nz <= r) {
+            taken |= zeros;
+            r -= nz;
+            active &= ~zeros;
+        } else {
+            active = zeros;
+        }
+        if (__builtin_popcountll(active) == r) {
+            taken |= active;
+            r = 0;
+        }
+    }
+    return taken;
+}
+
 // Steps 2 to 4 in one workgroup per row, for rows of at most kRowTopkWidth keys and 64
-// segments: the threshold bin from the row's histograms (the same two levels and sums as
-// topk_threshold), then the row's keys once -- positions above the bin to the output, in
-// ascending order, (key, position) pairs inside it to LDS -- then the radix select of step 4 on
-// those candidates, all without leaving the workgroup: one launch instead of two. Measured, it
-// wins only while a row is one chunk of 8192 keys: classifying 32K-key rows on one compute
-// unit took longer than the two segmented launches (decode workload step 49 -> 57 us).
+// segments, with the whole row in the workgroup's registers (16 keys per lane). The threshold
+// bin in the two levels of topk_threshold: every wavefront sums the coarse counts of all the
+// row's segments itself (so none waits for another), and the fine counts inside the coarse bin
+// come from the row's own keys (LDS counts). Then the keys are classified once: positions above
+// the bin go to the output, in ascending order, and (key, position) pairs inside it to LDS,
+// placed by a workgroup prefix sum. The candidates are taken whole when they all fit, selected
+// by one wavefront when there are at most 64 of them (the usual case), and by the radix select
+// of step 4 otherwise. Four workgroup barriers in all. Measured, one workgroup per row wins
+// only while a row is one chunk of 8192 keys: classifying 32K-key rows on one compute unit
+// took longer than the two segmented launches (decode workload step 49 -> 57 us).
 constexpr int kRowTopkWidth = 8192;
-static_assert(kSelectThreads == 512 && kFusedSegments == 64, "lane t covers word t % 8 of segment t / 8");
+static_assert(kSelectThreads == 512 && kFusedSegments == 64, "lane l covers word l % 8 of segments l / 8 + 8 i");
+static_assert(kRowTopkWidth == kCollectPer * kSelectThreads, "a row is one chunk, all in registers");
+static_assert(kRowTopkWidth <= kCandCap, "every key of a row fits the LDS candidate list");
 
 template <int VEC>
 __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     const int32_t *__restrict__ row_ends, const uint16_t *__restrict__ coarse_hist,
     const float *__restrict__ logits, int64_t logits_row_stride, int64_t width, int nseg,
-    int seg_len, int k, const uint16_t *__restrict__ fine_hist, int32_t *__restrict__ indices,
-    int64_t indices_row_stride) {
+    int seg_len, int k, int32_t *__restrict__ indices, int64_t indices_row_stride) {
+    constexpr int kWaves = kSelectThreads / 64;
     __shared__ uint64_t cands[kCandCap];
     __shared__ SelectShared sh;
-    __shared__ uint32_t part[kSelectThreads / 64][64];
-    __shared__ uint32_t found_c, found_f, count_c, count_f;
-    __shared__ int above_c, above_f;
+    __shared__ uint32_t part[kWaves][64];
+    __shared__ uint32_t fine_count[64];
+    __shared__ int wave_total[kWaves];
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int p8 = t & 7, sg = t >> 3;  // word p8 of segment sg
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    const int p8 = lane & 7, s8 = lane >> 3;  // word p8 of segments s8 + 8 i
+    const int64_t first = (int64_t)t * kCollectPer;
 
-    // issued at once: the row bound, the coarse words of the row's segments (every lane loads,
-    // at a segment clamped below nseg, in the workspace; those past the row's keys are masked
-    // at their use), with whole 16-key runs the row's keys up to its width (a row here is one
-    // chunk), and the other arguments. Unconditional loads masked at use keep the compiler's
-    // waits exact.
-    const int64_t n = row_bound(row_ends, row, width);
+    // Issued at once: the coarse words of all the row's segments in every wavefront (segments
+    // clamped below nseg, in the workspace; those past the row's keys are masked at their use),
+    // with whole 16-key runs the row's keys up to its width, the row bound and the other
+    // arguments. Unconditional loads masked at use keep the compiler's waits exact; the
+    // scheduling barrier keeps everything that needs the bound below the loads, so they all
+    // leave in one round trip, and the first workgroup barrier (the fine counts' zeroing)
+    // passes while they are in flight.
     const uint4 *coarse = reinterpret_cast<const uint4 *>(coarse_hist + row * nseg * kCoarseBins);
-    const uint4 cl = coarse[(sg < nseg ? sg : nseg - 1) * (kCoarseBins / 8) + p8];
+    uint4 cl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int sg = s8 + 8 * i;
+        cl[i] = coarse[(sg < nseg ? sg : nseg - 1) * (kCoarseBins / 8) + p8];
+    }
     const float *x = logits + row * logits_row_stride;
-    constexpr int kChunk = kCollectPer * kSelectThreads;
     float raw[kCollectPer];
-    if constexpr (VEC == 16) load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, width, width);
-    asm volatile("" ::: "memory");
-    hoist_args(fine_hist, indices, indices_row_stride);
+    if constexpr (VEC == 16) load_keys16<VEC>(raw, x, first, width, width);
+    const int32_t end = row_ends[row];
+    hoist_args(indices, indices_row_stride);
+    if (t < 64) fine_count[t] = 0;
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // 1: fine_count is zero
+    const int64_t n = end < 0 ? 0 : (end > width ? width : (int64_t)end);
     int32_t *out = indices + row * indices_row_stride;
     if (n <= k) {
         for (int i = t; i < k; i += kSelectThreads) out[i] = i < n ? i : -1;
-        keep_loaded(cl.x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) keep_loaded(cl[i].x);
         if constexpr (VEC == 16) keep_loaded(__float_as_uint(raw[0]));
         return;
     }
-    // otherwise the first chunk of keys goes out here, in flight while the threshold is found
-    if constexpr (VEC != 16) load_keys16<VEC>(raw, x, (int64_t)t * kCollectPer, n, width);
+    if constexpr (VEC != 16) load_keys16<VEC>(raw, x, first, n, width);
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
-    const uint4 cw = sg < row_segments ? cl : zero4;
-    if (t == 0) {
-        found_c = 0;  // kept only if the counts do not reach k (they always do)
-        above_c = 0;
-        count_c = 0;
-        found_f = 0;
-        above_f = 0;
-        count_f = 0;
-    }
-    // (a) coarse totals and the coarse bin B holding the k-th largest key
+    // wavefronts past the row's keys skip the per-key steps (still at every barrier, as the
+    // radix select needs them), so that a short row costs its own wavefronts' issue time only
+    const bool has_keys = (int64_t)wave * (64 * kCollectPer) < n;
+
+    // (a) coarse totals, per wavefront: bins 8 p8 + e summed over the lane's segments and then
+    // over the lanes sharing p8, turned to one bin per lane (descending) through the
+    // wavefront's own LDS row, and the coarse bin B holding the k-th largest key
     uint32_t csum[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) csum[e] = sum_over_segments_in_wave(count8(cw, e));
+    for (int e = 0; e < 8; ++e) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += s8 + 8 * i < row_segments ? count8(cl[i], e) : 0u;
+        csum[e] = sum_over_segments_in_wave(v);
+    }
     if (lane < 8) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = csum[e];
     }
-    __syncthreads();
-    if (wave == 0) {  // lane l holds coarse bin 63 - l (descending)
-        uint32_t c = 0;
+    __builtin_amdgcn_wave_barrier();
+    const Found64 fc = find_in_64_wave(part[wave][63 - lane], k);
+    const uint32_t B = 63u - (uint32_t)fc.lane;  // ascending coarse bin
+
+    // (b) fine counts inside B from the keys in registers, then the fine bin f in every
+    // wavefront
+    if (has_keys) {
+        const int64_t live = n - first;
 #pragma unroll
-        for (int w = 0; w < kSelectThreads / 64; ++w) c += part[w][63 - lane];
-        find_in_64(c, k, &found_c, &above_c, &count_c);
+        for (int j = 0; j < kCollectPer; ++j) {
+            const uint32_t u = order_key(raw[j]);
+            if (j < live && (u >> (kBinShift + 6)) == B)
+                atomicAdd(&fine_count[(u >> kBinShift) & 63u], 1u);
+        }
     }
-    __syncthreads();
-    const uint32_t B = 63u - found_c;
-    // (b) the fine bins inside B and the fine bin f
-    const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
-    const uint4 fw = fine_word(fine, sg, nseg, B, p8, cw);
-    uint32_t fsum[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw, e));
-    __syncthreads();  // part[] is rewritten below
-    if (lane < 8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = fsum[e];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int w = 0; w < kSelectThreads / 64; ++w) c += part[w][63 - lane];
-        find_in_64(c, k - above_c, &found_f, &above_f, &count_f);
-    }
-    __syncthreads();
-    const uint32_t bin = B * 64 + (63u - found_f);
-    const int above = above_c + above_f;
-    const uint32_t ncand = count_f;
-    const bool keep = ncand <= (uint32_t)kCandCap;  // else step 4 reads the row again
+    __syncthreads();  // 2: the fine counts are complete
+    const Found64 ff = find_in_64_wave(fine_count[63 - lane], k - fc.before);
+    const uint32_t bin = B * 64 + (63u - (uint32_t)ff.lane);
+    const int above = fc.before + ff.before;
+    const int m = (int)ff.count;  // keys inside the bin
+    const int r = k - above;      // of which the r largest are taken (1 <= r <= m)
     int pos_bits = 1;
     while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
 
-    // (c) the row's keys once: lane counts and a workgroup prefix sum place every key
-    const BinBounds bb(bin);
-    uint32_t base_above = 0, base_in = 0;
-    for (int64_t cbase = 0; cbase < n; cbase += kChunk) {
-        const int64_t first = cbase + (int64_t)t * kCollectPer;
-        if (cbase != 0) load_keys16<VEC>(raw, x, first, n, width);
-        const Masks16 m = classify16(raw, n - first, bb);
-        loads_done();
-        const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
-        const int incl = scan_block<kSelectThreads>(mine, sh.partials);
-        // the keys' last use before any store (see collect_segment)
-        if (keep && m.in) {
-            uint32_t pc = base_in + ((incl - mine) >> 16);
+    // (c) the keys once: lane counts and a workgroup prefix sum place every key (the
+    // wavefronts past the keys have none and come after every wavefront that has some)
+    Masks16 mk{0u, 0u};
+    int mine = 0, incl = 0;
+    if (has_keys) {
+        mk = classify16(raw, n - first, BinBounds(bin));
+        mine = __builtin_popcount(mk.above) | (__builtin_popcount(mk.in) << 16);
+        incl = wave_incl_scan(mine);
+        if (lane == 63) wave_total[wave] = incl;
+    }
+    __syncthreads();  // 3: the wavefront totals
+    if (has_keys) {
+        int excl = incl - mine;
 #pragma unroll
-            for (int j = 0; j < kCollectPer; ++j) {
-                if (!((m.in >> j) & 1u)) continue;
-                if (pc < (uint32_t)kCandCap)
-                    cands[pc] = composite(order_key(raw[j]), (uint32_t)(first + j), pos_bits);
-                ++pc;
+        for (int w = 0; w < kWaves; ++w) excl += w < wave ? wave_total[w] : 0;
+        uint32_t pc = (uint32_t)excl >> 16;
+        if (r == m) {  // every key inside the bin is taken
+            for (uint32_t in = mk.in; in; in &= in - 1u, ++pc)
+                out[above + pc] = (int32_t)(first + __builtin_ctz(in));
+        } else {
+            for (uint32_t in = mk.in; in; in &= in - 1u, ++pc) {
+                const uint32_t j = __builtin_ctz(in);
+                cands[pc] = composite(order_key(pick16(raw, j)), (uint32_t)(first + j), pos_bits);
             }
         }
-        write_above(m.above, first, base_above + ((incl - mine) & 0xFFFF), (uint32_t)above, out);
-        int tot = 0;
-#pragma unroll
-        for (int w = 0; w < kSelectThreads / 64; ++w) tot += sh.partials[w];
-        base_above += (uint32_t)(tot & 0xFFFF);
-        base_in += (uint32_t)(tot >> 16);
-        __syncthreads();  // `partials` is written again; the candidates are complete in LDS
+        write_above(mk.above, first, (uint32_t)excl & 0xFFFFu, (uint32_t)above, out);
     }
-    // (d) the k - above smallest composites inside the bin
-    const int remaining = k - above;
+    if (r == m) return;
+    __syncthreads();  // 4: the candidates are in LDS
+
+    // (d) the r smallest composites inside the bin
     const int bits = 20 + pos_bits;
-    if (keep)
-        select_smallest(LdsCandidates{cands, (int)ncand}, remaining, bits, pos_bits, out + above, sh);
-    else
-        select_smallest(RowBin{x, n, bin, pos_bits}, remaining, bits, pos_bits, out + above, sh);
+    if (m <= 64) {
+        if (wave == 0) {
+            const uint64_t c = lane < m ? cands[lane] : ~(uint64_t)0;
+            const uint64_t taken = wave_select_smallest(c, m, r, bits);
+            if ((taken >> lane) & 1ull) {
+                const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(taken >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)taken, 0u));
+                out[above + slot] = (int32_t)(c & (((uint64_t)1 << pos_bits) - 1));
+            }
+        }
+    } else {
+        select_smallest(LdsCandidates{cands, m}, r, bits, pos_bits, out + above, sh);
+    }
 }
 
 size_t topk_workspace_bytes(int64_t rows, int64_t width, int) {
@@ -915,18 +994,15 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
         if (runs)
             hipLaunchKernelGGL(topk_row_kernel<16>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
                                stream, row_ends, ws.coarse, logits, logits_row_stride, width,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride);
+                               (int)nseg, (int)seg_len, k, indices, indices_row_stride);
         else if (vec)
             hipLaunchKernelGGL(topk_row_kernel<4>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
                                stream, row_ends, ws.coarse, logits, logits_row_stride, width,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride);
+                               (int)nseg, (int)seg_len, k, indices, indices_row_stride);
         else
             hipLaunchKernelGGL(topk_row_kernel<1>, dim3((unsigned)rows), dim3(kSelectThreads), 0,
                                stream, row_ends, ws.coarse, logits, logits_row_stride, width,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride);
+                               (int)nseg, (int)seg_len, k, indices, indices_row_stride);
         return hipGetLastError();
     }
     if (nseg <= kFusedSegments) {

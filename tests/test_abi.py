@@ -417,3 +417,20 @@ def test_binding_refuses_cpu_tensors():
         dsa.quantize_queries(torch.zeros((1, 32, 128), dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         dsa.topk(torch.zeros((1, 8)), torch.zeros(1, dtype=torch.int32), 2)
+
+
+def test_build_reads_kernel_resource_remarks():
+    # the build rejects kernels that spill to scratch; its parser of hipcc's remarks
+    from sparse_attention_indexer_quant_amd import build as b
+    text = "\n".join([
+        "a.hip:9:1: remark: Function Name: k1 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     VGPRs: 27 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark: Function Name: k2 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark:     ScratchSize [bytes/lane]: 64 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: warning: unrelated",
+    ])
+    res = b.kernel_resources(text)
+    assert res["k1"]["VGPRs"] == "27"
+    assert res["k1"]["ScratchSize [bytes/lane]"] == "0"
+    assert res["k2"]["ScratchSize [bytes/lane]"] == "64"
