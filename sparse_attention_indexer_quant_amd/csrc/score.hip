@@ -40,6 +40,7 @@
 #include "device_common.h"
 #include "key_norm.h"
 #include "launch.h"
+#include "select.h"
 #include "topk_layout.h"
 
 namespace dsaidx {
@@ -606,13 +607,76 @@ __device__ __forceinline__ int64_t finish_first_row(const FirstRowLoads &f, cons
     return __builtin_amdgcn_readfirstlane(acc);
 }
 
+// Value of request slot q (q < 256) of a per-lane array holding request 64 u + lane in a[u].
+__device__ __forceinline__ int request_value(const int (&a)[4], uint32_t q) {
+    const uint32_t u = q >> 6;
+    const int v = u == 0 ? a[0] : u == 1 ? a[1] : u == 2 ? a[2] : a[3];
+    return __builtin_amdgcn_readlane(v, (int)(q & 63u));
+}
+
+// Work item of workgroup b in a longest-first order, for launches whose requests have different
+// row counts (multi-row groups): request q holds nch[q] chunks of keys, each costing about its
+// row count lvl[q] (1..4) times its pages; items run by level, most rows first, then by chunk,
+// then by request (consecutive workgroups, on consecutive XCDs, take different requests). The
+// hardware starts workgroups in index order, so the heaviest items start first and the light
+// ones fill the machine at the end, instead of four-row chunks starting last and finishing
+// long after the rest. A workgroup past every item gets chunk == chunks (nothing to score).
+// Inputs per lane: request 64 u + lane in slot u (R <= 256 requests); output uniform.
+struct WorkItem {
+    uint32_t req, chunk;
+};
+__device__ __forceinline__ WorkItem longest_first_item(uint32_t b, const int (&lvl)[4],
+                                                       const int (&nch)[4], uint32_t chunks) {
+    auto add = [](int a, int c) { return a + c; };
+    int level = 0;
+    for (int L = 4; L >= 1 && level == 0; --L) {
+        int t = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t += lvl[u] == L ? nch[u] : 0;
+        t = xor_combine<1>(t, add);
+        t = xor_combine<2>(t, add);
+        t = xor_combine<4>(t, add);
+        t = xor_combine<8>(t, add);
+        t = xor_combine<16>(t, add);
+        t = xor_combine<32>(t, add);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readfirstlane(t);
+        if (b < tot) level = L;
+        else b -= tot;
+    }
+    if (level == 0) return {0u, chunks};
+    for (uint32_t c = 0; c < chunks; ++c) {
+        uint64_t m[4];
+        uint32_t n = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m[u] = __ballot(lvl[u] == level && (uint32_t)nch[u] > c);
+            n += (uint32_t)__builtin_popcountll(m[u]);
+        }
+        if (b < n) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t k = (uint32_t)__builtin_popcountll(m[u]);
+                if (b < k) {
+                    uint64_t mm = m[u];
+                    for (uint32_t i = 0; i < b; ++i) mm &= mm - 1;
+                    return {64u * u + (uint32_t)__builtin_ctzll(mm), c};
+                }
+                b -= k;
+            }
+        }
+        b -= n;
+    }
+    return {0u, chunks};
+}
+
 // a staged new key: MXFP4 64 payload + 4 scale bytes, FP8 128 code bytes + the scale word,
 // padded to 16
 template <int FMT>
 constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 
 // Grid: requests x chunks; a workgroup's chunk is 4 PW consecutive pages of the request, which
-// its 4 wavefronts take in turn (PW pages each). Each wavefront streams its pages through a
+// its 4 wavefronts take in turn (PW pages each). Workgroups map to (request, chunk) items
+// chunk-major, or, for multi-row groups, longest first (longest_first_item). Each wavefront streams its pages through a
 // ring of NB page buffers: the next NB - 1 pages' loads are in flight while one page is
 // scored. Every prefetch is issued unconditionally (a page that is not scored reads page 0
 // instead), so the loop carries the same loads across its back edge on every path and the
@@ -631,7 +695,11 @@ constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 // the wavefront that scores a page holding a
 // new key normalizes, quantizes and inserts that key and scores its own copy of it, and the
 // workgroups of chunk 0 write query_starts and row_ends.
-template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false>
+//
+// MULTI: a request may have more rows than one group (max_query_len > RG), so the pages are
+// streamed once per group. Without it the group loop runs once, which the compiler then knows:
+// nothing is carried from one group to the next, which took 20-40 registers per wavefront.
+template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false, bool MULTI = false>
 __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
     int64_t max_blocks, int64_t num_requests, int pages_per_wave,
@@ -640,8 +708,9 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
     int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
     uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin,
-    int64_t row_lo) {
+    int64_t row_lo, int order_work) {
     static_assert(!FUSED || HIST, "fused inputs: with histograms");
+    static_assert(!(FUSED && MULTI), "a fused launch has one row group");
     constexpr int kStagedKeyBytes = staged_key_bytes<FMT>();
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
@@ -664,15 +733,57 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     // turn, so every XCD gets an equal share of every request's work however the requests'
     // lengths differ, and a grid of one workgroup per compute unit still gives each XCD as many
     // workgroups as it has compute units.
+    //
+    // Multi-row groups of at most 256 requests and 64 chunks (order_work: not the row tiles of a
+    // tiled selection, whose grids are mostly requests outside the tile) instead take the longest-first
+    // order (longest_first_item) from the requests' row counts, loaded first: one more round
+    // trip before the table slice, against a shorter tail. The fused form also has each
+    // request's sequence length, so its chunks past the request's keys are not items at all;
+    // the plain form keeps every chunk of a request with rows (those past its keys leave at once).
     const uint32_t R = (uint32_t)num_requests;
-    const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(blockIdx.x / R);
-    const uint32_t rot = chunk32 % R;
-    uint32_t req32 = blockIdx.x - chunk32 * R + rot;
-    if (req32 >= R) req32 -= R;
+    const int PW = pages_per_wave;
+    const bool ordered = RG > 1 && order_work != 0 && R <= 256u && chunks <= 64;
+    int ord_q[4] = {0, 0, 0, 0}, ord_s[4] = {0, 0, 0, 0};  // FUSED: lengths of request 64 u + lane
+    uint32_t chunk32, req32;
+    if (ordered) {
+        int lvl[4], nch[4];
+        const int64_t span = (int64_t)kWaves * PW * kPageTokens;  // keys per chunk
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t qi = 64u * u + (uint32_t)lane;
+            const uint32_t qc = qi < R ? qi : R - 1;
+            if constexpr (FUSED) {
+                ord_q[u] = query_starts[qc];
+                ord_s[u] = fin.seq_lens[qc];
+            } else {  // query_starts holds the rows' prefix sums
+                ord_q[u] = query_starts[qc + 1] - query_starts[qc];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool live = 64u * u + (uint32_t)lane < R;
+            int rows_q = live ? ord_q[u] : 0;
+            rows_q = rows_q < 0 ? 0 : (rows_q > max_query_len ? max_query_len : rows_q);
+            int64_t c = chunks;
+            if constexpr (FUSED) {
+                const int64_t keys = live && ord_s[u] > 0 ? ord_s[u] : 0;
+                c = (keys + span - 1) / span;
+            }
+            lvl[u] = rows_q > 4 ? 4 : rows_q;
+            nch[u] = rows_q > 0 ? (int)(c < chunks ? c : chunks) : 0;
+        }
+        const WorkItem it = longest_first_item(blockIdx.x, lvl, nch, (uint32_t)chunks);
+        chunk32 = __builtin_amdgcn_readfirstlane(it.chunk);
+        req32 = __builtin_amdgcn_readfirstlane(it.req);
+    } else {
+        chunk32 = __builtin_amdgcn_readfirstlane(blockIdx.x / R);
+        const uint32_t rot = chunk32 % R;
+        req32 = blockIdx.x - chunk32 * R + rot;
+        if (req32 >= R) req32 -= R;
+    }
     const int64_t chunk = chunk32;
     const int64_t req = req32;
     const int64_t width = max_blocks * kPageTokens;
-    const int PW = pages_per_wave;
     // The workgroup's chunk is blocks [chunk_begin, chunk_begin + 4 PW); its wavefronts take
     // them in turn (wavefront w: blocks chunk_begin + w + 4 p), so a chunk that the request's
     // keys only partly fill still gives its four wavefronts equal work.
@@ -700,7 +811,14 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     // FUSED: `query_starts` holds the query lengths; the first round of the first-row sum's
     // loads goes out in the same round trip (after the query's, which arrive with them)
     FirstRowLoads first_row_loads;
-    if constexpr (FUSED) first_row_loads = issue_first_row(query_starts, num_requests, lane);
+    if constexpr (FUSED) {
+        if (ordered) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) first_row_loads.v[u] = ord_q[u];
+        } else {
+            first_row_loads = issue_first_row(query_starts, num_requests, lane);
+        }
+    }
 
     // Table entry of run page p (uniform), or -1 if it names no page of the cache.
     const uint32_t npages = num_pages < INT32_MAX ? (uint32_t)num_pages : (uint32_t)INT32_MAX;
@@ -742,16 +860,43 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     if constexpr (FUSED) {
         hoist_args(fin.key_in, fin.w_in, fin.proj_row_stride, fin.q_head_stride, fin.gamma,
                    fin.beta, fin.eps, fin.c_h, fin.query_starts, fin.row_ends);
-        // decode_layout's outputs, from the workgroups of chunk 0 (before any early exit)
-        if (chunk == 0 && wave == 0) {
-            if (req == 0 && lane == 0) fin.query_starts[0] = 0;
-            if (lane == 0) fin.query_starts[req + 1] = (int32_t)(r0 + qlen);
-            for (int64_t i = lane; r0 >= 0 && i < qlen && r0 + i < num_rows; i += 64) {
-                const int64_t e = (int64_t)seq - qlen + i + 1;
-                fin.row_ends[r0 + i] = (int32_t)(e < 0 ? 0 : e);
+        // decode_layout's outputs (before any early exit): request lq's, from the workgroups
+        // of its chunk 0, or in the longest-first order from workgroup lq (every request has a
+        // workgroup of that index: the grid holds chunks x R >= R of them)
+        int64_t lq = -1, lr0 = 0;
+        int lqlen = 0, lseq = 0;
+        if (!ordered) {
+            if (chunk == 0) {
+                lq = req;
+                lr0 = r0;
+                lqlen = qlen;
+                lseq = seq;
             }
-            if (req == (int64_t)R - 1) {  // rows from query_starts[R] on are graph padding
-                const int64_t total = r0 + qlen;
+        } else if (blockIdx.x < R) {
+            lq = blockIdx.x;
+            lqlen = request_value(ord_q, (uint32_t)lq);
+            lseq = request_value(ord_s, (uint32_t)lq);
+            int acc = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += 64 * u + lane < lq ? ord_q[u] : 0;
+            auto add = [](int a, int c) { return a + c; };
+            acc = xor_combine<1>(acc, add);
+            acc = xor_combine<2>(acc, add);
+            acc = xor_combine<4>(acc, add);
+            acc = xor_combine<8>(acc, add);
+            acc = xor_combine<16>(acc, add);
+            acc = xor_combine<32>(acc, add);
+            lr0 = __builtin_amdgcn_readfirstlane(acc);
+        }
+        if (lq >= 0 && wave == 0) {
+            if (lq == 0 && lane == 0) fin.query_starts[0] = 0;
+            if (lane == 0) fin.query_starts[lq + 1] = (int32_t)(lr0 + lqlen);
+            for (int64_t i = lane; lr0 >= 0 && i < lqlen && lr0 + i < num_rows; i += 64) {
+                const int64_t e = (int64_t)lseq - lqlen + i + 1;
+                fin.row_ends[lr0 + i] = (int32_t)(e < 0 ? 0 : e);
+            }
+            if (lq == (int64_t)R - 1) {  // rows from query_starts[R] on are graph padding
+                const int64_t total = lr0 + lqlen;
                 for (int64_t row = (total > 0 ? total : 0) + lane; row < num_rows; row += 64)
                     fin.row_ends[row] = 0;
             }
@@ -769,7 +914,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     if (nrows <= 0) return;
 
     // Query operands of the first row group, in flight together with the row bounds.
-    const int ngroups = (nrows + RG - 1) / RG;
+    const int ngroups = MULTI ? (nrows + RG - 1) / RG : 1;  // nrows <= max_query_len <= RG otherwise
     // the fused operands of four-row MXFP4 groups and two-row FP8 groups (FP8 operands are
     // widened to BF16, twice the registers) stay in the LDS
     RowGroup<FMT, H, RG, FUSED && (RG == 4 || (is_fp8(FMT) && RG == 2))> rows;
@@ -991,7 +1136,7 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
     return g;
 }
 
-template <int FMT, int H, int RG, bool HIST, bool FUSED = false>
+template <int FMT, int H, int RG, bool HIST, bool FUSED = false, bool MULTI = false>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream,
                                   const FusedInputs &fin = FusedInputs{}) {
     const ScoreGeometry geo = score_geometry(a.geometry_requests > 0 ? a.geometry_requests
@@ -1002,13 +1147,13 @@ static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, h
     // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
     // take the registers a deeper ring would need)
     constexpr int NB = FMT == kFmtMxfp4 ? 3 : 2;
-    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST, FUSED>), grid, block, 0, stream,
+    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST, FUSED, MULTI>), grid, block, 0, stream,
                        a.block_table, a.query_starts, a.max_blocks, a.num_requests,
                        geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,
                        a.num_pages, geo.chunks, static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
-                       ws.coarse, fin, a.row_lo);
+                       ws.coarse, fin, a.row_lo, a.geometry_requests > 0 ? 0 : 1);
     return hipGetLastError();
 }
 
@@ -1017,10 +1162,12 @@ static hipError_t launch_score_h(const ScoreArgs &a, const TopkWorkspace &ws, hi
     if (a.max_query_len <= 1) return launch_score_rg<FMT, H, 1, HIST>(a, ws, stream);
     if constexpr (is_fp8(FMT)) {
         // FP8 queries occupy 4x the registers once widened to BF16: at most 2 rows per group
-        return launch_score_rg<FMT, H, 2, HIST>(a, ws, stream);
+        if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, HIST>(a, ws, stream);
+        return launch_score_rg<FMT, H, 2, HIST, false, true>(a, ws, stream);
     } else {
         if (a.max_query_len <= 2) return launch_score_rg<FMT, H, 2, HIST>(a, ws, stream);
-        return launch_score_rg<FMT, H, 4, HIST>(a, ws, stream);
+        if (a.max_query_len <= 4) return launch_score_rg<FMT, H, 4, HIST>(a, ws, stream);
+        return launch_score_rg<FMT, H, 4, HIST, false, true>(a, ws, stream);
     }
 }
 

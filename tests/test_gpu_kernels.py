@@ -637,6 +637,92 @@ def test_score_topk_rows_of_many_segments(name, k):
     assert_topk_sets(fidx.cpu().numpy(), want, range(wl.num_rows), f"{name} fused k={k}")
 
 
+# Rows of 8K-40K keys in at most 64 scoring segments (the selection's one-launch threshold and
+# collect, then the select) whose threshold bin is not the usual few hundred keys: a segment of
+# identical keys that align with the row's most weighted query head (a tie of 1024+ keys at the
+# top, all in one segment), rows whose query is zero (every logit +0: one bin of every key, more
+# than the candidate list holds, selected from the row itself), next to random rows, for decode,
+# uneven and verify-shaped batches, FP8 and merged 64-head pages.
+ADVERSARIAL_CASES = {
+    "fp4_decode_32seg": dict(fmt="mxfp4", heads=32, seq_lens=[32768] * 8, query_lens=[1] * 8),
+    "fp4_uneven_rows": dict(fmt="mxfp4", heads=32, seq_lens=[30000, 9000, 20000, 12000, 9100, 15000],
+                            query_lens=[2, 0, 1, 3, 0, 0]),
+    "fp8_decode": dict(fmt="fp8", heads=32, seq_lens=[20000, 17000, 9000, 20000, 3000, 15000],
+                       query_lens=[1] * 6, outlier_frac=0.01, outlier_gain=20.0),
+    "fp4_h64_merged": dict(fmt="mxfp4", heads=64, seq_lens=[40000, 23000, 8300, 40000],
+                           query_lens=[1, 1, 1, 1], page_stride=8192, section_offset=3840),
+    "fp4_verify_ragged": dict(fmt="mxfp4", heads=32, seq_lens=[30000, 9000, 4200, 20000, 12000, 65, 9100],
+                              query_lens=[4, 1, 3, 2, 4, 1, 2], num_rows=20),
+}
+
+
+def _hot_segment(wl, req, lo, hi):
+    """Keys [lo, hi) of request `req` made equal to its first row's most weighted query head
+    (pre-norm), so that they tie near the top of that row."""
+    r0 = int(np.sum(wl.query_lens[:req]))
+    h = int(np.argmax(bf16_to_f32(wl.wv_bits[r0])))
+    off = int(wl.key_offsets[req])
+    wl.key_bits[off + lo:off + hi] = wl.q_bits[r0, h]
+
+
+@pytest.mark.parametrize("name", list(ADVERSARIAL_CASES))
+@pytest.mark.parametrize("variant", ["random", "hot_segment", "zero_query"])
+@pytest.mark.parametrize("k", [1, 64, 2048, 6000])
+def test_score_topk_adversarial_rows(name, variant, k):
+    # score_topk and index_score_topk: logits bit for bit equal to score_paged's and close to the
+    # oracle's, index sets equal to the oracle's top-k of the same logits, on a workspace of
+    # arbitrary bytes
+    kw = ADVERSARIAL_CASES[name]
+    wl = make_workload(name, topk=k, seed=31, extra_pages=1, **kw)
+    seg = dsa.score_segment_keys(wl.num_requests, wl.max_blocks)
+    assert wl.width > 8192 and -(-wl.width // seg) <= 64, "not the one-launch threshold and collect"
+    if variant == "hot_segment":
+        for q in range(wl.num_requests):
+            n = int(wl.seq_lens[q])
+            if n > 3 * seg and wl.query_lens[q] > 0:
+                _hot_segment(wl, q, seg, seg + max(1024, seg))
+    elif variant == "zero_query":
+        wl.q_bits[::2] = 0
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, ends = dw.layout()
+    oe = ends.cpu().numpy()
+    plain = dw.score(q_rows, w, starts, ends)
+    ws = torch.full((dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows),),
+                    0x3C, dtype=torch.uint8, device="cuda")
+    la = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, idx = dsa.score_topk(q_rows, wl.heads, w, dw.cache, wl.num_pages, wl.page_stride,
+                            dw.block_table, starts, ends, wl.max_query_len, k, wl.fmt,
+                            wl.section_offset, out=la, workspace=ws)
+    cols = torch.arange(wl.width, device="cuda")
+    valid = cols[None, :] < ends.to(torch.int64)[:, None]
+    assert torch.equal(la.view(torch.int32)[valid], plain.view(torch.int32)[valid]), f"{name}: logits"
+    got = la.cpu().numpy()
+    if k == 64:  # the logits do not depend on k: compared with the oracle's once per workload
+        oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+        os_, _ = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+        ref = oracle.score_paged(oq, wl.heads, ow, oracle_cache(wl), wl.num_pages, wl.page_stride,
+                                 wl.block_table, os_, oe, wl.fmt, wl.section_offset)
+        assert_logits_close(got, ref, oe, range(wl.num_rows), name)
+    want = oracle.topk(np.nan_to_num(got, nan=0.0), oe, k)
+    what = f"{name} {variant} k={k}"
+    assert_topk_sets(idx.cpu().numpy(), want, range(wl.num_rows), what)
+    # the fused step from a cache without the step keys, on the same (reused) workspace
+    rng = np.random.default_rng(12)
+    proj, _ = _step_projection(wl, 0, 128, 128 + wl.heads, rng)
+    b = _cache_without_step_keys(wl)
+    lb = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    _, fe, _, fidx = dsa.index_score_topk(
+        bf16_dev(proj), 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens,
+        wl.num_rows, b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, k,
+        wl.fmt, wl.section_offset, out=lb, workspace=ws)
+    assert torch.equal(b.cache, dw.cache), f"{what}: fused cache bytes"
+    assert torch.equal(fe, ends)
+    assert torch.equal(lb.view(torch.int32)[valid], plain.view(torch.int32)[valid]), f"{what}: fused logits"
+    assert_topk_sets(fidx.cpu().numpy(), want, range(wl.num_rows), f"{what} fused")
+
+
 def test_index_score_degenerate_sizes():
     # no pages or no blocks: only the row layout is written; more than 4 rows per request
     # (MXFP4) or 2 (FP8) are refused
