@@ -261,6 +261,12 @@ class Setup:
         self.inputs_layout, self.index_score = [], []
         # the step's inputs made inside the scorer: at most 4 rows per request (MXFP4), 2 (FP8)
         self.inline_ok = wl.max_query_len <= (4 if wl.fmt == "mxfp4" else 2)
+        # ... and the step timed as the workload's step where every request has one row. With
+        # several rows per request every scoring workgroup of a request would read and quantize
+        # the request's BF16 query rows again (on the verify workload about 21 MB more reads per
+        # step than its 26 MB of quantized rows); the separate input launch measured faster
+        # there (117.3 against 112.7 us per step), and the fused step is reported beside it.
+        self.inline_step = self.inline_ok and wl.max_query_len <= 1
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(
@@ -643,10 +649,13 @@ def run_config(name, args, steps, warmup, cpu_budget):
     wall_u, score_ms_u = time_steps(s, steps, warmup, mode="unfused")
     wall_f, score_ms_f = time_steps(s, steps, warmup, mode="fused")
     wall_t, tiled_ms = time_steps(s, steps, warmup, mode="tiled")
-    # the step the library offers for this workload: the inputs made inside the scorer where
-    # that path applies (MXFP4, at most 4 rows per request), else the separate input launch
+    # the step for this workload: the inputs made inside the scorer where every request has one
+    # row, else the separate input launch (the fused form is timed as well where it applies)
+    wall_i = score_ms_i = None
     if s.inline_ok:
-        wall, score_ms = time_steps(s, steps, warmup, mode="inline")
+        wall_i, score_ms_i = time_steps(s, steps, warmup, mode="inline")
+    if s.inline_step:
+        wall, score_ms = wall_i, score_ms_i
         kernel, kbytes = "index_score_hist", s.inline_bytes
     else:
         wall, score_ms = wall_f, score_ms_f
@@ -672,8 +681,10 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "score_algorithmic_bytes": kbytes,
         "score_histogram_bytes": s.hist_bytes,
         "score_kernel": kernel,
-        "step": "index_score_hist + topk_scored" if s.inline_ok else
+        "step": "index_score_hist + topk_scored" if s.inline_step else
                 "index_inputs_layout + score_paged_hist + topk_scored",
+        "ms_per_step_fused_inputs": wall_i / steps * 1e3 if wall_i is not None else None,
+        "index_score_hist_us_mean": float(score_ms_i.mean() * 1e3) if score_ms_i is not None else None,
         "ms_per_step_separate_inputs": wall_f / steps * 1e3,
         "score_paged_hist_us_mean": score_us_f,
         "score_paged_hist_algorithmic_GBps": s.score_hist_bytes / (score_us_f / 1e6) / 1e9,
