@@ -41,7 +41,7 @@ MAIN_CONFIG = "long_mxfp4"
 # counters count only while those are unchanged)
 PROFILE_PMC = os.path.join(ROOT, "profiles", "{kernel}_{workload}_pmc.txt")
 SCORE_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_quant_amd", "csrc", f)
-                 for f in ("score.hip", "device_common.h", "key_norm.h")]
+                 for f in ("score.hip", "device_common.h", "key_norm.h", "select.h", "topk_layout.h")]
 
 
 def parse():
