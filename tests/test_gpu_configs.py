@@ -3,9 +3,9 @@ the whole cache, every quantized query byte and every row bound bit-exact; the l
 every row within 1e-5 * max |logit| of the oracle; top-k sets equal on identical (oracle)
 logits; end-to-end top-k differing only by boundary swaps that the measured logit error
 explains; and
-the step bench.py times (the inputs made inside the scorer where that path applies), run
-from a cache without the step's keys, giving the same cache bytes, row layout and logits
-bit for bit, and the oracle's top-k sets of those logits."""
+both step forms bench.py times (the inputs made inside the scorer where that path applies,
+and the separate input launch), run from a cache without the step's keys, giving the same
+cache bytes, row layout and logits bit for bit, and the oracle's top-k sets of those logits."""
 import gc
 import sys
 
@@ -113,9 +113,11 @@ def test_topk_end_to_end_boundary_swaps_only(run):
 
 
 def test_bench_step_path(run):
-    # At most 4 rows per request (MXFP4) or 2 (FP8): index_score_hist + topk_scored; otherwise
-    # index_inputs_layout + score_paged_hist + topk_scored. Packed projection rows
-    # [key 128 | head weights H] per query row, as bench.py builds them.
+    # The step bench.py times, and the other step form where it applies: index_score_hist +
+    # topk_scored (at most 4 rows per request for MXFP4, 2 for FP8; the bench's step where every
+    # request has one row) and index_inputs_layout + score_paged_hist + topk_scored (the bench's
+    # step for multi-row batches), each from a cache without the step's keys. Packed projection
+    # rows [key 128 | head weights H] per query row, as bench.py builds them.
     wl = run["wl"]
     sk = wl.step_key_index()
     proj = np.zeros((wl.num_rows, 128 + wl.heads), np.uint16)
@@ -125,38 +127,43 @@ def test_bench_step_path(run):
     slots[:sk.size] = wl.key_slots[sk]
     keep = np.ones(wl.total_keys, bool)
     keep[sk] = False
-    b = DeviceWorkload(wl)
-    chunk = 1 << 21
     rest = np.flatnonzero(keep)
-    for s in range(0, rest.size, chunk):
-        part = rest[s:s + chunk]
-        dsa.store_keys(bf16_dev(wl.key_bits[part]), b.gamma, b.beta, wl.eps, dev(wl.key_slots[part]),
-                       b.cache, wl.num_pages, wl.page_stride, wl.fmt, wl.section_offset)
     pd = bf16_dev(proj)
-    inline = wl.max_query_len <= (4 if wl.fmt == "mxfp4" else 2)
-    if inline:
-        starts, ends, logits, idx = dsa.index_score_topk(
-            pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens, wl.num_rows,
-            b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, wl.topk,
-            wl.fmt, wl.section_offset)
-    else:
-        q_rows, w, starts, ends = dsa.index_inputs_layout(
-            pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, dev(slots), b.cache, wl.num_pages,
-            wl.page_stride, b.seq_lens, b.query_lens, wl.num_rows, wl.fmt, wl.section_offset)
-        logits, idx = dsa.score_topk(q_rows, wl.heads, w, b.cache, wl.num_pages, wl.page_stride,
-                                     b.block_table, starts, ends, wl.max_query_len, wl.topk,
-                                     wl.fmt, wl.section_offset)
-    torch.cuda.synchronize()
-    print(f"[config {run['name']}] bench step path ({'inline inputs' if inline else 'separate inputs'})",
-          flush=True)
-    assert torch.equal(b.cache, run["dw"].cache), f"{run['name']}: cache bytes"
-    assert np.array_equal(starts.cpu().numpy(), run["os"]) and np.array_equal(ends.cpu().numpy(), run["oe"])
-    cols = torch.arange(wl.width, device=logits.device)
-    valid = cols[None, :] < ends.to(torch.int64)[:, None]
-    assert torch.equal(logits.view(torch.int32)[valid], run["logits"].view(torch.int32)[valid]), \
-        f"{run['name']}: logits bits"
     rows = run["rows"]
-    lg = np.nan_to_num(logits[rows].cpu().numpy(), nan=0.0)
-    want = oracle.topk(lg, run["oe"][rows].astype(np.int32), wl.topk)
-    assert_topk_sets(idx[rows].cpu().numpy(), want, range(len(rows)), run["name"])
-    del b, logits, idx, valid
+    forms = ["separate inputs"]
+    if wl.max_query_len <= (4 if wl.fmt == "mxfp4" else 2):
+        forms.append("inline inputs")
+    for form in forms:
+        b = DeviceWorkload(wl)
+        chunk = 1 << 21
+        for s in range(0, rest.size, chunk):
+            part = rest[s:s + chunk]
+            dsa.store_keys(bf16_dev(wl.key_bits[part]), b.gamma, b.beta, wl.eps,
+                           dev(wl.key_slots[part]), b.cache, wl.num_pages, wl.page_stride, wl.fmt,
+                           wl.section_offset)
+        if form == "inline inputs":
+            starts, ends, logits, idx = dsa.index_score_topk(
+                pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens, wl.num_rows,
+                b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, wl.topk,
+                wl.fmt, wl.section_offset)
+        else:
+            q_rows, w, starts, ends = dsa.index_inputs_layout(
+                pd, 0, 128, b.q, b.gamma, b.beta, wl.eps, dev(slots), b.cache, wl.num_pages,
+                wl.page_stride, b.seq_lens, b.query_lens, wl.num_rows, wl.fmt, wl.section_offset)
+            logits, idx = dsa.score_topk(q_rows, wl.heads, w, b.cache, wl.num_pages,
+                                         wl.page_stride, b.block_table, starts, ends,
+                                         wl.max_query_len, wl.topk, wl.fmt, wl.section_offset)
+        torch.cuda.synchronize()
+        what = f"{run['name']} ({form})"
+        print(f"[config {what}] step form", flush=True)
+        assert torch.equal(b.cache, run["dw"].cache), f"{what}: cache bytes"
+        assert np.array_equal(starts.cpu().numpy(), run["os"]) and \
+            np.array_equal(ends.cpu().numpy(), run["oe"]), f"{what}: row layout"
+        cols = torch.arange(wl.width, device=logits.device)
+        valid = cols[None, :] < ends.to(torch.int64)[:, None]
+        assert torch.equal(logits.view(torch.int32)[valid], run["logits"].view(torch.int32)[valid]), \
+            f"{what}: logits bits"
+        lg = np.nan_to_num(logits[rows].cpu().numpy(), nan=0.0)
+        want = oracle.topk(lg, run["oe"][rows].astype(np.int32), wl.topk)
+        assert_topk_sets(idx[rows].cpu().numpy(), want, range(len(rows)), what)
+        del b, logits, idx, valid
