@@ -3,10 +3,10 @@
 One step = one pass of the whole path over one decode batch, inputs resident in HBM: every
 row's query quantized with its head weights, the step's new keys normalized, quantized and
 inserted, the decode_layout row bounds, scoring that also writes the top-k segment
-histograms, and topk_scored. With at most 4 rows per request (MXFP4) or 2 (FP8) the first
-four are one launch (index_score_hist); otherwise index_inputs_layout + score_paged_hist. The
-separate-input form and the form with score_paged + topk are timed too (per_config
-..._separate_inputs, ..._unfused). Prints ONE JSON line: scored (row, key) pairs per second of
+histograms, and topk_scored. With one row per request the first four are one launch
+(index_score_hist), and where every row's keys also lie in one scoring workgroup the whole
+step is (index_score_topk); otherwise index_inputs_layout + score_paged_hist. The other forms
+are timed too (per_config ..._fused_inputs, ..._separate_inputs, ..._unfused, ..._tiled). Prints ONE JSON line: scored (row, key) pairs per second of
 the whole step, plus the scoring kernel's key-cache GB/s and its roofline fraction (HIP events
 on the launch stream around the scoring launch of sampled timed steps, created without the
 system-scope cache fence a default event's record adds), and the CPU oracle timed on a
@@ -267,6 +267,10 @@ class Setup:
         # step than its 26 MB of quantized rows); the separate input launch measured faster
         # there (117.3 against 112.7 us per step), and the fused step is reported beside it.
         self.inline_step = self.inline_ok and wl.max_query_len <= 1
+        # ... in one launch with the selection (index_score_topk) where each row's keys lie in
+        # one scoring workgroup
+        self.one_launch = self.inline_step and hist_segment_keys(wl) >= wl.width
+        self.index_topk = []
         for c in self.caches:
             base = c.data_ptr() + wl.section_offset
             self.inputs.append(Prepared(
@@ -306,6 +310,17 @@ class Setup:
                     base, wl.num_pages, wl.page_stride, self.block_table.data_ptr(),
                     wl.max_blocks, self.starts.data_ptr(), self.ends.data_ptr(),
                     self.logits.data_ptr(), self.logits.stride(0), self.hws.data_ptr(), hwsb, sp))
+            if self.one_launch:
+                self.index_topk.append(Prepared(
+                    lib.dsaidx_index_score_topk, fmt, self.projected.data_ptr(),
+                    self.projected.stride(0), 0, 128, self.q.data_ptr(), wl.heads,
+                    self.q.stride(0), self.q.stride(1), self.gamma.data_ptr(),
+                    self.beta.data_ptr(), ctypes.c_float(wl.eps), self.seq_lens.data_ptr(),
+                    self.query_lens.data_ptr(), wl.num_requests, wl.num_rows, wl.max_query_len,
+                    base, wl.num_pages, wl.page_stride, self.block_table.data_ptr(),
+                    wl.max_blocks, self.starts.data_ptr(), self.ends.data_ptr(),
+                    self.logits.data_ptr(), self.logits.stride(0), wl.topk, self.idx.data_ptr(),
+                    self.idx.stride(0), self.hws.data_ptr(), hwsb, sp))
             self.tiled.append(Prepared(
                 lib.dsaidx_score_topk_tiled, fmt, self.q_rows.data_ptr(), self.q_rows.stride(0),
                 wl.heads, self.w_out.data_ptr(), self.w_out.stride(0), base, wl.num_pages,
@@ -349,6 +364,9 @@ class Setup:
                              + wl.num_rows * (wl.heads * 256 + 2 * wl.heads + 256)
                              + live * (wl.section_bytes // 64)
                              + 4 * wl.num_rows + 4 * (wl.num_requests + 1) + 8 * wl.num_requests)
+        # index_score_topk writes the row's positions instead of the histograms (it reads its
+        # own logits back within the launch: on-chip traffic, not counted)
+        self.one_launch_bytes = self.inline_bytes - self.hist_bytes + 4 * wl.topk * wl.num_rows
 
     def prologue(self, i):
         """index_inputs and decode_layout in one launch (index_inputs_layout). (Running
@@ -375,6 +393,15 @@ class Setup:
         if ev is not None:
             ev[1].record(self.stream)
         self.topk_scored()
+
+    def step_one_launch(self, i, ev=None):
+        """index_score_topk: the step's inputs, layout, logits and every row's top-k in one
+        scoring launch (timed)."""
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.index_topk[i % len(self.caches)]()
+        if ev is not None:
+            ev[1].record(self.stream)
 
     def step_tiled(self, i, ev=None):
         """index_inputs, decode_layout, then score_topk_tiled (scoring + selection per tile of
@@ -415,7 +442,7 @@ def time_steps(s: Setup, steps: int, warmup: int, mode: str = "fused"):
     samples to MIN_SAMPLES)."""
     import torch
     step = {"inline": s.step_inline, "fused": s.step, "unfused": s.step_unfused,
-            "tiled": s.step_tiled}[mode]
+            "tiled": s.step_tiled, "one_launch": s.step_one_launch}[mode]
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -451,6 +478,8 @@ def kernel_times(s: Setup, reps: int = 30, score_reps: int = 100):
               ("topk_scored", lambda i: s.topk_scored())]
     if s.inline_ok:
         stages.append(("index_score_hist", lambda i: s.index_score[i % len(s.caches)]()))
+    if s.one_launch:
+        stages.append(("index_score_topk", lambda i: s.index_topk[i % len(s.caches)]()))
     for name, fn in stages:
         # launched back to back, each between its own pair of events, read after the last
         n = score_reps if name.startswith(("score", "index_score")) else reps
@@ -650,11 +679,18 @@ def run_config(name, args, steps, warmup, cpu_budget):
     wall_f, score_ms_f = time_steps(s, steps, warmup, mode="fused")
     wall_t, tiled_ms = time_steps(s, steps, warmup, mode="tiled")
     # the step for this workload: the inputs made inside the scorer where every request has one
-    # row, else the separate input launch (the fused form is timed as well where it applies)
-    wall_i = score_ms_i = None
+    # row (with the selection in the same launch where every row's keys lie in one scoring
+    # workgroup), else the separate input launch (the fused forms are timed as well where they
+    # apply)
+    wall_i = score_ms_i = wall_o = score_ms_o = None
     if s.inline_ok:
         wall_i, score_ms_i = time_steps(s, steps, warmup, mode="inline")
-    if s.inline_step:
+    if s.one_launch:
+        wall_o, score_ms_o = time_steps(s, steps, warmup, mode="one_launch")
+    if s.one_launch:
+        wall, score_ms = wall_o, score_ms_o
+        kernel, kbytes = "index_score_topk", s.one_launch_bytes
+    elif s.inline_step:
         wall, score_ms = wall_i, score_ms_i
         kernel, kbytes = "index_score_hist", s.inline_bytes
     else:
@@ -681,8 +717,10 @@ def run_config(name, args, steps, warmup, cpu_budget):
         "score_algorithmic_bytes": kbytes,
         "score_histogram_bytes": s.hist_bytes,
         "score_kernel": kernel,
-        "step": "index_score_hist + topk_scored" if s.inline_step else
+        "step": "index_score_topk (one launch)" if s.one_launch else
+                "index_score_hist + topk_scored" if s.inline_step else
                 "index_inputs_layout + score_paged_hist + topk_scored",
+        "ms_per_step_one_launch": wall_o / steps * 1e3 if wall_o is not None else None,
         "ms_per_step_fused_inputs": wall_i / steps * 1e3 if wall_i is not None else None,
         "index_score_hist_us_mean": float(score_ms_i.mean() * 1e3) if score_ms_i is not None else None,
         "ms_per_step_separate_inputs": wall_f / steps * 1e3,

@@ -389,6 +389,30 @@ dsaidx_status dsaidx_index_score_hist(
     size_t workspace_bytes, void *stream);
 
 /*
+ * index_score_topk -- one step of the indexer path with its selection: dsaidx_index_score_hist
+ * followed by dsaidx_topk_scored ([idx] DsaIndex; [fp4ops] decode_layout, score_paged; [ovl]
+ * module text: scoring and then top-k), with the same results (row layout, cache bytes and
+ * logits bit for bit, the same index sets). Where every request has one row (max_query_len 1)
+ * and every row's keys lie in one scoring workgroup (dsaidx_score_segment_keys(num_requests,
+ * max_blocks) >= max_blocks * 64: short rows, or many requests), it is one launch: each
+ * workgroup selects its row's top-k from its own histogram and logits, and the workspace is
+ * not touched. Otherwise it is the two calls, two or three launches on `stream`.
+ *  All arguments of dsaidx_index_score_hist, and
+ *  k, indices, indices_row_stride  as dsaidx_topk: every row's selection (graph padding rows
+ *           and rows without keys select none: -1), width max_blocks * 64.
+ *  Errors: as the two calls; k < 1 gives DSAIDX_EINVAL. With num_rows, num_requests,
+ *  max_blocks or num_pages == 0 only the row layout is written (as dsaidx_index_score_hist).
+ */
+dsaidx_status dsaidx_index_score_topk(
+    int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+    const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
+    const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
+    int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
+    int32_t *row_ends, float *logits, int64_t logits_row_stride, int32_t k, int32_t *indices,
+    int64_t indices_row_stride, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * topk_scored -- the per-row top-k of logits that dsaidx_score_paged_hist has just written,
  * using its histograms. Rows, bounds and output as dsaidx_topk with width = max_blocks * 64.
  *  num_requests, max_blocks, workspace  exactly as passed to the dsaidx_score_paged_hist call

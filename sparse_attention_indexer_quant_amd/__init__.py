@@ -77,6 +77,9 @@ def library():
             "dsaidx_index_score_hist": (I32, [I32, P, I64, I64, I64, P, I32, I64, I64, P, P, F32,
                                               P, P, I64, I64, I32, P, I64, I64, P, I64, P, P, P,
                                               I64, P, SZ, P]),
+            "dsaidx_index_score_topk": (I32, [I32, P, I64, I64, I64, P, I32, I64, I64, P, P, F32,
+                                              P, P, I64, I64, I32, P, I64, I64, P, I64, P, P, P,
+                                              I64, I32, P, I64, P, SZ, P]),
             "dsaidx_topk_scored": (I32, [P, I64, I64, P, I32, P, I64, I64, I64, P, SZ, P]),
             "dsaidx_topk": (I32, [P, I64, I64, I64, P, I32, P, I64, P, SZ, P]),
             "dsaidx_topk_noalloc": (I32, [P, I64, I64, I64, P, I32, P, I64, P]),
@@ -442,9 +445,11 @@ def score_topk_tiled(q_rows, heads, weights, cache, num_pages, page_stride, bloc
 def index_score_topk(projected, key_col, weight_col, q, gamma, beta, eps, seq_lens, query_lens,
                      num_rows, cache, num_pages, page_stride, block_table, max_query_len, k,
                      fmt="mxfp4", section_offset=0, out=None, indices=None, workspace=None):
-    """One step in two launches: the step's inputs made inside the scorer (index_score_hist:
-    query quantization, key insert at the block table's positions, row layout, logits and
-    histograms), then topk_scored. Returns (query_starts, row_ends, logits, indices)."""
+    """One step with its selection (dsaidx_index_score_topk): the step's inputs made inside the
+    scorer (query quantization, key insert at the block table's positions, row layout, logits),
+    then every row's top-k -- in the scoring launch itself where every request has one row that
+    one scoring workgroup covers, else on the scorer's histograms (topk_scored). Returns
+    (query_starts, row_ends, logits, indices)."""
     import torch
     _dev(projected, "projected", torch.bfloat16)
     _dev(q, "q", torch.bfloat16)
@@ -473,19 +478,15 @@ def index_score_topk(projected, key_col, weight_col, q, gamma, beta, eps, seq_le
         need = score_topk_workspace_bytes(R, mb, num_rows)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     lib = library()
-    st = lib.dsaidx_index_score_hist(
+    st = lib.dsaidx_index_score_topk(
         _fmt(fmt), projected.data_ptr(), projected.stride(0), int(key_col), int(weight_col),
         q.data_ptr(), q.shape[1], q.stride(0), q.stride(1), gamma.data_ptr(), beta.data_ptr(),
         float(eps), seq_lens.contiguous().data_ptr(), query_lens.contiguous().data_ptr(), R,
         num_rows, int(max_query_len), cache.data_ptr() + int(section_offset), int(num_pages),
         int(page_stride), block_table.data_ptr(), mb, starts.data_ptr(), ends.data_ptr(),
-        logits.data_ptr(), logits.stride(0), workspace.data_ptr(), workspace.numel(), _stream(q))
-    _check("index_score_hist", st)
-    if num_rows > 0 and R > 0 and mb > 0 and int(num_pages) > 0:
-        st = lib.dsaidx_topk_scored(logits.data_ptr(), num_rows, logits.stride(0), ends.data_ptr(),
-                                    int(k), indices.data_ptr(), indices.stride(0), R, mb,
-                                    workspace.data_ptr(), workspace.numel(), _stream(q))
-        _check("topk_scored", st)
+        logits.data_ptr(), logits.stride(0), int(k), indices.data_ptr(), indices.stride(0),
+        workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check("index_score_topk", st)
     return starts, ends, logits, indices
 
 

@@ -418,14 +418,16 @@ dsaidx_status dsaidx_score_topk_tiled(int fmt, const void *q, int64_t q_row_stri
                                                       workspace, as_stream(stream)));
 }
 
-dsaidx_status dsaidx_index_score_hist(
+// The checks of the step calls (index_score_hist, index_score_topk) and their launch arguments.
+// Returns DSAIDX_OK with `*layout_only` set where nothing is scored (the row layout alone).
+static dsaidx_status index_step_args(
     int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
     const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
     const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
     int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
     int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
     int32_t *row_ends, float *logits, int64_t logits_row_stride, void *workspace,
-    size_t workspace_bytes, void *stream) {
+    size_t workspace_bytes, bool *layout_only, dsaidx::ScoreArgs *args, dsaidx::FusedInputs *fin) {
     if (!valid_fmt(fmt) || num_rows < 0 || num_requests < 0 || max_blocks < 0 || num_pages < 0 ||
         key_col < 0 || weight_col < 0 || !std::isfinite(eps) || eps < 0.0f)
         return DSAIDX_EINVAL;
@@ -436,10 +438,8 @@ dsaidx_status dsaidx_index_score_hist(
                                     query_starts, row_ends);
     if (st != DSAIDX_OK) return st;
     // nothing to score and no key with a place in the cache: the row layout alone
-    if (num_rows == 0 || num_requests == 0 || max_blocks == 0 || num_pages == 0)
-        return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests,
-                                                       num_rows, 0, 1, 1, query_starts,
-                                                       row_ends, as_stream(stream)));
+    *layout_only = num_rows == 0 || num_requests == 0 || max_blocks == 0 || num_pages == 0;
+    if (*layout_only) return DSAIDX_OK;
     if (!projected || !q || !gamma || !beta || !cache || !block_table || !logits)
         return DSAIDX_EINVAL;
     // the index-input rules (packed rows, BF16 query rows, LayerNorm parameters)
@@ -463,15 +463,72 @@ dsaidx_status dsaidx_index_score_hist(
     if (!workspace || workspace_bytes < need) return DSAIDX_EINVAL;
     if (!aligned(workspace, 256)) return DSAIDX_ELAYOUT;
     // `q` carries the BF16 query and `query_starts` the query lengths in this mode
-    const dsaidx::ScoreArgs a{fmt,          q,          q_row_stride, heads,      nullptr,
+    *args = dsaidx::ScoreArgs{fmt,          q,          q_row_stride, heads,      nullptr,
                               0,            cache,      num_pages,    page_stride, block_table,
                               num_requests, max_blocks, query_lens,   nullptr,    num_rows,
                               max_query_len, logits,    logits_row_stride};
     auto *pp = static_cast<const uint16_t *>(projected);
-    const dsaidx::FusedInputs fin{seq_lens, pp + key_col, pp + weight_col, proj_row_stride,
-                                  q_head_stride, gamma, beta, eps, head_weight_scale(heads),
-                                  query_starts, row_ends};
+    *fin = dsaidx::FusedInputs{seq_lens, pp + key_col, pp + weight_col, proj_row_stride,
+                               q_head_stride, gamma, beta, eps, head_weight_scale(heads),
+                               query_starts, row_ends};
+    return DSAIDX_OK;
+}
+
+dsaidx_status dsaidx_index_score_hist(
+    int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+    const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
+    const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
+    int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
+    int32_t *row_ends, float *logits, int64_t logits_row_stride, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    bool layout_only = false;
+    dsaidx::ScoreArgs a{};
+    dsaidx::FusedInputs fin{};
+    const dsaidx_status st = index_step_args(
+        fmt, projected, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, seq_lens, query_lens, num_requests, num_rows,
+        max_query_len, cache, num_pages, page_stride, block_table, max_blocks, query_starts,
+        row_ends, logits, logits_row_stride, workspace, workspace_bytes, &layout_only, &a, &fin);
+    if (st != DSAIDX_OK) return st;
+    if (layout_only)
+        return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests,
+                                                       num_rows, 0, 1, 1, query_starts,
+                                                       row_ends, as_stream(stream)));
     return hip_status(dsaidx::launch_index_score_hist(a, fin, workspace, as_stream(stream)));
+}
+
+dsaidx_status dsaidx_index_score_topk(
+    int fmt, const void *projected, int64_t proj_row_stride, int64_t key_col, int64_t weight_col,
+    const void *q, int32_t heads, int64_t q_row_stride, int64_t q_head_stride, const float *gamma,
+    const float *beta, float eps, const int32_t *seq_lens, const int32_t *query_lens,
+    int64_t num_requests, int64_t num_rows, int32_t max_query_len, void *cache, int64_t num_pages,
+    int64_t page_stride, const int32_t *block_table, int64_t max_blocks, int32_t *query_starts,
+    int32_t *row_ends, float *logits, int64_t logits_row_stride, int32_t k, int32_t *indices,
+    int64_t indices_row_stride, void *workspace, size_t workspace_bytes, void *stream) {
+    if (k < 1) return DSAIDX_EINVAL;
+    bool layout_only = false;
+    dsaidx::ScoreArgs a{};
+    dsaidx::FusedInputs fin{};
+    const dsaidx_status st = index_step_args(
+        fmt, projected, proj_row_stride, key_col, weight_col, q, heads, q_row_stride,
+        q_head_stride, gamma, beta, eps, seq_lens, query_lens, num_requests, num_rows,
+        max_query_len, cache, num_pages, page_stride, block_table, max_blocks, query_starts,
+        row_ends, logits, logits_row_stride, workspace, workspace_bytes, &layout_only, &a, &fin);
+    if (st != DSAIDX_OK) return st;
+    if (layout_only)
+        return hip_status(dsaidx::launch_decode_layout(seq_lens, query_lens, num_requests,
+                                                       num_rows, 0, 1, 1, query_starts,
+                                                       row_ends, as_stream(stream)));
+    // the selection's rules (as topk_scored)
+    if (!indices) return DSAIDX_EINVAL;
+    if (indices_row_stride < k || !aligned(indices, 4)) return DSAIDX_ELAYOUT;
+    const int64_t chunks = dsaidx::score_geometry(num_requests, max_blocks).chunks;
+    if (num_rows * (chunks + 1) > kMaxGrid) return DSAIDX_EUNSUPPORTED;
+    a.select_k = k;
+    a.select_out = indices;
+    a.select_stride = indices_row_stride;
+    return hip_status(dsaidx::launch_index_score_topk(a, fin, workspace, as_stream(stream)));
 }
 
 dsaidx_status dsaidx_topk_scored(const float *logits, int64_t num_rows, int64_t logits_row_stride,

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void dcp_candidates_kernel(
 
 struct MergeShared {
     uint64_t cand[kMergeCap];
-    SelectShared sel;
+    SelectShared<> sel;
     uint32_t n_valid;
     uint32_t n_local;
 };
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kSelectThreads) void dcp_merge_kernel(
     int32_t *out = merged + row * merged_row_stride;
     int32_t *loc = local_slots ? local_slots + row * local_row_stride : nullptr;
     if (take > 0) {
-        const uint64_t t = select_threshold(LdsCandidates{sh.cand, m}, take, 63, sh.sel);
+        const uint64_t t = select_threshold(LdsCandidates<>{sh.cand, m}, take, 63, sh.sel);
         if (threadIdx.x == 0) sh.sel.n_out = 0;
         __syncthreads();
         for (int i = threadIdx.x; i < m; i += kSelectThreads) {

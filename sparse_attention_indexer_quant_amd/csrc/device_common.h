@@ -205,6 +205,12 @@ __device__ __forceinline__ void hoist_args(const T &...v) {
 // (an early return).
 __device__ __forceinline__ void keep_loaded(uint32_t v) { asm volatile("" ::"v"(v)); }
 
+// Waits for every vector memory operation in flight, so that no later instruction does: placed
+// after a batch of loads and before any store, it keeps the compiler from waiting on a register
+// a load might still write at a point where stores are in flight too -- one counter counts both,
+// so every such use after a store would wait for the stores as well.
+__device__ __forceinline__ void loads_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Order-preserving 32-bit key of a logit for the top-k selection: unsigned comparison of
 // keys is the float order, with -0 mapped to +0 so the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -59,6 +59,11 @@ struct ScoreArgs {
     int64_t row_lo = 0;
     // requests the launch geometry is sized for (0: num_requests)
     int64_t geometry_requests = 0;
+    // the selection made by the scoring launch itself (launch_index_score_topk, rows of one
+    // scoring workgroup each): k, and the [num_rows, >= k] positions with their row stride
+    int select_k = 0;
+    int32_t *select_out = nullptr;
+    int64_t select_stride = 0;
 };
 
 hipError_t launch_score_paged(const ScoreArgs &args, hipStream_t stream);
@@ -82,6 +87,12 @@ hipError_t launch_index_score_hist(const ScoreArgs &args, const FusedInputs &fin
                                    void *workspace, hipStream_t stream);
 // The most rows per request index_score_hist takes for a format (4 MXFP4, 2 FP8).
 int index_score_max_query_len(int fmt);
+// index_score_hist and the selection of every row's top-k (a.select_k, a.select_out,
+// a.select_stride): one launch where each request has one row and every row's keys lie in one
+// scoring workgroup (the workgroup selects from its own histogram and logits), else
+// index_score_hist followed by the selection on its histograms (topk_scored).
+hipError_t launch_index_score_topk(const ScoreArgs &args, const FusedInputs &fin,
+                                   void *workspace, hipStream_t stream);
 
 // How score_paged splits a request's pages: pages per wavefront, workgroups ("chunks") per
 // request, and the keys one workgroup covers (the top-k segment when the scorer writes the

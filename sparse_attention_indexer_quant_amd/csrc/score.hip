@@ -37,6 +37,8 @@
 // "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.index", DsaIndex; page
 // "vllm.models.kimi_k3.amd.ops.fp4_indexer", decode_layout): the MXFP4 query operands, the
 // head weights, the new keys' LayerNorm, quantization and insert, and the row layout.
+#include <type_traits>
+
 #include "device_common.h"
 #include "key_norm.h"
 #include "launch.h"
@@ -313,10 +315,11 @@ struct RowGroup {
     __device__ __forceinline__ void score(const PageRegs<FMT> &pg, int kbase, int count,
                                           float *logits, int64_t first_row,
                                           int64_t logits_row_stride, int lane, int grp,
-                                          uint32_t *hist, uint32_t sel32, uint32_t sel16) const {
+                                          uint32_t *hist, uint32_t sel32, uint32_t sel16,
+                                          float *keep = nullptr) const {
         const uint32_t ksw = FMT == kFmtMxfp4 ? tile_scales(pg.ks[0], sel32, sel16) : 0u;
         score_rows<0, 1>(pg, ksw, kbase, count, logits, first_row, logits_row_stride, lane, grp,
-                         hist);
+                         hist, keep);
         if constexpr (RG > 1) {
             if (count > 1)
                 score_rows<1, 2>(pg, ksw, kbase, count, logits, first_row, logits_row_stride,
@@ -342,7 +345,7 @@ struct RowGroup {
                                                int count,
                                                float *logits, int64_t first_row,
                                                int64_t logits_row_stride, int lane, int grp,
-                                               uint32_t *hist) const {
+                                               uint32_t *hist, float *keep = nullptr) const {
         float part[RG][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -380,6 +383,7 @@ struct RowGroup {
             float *row = logits + (first_row + j) * logits_row_stride + kbase;
             if (kbase + lane < rend[j]) {
                 row[lane] = out;
+                if (j == 0 && keep) keep[kbase + lane] = out;  // at the key's position
                 if (hist) {
                     const uint32_t bin = order_key(out) >> kBinShift;
                     atomicAdd(&hist[j * (kBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -699,7 +703,13 @@ constexpr int staged_key_bytes() { return FMT == kFmtMxfp4 ? 80 : 144; }
 // MULTI: a request may have more rows than one group (max_query_len > RG), so the pages are
 // streamed once per group. Without it the group loop runs once, which the compiler then knows:
 // nothing is carried from one group to the next, which took 20-40 registers per wavefront.
-template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false, bool MULTI = false>
+//
+// SELECT (FUSED one-row groups, one chunk per request): the workgroup holds every key of its
+// row, so it also selects the row's top-k from its LDS histogram and its own logits (the
+// selection's steps in one workgroup) and writes the positions instead of the workspace
+// histograms.
+template <int FMT, int H, int RG, int NB, bool HIST, bool FUSED = false, bool MULTI = false,
+          bool SELECT = false>
 __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ query_starts,
     int64_t max_blocks, int64_t num_requests, int pages_per_wave,
@@ -708,9 +718,11 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     int64_t w_row_stride, const int32_t *__restrict__ row_ends, int64_t num_rows,
     int max_query_len, float *__restrict__ logits, int64_t logits_row_stride,
     uint16_t *__restrict__ seghist, uint16_t *__restrict__ coarse, FusedInputs fin,
-    int64_t row_lo, int order_work) {
+    int64_t row_lo, int order_work, int select_k, int32_t *__restrict__ select_out,
+    int64_t select_stride) {
     static_assert(!FUSED || HIST, "fused inputs: with histograms");
     static_assert(!(FUSED && MULTI), "a fused launch has one row group");
+    static_assert(!SELECT || (FUSED && RG == 1), "the selection in the launch: one-row requests");
     constexpr int kStagedKeyBytes = staged_key_bytes<FMT>();
     // HIST: per-row histograms of this workgroup's logits; every wavefront reaches the
     // workgroup barriers below, so no wavefront returns early on a wavefront-level condition
@@ -719,6 +731,17 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     __shared__ __align__(16) uint8_t step_lds_bytes[FUSED ? sizeof(StepQueryLds<FMT, H, RG>) : 16];
     __shared__ __align__(16) uint8_t staged_keys[FUSED ? kWaves * RG * kStagedKeyBytes : 16];
     auto &step_lds = *reinterpret_cast<StepQueryLds<FMT, H, RG> *>(step_lds_bytes);
+    // SELECT: the radix select's LDS, the coarse counts, the selection's state, and a copy of
+    // the row's logits (every key of the row is this workgroup's: positions below 4096)
+    struct SelectState {
+        uint32_t bin;
+        int above, m;
+        uint32_t n_above, n_cand;
+    };
+    __shared__ std::conditional_t<SELECT, SelectShared<64 * kWaves>, int> sel_sh;
+    __shared__ uint32_t sel_coarse[SELECT ? kCoarseBins : 1];
+    __shared__ SelectState sel_st;
+    __shared__ float sel_logits[SELECT ? kWaves * kMaxPagesPerWave * kPageTokens : 1];
     const int lane = threadIdx.x & 63;
     // uniform across the wavefront; said explicitly so that all page and bound arithmetic
     // below stays in scalar registers
@@ -899,6 +922,10 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 const int64_t total = lr0 + lqlen;
                 for (int64_t row = (total > 0 ? total : 0) + lane; row < num_rows; row += 64)
                     fin.row_ends[row] = 0;
+                if constexpr (SELECT) {  // ... which select nothing
+                    for (int64_t row = total > 0 ? total : 0; row < num_rows; ++row)
+                        for (int i = lane; i < select_k; i += 64) select_out[row * select_stride + i] = -1;
+                }
             }
         }
     }
@@ -930,8 +957,14 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
         const int64_t e = (int64_t)seq - qlen + nrows;  // the last row's bound is the largest
         kmax = (int)(e < 0 ? 0 : (e > width ? width : e));
         // the bounds need no loads here: a chunk past the request's keys leaves before any
-        // query work (no new key lies in it: every key's position is below the last bound)
-        if (chunk_begin * kPageTokens >= kmax) return;
+        // query work (no new key lies in it: every key's position is below the last bound);
+        // SELECT: its one chunk has no keys, the row selects none
+        if (chunk_begin * kPageTokens >= kmax) {
+            if constexpr (SELECT)
+                for (int i = threadIdx.x; i < select_k; i += 64 * kWaves)
+                    select_out[r0 * select_stride + i] = -1;
+            return;
+        }
         if (!kSpecQuery || r0 != spec_row)
             sq.load(reinterpret_cast<const uint16_t *>(q), q_row_stride, fin.q_head_stride,
                     fin.w_in, fin.proj_row_stride, r0, r1, wave, l16, grp);
@@ -1014,11 +1047,98 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     const int64_t nblk = (kext + kPageTokens - 1) / kPageTokens;
     // a chunk past the request's keys has nothing to score and no histogram to write (the
     // selection reads only segments that hold keys of the row): the whole workgroup leaves
-    if (chunk_begin >= nblk) return;
+    if (chunk_begin >= nblk) {
+        if constexpr (SELECT)  // (not reached: kmax > 0 above)
+            for (int i = threadIdx.x; i < select_k; i += 64 * kWaves)
+                select_out[r0 * select_stride + i] = -1;
+        return;
+    }
     const int64_t chunk_end = chunk_begin + kWaves * (int64_t)PW < nblk
                                   ? chunk_begin + kWaves * (int64_t)PW : nblk;
     // pages of this wavefront below chunk_end
     const int run = blk_first < chunk_end ? (int)((chunk_end - blk_first + kWaves - 1) / kWaves) : 0;
+
+    // SELECT: the top-k of the row (bound n) into out[0..k), from the workgroup's LDS histogram
+    // and LDS copy of the row's logits (every key of the row is this workgroup's) -- the
+    // selection's steps in one workgroup: the coarse bin holding the k-th largest key, the fine
+    // bin inside it, then each wavefront's keys above the bin to the output and inside it to a
+    // candidate list in the histogram's LDS, and the candidates' radix select (one wavefront's
+    // for at most 64).
+    auto select_row = [&](int64_t n, int64_t row) {
+        if constexpr (SELECT) {
+            int32_t *out = select_out + row * select_stride;
+            const int k = select_k;
+            if (n <= k) {
+                for (int i = threadIdx.x; i < k; i += 64 * kWaves) out[i] = i < n ? (int32_t)i : -1;
+                return;
+            }
+            {  // coarse bin c = the 64 fine bins of lanes 4 c .. 4 c + 3
+                const uint4 *src = reinterpret_cast<const uint4 *>(hist) + 2 * threadIdx.x;
+                const uint4 a = src[0], b = src[1];
+                const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t s16 = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s16 += (w8[e] & 0xFFFFu) + (w8[e] >> 16);
+                s16 += lane_xor<1>(s16);
+                s16 += lane_xor<2>(s16);
+                if ((threadIdx.x & 3) == 0) sel_coarse[threadIdx.x >> 2] = s16;
+            }
+            __syncthreads();
+            if (wave == 0) {  // lane l: coarse bin 63 - l, then fine bin 63 - l of the coarse bin
+                const Found64 fc = find_in_64_wave(sel_coarse[63 - lane], k);
+                const uint32_t B = 63u - (uint32_t)fc.lane;
+                const uint32_t fb = B * 64u + (63u - (uint32_t)lane);
+                const uint32_t cnt = (hist[fb >> 1] >> (16u * (fb & 1u))) & 0xFFFFu;
+                const Found64 ff = find_in_64_wave(cnt, k - fc.before);
+                if (lane == 0) {
+                    sel_st.bin = B * 64u + 63u - (uint32_t)ff.lane;
+                    sel_st.above = fc.before + ff.before;
+                    sel_st.m = (int)ff.count;
+                    sel_st.n_above = 0;
+                    sel_st.n_cand = 0;
+                }
+            }
+            __syncthreads();
+            const uint32_t bin = sel_st.bin;
+            const int above = sel_st.above, m = sel_st.m, r = k - above;  // 1 <= r <= m
+            int pos_bits = 1;
+            while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
+            uint64_t *cands = reinterpret_cast<uint64_t *>(hist);  // the histogram is read
+            constexpr int kCap = (int)(sizeof(hist) / (sizeof(uint64_t)));
+#pragma unroll
+            for (int p = 0; p < kMaxPagesPerWave; ++p) {
+                if (!(p < run && table_page(p) >= 0)) continue;  // uniform
+                const int64_t kb = block_of(p) * kPageTokens;
+                const bool live = (int64_t)lane < n - kb;
+                const uint32_t u = order_key(sel_logits[kb + lane]);
+                const bool ab = live && (u >> kBinShift) > bin;
+                const bool in = live && (u >> kBinShift) == bin;
+                const uint32_t pos = (uint32_t)kb + (uint32_t)lane;
+                const uint32_t sa = wave_slot(ab, &sel_st.n_above);
+                if (ab && sa < (uint32_t)above) out[sa] = (int32_t)pos;
+                const uint32_t sc = wave_slot(in, &sel_st.n_cand);
+                if (in) {
+                    if (r == m) {  // every key inside the bin is taken
+                        if (above + (int)sc < k) out[above + sc] = (int32_t)pos;
+                    } else if (sc < (uint32_t)kCap) {
+                        cands[sc] = composite(u, pos, pos_bits);
+                    }
+                }
+            }
+            if (r == m) return;
+            __syncthreads();  // the candidates are in the LDS
+            const int bits = 20 + pos_bits;
+            if (m <= 64) {
+                if (wave == 0) wave_select_out(cands, m, r, bits, pos_bits, out + above);
+            } else if (m <= kCap) {
+                select_smallest(LdsCandidates<64 * kWaves>{cands, m}, r, bits, pos_bits, out + above,
+                                sel_sh);
+            } else {  // the bin overflowed the list: its keys again from the logits' copy
+                select_smallest(RowBin<64 * kWaves>{sel_logits, n, bin, pos_bits}, r, bits,
+                                pos_bits, out + above, sel_sh);
+            }
+        }
+    };
 
     // Requests with more rows than one register group stream their pages once per group
     // (the second and later passes mostly hit the L2).
@@ -1045,7 +1165,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                                   own_o[i], l16, grp);
                 rows.score(own_pg, (int)(block_of(own_pp) * kPageTokens), count, logits,
                            first - row_lo, logits_row_stride, lane, grp, HIST ? hist : nullptr,
-                           sel32, sel16);
+                           sel32, sel16, SELECT ? sel_logits : nullptr);
             }
         }
         for (int base = 0; base < run; base += NB) {
@@ -1060,10 +1180,14 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 if (p < run && table_page(p) >= 0 && (!FUSED || p != own_pp))
                     rows.score(buf[slot], (int)(block_of(p) * kPageTokens), count, logits,
                                first - row_lo, logits_row_stride, lane, grp,
-                               HIST ? hist : nullptr, sel32, sel16);
+                               HIST ? hist : nullptr, sel32, sel16,
+                               SELECT ? sel_logits : nullptr);
             }
         }
-        if constexpr (HIST) {
+        if constexpr (SELECT) {
+            __syncthreads();  // the row's histogram is complete
+            select_row(rows.rend[0], first);
+        } else if constexpr (HIST) {
             // (row, segment = chunk) histograms of the rows whose keys reach this chunk; the
             // packed 16-bit counts are already the workspace's layout
             __syncthreads();
@@ -1136,7 +1260,8 @@ ScoreGeometry score_geometry(int64_t num_requests, int64_t max_blocks) {
     return g;
 }
 
-template <int FMT, int H, int RG, bool HIST, bool FUSED = false, bool MULTI = false>
+template <int FMT, int H, int RG, bool HIST, bool FUSED = false, bool MULTI = false,
+          bool SELECT = false>
 static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, hipStream_t stream,
                                   const FusedInputs &fin = FusedInputs{}) {
     const ScoreGeometry geo = score_geometry(a.geometry_requests > 0 ? a.geometry_requests
@@ -1147,13 +1272,14 @@ static hipError_t launch_score_rg(const ScoreArgs &a, const TopkWorkspace &ws, h
     // workload, and better than 2 on the verify workload's 4-row groups), else 2 (FP8 pages
     // take the registers a deeper ring would need)
     constexpr int NB = FMT == kFmtMxfp4 ? 3 : 2;
-    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST, FUSED, MULTI>), grid, block, 0, stream,
+    hipLaunchKernelGGL((score_paged_kernel<FMT, H, RG, NB, HIST, FUSED, MULTI, SELECT>), grid, block, 0, stream,
                        a.block_table, a.query_starts, a.max_blocks, a.num_requests,
                        geo.pages_per_wave, static_cast<const uint8_t *>(a.cache), a.page_stride,
                        a.num_pages, geo.chunks, static_cast<const uint8_t *>(a.q), a.q_row_stride,
                        static_cast<const uint16_t *>(a.w), a.w_row_stride, a.row_ends,
                        a.num_rows, a.max_query_len, a.logits, a.logits_row_stride, ws.seghist,
-                       ws.coarse, fin, a.row_lo, a.geometry_requests > 0 ? 0 : 1);
+                       ws.coarse, fin, a.row_lo, a.geometry_requests > 0 ? 0 : 1, a.select_k,
+                       a.select_out, a.select_stride);
     return hipGetLastError();
 }
 
@@ -1287,6 +1413,36 @@ hipError_t launch_index_score_hist(const ScoreArgs &a, const FusedInputs &fin, v
         case kFmtFp8: return launch_index_score_fmt<kFmtFp8>(a, fin, ws, stream);
         default: return launch_index_score_fmt<kFmtFp8Mx>(a, fin, ws, stream);
     }
+}
+
+// The step with its selection made in the scoring launch (one-row requests, one chunk each):
+// score_paged_kernel<..., SELECT = true>.
+template <int FMT>
+static hipError_t launch_index_select_fmt(const ScoreArgs &a, const FusedInputs &fin,
+                                          hipStream_t stream) {
+    switch (a.heads) {
+        case 16: return launch_score_rg<FMT, 16, 1, true, true, false, true>(a, TopkWorkspace{}, stream, fin);
+        case 32: return launch_score_rg<FMT, 32, 1, true, true, false, true>(a, TopkWorkspace{}, stream, fin);
+        default: return launch_score_rg<FMT, 64, 1, true, true, false, true>(a, TopkWorkspace{}, stream, fin);
+    }
+}
+
+hipError_t launch_index_score_topk(const ScoreArgs &a, const FusedInputs &fin, void *workspace,
+                                   hipStream_t stream) {
+    const ScoreGeometry geo = score_geometry(a.num_requests, a.max_blocks);
+    if (a.max_query_len <= 1 && geo.chunks == 1) {
+        switch (a.fmt) {
+            case kFmtMxfp4: return launch_index_select_fmt<kFmtMxfp4>(a, fin, stream);
+            case kFmtFp8: return launch_index_select_fmt<kFmtFp8>(a, fin, stream);
+            default: return launch_index_select_fmt<kFmtFp8Mx>(a, fin, stream);
+        }
+    }
+    hipError_t e = launch_index_score_hist(a, fin, workspace, stream);
+    if (e != hipSuccess) return e;
+    return launch_topk_after_histograms(a.logits, a.num_rows, a.max_blocks * kPageTokens,
+                                        a.logits_row_stride, fin.row_ends, a.select_k,
+                                        a.select_out, a.select_stride, workspace, geo.chunks,
+                                        geo.segment_keys, stream);
 }
 
 }  // namespace dsaidx

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+#include "topk_layout.h"
+
 namespace dsaidx {
 
 constexpr int kSelectThreads = 512;
@@ -38,18 +41,21 @@ __device__ __forceinline__ int scan_block(int v, int *partials) {
     return v + before;
 }
 
+// NT: the workgroup's lanes (every lane takes part)
+template <int NT = kSelectThreads>
 struct LdsCandidates {  // composites already in LDS (distinct)
     const uint64_t *c;
     int m;
     template <typename F>
     __device__ __forceinline__ void for_each(F &&f) const {
-        for (int j = threadIdx.x; j < m; j += kSelectThreads) f(c[j]);
+        for (int j = threadIdx.x; j < m; j += NT) f(c[j]);
     }
 };
 
+template <int NT = kSelectThreads>
 struct SelectShared {
     uint32_t hist[kRadixBins];
-    int partials[kSelectThreads / 64];
+    int partials[NT / 64];
     uint64_t prefix;
     int below;
     int count;
@@ -59,15 +65,15 @@ struct SelectShared {
 // The r-th smallest of the distinct composites (of `bits` significant bits, 1 <= r <= their
 // count) that `src` yields, by a most-significant-digit radix select in LDS: exactly r
 // composites are <= the returned value. Every lane of the workgroup must call it.
-template <typename Source>
-__device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectShared &sh) {
+template <typename Source, int NT>
+__device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectShared<NT> &sh) {
     uint64_t prefix = 0;
     int done = 0;  // high composite bits fixed in `prefix`
     uint64_t threshold = ~(uint64_t)0;
     while (done < bits) {
         const int digit = bits - done >= kRadixBits ? kRadixBits : bits - done;
         const int shift = bits - done - digit;
-        for (int b = threadIdx.x; b < kRadixBins; b += kSelectThreads) sh.hist[b] = 0;
+        for (int b = threadIdx.x; b < kRadixBins; b += NT) sh.hist[b] = 0;
         __syncthreads();
         const uint64_t want = prefix >> (shift + digit);
         src.for_each([&](uint64_t c) {
@@ -75,7 +81,7 @@ __device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectS
                 atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)((1 << digit) - 1)], 1u);
         });
         __syncthreads();
-        constexpr int per = kRadixBins / kSelectThreads;  // ascending: lane t owns per*t ..
+        constexpr int per = kRadixBins / NT;  // ascending: lane t owns per*t ..
         int own = 0;
         uint32_t mine[per];
 #pragma unroll
@@ -83,7 +89,7 @@ __device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectS
             mine[j] = sh.hist[threadIdx.x * per + j];
             own += (int)mine[j];
         }
-        const int incl = scan_block<kSelectThreads>(own, sh.partials);
+        const int incl = scan_block<NT>(own, sh.partials);
         int before = incl - own;
 #pragma unroll
         for (int j = 0; j < per; ++j) {
@@ -109,6 +115,26 @@ __device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectS
     return threshold;
 }
 
+// Composite of a key inside the threshold bin: smaller for a larger value, and for equal
+// values smaller for the lower position; unique per position.
+__device__ __forceinline__ uint64_t composite(uint32_t u, uint32_t pos, int pos_bits) {
+    return ((uint64_t)(~u & 0xFFFFFu) << pos_bits) | pos;
+}
+
+// The lane of a wavefront holding the k-th largest of 64 descending counts (one per lane), the
+// count before it and its own count, as wavefront-uniform values. The counts reach k.
+struct Found64 {
+    int lane, before;
+    uint32_t count;
+};
+__device__ __forceinline__ Found64 find_in_64_wave(uint32_t c, int k) {
+    const int incl = wave_incl_scan((int)c);
+    const int before = incl - (int)c;
+    const uint64_t hit = __ballot(before < k && incl >= k);
+    const int L = hit ? __builtin_ctzll(hit) : 63;
+    return {L, __builtin_amdgcn_readlane(before, L), (uint32_t)__builtin_amdgcn_readlane((int)c, L)};
+}
+
 // Slots for the lanes of a wavefront whose `take` is set (among the active lanes), from the
 // counter `n`: one atomic per wavefront, then each lane's rank among the taken lanes.
 __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t *n) {
@@ -123,11 +149,50 @@ __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t *n) {
                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// The r smallest of m <= 64 distinct composites (`bits` significant bits), one per lane of a
+// wavefront in lanes [0, m): bit by bit from the top, the undecided composites whose bit is 0
+// are all taken if they fit in what is left of r, else the search continues among them.
+// Returns the mask of the taken lanes.
+__device__ __forceinline__ uint64_t wave_select_smallest(uint64_t c, int m, int r, int bits) {
+    const int lane = threadIdx.x & 63;
+    uint64_t active = __ballot(lane < m), taken = 0;
+    for (int b = bits - 1; b >= 0 && r > 0; --b) {
+        const uint64_t zeros = active & __ballot(((c >> b) & 1ull) == 0);
+        const int nz = __builtin_popcountll(zeros);
+        if (nz <= r) {
+            taken |= zeros;
+            r -= nz;
+            active &= ~zeros;
+        } else {
+            active = zeros;
+        }
+        if (__builtin_popcountll(active) == r) {
+            taken |= active;
+            r = 0;
+        }
+    }
+    return taken;
+}
+
+// The r smallest of m <= 64 distinct composites c[0..m) (in LDS) to out[0..r), by one
+// wavefront's bit-by-bit select; the composite's low `pos_bits` bits are the position written.
+__device__ __forceinline__ void wave_select_out(const uint64_t *c, int m, int r, int bits,
+                                                int pos_bits, int32_t *out) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t v = lane < m ? c[lane] : ~(uint64_t)0;
+    const uint64_t taken = wave_select_smallest(v, m, r, bits);
+    if ((taken >> lane) & 1ull) {
+        const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(taken >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)taken, 0u));
+        out[slot] = (int32_t)(v & (((uint64_t)1 << pos_bits) - 1));
+    }
+}
+
 // Writes the low `pos_bits` bits (the position) of the r smallest composites to out[0..r),
 // in no particular order.
-template <typename Source>
+template <typename Source, int NT>
 __device__ void select_smallest(const Source &src, int r, int bits, int pos_bits, int32_t *out,
-                                SelectShared &sh) {
+                                SelectShared<NT> &sh) {
     const uint64_t threshold = select_threshold(src, r, bits, sh);
     if (threadIdx.x == 0) sh.n_out = 0;
     __syncthreads();
@@ -138,5 +203,20 @@ __device__ void select_smallest(const Source &src, int r, int bits, int pos_bits
         if (take && slot < (uint32_t)r) out[slot] = (int32_t)(c & pos_mask);
     });
 }
+
+template <int NT = kSelectThreads>
+struct RowBin {  // every key of the row inside the threshold bin, read from the logits
+    const float *x;
+    int64_t n;
+    uint32_t bin;
+    int pos_bits;
+    template <typename F>
+    __device__ __forceinline__ void for_each(F &&f) const {
+        for (int64_t i = threadIdx.x; i < n; i += NT) {
+            const uint32_t u = order_key(x[i]);
+            if ((u >> kBinShift) == bin) f(composite(u, (uint32_t)i, pos_bits));
+        }
+    }
+};
 
 }  // namespace dsaidx

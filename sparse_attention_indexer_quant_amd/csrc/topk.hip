@@ -460,11 +460,6 @@ __device__ __forceinline__ Masks16 classify16(const float (&raw)[kCollectPer], i
     return m;
 }
 
-// Waits for every load in flight, so that no later instruction does: placed after the keys'
-// loads and before any store, it keeps the compiler from waiting on a register a load might
-// still write (a path that skips the keys' use) at a point where stores are in flight too --
-// the counter it waits on counts both, and a store's round trip is as long as a load's.
-__device__ __forceinline__ void loads_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Positions of the lane's keys above the bin to out[pa], out[pa + 1], .. (while below `cap`),
 // in ascending order: one step per set bit.
@@ -702,32 +697,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
                          partials);
 }
 
-// Composite of a key inside the threshold bin: smaller for a larger value, and for equal
-// values smaller for the lower position; unique per position.
-__device__ __forceinline__ uint64_t composite(uint32_t u, uint32_t pos, int pos_bits) {
-    return ((uint64_t)(~u & 0xFFFFFu) << pos_bits) | pos;
-}
-
-struct RowBin {  // every key of the row inside the threshold bin, read from the logits
-    const float *x;
-    int64_t n;
-    uint32_t bin;
-    int pos_bits;
-    template <typename F>
-    __device__ __forceinline__ void for_each(F &&f) const {
-        for (int64_t i = threadIdx.x; i < n; i += kSelectThreads) {
-            const uint32_t u = order_key(x[i]);
-            if ((u >> kBinShift) == bin) f(composite(u, (uint32_t)i, pos_bits));
-        }
-    }
-};
 
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     const uint2 *__restrict__ cand_all, const RowState *__restrict__ state,
     const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
     int64_t indices_row_stride, const float *__restrict__ logits, int64_t logits_row_stride) {
     __shared__ uint64_t cands[kCandCap];
-    __shared__ SelectShared sh;
+    __shared__ SelectShared<> sh;
     const int64_t row = blockIdx.x;
     // the first kSpec candidates, loaded before their count is known (the list always has
     // kCandCap slots; slots past the count are ignored)
@@ -775,49 +751,10 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
             cands[j] = composite(e.x, e.y, pos_bits);
         }
         __syncthreads();
-        select_smallest(LdsCandidates{cands, (int)ncand}, remaining, bits, pos_bits, out, sh);
+        select_smallest(LdsCandidates<>{cands, (int)ncand}, remaining, bits, pos_bits, out, sh);
     } else {
-        select_smallest(RowBin{x, n, bin, pos_bits}, remaining, bits, pos_bits, out, sh);
+        select_smallest(RowBin<>{x, n, bin, pos_bits}, remaining, bits, pos_bits, out, sh);
     }
-}
-
-// The lane of a wavefront holding the k-th largest of 64 descending counts (one per lane), the
-// count before it and its own count, as wavefront-uniform values. The counts reach k.
-struct Found64 {
-    int lane, before;
-    uint32_t count;
-};
-__device__ __forceinline__ Found64 find_in_64_wave(uint32_t c, int k) {
-    const int incl = wave_incl_scan((int)c);
-    const int before = incl - (int)c;
-    const uint64_t hit = __ballot(before < k && incl >= k);
-    const int L = hit ? __builtin_ctzll(hit) : 63;
-    return {L, __builtin_amdgcn_readlane(before, L), (uint32_t)__builtin_amdgcn_readlane((int)c, L)};
-}
-
-// The r smallest of m <= 64 distinct composites (`bits` significant bits), one per lane of a
-// wavefront in lanes [0, m): bit by bit from the top, the undecided composites whose bit is 0
-// are all taken if they fit in what is left of r, else the search continues among them.
-// Returns the mask of the taken lanes.
-__device__ __forceinline__ uint64_t wave_select_smallest(uint64_t c, int m, int r, int bits) {
-    const int lane = threadIdx.x & 63;
-    uint64_t active = __ballot(lane < m), taken = 0;
-    for (int b = bits - 1; b >= 0 && r > 0; --b) {
-        const uint64_t zeros = active & __ballot(((c >> b) & 1ull) == 0);
-        const int nz = __builtin_popcountll(zeros);
-        if (nz <= r) {
-            taken |= zeros;
-            r -= nz;
-            active &= ~zeros;
-        } else {
-            active = zeros;
-        }
-        if (__builtin_popcountll(active) == r) {
-            taken |= active;
-            r = 0;
-        }
-    }
-    return taken;
 }
 
 // Steps 2 to 4 in one workgroup per row, for rows of at most kRowTopkWidth keys and 64
@@ -843,7 +780,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
     int seg_len, int k, int32_t *__restrict__ indices, int64_t indices_row_stride) {
     constexpr int kWaves = kSelectThreads / 64;
     __shared__ uint64_t cands[kCandCap];
-    __shared__ SelectShared sh;
+    __shared__ SelectShared<> sh;
     __shared__ uint32_t part[kWaves][64];
     __shared__ uint32_t fine_count[64];
     __shared__ int wave_total[kWaves];
@@ -971,7 +908,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
             }
         }
     } else {
-        select_smallest(LdsCandidates{cands, m}, r, bits, pos_bits, out + above, sh);
+        select_smallest(LdsCandidates<>{cands, m}, r, bits, pos_bits, out + above, sh);
     }
 }
 

@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
               "dsaidx_dcp_merge", "dsaidx_index_inputs_layout", "dsaidx_score_segment_keys",
               "dsaidx_read_sections", "dsaidx_read_sections_words", "dsaidx_read_stream",
               "dsaidx_topk_noalloc", "dsaidx_decode_tile_size", "dsaidx_score_topk_tiled",
-              "dsaidx_score_topk_tiled_workspace_bytes"):
+              "dsaidx_score_topk_tiled_workspace_bytes", "dsaidx_index_score_hist",
+              "dsaidx_index_score_topk"):
         assert n in names
 
 
@@ -375,6 +376,49 @@ def test_topk_scored_checks(lib):
     assert topk_scored(lib, ls=255) == ELAYOUT
     assert topk_scored(lib, os=7) == ELAYOUT
     assert topk_scored(lib, ws=P + 8) == ELAYOUT
+
+
+def index_step(lib, call, **kw):
+    """dsaidx_index_score_hist (call "hist") or dsaidx_index_score_topk (call "topk")."""
+    a = dict(fmt=MX, proj=P, ps_=256, kc=0, wc=128, q=P, h=32, qs=32 * 128, qh=128, g=P, b=P,
+             eps=1e-6, seq=P, ql=P, r=2, rows=2, mq=1, cache=P, pages=8, ps=4352, bt=P, mb=4,
+             starts=P, ends=P, lg=P, ls=256, k=8, idx=P, istr=8, wk=P, wkb=1 << 30)
+    a.update(kw)
+    head = [a["fmt"], a["proj"], a["ps_"], a["kc"], a["wc"], a["q"], a["h"], a["qs"], a["qh"],
+            a["g"], a["b"], ctypes.c_float(a["eps"]), a["seq"], a["ql"], a["r"], a["rows"], a["mq"],
+            a["cache"], a["pages"], a["ps"], a["bt"], a["mb"], a["starts"], a["ends"], a["lg"],
+            a["ls"]]
+    if call == "hist":
+        return lib.dsaidx_index_score_hist(*head, a["wk"], a["wkb"], None)
+    return lib.dsaidx_index_score_topk(*head, a["k"], a["idx"], a["istr"], a["wk"], a["wkb"], None)
+
+
+@pytest.mark.parametrize("call", ["hist", "topk"])
+def test_index_step_checks(lib, call):
+    # the checks both step calls share (every case returns before any launch)
+    assert index_step(lib, call, fmt=3) == EINVAL
+    assert index_step(lib, call, eps=-1.0) == EINVAL
+    assert index_step(lib, call, h=20) == EUNSUP
+    assert index_step(lib, call, mq=5) == EUNSUP
+    assert index_step(lib, call, fmt=FP8, mq=3) == EUNSUP
+    assert index_step(lib, call, starts=None) == EINVAL
+    assert index_step(lib, call, proj=None) == EINVAL
+    assert index_step(lib, call, ps_=130) == ELAYOUT  # the key's 128 columns do not fit
+    assert index_step(lib, call, q=P + 8) == ELAYOUT
+    assert index_step(lib, call, ps=4350) == ELAYOUT
+    assert index_step(lib, call, ls=255) == ELAYOUT
+    assert index_step(lib, call, wk=None) == EINVAL
+    assert index_step(lib, call, wkb=16) == EINVAL
+    assert index_step(lib, call, wk=P + 16) == ELAYOUT
+
+
+def test_index_score_topk_checks(lib):
+    # the selection's own checks
+    assert index_step(lib, "topk", k=0) == EINVAL
+    assert index_step(lib, "topk", k=0, rows=0) == EINVAL
+    assert index_step(lib, "topk", idx=None) == EINVAL
+    assert index_step(lib, "topk", istr=7) == ELAYOUT
+    assert index_step(lib, "topk", idx=P + 2) == ELAYOUT
 
 
 def cand(lib, **kw):

@@ -723,6 +723,92 @@ def test_score_topk_adversarial_rows(name, variant, k):
     assert_topk_sets(fidx.cpu().numpy(), want, range(wl.num_rows), f"{what} fused")
 
 
+def _one_launch_case(name):
+    """Batches whose requests each have at most one row, every row's keys in one scoring
+    workgroup: index_score_topk selects inside the scoring launch."""
+    rng = np.random.default_rng(41)
+    if name == "fp4_tiny":
+        return dict(fmt="mxfp4", heads=32, seq_lens=[256], query_lens=[1])
+    if name == "fp4_h64_one_short_padded":  # a ragged last page and two padding rows
+        return dict(fmt="mxfp4", heads=64, seq_lens=[200], query_lens=[1], num_rows=3)
+    if name == "fp4_many_short":  # requests without rows, one-key rows, padding rows
+        seq = rng.integers(1, 4097, size=300)
+        seq[:3] = [1, 64, 65]
+        ql = (rng.random(300) < 0.9).astype(np.int32)
+        ql[:3] = 1
+        return dict(fmt="mxfp4", heads=32, seq_lens=seq, query_lens=ql, num_rows=int(ql.sum()) + 5)
+    if name == "fp8_many_short":
+        return dict(fmt="fp8", heads=32, seq_lens=rng.integers(1, 4097, size=256),
+                    query_lens=[1] * 256, outlier_frac=0.01, outlier_gain=20.0)
+    if name == "fp8mx_h16_many_short":
+        return dict(fmt="fp8_mx", heads=16, seq_lens=rng.integers(1, 2049, size=260),
+                    query_lens=[1] * 260)
+    if name == "fp4_h64_merged_many_short":
+        return dict(fmt="mxfp4", heads=64, seq_lens=rng.integers(1, 3001, size=256),
+                    query_lens=[1] * 256, page_stride=8192, section_offset=3840)
+    raise KeyError(name)
+
+
+ONE_LAUNCH_CASES = ["fp4_tiny", "fp4_h64_one_short_padded", "fp4_many_short", "fp8_many_short",
+                    "fp8mx_h16_many_short", "fp4_h64_merged_many_short"]
+
+
+@pytest.mark.parametrize("name", ONE_LAUNCH_CASES)
+@pytest.mark.parametrize("variant", ["random", "hot_segment", "zero_query"])
+@pytest.mark.parametrize("k", [1, 64, 2048])
+def test_index_score_topk_one_launch(name, variant, k):
+    # the step with its selection in the scoring launch: cache bytes and row layout as the
+    # oracle's, logits bit for bit equal to score_paged's (and close to the oracle's), index
+    # sets equal to the oracle's top-k of the same logits -- with rows of at most k keys, ties
+    # of a thousand keys at the top of a row, and rows whose logits are all +0 (one bin of every
+    # key: up to 64 candidates, up to the LDS list's 1024, and more), padding rows and rows of
+    # requests without keys selecting none
+    wl = make_workload(name, topk=k, seed=37, extra_pages=1, **_one_launch_case(name))
+    assert dsa.score_segment_keys(wl.num_requests, wl.max_blocks) >= wl.width, "not one launch"
+    if variant == "hot_segment":
+        for q in range(wl.num_requests):
+            n = int(wl.seq_lens[q])
+            if n > 1200 and wl.query_lens[q] > 0:
+                _hot_segment(wl, q, 64, 64 + 1024)
+    elif variant == "zero_query":
+        wl.q_bits[::2] = 0
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    q_rows, w = dw.quantize()
+    starts, ends = dw.layout()
+    oe = ends.cpu().numpy()
+    plain = dw.score(q_rows, w, starts, ends)
+    cols = torch.arange(wl.width, device="cuda")
+    valid = cols[None, :] < ends.to(torch.int64)[:, None]
+    what = f"{name} {variant} k={k}"
+
+    rng = np.random.default_rng(14)
+    proj, _ = _step_projection(wl, 2, 140, 140 + wl.heads, rng)
+    b = _cache_without_step_keys(wl)
+    lb = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    ws = torch.full((dsa.score_topk_workspace_bytes(wl.num_requests, wl.max_blocks, wl.num_rows),),
+                    0x77, dtype=torch.uint8, device="cuda")
+    idx = torch.full((wl.num_rows, k + 3), 0x3FFFFFFF, dtype=torch.int32, device="cuda")
+    fs, fe, _, _ = dsa.index_score_topk(
+        bf16_dev(proj), 2, 140, b.q, b.gamma, b.beta, wl.eps, b.seq_lens, b.query_lens,
+        wl.num_rows, b.cache, wl.num_pages, wl.page_stride, b.block_table, wl.max_query_len, k,
+        wl.fmt, wl.section_offset, out=lb, indices=idx[:, :k], workspace=ws)
+    assert torch.equal(b.cache, dw.cache), f"{what}: cache bytes"
+    assert torch.equal(fs, starts) and torch.equal(fe, ends), f"{what}: row layout"
+    assert torch.equal(lb.view(torch.int32)[valid], plain.view(torch.int32)[valid]), f"{what}: logits"
+    assert torch.all(ws == 0x77), f"{what}: the one-launch form touches no workspace"
+    assert torch.all(idx[:, k:] == 0x3FFFFFFF), f"{what}: written past k"
+    got = lb.cpu().numpy()
+    if k == 64:  # the logits do not depend on k: compared with the oracle's once per workload
+        oq, ow = oracle.quantize_queries(wl.q_bits, wl.wv_bits, wl.fmt)
+        os_, _ = oracle.decode_layout(wl.seq_lens, wl.query_lens, wl.num_rows)
+        ref = oracle.score_paged(oq, wl.heads, ow, oracle_cache(wl), wl.num_pages, wl.page_stride,
+                                 wl.block_table, os_, oe, wl.fmt, wl.section_offset)
+        assert_logits_close(got, ref, oe, range(wl.num_rows), name)
+    want = oracle.topk(np.nan_to_num(got, nan=0.0), oe, k)
+    assert_topk_sets(idx[:, :k].cpu().numpy(), want, range(wl.num_rows), what)
+
+
 def test_index_score_degenerate_sizes():
     # no pages or no blocks: only the row layout is written; more than 4 rows per request
     # (MXFP4) or 2 (FP8) are refused
