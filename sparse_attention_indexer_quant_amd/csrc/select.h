@@ -59,49 +59,62 @@ struct SelectShared {
     uint64_t prefix;
     int below;
     int count;
-    uint32_t n_out;
+    uint32_t n_out, n_tie;
+    uint64_t ties[64];  // the composites of the threshold digit (select_smallest)
 };
+
+// One digit of the radix select in LDS: among the composites whose bits above `shift + digit`
+// equal those of `prefix`, the value d of the next `digit` bits that holds the r-th smallest
+// of them (1 <= r <= their count). On return sh.prefix = prefix with d placed at `shift`,
+// sh.below = how many of them have a smaller digit, sh.count = how many have d. Every lane of
+// the workgroup must call it.
+template <typename Source, int NT>
+__device__ void radix_digit(const Source &src, uint64_t prefix, int digit, int shift, int r,
+                            SelectShared<NT> &sh) {
+    for (int b = threadIdx.x; b < kRadixBins; b += NT) sh.hist[b] = 0;
+    __syncthreads();
+    const uint64_t want = prefix >> (shift + digit);
+    src.for_each([&](uint64_t c) {
+        if ((c >> (shift + digit)) == want)
+            atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)((1 << digit) - 1)], 1u);
+    });
+    __syncthreads();
+    constexpr int per = kRadixBins / NT;  // ascending: lane t owns per*t ..
+    int own = 0;
+    uint32_t mine[per];
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+        mine[j] = sh.hist[threadIdx.x * per + j];
+        own += (int)mine[j];
+    }
+    const int incl = scan_block<NT>(own, sh.partials);
+    int before = incl - own;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+        const int c = (int)mine[j];
+        if (before < r && before + c >= r) {
+            sh.prefix = prefix | ((uint64_t)(threadIdx.x * per + j) << shift);
+            sh.below = before;
+            sh.count = c;
+        }
+        before += c;
+    }
+    __syncthreads();
+}
 
 // The r-th smallest of the distinct composites (of `bits` significant bits, 1 <= r <= their
 // count) that `src` yields, by a most-significant-digit radix select in LDS: exactly r
-// composites are <= the returned value. Every lane of the workgroup must call it.
+// composites are <= the returned value. A caller that has already fixed the top `done` bits
+// passes them in `prefix` with r counted among the composites that share them. Every lane of
+// the workgroup must call it.
 template <typename Source, int NT>
-__device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectShared<NT> &sh) {
-    uint64_t prefix = 0;
-    int done = 0;  // high composite bits fixed in `prefix`
-    uint64_t threshold = ~(uint64_t)0;
+__device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectShared<NT> &sh,
+                                     uint64_t prefix = 0, int done = 0) {
+    uint64_t threshold = prefix;
     while (done < bits) {
         const int digit = bits - done >= kRadixBits ? kRadixBits : bits - done;
         const int shift = bits - done - digit;
-        for (int b = threadIdx.x; b < kRadixBins; b += NT) sh.hist[b] = 0;
-        __syncthreads();
-        const uint64_t want = prefix >> (shift + digit);
-        src.for_each([&](uint64_t c) {
-            if ((c >> (shift + digit)) == want)
-                atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)((1 << digit) - 1)], 1u);
-        });
-        __syncthreads();
-        constexpr int per = kRadixBins / NT;  // ascending: lane t owns per*t ..
-        int own = 0;
-        uint32_t mine[per];
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            mine[j] = sh.hist[threadIdx.x * per + j];
-            own += (int)mine[j];
-        }
-        const int incl = scan_block<NT>(own, sh.partials);
-        int before = incl - own;
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            const int c = (int)mine[j];
-            if (before < r && before + c >= r) {
-                sh.prefix = prefix | ((uint64_t)(threadIdx.x * per + j) << shift);
-                sh.below = before;
-                sh.count = c;
-            }
-            before += c;
-        }
-        __syncthreads();
+        radix_digit(src, prefix, digit, shift, r, sh);
         prefix = sh.prefix;
         done += digit;
         if (sh.below + sh.count == r) {  // the whole digit bin is taken: stop early
@@ -110,7 +123,6 @@ __device__ uint64_t select_threshold(const Source &src, int r, int bits, SelectS
         }
         r -= sh.below;
         threshold = prefix;
-        __syncthreads();
     }
     return threshold;
 }
@@ -189,19 +201,77 @@ __device__ __forceinline__ void wave_select_out(const uint64_t *c, int m, int r,
 }
 
 // Writes the low `pos_bits` bits (the position) of the r smallest composites to out[0..r),
-// in no particular order.
+// in no particular order. A first digit of the top 8 bits (256 counts, scanned by one
+// wavefront) finds the digit d holding the r-th smallest; one pass then takes every composite
+// of a smaller digit and gathers those of digit d, and, unless d is taken whole, one wavefront
+// selects among them bit by bit: four workgroup barriers. Only when more than 64 composites
+// share d (long runs of equal keys) do further digits follow (select_threshold), and then a
+// last pass takes every composite up to the threshold.
+constexpr int kFirstDigitBits = 8;
 template <typename Source, int NT>
 __device__ void select_smallest(const Source &src, int r, int bits, int pos_bits, int32_t *out,
                                 SelectShared<NT> &sh) {
-    const uint64_t threshold = select_threshold(src, r, bits, sh);
-    if (threadIdx.x == 0) sh.n_out = 0;
+    constexpr int kFirstBins = 1 << kFirstDigitBits;
+    static_assert(NT >= kFirstBins && kFirstBins == 4 * 64, "four counts per lane of wavefront 0");
+    const int digit = bits >= kFirstDigitBits ? kFirstDigitBits : bits;
+    const int shift = bits - digit;
+    if (threadIdx.x < kFirstBins) sh.hist[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        sh.n_out = 0;
+        sh.n_tie = 0;
+    }
     __syncthreads();
+    src.for_each([&](uint64_t c) { atomicAdd(&sh.hist[(uint32_t)(c >> shift)], 1u); });
+    __syncthreads();
+    if (threadIdx.x < 64) {  // lane l: digits 4 l .. 4 l + 3, ascending
+        uint32_t c4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c4[j] = sh.hist[4 * threadIdx.x + j];
+        const int own = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+        const int incl = wave_incl_scan(own);
+        int before = incl - own;
+        if (before < r && incl >= r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = (int)c4[j];
+                if (before < r && before + c >= r) {
+                    sh.prefix = (uint64_t)(4 * threadIdx.x + j) << shift;
+                    sh.below = before;
+                    sh.count = c;
+                }
+                before += c;
+            }
+        }
+    }
+    __syncthreads();
+    const uint64_t top = sh.prefix;
+    const uint64_t d = top >> shift;
+    const int below = sh.below, cnt = sh.count;
+    const bool whole = below + cnt == r;
     const uint64_t pos_mask = ((uint64_t)1 << pos_bits) - 1;
+    if (!whole && cnt > 64) {
+        const uint64_t threshold = select_threshold(src, r - below, bits, sh, top, digit);
+        src.for_each([&](uint64_t c) {  // (n_out is still zero)
+            const bool take = c <= threshold;  // the smaller digits too
+            const uint32_t slot = wave_slot(take, &sh.n_out);
+            if (take && slot < (uint32_t)r) out[slot] = (int32_t)(c & pos_mask);
+        });
+        return;
+    }
     src.for_each([&](uint64_t c) {
-        const bool take = c <= threshold;
+        const uint64_t cd = c >> shift;
+        const bool take = cd < d || (whole && cd == d);
         const uint32_t slot = wave_slot(take, &sh.n_out);
         if (take && slot < (uint32_t)r) out[slot] = (int32_t)(c & pos_mask);
+        if (!whole) {
+            const bool tie = cd == d;
+            const uint32_t ts = wave_slot(tie, &sh.n_tie);
+            if (tie && ts < 64u) sh.ties[ts] = c;
+        }
     });
+    if (whole) return;
+    __syncthreads();  // the composites of digit d are in sh.ties
+    if (threadIdx.x < 64) wave_select_out(sh.ties, cnt, r - below, shift, pos_bits, out + below);
 }
 
 template <int NT = kSelectThreads>
