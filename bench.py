@@ -111,15 +111,28 @@ class TimingEvent:
 
 
 class Prepared:
-    """A C-ABI call with its argument tuple marshalled once (plain integers and pointers)."""
+    """A C-ABI call with its arguments converted to their C types once: each call then passes
+    the ready ctypes values to an unchecked handle of the same entry point (converting 30-odd
+    Python integers per call cost the host 1-1.5 us per launch, which the small workloads'
+    steps, bound by the host's launch rate, paid in full)."""
 
     def __init__(self, fn, *args):
-        self.fn, self.args = fn, args
+        self.fn = fn
+        assert len(args) == len(fn.argtypes), fn.__name__
+        self.args = tuple(a if a is None or isinstance(a, ctypes._SimpleCData) else t(a)
+                          for t, a in zip(fn.argtypes, args))
+        self.raw = getattr(ctypes.CDLL(fn_library_path()), fn.__name__)
+        self.raw.restype = fn.restype
 
     def __call__(self):
-        st = self.fn(*self.args)
+        st = self.raw(*self.args)
         if st != 0:
             raise RuntimeError(f"{self.fn.__name__} returned status {st}")
+
+
+def fn_library_path():
+    import sparse_attention_indexer_quant_amd as dsa
+    return dsa.LIBRARY
 
 
 def packed_rows(wl):
