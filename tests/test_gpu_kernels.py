@@ -653,6 +653,12 @@ ADVERSARIAL_CASES = {
                            query_lens=[1, 1, 1, 1], page_stride=8192, section_offset=3840),
     "fp4_verify_ragged": dict(fmt="mxfp4", heads=32, seq_lens=[30000, 9000, 4200, 20000, 12000, 65, 9100],
                               query_lens=[4, 1, 3, 2, 4, 1, 2], num_rows=20),
+    # more (row, segment) items than the chip holds workgroups at once: 300 requests of 1-20000
+    # keys, some without rows, rows of at most k keys, 40 padding rows
+    "fp4_many_uneven": dict(fmt="mxfp4", heads=32,
+                            seq_lens=np.random.default_rng(43).integers(1, 20001, size=300),
+                            query_lens=(np.random.default_rng(44).random(300) < 0.93).astype(np.int32),
+                            num_rows=int((np.random.default_rng(44).random(300) < 0.93).sum()) + 40),
 }
 
 
