@@ -98,6 +98,8 @@ hipError_t launch_index_score_topk(const ScoreArgs &args, const FusedInputs &fin
 // request, and the keys one workgroup covers (the top-k segment when the scorer writes the
 // selection's histograms). Depends on the current device's compute-unit count.
 constexpr int kScoreWaves = 4;  // wavefronts per scoring workgroup
+// Compute units of the current device (queried once per device).
+int device_cus();
 struct ScoreGeometry {
     int pages_per_wave;
     int64_t chunks;

@@ -1221,7 +1221,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     }
 }
 
-static int device_cus() {
+int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

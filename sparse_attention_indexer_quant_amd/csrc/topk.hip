@@ -474,17 +474,25 @@ __device__ __forceinline__ void write_above(uint32_t mask, int64_t first, uint32
 // row's width: keys past `hi` are masked here). Positions of keys above bin `bin` go to the output
 // and (key, position) pairs inside it to the candidate list, after the segment's offsets `off`
 // and the earlier chunks' keys (lane counts and a workgroup prefix sum place every key).
-template <int VEC>
+template <int VEC, bool NEXT = false>
 __device__ __forceinline__ void collect_segment(float (&raw)[kCollectPer], const float *x,
                                                 int64_t lo, int64_t hi, int64_t width, uint32_t bin,
                                                 uint32_t above, uint2 off, int32_t *out,
-                                                uint2 *cand, int *partials) {
+                                                uint2 *cand, int *partials,
+                                                const float *next = nullptr) {
     constexpr int kChunk = kCollectPer * kTopkThreads;
     const BinBounds bb(bin);
     uint32_t base_above = off.x, base_in = off.y;
     for (int64_t cbase = lo; cbase < hi; cbase += kChunk) {
         const int64_t first = cbase + (int64_t)threadIdx.x * kCollectPer;
-        if (cbase != lo) load_keys16<VEC>(raw, x, first, hi, width);
+        if (cbase != lo) {
+            if (NEXT && cbase == lo + kChunk) {  // NEXT: the second chunk, loaded by the caller
+#pragma unroll
+                for (int j = 0; j < kCollectPer; ++j) raw[j] = next[j];
+            } else {
+                load_keys16<VEC>(raw, x, first, hi, width);
+            }
+        }
         const Masks16 m = classify16(raw, hi - first, bb);
         loads_done();
         const int mine = __builtin_popcount(m.above) | (__builtin_popcount(m.in) << 16);
@@ -541,15 +549,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(
 }
 
 // Steps 2 and 3 in one kernel, for rows of at most kFusedSegments segments (segments x rows
-// workgroups): every workgroup of a row finds the row's threshold bin and its own segment's
-// offsets from the row's histograms as topk_threshold does (its two levels, the same sums),
-// reading 2 x 128 B per segment of the row, then collects its segment. The row's first
-// segment also stores the threshold state for step 4, or, for a row of at most k keys, the
-// whole output.
+// workgroups, or, with CH = 2, pairs of segments x rows): every workgroup of a row finds the
+// row's threshold bin and its own segment's offsets from the row's histograms as
+// topk_threshold does (its two levels, the same sums), reading 2 x 128 B per segment of the
+// row, then collects its segment (pair). The row's first segment also stores the threshold
+// state for step 4, or, for a row of at most k keys, the whole output. Pairs halve the
+// workgroups that large batches of uneven rows dispatch, most of them past the rows' keys (a
+// row past its keys costs one round trip per workgroup), and the threshold work per key.
 constexpr int kFusedSegments = 64;
 static_assert(kFusedSegments == 64 && kTopkThreads == 256, "lane t covers word t % 8 of two segments");
 
-template <int VEC>
+template <int VEC, int CH>
 __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     const float *__restrict__ logits, int64_t logits_row_stride, int64_t width,
     const int32_t *__restrict__ row_ends, const uint16_t *__restrict__ coarse_hist, int rows,
@@ -562,8 +572,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     __shared__ uint32_t found_c, found_f, count_c, count_f;
     __shared__ int above_c, above_f;
     __shared__ uint2 my_off;
+    static_assert(CH == 1 || CH == 2, "one or two segments per workgroup");
     const RowSeg rs = row_segment(rows);
-    const int64_t row = rs.row, seg = rs.seg;
+    const int64_t row = rs.row, seg = rs.seg * CH;  // the workgroup's first segment
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int p8 = t & 7, s0 = t >> 3;  // word p8 of segments s0 and s0 + 32
     const float *x = logits + row * logits_row_stride;
@@ -599,9 +610,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         return;
     }
     if (lo >= n) return;
-    const int64_t hi = lo + seg_len < n ? lo + seg_len : n;
-    float raw[kCollectPer];
+    const int64_t hi = lo + (int64_t)CH * seg_len < n ? lo + (int64_t)CH * seg_len : n;
+    float raw[kCollectPer], raw2[CH == 2 ? kCollectPer : 1];
     load_keys16<VEC>(raw, x, lo + (int64_t)t * kCollectPer, hi, width);
+    if constexpr (CH == 2)  // the second chunk of keys too, in the same round trip
+        load_keys16<VEC>(raw2, x, lo + (int64_t)(kTopkThreads + t) * kCollectPer, hi, width);
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
     const uint4 cw0 = s0 < row_segments ? cl0 : zero4;
     const uint4 cw1 = s0 + 32 < row_segments ? cl1 : zero4;
@@ -692,9 +705,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         }
     }
     __syncthreads();
-    collect_segment<VEC>(raw, x, lo, hi, width, bin, (uint32_t)above, my_off,
-                         indices + row * indices_row_stride, cand_all + row * kCandCap,
-                         partials);
+    collect_segment<VEC, CH == 2>(raw, x, lo, hi, width, bin, (uint32_t)above, my_off,
+                                  indices + row * indices_row_stride, cand_all + row * kCandCap,
+                                  partials, raw2);
 }
 
 
@@ -916,6 +929,32 @@ size_t topk_workspace_bytes(int64_t rows, int64_t width, int) {
     return topk_layout_bytes(rows, topk_nseg(width, topk_segment(rows, width)));
 }
 
+// topk_threshold_collect_kernel with CH segments per workgroup, with the widest key loads the
+// rows allow.
+template <int CH>
+static void launch_threshold_collect(bool runs, bool vec, hipStream_t stream, const float *logits,
+                                     int64_t logits_row_stride, int64_t width,
+                                     const int32_t *row_ends, const TopkWorkspace &ws, int64_t rows,
+                                     int64_t nseg, int64_t seg_len, int k, int32_t *indices,
+                                     int64_t indices_row_stride) {
+    const dim3 grid((unsigned)(rows * ((nseg + CH - 1) / CH))), block(kTopkThreads);
+    if (runs)
+        hipLaunchKernelGGL((topk_threshold_collect_kernel<16, CH>), grid, block, 0, stream, logits,
+                           logits_row_stride, width, row_ends, ws.coarse, (int)rows, (int)nseg,
+                           (int)seg_len, k, ws.seghist, indices, indices_row_stride, ws.state,
+                           ws.cand);
+    else if (vec)
+        hipLaunchKernelGGL((topk_threshold_collect_kernel<4, CH>), grid, block, 0, stream, logits,
+                           logits_row_stride, width, row_ends, ws.coarse, (int)rows, (int)nseg,
+                           (int)seg_len, k, ws.seghist, indices, indices_row_stride, ws.state,
+                           ws.cand);
+    else
+        hipLaunchKernelGGL((topk_threshold_collect_kernel<1, CH>), grid, block, 0, stream, logits,
+                           logits_row_stride, width, row_ends, ws.coarse, (int)rows, (int)nseg,
+                           (int)seg_len, k, ws.seghist, indices, indices_row_stride, ws.state,
+                           ws.cand);
+}
+
 // Steps 2-4 of the selection, on segment histograms already in the workspace.
 hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64_t width,
                                         int64_t logits_row_stride, const int32_t *row_ends, int k,
@@ -943,21 +982,17 @@ hipError_t launch_topk_after_histograms(const float *logits, int64_t rows, int64
         return hipGetLastError();
     }
     if (nseg <= kFusedSegments) {
-        if (runs)
-            hipLaunchKernelGGL(topk_threshold_collect_kernel<16>, grid, block, 0, stream, logits,
-                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride, ws.state, ws.cand);
-        else if (vec)
-            hipLaunchKernelGGL(topk_threshold_collect_kernel<4>, grid, block, 0, stream, logits,
-                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride, ws.state, ws.cand);
+        // launches of many more (row, segment) items than about four workgroups per compute
+        // unit, of segments of at most one chunk: two segments per workgroup, their keys
+        // loaded together (two segments of several chunks each measured slower)
+        if (rows * nseg > (int64_t)device_cus() * 4 && seg_len <= kCollectPer * kTopkThreads)
+            launch_threshold_collect<2>(runs, vec, stream, logits, logits_row_stride, width,
+                                        row_ends, ws, rows, nseg, seg_len, k, indices,
+                                        indices_row_stride);
         else
-            hipLaunchKernelGGL(topk_threshold_collect_kernel<1>, grid, block, 0, stream, logits,
-                               logits_row_stride, width, row_ends, ws.coarse, (int)rows,
-                               (int)nseg, (int)seg_len, k, ws.seghist, indices,
-                               indices_row_stride, ws.state, ws.cand);
+            launch_threshold_collect<1>(runs, vec, stream, logits, logits_row_stride, width,
+                                        row_ends, ws, rows, nseg, seg_len, k, indices,
+                                        indices_row_stride);
         hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads), 0,
                            stream, ws.cand, ws.state, row_ends, width, k, indices,
                            indices_row_stride, logits, logits_row_stride);
