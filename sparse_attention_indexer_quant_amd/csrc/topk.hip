@@ -567,11 +567,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     int32_t *__restrict__ indices, int64_t indices_row_stride, RowState *__restrict__ state,
     uint2 *__restrict__ cand_all) {
     __shared__ int partials[kTopkThreads / 64];
-    __shared__ uint32_t part[kTopkThreads / 64][64];
+    __shared__ uint32_t part[kTopkThreads / 64][64], part_f[kTopkThreads / 64][64];
     __shared__ uint32_t seg_above[kFusedSegments], seg_in[kFusedSegments];
-    __shared__ uint32_t found_c, found_f, count_c, count_f;
-    __shared__ int above_c, above_f;
-    __shared__ uint2 my_off;
     static_assert(CH == 1 || CH == 2, "one or two segments per workgroup");
     const RowSeg rs = row_segment(rows);
     const int64_t row = rs.row, seg = rs.seg * CH;  // the workgroup's first segment
@@ -618,17 +615,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     const int row_segments = (int)((n + seg_len - 1) / seg_len);
     const uint4 cw0 = s0 < row_segments ? cl0 : zero4;
     const uint4 cw1 = s0 + 32 < row_segments ? cl1 : zero4;
-    if (t == 0) {
-        found_c = 0;  // kept only if the counts do not reach k (they always do)
-        above_c = 0;
-        count_c = 0;
-        found_f = 0;
-        above_f = 0;
-        count_f = 0;
-    }
 
     // (a) coarse totals: bins [8 p8, 8 p8 + 8) over this lane's segments, then over the lanes
-    // sharing p8 (in the wavefront by lane swaps, across wavefronts in LDS)
+    // sharing p8 (in the wavefront by lane swaps, across wavefronts in LDS); after one barrier
+    // every wavefront reads the four partial rows and finds the bin itself (lane l: coarse bin
+    // 63 - l, descending), so no wavefront waits on another's result
     uint32_t csum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) csum[e] = sum_over_segments_in_wave(count8(cw0, e) + count8(cw1, e));
@@ -637,14 +628,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = csum[e];
     }
     __syncthreads();
-    if (wave == 0) {  // lane l holds coarse bin 63 - l (descending)
-        uint32_t c = 0;
+    uint32_t cc = 0;
 #pragma unroll
-        for (int w = 0; w < kTopkThreads / 64; ++w) c += part[w][63 - lane];
-        find_in_64(c, k, &found_c, &above_c, &count_c);
-    }
-    __syncthreads();
-    const uint32_t B = 63u - found_c;  // coarse bin, in ascending order
+    for (int w = 0; w < kTopkThreads / 64; ++w) cc += part[w][63 - lane];
+    const Found64 fc = find_in_64_wave(cc, k);
+    const uint32_t B = 63u - (uint32_t)fc.lane;  // coarse bin, in ascending order
 
     // (b) fine bins inside B: word p8 of segment sg covers fine bins 64 B + 8 p8 .. + 8
     const uint4 *fine = reinterpret_cast<const uint4 *>(fine_hist + row * nseg * kBins);
@@ -653,25 +641,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
     uint32_t fsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) fsum[e] = sum_over_segments_in_wave(count8(fw0, e) + count8(fw1, e));
-    __syncthreads();  // part[] is rewritten below
-    if (lane < 8) {
+    if (lane < 8) {  // (a row of its own: the coarse rows may still be read)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[wave][8 * lane + e] = fsum[e];
+        for (int e = 0; e < 8; ++e) part_f[wave][8 * lane + e] = fsum[e];
     }
     __syncthreads();
-    if (wave == 0) {
-        uint32_t c = 0;
+    uint32_t fc2 = 0;
 #pragma unroll
-        for (int w = 0; w < kTopkThreads / 64; ++w) c += part[w][63 - lane];
-        find_in_64(c, k - above_c, &found_f, &above_f, &count_f);
-    }
-    __syncthreads();
-    const uint32_t f = 63u - found_f;  // fine bin inside B, ascending
-    const uint32_t bin = B * 64 + f;   // threshold bin of the 4096
-    const int above = above_c + above_f;
+    for (int w = 0; w < kTopkThreads / 64; ++w) fc2 += part_f[w][63 - lane];
+    const Found64 ff = find_in_64_wave(fc2, k - fc.before);
+    const uint32_t f = 63u - (uint32_t)ff.lane;  // fine bin inside B, ascending
+    const uint32_t bin = B * 64 + f;             // threshold bin of the 4096
+    const int above = fc.before + ff.before;
 
-    // (c) per segment: coarse bins above B, fine bins in B above f, and fine bin f; wavefront 0
-    // then takes the exclusive prefix sums over the segments for this workgroup's segment
+    // (c) per segment: coarse bins above B, fine bins in B above f, and fine bin f; after one
+    // barrier every wavefront takes the exclusive prefix sums over the segments for this
+    // workgroup's segment itself
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint4 &cw = h ? cw1 : cw0;
@@ -692,19 +677,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        const int a = (int)seg_above[lane], c = (int)seg_in[lane];
-        const int ia = wave_incl_scan(a), ic = wave_incl_scan(c);
-        if (lane == (int)seg) my_off = make_uint2((uint32_t)(ia - a), (uint32_t)(ic - c));
-        if (seg == 0 && lane == 0) {
-            RowState &st = state[row];
-            st.bin = bin;
-            st.above = above;
-            st.remaining = k - above;
-            st.n_cand = count_f;
-        }
+    const int sa_ = (int)seg_above[lane], sc_ = (int)seg_in[lane];
+    const int ia = wave_incl_scan(sa_), ic = wave_incl_scan(sc_);
+    const uint2 my_off = make_uint2((uint32_t)__builtin_amdgcn_readlane(ia - sa_, (int)seg),
+                                    (uint32_t)__builtin_amdgcn_readlane(ic - sc_, (int)seg));
+    if (seg == 0 && t == 0) {
+        RowState &st = state[row];
+        st.bin = bin;
+        st.above = above;
+        st.remaining = k - above;
+        st.n_cand = ff.count;
     }
-    __syncthreads();
     collect_segment<VEC, CH == 2>(raw, x, lo, hi, width, bin, (uint32_t)above, my_off,
                                   indices + row * indices_row_stride, cand_all + row * kCandCap,
                                   partials, raw2);
