@@ -694,6 +694,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_threshold_collect_kernel(
 }
 
 
+// Composites held in registers, S per lane: lane t's i-th is candidate t + i * kSelectThreads
+// of m.
+template <int S>
+struct RegCandidates {
+    uint64_t c[S];
+    int m;
+    template <typename F>
+    __device__ __forceinline__ void for_each(F &&f) const {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if ((int)threadIdx.x + i * kSelectThreads < m) f(c[i]);
+    }
+};
+
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     const uint2 *__restrict__ cand_all, const RowState *__restrict__ state,
     const int32_t *__restrict__ row_ends, int64_t width, int k, int32_t *__restrict__ indices,
@@ -736,7 +750,13 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(
     int pos_bits = 1;
     while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
     const int bits = 20 + pos_bits;
-    if (ncand <= (uint32_t)kCandCap) {
+    if (ncand <= (uint32_t)(kSpec * kSelectThreads)) {  // all of them already in registers
+        RegCandidates<kSpec> rc;
+#pragma unroll
+        for (int i = 0; i < kSpec; ++i) rc.c[i] = composite(pre[i].x, pre[i].y, pos_bits);
+        rc.m = (int)ncand;
+        select_smallest(rc, remaining, bits, pos_bits, out, sh);
+    } else if (ncand <= (uint32_t)kCandCap) {
 #pragma unroll
         for (int i = 0; i < kSpec; ++i) {
             const int j = threadIdx.x + i * kSelectThreads;
