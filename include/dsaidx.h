@@ -418,7 +418,9 @@ dsaidx_status dsaidx_index_score_topk(
  *  num_requests, max_blocks, workspace  exactly as passed to the dsaidx_score_paged_hist call
  *           that wrote the logits and histograms (same stream, ordered after it; the same
  *           device). A row whose keys that call did not score (a row beyond max_query_len
- *           of its request) gets unspecified positions, as its logits are unwritten.
+ *           of its request, or keys on block-table entries outside the cache) gets
+ *           unspecified positions, as its logits are unwritten; even then nothing is written
+ *           at or past column k of any row.
  *  Errors: k < 1 or negative sizes give DSAIDX_EINVAL, as do num_requests or max_blocks of
  *  0 with rows to select; a short workspace gives DSAIDX_EINVAL.
  */

@@ -922,10 +922,14 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                 const int64_t total = lr0 + lqlen;
                 for (int64_t row = (total > 0 ? total : 0) + lane; row < num_rows; row += 64)
                     fin.row_ends[row] = 0;
-                if constexpr (SELECT) {  // ... which select nothing
-                    for (int64_t row = total > 0 ? total : 0; row < num_rows; ++row)
-                        for (int i = lane; i < select_k; i += 64) select_out[row * select_stride + i] = -1;
-                }
+            }
+        }
+        if constexpr (SELECT) {  // ... which select nothing (the whole workgroup writes them)
+            if (lq == (int64_t)R - 1) {
+                const int64_t total = lr0 + lqlen;
+                for (int64_t row = total > 0 ? total : 0; row < num_rows; ++row)
+                    for (int i = threadIdx.x; i < select_k; i += 64 * kWaves)
+                        select_out[row * select_stride + i] = -1;
             }
         }
     }

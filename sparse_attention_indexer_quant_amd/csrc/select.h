@@ -219,6 +219,12 @@ __device__ void select_smallest(const Source &src, int r, int bits, int pos_bits
     if (threadIdx.x == 0) {
         sh.n_out = 0;
         sh.n_tie = 0;
+        // kept if fewer than r composites come (inputs that break their contract: a row's
+        // counts short of its bound): a digit past every composite, so that all are taken and
+        // nothing is written at or past out[r]
+        sh.prefix = (uint64_t)kFirstBins << shift;
+        sh.below = 0;
+        sh.count = 0;
     }
     __syncthreads();
     src.for_each([&](uint64_t c) { atomicAdd(&sh.hist[(uint32_t)(c >> shift)], 1u); });

@@ -899,7 +899,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_row_kernel(
         uint32_t pc = (uint32_t)excl >> 16;
         if (r == m) {  // every key inside the bin is taken
             for (uint32_t in = mk.in; in; in &= in - 1u, ++pc)
-                out[above + pc] = (int32_t)(first + __builtin_ctz(in));
+                if (above + (int)pc < k) out[above + pc] = (int32_t)(first + __builtin_ctz(in));
         } else {
             for (uint32_t in = mk.in; in; in &= in - 1u, ++pc) {
                 const uint32_t j = __builtin_ctz(in);

@@ -815,6 +815,47 @@ def test_index_score_topk_one_launch(name, variant, k):
     assert_topk_sets(idx[:, :k].cpu().numpy(), want, range(wl.num_rows), what)
 
 
+@pytest.mark.parametrize("shape", ["one_launch", "row", "segmented"])
+def test_selection_stays_in_bounds_when_pages_are_missing(shape):
+    # Block-table entries outside [0, num_pages) inside rows' bounds break the caller contract:
+    # the scorer skips those pages (their keys are neither scored nor counted), so a row's
+    # counts fall short of its bound. Whatever the selection then returns, it writes nothing
+    # at or past k in any row: the columns after k keep their sentinel, and every written
+    # position is -1 or below the row's bound.
+    cases = {"one_launch": dict(seq_lens=[256, 200, 130], k=64),      # one chunk per request
+             "row": dict(seq_lens=[3000, 2500, 1500], k=700),         # rows of <= 8192 keys
+             "segmented": dict(seq_lens=[30000, 20000, 9000], k=1500)}  # segments of 4096
+    c = cases[shape]
+    wl = make_workload("missing", fmt="mxfp4", heads=32, seq_lens=c["seq_lens"],
+                       query_lens=[1] * len(c["seq_lens"]), topk=c["k"], seed=51)
+    k = c["k"]
+    bt = wl.block_table.copy()
+    for q, n in enumerate(wl.seq_lens):
+        nb = (int(n) + 63) // 64
+        bt[q, nb // 2] = wl.num_pages + 7   # one page of each row is no page of the cache
+        bt[q, 0] = -3
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    rng = np.random.default_rng(3)
+    proj, _ = _step_projection(wl, 0, 128, 128 + wl.heads, rng)
+    idx = torch.full((wl.num_rows, k + 64), 0x3FFFFFFF, dtype=torch.int32, device="cuda")
+    lg = torch.full((wl.num_rows, wl.width), float("nan"), device="cuda")
+    if shape == "one_launch":
+        assert dsa.score_segment_keys(wl.num_requests, wl.max_blocks) >= wl.width
+    _, ends, _, _ = dsa.index_score_topk(
+        bf16_dev(proj), 0, 128, dw.q, dw.gamma, dw.beta, wl.eps, dw.seq_lens, dw.query_lens,
+        wl.num_rows, dw.cache, wl.num_pages, wl.page_stride, dev(bt), wl.max_query_len, k,
+        wl.fmt, out=lg, indices=idx[:, :k])
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert np.all(got[:, k:] == 0x3FFFFFFF), f"{shape}: written past k"
+    e = ends.cpu().numpy()
+    for r in range(wl.num_rows):
+        row = got[r, :k]
+        assert np.all((row == -1) | (row == 0x3FFFFFFF) | ((row >= 0) & (row < e[r]))), \
+            f"{shape} row {r}: positions outside the row"
+
+
 def test_index_score_degenerate_sizes():
     # no pages or no blocks: only the row layout is written; more than 4 rows per request
     # (MXFP4) or 2 (FP8) are refused
