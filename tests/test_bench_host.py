@@ -55,3 +55,25 @@ def test_histogram_bytes_count_the_coarse_bins_reached():
     assert bench.histogram_bytes(lg, np.array([0]), 2, 8) == 0
     # bound clamped to the width; 7.0 shares coarse bin 48 with 2.0
     assert bench.histogram_bytes(lg, np.array([99]), 8, 8) == 128 + 4 * 128
+
+
+def test_prepared_call_converts_arguments_once():
+    # the bench's pre-marshalled calls: arguments converted to their C types when prepared,
+    # a nonzero status raised (here the step call's own check of k, before any launch)
+    import ctypes
+    import pytest
+    import sparse_attention_indexer_quant_amd as dsa
+    if not os.path.exists(dsa.LIBRARY):
+        pytest.skip("libdsaidx.so not built")
+    lib = dsa.library()
+    P = 0x10000
+    args = [0, P, 256, 0, 128, P, 32, 4096, 128, P, P, ctypes.c_float(1e-6), P, P, 1, 1, 1, P, 8,
+            4352, P, 4, P, P, P, 256, 0, P, 64, P, 1 << 20, None]
+    call = bench.Prepared(lib.dsaidx_index_score_topk, *args)
+    assert all(a is None or isinstance(a, ctypes._SimpleCData) for a in call.args)
+    assert isinstance(call.args[11], ctypes.c_float) and call.args[11].value == np.float32(1e-6)
+    assert call.args[26].value == 0  # k, as c_int32
+    with pytest.raises(RuntimeError, match="status 1"):
+        call()
+    with pytest.raises(AssertionError):
+        bench.Prepared(lib.dsaidx_index_score_topk, *args[:-1])
