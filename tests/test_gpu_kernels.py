@@ -815,6 +815,28 @@ def test_index_score_topk_one_launch(name, variant, k):
     assert_topk_sets(idx[:, :k].cpu().numpy(), want, range(wl.num_rows), what)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_index_score_topk_one_launch_only_padding_rows(fmt):
+    # no request has a row: every row is graph padding, selects nothing (-1) and ends at 0,
+    # and the cache is untouched
+    wl = make_workload("pad_only", fmt=fmt, heads=32, seq_lens=[100, 50, 7], query_lens=[0, 0, 0],
+                       num_rows=3, topk=16, seed=53)
+    dw = DeviceWorkload(wl)
+    dw.fill_cache()
+    before = dw.cache.clone()
+    proj = np.zeros((3, 128 + 32), np.uint16)
+    q = bf16_dev(bf16_bits(np.random.default_rng(1).standard_normal((3, 32, 128)).astype(np.float32)))
+    assert dsa.score_segment_keys(wl.num_requests, wl.max_blocks) >= wl.width
+    idx = torch.full((3, 20), 0x3FFFFFFF, dtype=torch.int32, device="cuda")
+    starts, ends, _, _ = dsa.index_score_topk(
+        bf16_dev(proj), 0, 128, q, dw.gamma, dw.beta, wl.eps, dw.seq_lens, dw.query_lens, 3,
+        dw.cache, wl.num_pages, wl.page_stride, dw.block_table, 1, 16, fmt, indices=idx[:, :16])
+    assert torch.equal(dw.cache, before)
+    assert starts.cpu().tolist() == [0, 0, 0, 0] and ends.cpu().tolist() == [0, 0, 0]
+    got = idx.cpu().numpy()
+    assert np.all(got[:, :16] == -1) and np.all(got[:, 16:] == 0x3FFFFFFF)
+
+
 @pytest.mark.parametrize("shape", ["one_launch", "row", "segmented"])
 def test_selection_stays_in_bounds_when_pages_are_missing(shape):
     # Block-table entries outside [0, num_pages) inside rows' bounds break the caller contract:
