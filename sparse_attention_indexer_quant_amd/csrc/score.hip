@@ -736,7 +736,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
     struct SelectState {
         uint32_t bin;
         int above, m;
-        uint32_t n_above, n_cand;
+        uint32_t n_taken;  // keys placed so far: above the bin (low 16 bits), inside it (high)
     };
     __shared__ std::conditional_t<SELECT, SelectShared<64 * kWaves>, int> sel_sh;
     __shared__ uint32_t sel_coarse[SELECT ? kCoarseBins : 1];
@@ -1098,8 +1098,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
                     sel_st.bin = B * 64u + 63u - (uint32_t)ff.lane;
                     sel_st.above = fc.before + ff.before;
                     sel_st.m = (int)ff.count;
-                    sel_st.n_above = 0;
-                    sel_st.n_cand = 0;
+                    sel_st.n_taken = 0;
                 }
             }
             __syncthreads();
@@ -1109,18 +1108,27 @@ __global__ __launch_bounds__(64 * kWaves) void score_paged_kernel(
             while (pos_bits < 31 && ((int64_t)1 << pos_bits) < n) ++pos_bits;
             uint64_t *cands = reinterpret_cast<uint64_t *>(hist);  // the histogram is read
             constexpr int kCap = (int)(sizeof(hist) / (sizeof(uint64_t)));
-#pragma unroll
-            for (int p = 0; p < kMaxPagesPerWave; ++p) {
-                if (!(p < run && table_page(p) >= 0)) continue;  // uniform
+            for (int p = 0; p < run; ++p) {  // (no register array indexed by p: not unrolled)
+                if (table_page(p) < 0) continue;  // uniform
                 const int64_t kb = block_of(p) * kPageTokens;
                 const bool live = (int64_t)lane < n - kb;
                 const uint32_t u = order_key(sel_logits[kb + lane]);
                 const bool ab = live && (u >> kBinShift) > bin;
                 const bool in = live && (u >> kBinShift) == bin;
                 const uint32_t pos = (uint32_t)kb + (uint32_t)lane;
-                const uint32_t sa = wave_slot(ab, &sel_st.n_above);
+                // both slots from one atomic on the packed counts (each below 2^16: n <= 4096)
+                const uint64_t mab = __ballot(ab), min_ = __ballot(in);
+                uint32_t base = 0;
+                if (mab | min_) {
+                    if (lane == 0)
+                        base = atomicAdd(&sel_st.n_taken,
+                                         (uint32_t)__builtin_popcountll(mab) |
+                                             ((uint32_t)__builtin_popcountll(min_) << 16));
+                    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                }
+                const uint32_t sa = (base & 0xFFFFu) + lanes_below(mab);
+                const uint32_t sc = (base >> 16) + lanes_below(min_);
                 if (ab && sa < (uint32_t)above) out[sa] = (int32_t)pos;
-                const uint32_t sc = wave_slot(in, &sel_st.n_cand);
                 if (in) {
                     if (r == m) {  // every key inside the bin is taken
                         if (above + (int)sc < k) out[above + sc] = (int32_t)pos;

@@ -147,6 +147,12 @@ __device__ __forceinline__ Found64 find_in_64_wave(uint32_t c, int k) {
     return {L, __builtin_amdgcn_readlane(before, L), (uint32_t)__builtin_amdgcn_readlane((int)c, L)};
 }
 
+// Set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Slots for the lanes of a wavefront whose `take` is set (among the active lanes), from the
 // counter `n`: one atomic per wavefront, then each lane's rank among the taken lanes.
 __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t *n) {
